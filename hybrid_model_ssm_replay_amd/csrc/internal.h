@@ -1,0 +1,148 @@
+// Internal declarations shared by the host entry points and the kernel files.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace rssm {
+
+constexpr uint32_t kCtxMagic = 0x52535331u;  // "RSS1"
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Ring layout.  Every field is float32 and indexed by ring slot; the record at
+// token position t lives in slot t % L, except the Mamba-2 B field, which is
+// shared by the heads of a group and lives in slot t % (2 L): a tile that
+// appends a record may then never overwrite a B record that another tile of
+// the same group is still folding or reading in the same launch (the window
+// plus the drafts of one call span at most 2 L positions).
+struct RingLayout {
+  // Mamba-2: f0 = x [B][H][L][P], f1 = B [B][G][2L][N], f2 = dt [B][H][L].
+  // GDN:     f0 = k [B][H][L][dk], f1 = v [B][H][L][dv], f2 = alpha [B][H][L],
+  //          f3 = beta [B][H][L].
+  size_t off[4];
+  size_t bytes;
+};
+
+inline RingLayout ring_layout(const replay_config &c) {
+  RingLayout r{};
+  const size_t B = c.batch, H = c.heads, G = c.groups, L = c.window, P = c.head_dim, N = c.state_dim;
+  size_t sz[4];
+  if (c.kind == REPLAY_KIND_MAMBA2) {
+    sz[0] = B * H * L * P;
+    sz[1] = B * G * 2 * L * N;
+    sz[2] = B * H * L;
+    sz[3] = 0;
+  } else {
+    sz[0] = B * H * L * N;
+    sz[1] = B * H * L * P;
+    sz[2] = B * H * L;
+    sz[3] = B * H * L;
+  }
+  size_t o = 0;
+  for (int i = 0; i < 4; ++i) {
+    r.off[i] = o;
+    o += align256(sz[i] * sizeof(float));
+  }
+  r.bytes = o;
+  return r;
+}
+
+// Shape of one launch, as the kernels see it.
+struct Shape {
+  int B, H, G, P, N, L;
+};
+
+// Mamba-2 ---------------------------------------------------------------
+struct M2Ring {
+  float *x;   // [B][H][L][P]
+  float *Bm;  // [B][G][2L][N]
+  float *dt;  // [B][H][L]
+};
+
+struct M2StepArgs {
+  Shape s;
+  float *ckpt;
+  M2Ring ring;
+  PtrHalves ptr;
+  int32_t *status;
+  const float *A, *D;
+  const float *x, *Bm, *Cm, *dt;  // this token: [B][H][P], [B][G][N], [B][G][N], [B][H]
+  float *y;                        // [B][H][P]
+};
+
+struct M2VerifyArgs {
+  Shape s;
+  int T;
+  float *ckpt;
+  M2Ring ring;
+  PtrHalves ptr;
+  int32_t *status;
+  const float *A, *D;
+  const float *x, *Bm, *Cm, *dt;  // drafts: [B][T][H][P], [B][T][G][N], [B][T][G][N], [B][T][H]
+  float *y;                        // [B][T][H][P]
+};
+
+struct M2FlushArgs {
+  Shape s;
+  float *ckpt;
+  M2Ring ring;
+  PtrHalves ptr;
+  int32_t *status;
+  const float *A;
+  const uint8_t *mask;  // [B] or NULL
+};
+
+struct M2ConvArgs {
+  Shape s;
+  float *state;  // [B][H][P][N]
+  const float *A, *D;
+  const float *x, *Bm, *Cm, *dt;
+  float *y;
+};
+
+struct M2SnapArgs {
+  Shape s;
+  int T, nslots;
+  float *slots;  // [B][nslots][H][P][N]
+  const int32_t *cur;
+  const float *A, *D;
+  const float *x, *Bm, *Cm, *dt;  // drafts, as M2VerifyArgs
+  float *y;
+};
+
+// Launchers (return a hipError_t value).
+int launch_m2_step(const M2StepArgs &a, hipStream_t st);
+int launch_m2_verify(const M2VerifyArgs &a, hipStream_t st);
+int launch_m2_flush(const M2FlushArgs &a, hipStream_t st);
+int launch_m2_conv(const M2ConvArgs &a, hipStream_t st);
+int launch_m2_snapshot(const M2SnapArgs &a, hipStream_t st);
+
+// Pointer kernels -------------------------------------------------------
+int launch_init_pointers(int32_t *words, int nwords, int32_t *status, hipStream_t st);
+int launch_commit(PtrHalves p, int B, const int32_t *accepted, int T, int32_t *status, hipStream_t st);
+int launch_snapshot_commit(int32_t *cur, const int32_t *accepted, int B, int T, int nslots, hipStream_t st);
+int launch_probe(const void *src, void *dst, size_t bytes, int mode, hipStream_t st);
+
+// Launch geometry shared by the tile kernels: one workgroup per (sequence,
+// head); one wave per 16-row block of the head's state, at most 4 waves, with
+// RBW row blocks per wave.
+inline bool tile_geometry(int P, int *waves, int *rbw) {
+  if (P % 16 || P < 16) return false;
+  const int rb = P / 16;
+  if (rb <= 4) {
+    *waves = rb;
+    *rbw = 1;
+    return true;
+  }
+  if (rb == 8) {
+    *waves = 4;
+    *rbw = 2;
+    return true;
+  }
+  return false;
+}
+
+}  // namespace rssm

@@ -1,0 +1,290 @@
+// Host side of the C ABI declared in include/replayssm.h: argument checks,
+// buffer sizing, pointer-half bookkeeping and kernel launches.  Nothing here
+// allocates device memory or synchronises the host.
+#include <string.h>
+
+#include "internal.h"
+
+using namespace rssm;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_cfg(const replay_config *c) {
+  if (!c) return REPLAY_EINVAL;
+  if (c->kind != REPLAY_KIND_MAMBA2 && c->kind != REPLAY_KIND_GDN) return REPLAY_EINVAL;
+  if (c->batch < 1 || c->heads < 1 || c->groups < 1) return REPLAY_EINVAL;
+  if (c->heads % c->groups) return REPLAY_EINVAL;
+  if (c->kind == REPLAY_KIND_GDN && c->groups != c->heads) return REPLAY_EINVAL;
+  int waves, rbw;
+  if (!tile_geometry(c->head_dim, &waves, &rbw)) return REPLAY_EINVAL;
+  if (c->state_dim != 16 && c->state_dim != 32 && c->state_dim != 64 && c->state_dim != 128) return REPLAY_EINVAL;
+  if (c->window < 1 || c->window > REPLAY_MAX_WINDOW) return REPLAY_EINVAL;
+  if (c->max_draft < 0 || c->max_draft > c->window) return REPLAY_EINVAL;
+  if ((int64_t)c->batch * c->heads > 0x7fffffffLL) return REPLAY_EINVAL;
+  if (c->ckpt_fmt < REPLAY_FMT_F32 || c->ckpt_fmt > REPLAY_FMT_F4E2M1_B16) return REPLAY_EINVAL;
+  if (c->read_fmt < REPLAY_FMT_F32 || c->read_fmt > REPLAY_FMT_F4E2M1_B16) return REPLAY_EINVAL;
+  if (!(c->ckpt_fmt == REPLAY_FMT_F32 && c->read_fmt == REPLAY_FMT_F32)) return REPLAY_ENOTSUP;
+  return REPLAY_OK;
+}
+
+int check_ctx(const replay_ctx *ctx) {
+  if (!ctx || ctx->magic != kCtxMagic) return REPLAY_EINVAL;
+  return REPLAY_OK;
+}
+
+Shape shape_of(const replay_config &c) {
+  return Shape{c.batch, c.heads, c.groups, c.head_dim, c.state_dim, c.window};
+}
+
+PtrHalves halves(const replay_ctx &ctx) {
+  const int B = ctx.cfg.batch;
+  int32_t *cur = ctx.buf.pointers + (size_t)(ctx.parity & 1) * 2 * B;
+  int32_t *nxt = ctx.buf.pointers + (size_t)((ctx.parity & 1) ^ 1) * 2 * B;
+  return PtrHalves{cur, cur + B, nxt, nxt + B};
+}
+
+M2Ring m2_ring(const replay_ctx &ctx) {
+  const RingLayout lay = ring_layout(ctx.cfg);
+  char *base = (char *)ctx.buf.ring;
+  return M2Ring{(float *)(base + lay.off[0]), (float *)(base + lay.off[1]), (float *)(base + lay.off[2])};
+}
+
+int hip_status(int e) { return e == 0 ? REPLAY_OK : REPLAY_EHIP; }
+
+bool rec_ok(const replay_record *r, int kind) {
+  if (!r || !r->f0 || !r->f1 || !r->f2 || !r->f3) return false;
+  if (kind == REPLAY_KIND_GDN && !r->f4) return false;
+  return aligned16(r->f0) && aligned16(r->f1) && aligned16(r->f2);
+}
+
+}  // namespace
+
+extern "C" {
+
+int replay_validate_config(const replay_config *cfg) { return check_cfg(cfg); }
+
+size_t replay_ckpt_bytes(const replay_config *c) {
+  if (check_cfg(c) != REPLAY_OK) return 0;
+  return (size_t)c->batch * c->heads * c->head_dim * c->state_dim * sizeof(float);
+}
+
+size_t replay_read_copy_bytes(const replay_config *c) {
+  if (check_cfg(c) != REPLAY_OK) return 0;
+  return 0;  // single F32 copy
+}
+
+size_t replay_ring_bytes(const replay_config *c) {
+  if (check_cfg(c) != REPLAY_OK) return 0;
+  return ring_layout(*c).bytes;
+}
+
+size_t replay_pointer_words(const replay_config *c) {
+  if (check_cfg(c) != REPLAY_OK) return 0;
+  return (size_t)4 * c->batch;
+}
+
+const char *replay_strerror(int code) {
+  switch (code) {
+    case REPLAY_OK: return "ok";
+    case REPLAY_EINVAL: return "invalid argument";
+    case REPLAY_EHIP: return "HIP launch failed";
+    case REPLAY_ENOTSUP: return "unsupported configuration";
+    default: return "unknown error";
+  }
+}
+
+size_t replay_abi_sizeof(int which) {
+  switch (which) {
+    case 0: return sizeof(replay_config);
+    case 1: return sizeof(replay_buffers);
+    case 2: return sizeof(replay_record);
+    case 3: return sizeof(replay_ctx);
+    default: return 0;
+  }
+}
+
+int replay_init(replay_ctx *ctx, const replay_config *cfg, const replay_buffers *buf, void *stream) {
+  if (!ctx || !buf) return REPLAY_EINVAL;
+  const int rc = check_cfg(cfg);
+  if (rc != REPLAY_OK) return rc;
+  if (!buf->ckpt || !buf->ring || !buf->pointers || !buf->status) return REPLAY_EINVAL;
+  if (!aligned16(buf->ckpt) || !aligned16(buf->ring) || ((uintptr_t)buf->ring & 255u)) return REPLAY_EINVAL;
+  if (!aligned16(buf->pointers)) return REPLAY_EINVAL;
+  if (cfg->kind == REPLAY_KIND_MAMBA2 && (!buf->A || !buf->D)) return REPLAY_EINVAL;
+  memset(ctx, 0, sizeof(*ctx));
+  ctx->cfg = *cfg;
+  ctx->buf = *buf;
+  ctx->parity = 0;
+  ctx->t_pending = 0;
+  const int e = launch_init_pointers(buf->pointers, (int)replay_pointer_words(cfg), buf->status, (hipStream_t)stream);
+  if (e) return REPLAY_EHIP;
+  ctx->magic = kCtxMagic;
+  return REPLAY_OK;
+}
+
+int replay_current_pointers(const replay_ctx *ctx, const int32_t **pos, const int32_t **ckpt_pos) {
+  if (check_ctx(ctx) != REPLAY_OK || !pos || !ckpt_pos) return REPLAY_EINVAL;
+  const PtrHalves p = halves(*ctx);
+  *pos = p.pos_in;
+  *ckpt_pos = p.ckpt_in;
+  return REPLAY_OK;
+}
+
+int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *stream) {
+  if (check_ctx(ctx) != REPLAY_OK) return REPLAY_EINVAL;
+  const replay_config &c = ctx->cfg;
+  if (!rec_ok(rec, c.kind) || !y || !aligned16(y)) return REPLAY_EINVAL;
+  int e;
+  if (c.kind == REPLAY_KIND_MAMBA2) {
+    M2StepArgs a{};
+    a.s = shape_of(c);
+    a.ckpt = (float *)ctx->buf.ckpt;
+    a.ring = m2_ring(*ctx);
+    a.ptr = halves(*ctx);
+    a.status = ctx->buf.status;
+    a.A = ctx->buf.A;
+    a.D = ctx->buf.D;
+    a.x = rec->f0;
+    a.Bm = rec->f1;
+    a.Cm = rec->f2;
+    a.dt = rec->f3;
+    a.y = y;
+    e = launch_m2_step(a, (hipStream_t)stream);
+  } else {
+    return REPLAY_ENOTSUP;
+  }
+  if (e) return REPLAY_EHIP;
+  ctx->parity ^= 1;
+  ctx->t_pending = 0;
+  return REPLAY_OK;
+}
+
+int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream) {
+  if (check_ctx(ctx) != REPLAY_OK) return REPLAY_EINVAL;
+  const replay_config &c = ctx->cfg;
+  int e;
+  if (c.kind == REPLAY_KIND_MAMBA2) {
+    M2FlushArgs a{};
+    a.s = shape_of(c);
+    a.ckpt = (float *)ctx->buf.ckpt;
+    a.ring = m2_ring(*ctx);
+    a.ptr = halves(*ctx);
+    a.status = ctx->buf.status;
+    a.A = ctx->buf.A;
+    a.mask = seq_mask;
+    e = launch_m2_flush(a, (hipStream_t)stream);
+  } else {
+    return REPLAY_ENOTSUP;
+  }
+  if (e) return REPLAY_EHIP;
+  ctx->parity ^= 1;
+  return REPLAY_OK;
+}
+
+int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float *y, void *stream) {
+  if (check_ctx(ctx) != REPLAY_OK) return REPLAY_EINVAL;
+  const replay_config &c = ctx->cfg;
+  if (T < 1 || T > c.max_draft || T > c.window) return REPLAY_EINVAL;
+  if (!rec_ok(drafts, c.kind) || !y || !aligned16(y)) return REPLAY_EINVAL;
+  int e;
+  if (c.kind == REPLAY_KIND_MAMBA2) {
+    M2VerifyArgs a{};
+    a.s = shape_of(c);
+    a.T = T;
+    a.ckpt = (float *)ctx->buf.ckpt;
+    a.ring = m2_ring(*ctx);
+    a.ptr = halves(*ctx);
+    a.status = ctx->buf.status;
+    a.A = ctx->buf.A;
+    a.D = ctx->buf.D;
+    a.x = drafts->f0;
+    a.Bm = drafts->f1;
+    a.Cm = drafts->f2;
+    a.dt = drafts->f3;
+    a.y = y;
+    e = launch_m2_verify(a, (hipStream_t)stream);
+  } else {
+    return REPLAY_ENOTSUP;
+  }
+  if (e) return REPLAY_EHIP;
+  ctx->parity ^= 1;
+  ctx->t_pending = T;
+  return REPLAY_OK;
+}
+
+int replay_commit(replay_ctx *ctx, const int32_t *accepted, void *stream) {
+  if (check_ctx(ctx) != REPLAY_OK || !accepted) return REPLAY_EINVAL;
+  const int e = launch_commit(halves(*ctx), ctx->cfg.batch, accepted, ctx->t_pending, ctx->buf.status,
+                              (hipStream_t)stream);
+  if (e) return REPLAY_EHIP;
+  ctx->parity ^= 1;
+  ctx->t_pending = 0;
+  return REPLAY_OK;
+}
+
+int replay_conv_step(const replay_config *cfg, float *state, const float *A, const float *D,
+                     const replay_record *rec, float *y, void *stream) {
+  const int rc = check_cfg(cfg);
+  if (rc != REPLAY_OK) return rc;
+  if (!state || !aligned16(state) || !rec_ok(rec, cfg->kind) || !y || !aligned16(y)) return REPLAY_EINVAL;
+  if (cfg->kind == REPLAY_KIND_MAMBA2) {
+    if (!A || !D) return REPLAY_EINVAL;
+    M2ConvArgs a{};
+    a.s = shape_of(*cfg);
+    a.state = state;
+    a.A = A;
+    a.D = D;
+    a.x = rec->f0;
+    a.Bm = rec->f1;
+    a.Cm = rec->f2;
+    a.dt = rec->f3;
+    a.y = y;
+    return hip_status(launch_m2_conv(a, (hipStream_t)stream));
+  }
+  return REPLAY_ENOTSUP;
+}
+
+int replay_snapshot_verify(const replay_config *cfg, float *slots, const int32_t *cur, int32_t T,
+                           const float *A, const float *D, const replay_record *drafts, float *y,
+                           void *stream) {
+  const int rc = check_cfg(cfg);
+  if (rc != REPLAY_OK) return rc;
+  if (T < 1 || T > cfg->max_draft) return REPLAY_EINVAL;
+  if (!slots || !aligned16(slots) || !cur || !rec_ok(drafts, cfg->kind) || !y || !aligned16(y)) return REPLAY_EINVAL;
+  if (cfg->kind == REPLAY_KIND_MAMBA2) {
+    if (!A || !D) return REPLAY_EINVAL;
+    M2SnapArgs a{};
+    a.s = shape_of(*cfg);
+    a.T = T;
+    a.nslots = cfg->max_draft + 1;
+    a.slots = slots;
+    a.cur = cur;
+    a.A = A;
+    a.D = D;
+    a.x = drafts->f0;
+    a.Bm = drafts->f1;
+    a.Cm = drafts->f2;
+    a.dt = drafts->f3;
+    a.y = y;
+    return hip_status(launch_m2_snapshot(a, (hipStream_t)stream));
+  }
+  return REPLAY_ENOTSUP;
+}
+
+int replay_snapshot_commit(const replay_config *cfg, int32_t *cur, const int32_t *accepted, int32_t T,
+                           void *stream) {
+  const int rc = check_cfg(cfg);
+  if (rc != REPLAY_OK) return rc;
+  if (!cur || !accepted || T < 0 || T > cfg->max_draft) return REPLAY_EINVAL;
+  return hip_status(launch_snapshot_commit(cur, accepted, cfg->batch, T, cfg->max_draft + 1, (hipStream_t)stream));
+}
+
+int replay_hbm_probe(const void *src, void *dst, size_t bytes, int mode, void *stream) {
+  if (!src || !dst || (bytes & 15) || (mode != 0 && mode != 1)) return REPLAY_EINVAL;
+  if (!aligned16(src) || !aligned16(dst)) return REPLAY_EINVAL;
+  return hip_status(launch_probe(src, dst, bytes, mode, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,233 @@
+/*
+ * replayssm.h -- C ABI of the ReplaySSM decode library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes one state-space layer's decode step with the state held
+ * as a checkpoint plus a ring buffer of the last L <= 16 input records, instead
+ * of a state that is read and written back at every token.  Pages cited:
+ *   [P1] "Hybrid-model decoding has a new bottleneck: stop writing the SSM state
+ *        every step, and speculative throughput reaches 2.10x"
+ *   [P2] "NVIDIA and Dao AI Lab speed up hybrid-model decoding"
+ *   [P3] "SSM decoding stops writing state every step: caching recent inputs
+ *        halves state traffic and matches vLLM speculation"
+ * The layer recurrences are the published Mamba-2 (SSD) and Gated DeltaNet
+ * decode updates:
+ *   Mamba-2, per head h with B/C group g = h / (heads / groups):
+ *       S_h <- exp(dt_h A_h) S_h + dt_h x_h B_g^T,   y_h = S_h C_g + D_h x_h
+ *   Gated DeltaNet, per head:
+ *       S <- alpha S (I - beta k k^T) + beta v k^T,  o = S q
+ * In both, the output is read from the state after the token's update.
+ *
+ * Conventions for every call:
+ *   - All array arguments are DEVICE pointers unless stated otherwise; the
+ *     library never allocates, frees or copies to the host.  The caller owns
+ *     every buffer and keeps it alive until the work queued on the stream ends.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns; none synchronises the host.
+ *   - Return value: REPLAY_OK, or a negative code.  REPLAY_EINVAL (bad shape,
+ *     NULL pointer, misaligned pointer, unsupported pair of formats) is returned
+ *     before anything is enqueued; REPLAY_EHIP reports a failed kernel launch.
+ *   - Floating-point arrays are float32, C-contiguous, 16-byte aligned.
+ *   - Calls on one context must be issued on one stream (or be ordered by the
+ *     caller): they read pointer words written by the previous call.
+ *   - Anomalies found on the device (a clamped accept count, a corrupted
+ *     pointer pair) set sticky bits in `status`; the affected sequence is
+ *     clamped or skipped, never read out of bounds.
+ */
+#ifndef REPLAYSSM_H
+#define REPLAYSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define REPLAY_MAX_WINDOW 16
+
+/* Layer families. */
+#define REPLAY_KIND_MAMBA2 0
+#define REPLAY_KIND_GDN 1
+
+/* Storage formats of the checkpoint (recurrence copy) and of the read copy. */
+#define REPLAY_FMT_F32 0
+#define REPLAY_FMT_F16_SR 1     /* IEEE binary16, written with stochastic rounding */
+#define REPLAY_FMT_F8E4M3 2     /* OCP FP8 e4m3fn, round to nearest even, saturating */
+#define REPLAY_FMT_F4E2M1_B16 3 /* 4-bit e2m1 values, one e4m3 scale per 16 */
+
+/* Return codes. */
+#define REPLAY_OK 0
+#define REPLAY_EINVAL (-1)
+#define REPLAY_EHIP (-2)
+#define REPLAY_ENOTSUP (-3)
+
+/* Sticky bits of the device status word. */
+#define REPLAY_STATUS_ACCEPT_CLAMPED 0x1 /* commit got accepted < 0 or > drafts pending */
+#define REPLAY_STATUS_BAD_POINTERS 0x2   /* pos - ckpt_pos outside 0..L: sequence skipped */
+
+/*
+ * Layer shape and options.
+ *   kind        REPLAY_KIND_MAMBA2 or REPLAY_KIND_GDN.
+ *   batch       sequences, >= 1.
+ *   heads       heads per sequence, >= 1.
+ *   groups      Mamba-2: B/C groups, heads % groups == 0 (contiguous blocks of
+ *               heads / groups heads share a group).  GDN: must equal heads.
+ *   head_dim    Mamba-2: P.  GDN: d_v.  Multiple of 16, at most 128.
+ *   state_dim   Mamba-2: N.  GDN: d_k.  One of 16, 32, 64, 128.
+ *   window      L, the ring length, 1..16.  A window folds into the checkpoint
+ *               only once it is full [P2, paragraph 3; P3, Interpretation 2].
+ *   max_draft   largest T a verify call will use, 0..L (sizes the ring).
+ *   ckpt_fmt    format of the checkpoint that carries the recurrence.
+ *   read_fmt    format of the copy non-fold steps read; equal to ckpt_fmt
+ *               means a single copy [P1, Interpretation 4; P3, Interpretation 3].
+ *   seed        key of the stochastic-rounding generator.
+ * Supported format pairs in this version: (F32, F32).
+ */
+typedef struct replay_config {
+  int32_t kind;
+  int32_t batch;
+  int32_t heads;
+  int32_t groups;
+  int32_t head_dim;
+  int32_t state_dim;
+  int32_t window;
+  int32_t max_draft;
+  int32_t ckpt_fmt;
+  int32_t read_fmt;
+  uint64_t seed;
+} replay_config;
+
+/*
+ * Device buffers of one layer, all allocated by the caller.
+ *   ckpt       replay_ckpt_bytes(cfg) bytes.  F32 layout [batch][heads][head_dim][state_dim]
+ *              (state_dim contiguous).  Its contents at replay_init are the
+ *              initial state; afterwards it changes only at a fold.
+ *   read_copy  replay_read_copy_bytes(cfg) bytes, or NULL when that is 0.
+ *   ring       replay_ring_bytes(cfg) bytes; layout private to the library.
+ *   pointers   replay_pointer_words(cfg) int32 words: two halves, each
+ *              {pos[batch], ckpt_pos[batch]}; see replay_current_pointers().
+ *   status     one int32, sticky anomaly bits (cleared by replay_init).
+ *   A, D       Mamba-2 per-head decay rate A[heads] (negative) and skip weight
+ *              D[heads]; NULL for GDN.
+ */
+typedef struct replay_buffers {
+  void *ckpt;
+  void *read_copy;
+  void *ring;
+  int32_t *pointers;
+  int32_t *status;
+  const float *A;
+  const float *D;
+} replay_buffers;
+
+/*
+ * One record per sequence (step) or T records per sequence (verify), float32:
+ *   Mamba-2: f0 = x [batch][heads][P], f1 = B [batch][groups][N],
+ *            f2 = C [batch][groups][N], f3 = dt [batch][heads] (already
+ *            positive, i.e. after any softplus), f4 unused.
+ *   GDN:     f0 = q [batch][heads][d_k], f1 = k [batch][heads][d_k],
+ *            f2 = v [batch][heads][d_v], f3 = alpha [batch][heads] in (0, 1],
+ *            f4 = beta [batch][heads].
+ * For verify every field has a draft axis after batch: x [batch][T][heads][P] etc.
+ */
+typedef struct replay_record {
+  const float *f0;
+  const float *f1;
+  const float *f2;
+  const float *f3;
+  const float *f4;
+} replay_record;
+
+/* Caller-owned context (plain data, no destroy call).  Fields are managed by the
+ * library; callers read them only through the functions below. */
+typedef struct replay_ctx {
+  replay_config cfg;
+  replay_buffers buf;
+  int32_t parity;    /* which half of buf.pointers holds the current pointers */
+  int32_t t_pending; /* drafts staged by the last verify and not yet committed */
+  uint32_t magic;
+  int32_t reserved;
+} replay_ctx;
+
+/* ---- sizes and checks (host only, no device work) ---------------------- */
+
+/* REPLAY_OK if the configuration is supported, REPLAY_EINVAL / REPLAY_ENOTSUP otherwise. */
+int replay_validate_config(const replay_config *cfg);
+/* Bytes of each device buffer; 0 for an invalid configuration. */
+size_t replay_ckpt_bytes(const replay_config *cfg);
+size_t replay_read_copy_bytes(const replay_config *cfg);
+size_t replay_ring_bytes(const replay_config *cfg);
+size_t replay_pointer_words(const replay_config *cfg);
+/* Static text for a return code. */
+const char *replay_strerror(int code);
+/* sizeof of the ABI structs, for bindings: 0 replay_config, 1 replay_buffers,
+ * 2 replay_record, 3 replay_ctx. */
+size_t replay_abi_sizeof(int which);
+
+/* ---- the decode calls -------------------------------------------------- */
+
+/* Fill *ctx from cfg and buf, and enqueue: pos = ckpt_pos = 0 for every
+ * sequence, status = 0.  The checkpoint buffer already holds the initial state. */
+int replay_init(replay_ctx *ctx, const replay_config *cfg, const replay_buffers *buf, void *stream);
+
+/* One decode token for every sequence [P1, Interpretation 2; P3, Interpretation 2]:
+ * if a sequence's window is full (L records) it is first folded into the
+ * checkpoint; then the record is appended and y is computed from one read of
+ * the checkpoint plus the buffered records, with no state write-back.
+ * y: Mamba-2 [batch][heads][P], GDN [batch][heads][d_v].  Discards drafts still
+ * pending from a verify (the same as commit of 0). */
+int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *stream);
+
+/* Fold every committed record of the sequences with seq_mask[b] != 0 (device
+ * uint8 [batch]; NULL = all) into the checkpoint.  Sequences with an empty
+ * window are left unchanged.  Pending drafts stay pending. */
+int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream);
+
+/* Speculative verification of T drafts per sequence, 1 <= T <= max_draft
+ * [P1, Interpretation 3; P3, Interpretation 3]: sequences whose window cannot
+ * hold T more records are folded first; the drafts are staged in the ring and
+ * y receives the T outputs each draft would produce, [batch][T][heads][head_dim],
+ * without writing any intermediate state. */
+int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float *y, void *stream);
+
+/* Accept the first accepted[b] drafts of each sequence (device int32 [batch]):
+ * a pointer move only.  Values outside 0..T_pending are clamped and set
+ * REPLAY_STATUS_ACCEPT_CLAMPED.  Rejected drafts are simply left behind. */
+int replay_commit(replay_ctx *ctx, const int32_t *accepted, void *stream);
+
+/* Device addresses of the current pos[batch] and ckpt_pos[batch] arrays (valid
+ * until the next call that enqueues work on ctx). */
+int replay_current_pointers(const replay_ctx *ctx, const int32_t **pos, const int32_t **ckpt_pos);
+
+/* ---- in-run baselines (for measurement, not part of the replay method) ---- */
+
+/* Conventional decode step: load the F32 state [batch][heads][head_dim][state_dim],
+ * update it, compute y from the updated state, store it back -- L reads and L
+ * writes per window [P1, Interpretation 2; P3, Interpretation 1].  cfg->window,
+ * max_draft and formats are ignored.  A, D: Mamba-2 parameters, NULL for GDN. */
+int replay_conv_step(const replay_config *cfg, float *state, const float *A, const float *D,
+                     const replay_record *rec, float *y, void *stream);
+
+/* Snapshot-per-draft verification, the scheme the method replaces
+ * [P1, Interpretation 3; P3, Interpretation 3]: slots holds cfg->max_draft + 1
+ * F32 states per sequence, [batch][max_draft + 1][heads][head_dim][state_dim];
+ * cur[b] names the current slot.  Reads slot cur[b] once, and after each draft
+ * i (0-based) writes the state to slot (cur[b] + 1 + i) mod (max_draft + 1):
+ * one read and T writes.  y as for replay_verify. */
+int replay_snapshot_verify(const replay_config *cfg, float *slots, const int32_t *cur, int32_t T,
+                           const float *A, const float *D, const replay_record *drafts, float *y,
+                           void *stream);
+/* cur[b] <- (cur[b] + clamp(accepted[b], 0, T)) mod (max_draft + 1). */
+int replay_snapshot_commit(const replay_config *cfg, int32_t *cur, const int32_t *accepted, int32_t T,
+                           void *stream);
+
+/* HBM ceiling probe: mode 0 reads `bytes` from src (dst receives at most 16
+ * bytes, written only if a never-occurring value is read); mode 1 copies
+ * src to dst.  bytes must be a multiple of 16. */
+int replay_hbm_probe(const void *src, void *dst, size_t bytes, int mode, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REPLAYSSM_H */
