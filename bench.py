@@ -1,0 +1,260 @@
+"""Benchmark of the replay decode path on one MI355X.
+
+Headline: one decode step (``replay_step``) of a Mamba-2 layer whose float32
+state is 4 MiB per sequence (128 heads, P = 64, N = 128, 8 B/C groups), batch
+256, window L = 16, with its inputs already resident in HBM.  K steps are timed
+(K a multiple of L covers whole windows, so folds are included in proportion).
+
+Printed: one JSON line with the headline (microseconds per step), the roofline
+of the step kernel (algorithmic bytes per launch over its measured average
+launch time), the CPU oracle timed on a bounded sample, and an ``extra`` block
+with the in-run baselines and the other layer measurements.
+
+  python bench.py [--gpus 1] [--steps 256] [--warmup 32] [--no-extra] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["hybrid_model_ssm_replay_amd/csrc/mamba2.hip", "hybrid_model_ssm_replay_amd/csrc/common.h",
+                  "hybrid_model_ssm_replay_amd/csrc/internal.h"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(name: str):
+    """Per-launch HBM bytes from a committed counter summary, if it matches the current kernel source."""
+    path = os.path.join(PROFILE_DIR, name)
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+class Timer:
+    """HIP events on the stream the library launches on (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, n):
+        t = self.torch
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        t.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n  # microseconds per call
+
+
+def dev_records(torch, ins, n):
+    return [{k: torch.from_numpy(v).cuda() for k, v in ins.record().items()} for _ in range(n)]
+
+
+def bench_replay(torch, shape, seed, steps, warmup, pool=32):
+    from hybrid_model_ssm_replay_amd.layer import ReplayLayer
+    from synth import InputStream
+    ins = InputStream(shape, seed)
+    recs = dev_records(torch, ins, pool)
+    kw = dict(A=ins.params["A"], D=ins.params["D"]) if shape.kind == "mamba2" else {}
+    lay = ReplayLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
+                      groups=shape.groups, **kw)
+    y = torch.empty((shape.batch, shape.heads, shape.head_dim), device="cuda")
+    tm = Timer(torch)
+    tm.run(lambda i: lay.step(recs[i % pool], y), warmup)
+    us = tm.run(lambda i: lay.step(recs[(warmup + i) % pool], y), steps)
+    if lay.status != 0:
+        raise RuntimeError(f"device status {lay.status:#x}")
+    return us
+
+
+def bench_conv(torch, shape, seed, steps, warmup, pool=32):
+    from hybrid_model_ssm_replay_amd.layer import ConvLayer
+    from synth import InputStream
+    ins = InputStream(shape, seed)
+    recs = dev_records(torch, ins, pool)
+    kw = dict(A=ins.params["A"], D=ins.params["D"]) if shape.kind == "mamba2" else {}
+    conv = ConvLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, groups=shape.groups, **kw)
+    y = torch.empty((shape.batch, shape.heads, shape.head_dim), device="cuda")
+    tm = Timer(torch)
+    tm.run(lambda i: conv.step(recs[i % pool], y), warmup)
+    return tm.run(lambda i: conv.step(recs[(warmup + i) % pool], y), steps)
+
+
+def bench_verify(torch, shape, T, seed, reps=16):
+    """Replay verify + commit vs snapshot verify + commit vs one conventional step, batch as in shape."""
+    from hybrid_model_ssm_replay_amd.layer import ReplayLayer, SnapshotLayer
+    from synth import InputStream
+    ins = InputStream(shape, seed)
+    drafts = [{k: torch.from_numpy(v).cuda() for k, v in ins.drafts(T).items()} for _ in range(4)]
+    accs = [torch.from_numpy(ins.accepted(T)).cuda() for _ in range(4)]
+    lay = ReplayLayer("mamba2", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
+                      groups=shape.groups, max_draft=T, A=ins.params["A"], D=ins.params["D"])
+    y = torch.empty((shape.batch, T, shape.heads, shape.head_dim), device="cuda")
+    tm = Timer(torch)
+
+    def rv(i):
+        lay.verify(drafts[i % 4], y)
+        lay.commit(accs[i % 4])
+
+    tm.run(rv, 8)
+    us_replay = tm.run(rv, reps)
+    del lay
+    snap = SnapshotLayer("mamba2", shape.batch, shape.heads, shape.head_dim, shape.state_dim, T, groups=shape.groups,
+                         A=ins.params["A"], D=ins.params["D"])
+
+    def sv(i):
+        snap.verify(drafts[i % 4], y)
+        snap.commit(accs[i % 4])
+
+    tm.run(sv, 4)
+    us_snap = tm.run(sv, reps)
+    del snap
+    torch.cuda.empty_cache()
+    return us_replay, us_snap
+
+
+def bench_probe(torch, nbytes=2 << 30):
+    from hybrid_model_ssm_replay_amd import binding as B
+    src = torch.zeros(nbytes // 4, device="cuda")
+    dst = torch.zeros(nbytes // 8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    tm = Timer(torch)
+    tm.run(lambda i: B.replay_hbm_probe(src.data_ptr(), dst.data_ptr(), nbytes, 0, st), 3)
+    us_read = tm.run(lambda i: B.replay_hbm_probe(src.data_ptr(), dst.data_ptr(), nbytes, 0, st), 10)
+    half = nbytes // 2
+    tm.run(lambda i: B.replay_hbm_probe(src.data_ptr(), dst.data_ptr(), half, 1, st), 3)
+    us_copy = tm.run(lambda i: B.replay_hbm_probe(src.data_ptr(), dst.data_ptr(), half, 1, st), 10)
+    del src, dst
+    torch.cuda.empty_cache()
+    return nbytes / us_read / 1e3, 2 * half / us_copy / 1e3
+
+
+def cpu_baseline(shape, seed, budget_s=12.0):
+    """The float64 stepwise oracle on a bounded sample of sequences, scaled to the full batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle.session import StepwiseSession
+    from synth import InputStream, take_batch
+    nseq = 4
+    ins = InputStream(shape, seed)
+    recs = [take_batch(ins.record(), np.arange(nseq)) for _ in range(8)]
+    ref = StepwiseSession(shape.kind, np.zeros((nseq, shape.heads, shape.head_dim, shape.state_dim)),
+                          ins.params)
+    steps = 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            ref.step(recs[steps % len(recs)])
+            steps += 1
+        el = time.perf_counter() - t0
+    us_per_step_full = el / steps * (shape.batch / nseq) * 1e6
+    return {"value": us_per_step_full, "unit": "us/step", "cores": 1, "kind": "oracle",
+            "sample": f"float64 stepwise oracle, {nseq} of {shape.batch} sequences, {steps} steps "
+                      f"({el:.1f} s), scaled linearly to the full batch"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--no-extra", action="store_true", help="skip baselines and other layers")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the replay decode path has no cross-GPU step "
+              "(sequences and heads shard with no exchange); --gpus above 1 is not measured.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from hybrid_model_ssm_replay_amd import load_library
+    from hybrid_model_ssm_replay_amd.traffic import Layer, conventional_step_bytes, replay_window_mean
+    from synth import WORKLOADS
+
+    load_library()
+    torch.cuda.set_device(0)
+    name = "mamba2_b256_h128_p64_n128_g8_l16"
+    shape = WORKLOADS[name]
+    L = shape.window
+    if args.steps % L or args.warmup % L:
+        log(f"note: steps/warmup not multiples of L={L}; the window mean is approximate")
+    log("replay step", name)
+    us = bench_replay(torch, shape, 1, args.steps, args.warmup)
+    lay = Layer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.groups, L)
+    rd, wr = replay_window_mean(lay)
+    gbs = (rd + wr) / us / 1e3
+    extra = {"replay_step_us": us, "replay_model_bytes_per_step": rd + wr, "replay_gbs": gbs,
+             "tokens_per_s": shape.batch / us * 1e6}
+    log("hbm probe")
+    rgbs, cgbs = bench_probe(torch)
+    extra.update({"hbm_probe_read_gbs": rgbs, "hbm_probe_copy_gbs": cgbs})
+    if not args.no_extra:
+        log("conventional step", name)
+        us_c = bench_conv(torch, shape, 1, args.steps, args.warmup)
+        crd, cwr = conventional_step_bytes(lay)
+        extra.update({"conventional_step_us": us_c, "conventional_gbs": (crd + cwr) / us_c / 1e3,
+                      "speedup_vs_conventional": us_c / us})
+        vshape = WORKLOADS["mamba2_b512_h128_p64_n128_g8_l16"]
+        for T in (4, 8):
+            log("verify T", T)
+            us_rv, us_sv = bench_verify(torch, vshape, T, 3)
+            extra[f"verify_b512_T{T}"] = {"replay_verify_commit_us": us_rv, "snapshot_verify_commit_us": us_sv}
+        us_std = bench_conv(torch, vshape, 3, 32, 8)
+        extra["conventional_step_b512_us"] = us_std
+        for T in (4, 8):
+            v = extra[f"verify_b512_T{T}"]
+            v["replay_over_standard_step"] = v["replay_verify_commit_us"] / us_std
+            v["snapshot_over_standard_step"] = v["snapshot_verify_commit_us"] / us_std
+
+    traffic = stored_traffic("m2_replay_step_b256_traffic.txt")
+    roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": traffic, "kernel": "m2_replay_step<8,1>",
+            "bytes_per_launch": rd + wr}
+    cpu = None if args.no_cpu else cpu_baseline(shape, 1)
+    out = {
+        "metric": "SSM decode us/step + achieved HBM GB/s, B=256 L=16 (Mamba-2 & GDN)",
+        "value": us, "unit": "us/step", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": us / 1e3, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "layer": "Mamba-2", "batch": shape.batch, "heads": shape.heads,
+                   "head_dim": shape.head_dim, "state_dim": shape.state_dim, "groups": shape.groups, "window": L,
+                   "state_mib_per_seq": shape.heads * shape.head_dim * shape.state_dim * 4 / 2 ** 20},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -86,6 +86,12 @@ def load_library(path: str | None = None):
     if _lib is not None:
         return _lib
     p = path or lib_path()
+    # The library must bind to the HIP runtime that PyTorch (which owns the
+    # device memory and streams) has loaded; load torch first if it is present.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(p):
         raise ImportError(f"{p} is not built; run `python -m hybrid_model_ssm_replay_amd.build`")
     lib = ctypes.CDLL(p)

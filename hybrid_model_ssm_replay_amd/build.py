@@ -24,6 +24,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-FP32 VALU forms are kept out of the generated code on purpose.
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 

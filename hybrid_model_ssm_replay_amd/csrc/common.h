@@ -88,3 +88,36 @@ struct PtrHalves {
 };
 
 }  // namespace rssm
+
+namespace rssm {
+
+// Division by a divisor fixed for the whole launch, as a multiply-high and a
+// shift (round-up method of Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994): with s = ceil(log2 d) and
+// m = floor(2^32 (2^s - d) / d) + 1, n / d = (umulhi(n, m) + n) >> s for
+// 0 <= n < 2^31.  The host fills it; kernels divide tile indices and token
+// positions with it instead of a ~20-instruction integer division.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, s};
+}
+
+__device__ __forceinline__ int fdiv(int n, const FastDiv &f) {
+  const uint32_t t = __umulhi((uint32_t)n, f.m);
+  return (int)((t + (uint32_t)n) >> f.s);
+}
+__device__ __forceinline__ int fmod_(int n, const FastDiv &f) { return n - fdiv(n, f) * (int)f.d; }
+
+// (s0 + j) mod d for 0 <= s0 < d and 0 <= j < d: one compare, no division.
+__device__ __forceinline__ int wrap(int s0, int j, int d) {
+  const int v = s0 + j;
+  return v >= d ? v - d : v;
+}
+
+}  // namespace rssm

@@ -19,7 +19,8 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // the same group is still folding or reading in the same launch (the window
 // plus the drafts of one call span at most 2 L positions).
 struct RingLayout {
-  // Mamba-2: f0 = x [B][H][L][P], f1 = B [B][G][2L][N], f2 = dt [B][H][L].
+  // Mamba-2: f0 = x [L][B][H][P] (slot-major: one step's appends form one
+  //          contiguous block), f1 = B [B][G][2L][N], f2 = dt [B][H][L].
   // GDN:     f0 = k [B][H][L][dk], f1 = v [B][H][L][dv], f2 = alpha [B][H][L],
   //          f3 = beta [B][H][L].
   size_t off[4];
@@ -50,14 +51,21 @@ inline RingLayout ring_layout(const replay_config &c) {
   return r;
 }
 
-// Shape of one launch, as the kernels see it.
+// Shape of one launch, as the kernels see it, with the launch-invariant
+// divisors the kernels need (heads, heads per group, L, 2 L).
 struct Shape {
   int B, H, G, P, N, L;
+  FastDiv fH, fHpg, fL, f2L;
 };
+
+inline Shape make_shape(int B, int H, int G, int P, int N, int L) {
+  return Shape{B, H, G, P, N, L, make_fastdiv((uint32_t)H), make_fastdiv((uint32_t)(H / G)),
+               make_fastdiv((uint32_t)L), make_fastdiv((uint32_t)(2 * L))};
+}
 
 // Mamba-2 ---------------------------------------------------------------
 struct M2Ring {
-  float *x;   // [B][H][L][P]
+  float *x;   // [L][B][H][P]
   float *Bm;  // [B][G][2L][N]
   float *dt;  // [B][H][L]
 };
@@ -126,23 +134,23 @@ int launch_commit(PtrHalves p, int B, const int32_t *accepted, int T, int32_t *s
 int launch_snapshot_commit(int32_t *cur, const int32_t *accepted, int B, int T, int nslots, hipStream_t st);
 int launch_probe(const void *src, void *dst, size_t bytes, int mode, hipStream_t st);
 
-// Launch geometry shared by the tile kernels: one workgroup per (sequence,
-// head); one wave per 16-row block of the head's state, at most 4 waves, with
-// RBW row blocks per wave.
-inline bool tile_geometry(int P, int *waves, int *rbw) {
+// Launch geometry of the per-head kernels: one workgroup per (sequence, head).
+// wave_per_head kernels (step, conventional, snapshot): RBW row blocks of 16
+// rows per wave, RBW = 2 when the number of row blocks is even, else 1.
+// Workgroup kernels (flush, verify): one wave per row block, at most 4 waves,
+// RBW = 2 at P = 128.  Supported P: 16, 32, 48, 64, 128.
+inline bool tile_geometry(int P, bool wave_per_head, int *waves, int *rbw) {
   if (P % 16 || P < 16) return false;
   const int rb = P / 16;
-  if (rb <= 4) {
-    *waves = rb;
-    *rbw = 1;
+  if (rb > 4 && rb != 8) return false;
+  if (wave_per_head) {
+    *rbw = (rb % 2 == 0) ? 2 : 1;
+    *waves = rb / *rbw;
     return true;
   }
-  if (rb == 8) {
-    *waves = 4;
-    *rbw = 2;
-    return true;
-  }
-  return false;
+  *waves = rb <= 4 ? rb : 4;
+  *rbw = rb / *waves;
+  return true;
 }
 
 }  // namespace rssm

@@ -92,7 +92,7 @@ __device__ __forceinline__ float suffix_sum16(float v, int lane, float *total) {
 template <int NCH, int RBW>
 __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm, int cnt, int base,
                                           float Ah, const float *rx, const float *rdt, const float *rB,
-                                          int L, int P, const TileCtx &t) {
+                                          int L, size_t xs, const TileCtx &t) {
   constexpr int N = 16 * NCH;
   // Stage B_r (cnt x N) in LDS; zero the rows up to the next multiple of 4.
   const int rows4 = (cnt + 3) & ~3;
@@ -118,7 +118,7 @@ __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm
     for (int st = 0; st < 4; ++st) {
       const int r = 4 * st + t.q;
       const float fr = __shfl(f, r, kWave);
-      xb[st] = (r < cnt) ? fr * rx[(size_t)((base + r) % L) * P + row] : 0.f;
+      xb[st] = (r < cnt) ? fr * rx[(size_t)((base + r) % L) * xs + row] : 0.f;
     }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -133,22 +133,180 @@ __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm
   __syncthreads();
 }
 
-// ---- replay step ----------------------------------------------------------
+// ---- replay step (one wave per head) -----------------------------------------
+// The whole head's checkpoint lives in one wave's registers (RBW row blocks of
+// 16 rows; a second wave takes the other half when P = 128).  Every load that
+// does not depend on the pointers is issued first, so the checkpoint stream is
+// in flight while the pointers, then the ring records, arrive.  No LDS and no
+// workgroup barrier on the non-fold path.
+//
+// Lane (r16, q) roles:  checkpoint rows 16 rb + r16, columns 16 c + 4 q + 0..3;
+// for the B_j . C dots lane r16 stands for window record j = r16 and sums over
+// the same columns as its checkpoint slice, so the C values it already holds
+// serve both products.
+
+// Fold the cnt committed records at positions base.. into the register tile,
+// wave-locally: s <- exp(A s_{1..cnt}) s + sum_r exp(A s_{r+1..cnt}) dt_r x_r B_r^T.
+// Split in two so that callers can issue the record loads before the
+// checkpoint stream: fold_load reads the records, fold_apply does the MFMAs.
+template <int NCH, int RBW>
+struct FoldIn {
+  float f;             // lanes 0..15: exp(A s_{r+1..cnt}) dt_r for record r = lane
+  float scale;         // exp(A s_{1..cnt})
+  float aB[NCH][4];    // MFMA A operand: B_{4 st + q}[16 c + r16]
+  float xraw[4][RBW];  // x_{4 st + q}[row of block k]
+  int nsteps;          // ceil(cnt / 4)
+};
+
+template <int NCH, int RBW>
+__device__ __forceinline__ void fold_load(FoldIn<NCH, RBW> &fi, int cnt, int s0, int s0b, const float *rx,
+                                          const float *rdt, const float *rB, int L, size_t xs, int rb0, int lane) {
+  // s0 = (position of record 0) mod L, s0b = the same mod 2 L; xs = x-ring slot stride.
+  const int q = lane >> 4, r16 = lane & 15;
+  const float dtl = rdt[wrap(s0, r16 < cnt ? r16 : cnt - 1, L)];
+  fi.f = lane < cnt ? dtl : 0.f;  // dt for now; fold_apply turns it into the weight
+  fi.nsteps = (cnt + 3) >> 2;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int r = 4 * st + q;
+    const int rc = r < cnt ? r : cnt - 1;
+    const float *Br = rB + wrap(s0b, rc, 2 * L) * (16 * NCH);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const float v = Br[16 * c + r16];
+      fi.aB[c][st] = r < cnt ? v : 0.f;
+    }
+    const float *xr = rx + wrap(s0, rc, L) * xs;
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      const float v = xr[(rb0 + k) * 16 + r16];
+      fi.xraw[st][k] = r < cnt ? v : 0.f;
+    }
+  }
+}
+
+template <int NCH, int RBW>
+__device__ __forceinline__ void fold_apply(float4 (&s)[RBW][NCH], FoldIn<NCH, RBW> &fi, float Ah, int lane) {
+  const int q = lane >> 4;
+  const float dtv = fi.f;
+  float total;
+  const float seg = suffix_sum16(dtv, lane, &total);
+  const float f = __expf(Ah * seg) * dtv;
+  const float scale = __expf(Ah * total);
+#pragma unroll
+  for (int k = 0; k < RBW; ++k) {
+    float xb[4];  // MFMA B operand: f_r x_r[row], r = 4 st + q  (K = record, N = row)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) xb[st] = __shfl(f, 4 * st + q, kWave) * fi.xraw[st][k];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      floatx4 acc = {s[k][c].x * scale, s[k][c].y * scale, s[k][c].z * scale, s[k][c].w * scale};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        if (st < fi.nsteps) acc = mfma_16x16x4(fi.aB[c][st], xb[st], acc);
+      s[k][c] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+  }
+}
+
+template <int NCH, int RBW>
+__device__ __forceinline__ void load_rows(float4 (&s)[RBW][NCH], const float *S, int rb0, int lane) {
+  constexpr int N = 16 * NCH;
+  const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int k = 0; k < RBW; ++k) {
+    const int row = (rb0 + k) * 16 + r16;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) s[k][c] = ld4(S + (size_t)row * N + 16 * c + 4 * q);
+  }
+}
+
+template <int NCH, int RBW>
+__device__ __forceinline__ void store_rows(const float4 (&s)[RBW][NCH], float *S, int rb0, int lane) {
+  constexpr int N = 16 * NCH;
+  const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int k = 0; k < RBW; ++k) {
+    const int row = (rb0 + k) * 16 + r16;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) st4(S + (size_t)row * N + 16 * c + 4 * q, s[k][c]);
+  }
+}
+
+// Value of acc[k] for k = sel (a per-lane index) without dynamic register indexing.
+template <int RBW>
+__device__ __forceinline__ float pick(const float (&acc)[RBW], int sel) {
+  float v = acc[0];
+#pragma unroll
+  for (int k = 1; k < RBW; ++k) v = (sel == k) ? acc[k] : v;
+  return v;
+}
+
+// Output of the newest of m window records from the checkpoint rows in s.
+// Inputs are the already-loaded pieces: cv (this token's C at the lane's
+// columns), bdot (the lane's partial B_{r16} . C), dtv (dt of record `lane`,
+// lanes 0..15), xr[st][k] (x of record 4 st + q at row block k).  Returns the
+// finished output of row 16 (rb0 + q) + r16 (lanes with q < RBW).
+template <int NCH, int RBW>
+__device__ __forceinline__ float replay_output(const float4 (&s)[RBW][NCH], const float4 (&cv)[NCH], float bdot,
+                                               float dtv, const float (&xr)[4][RBW], int m, float Ah, int lane) {
+  const int q = lane >> 4;
+  const float dot = sum_quarters(bdot);
+  float total;
+  const float seg = suffix_sum16(dtv, lane, &total);
+  const float w = lane < m ? __expf(Ah * seg) * dtv * dot : 0.f;
+  const float scale = __expf(Ah * total);
+  float acc[RBW];
+#pragma unroll
+  for (int k = 0; k < RBW; ++k) {
+    float v = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) v += dot4(s[k][c], cv[c]);
+    v *= scale;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) v += __shfl(w, 4 * st + q, kWave) * xr[st][k];
+    acc[k] = sum_quarters(v);
+  }
+  return pick<RBW>(acc, q);
+}
+
 template <int NCH, int RBW>
 __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   constexpr int N = 16 * NCH;
-  __shared__ M2Smem<NCH> sm;
-  const TileCtx t = tile_ctx();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int q = lane >> 4, r16 = lane & 15;
   const Shape &sh = a.s;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = tile / sh.H, h = tile - b * sh.H;
-  const int hpg = sh.H / sh.G, g = h / hpg;
+  const int b = fdiv(tile, sh.fH), h = tile - b * sh.H;
+  const int g = fdiv(h, sh.fHpg);
   const int P = sh.P, L = sh.L;
+  const int rb0 = wave * RBW;
+  float *S = a.ckpt + ((size_t)b * sh.H + h) * P * N;
+  const size_t xs = (size_t)sh.B * sh.H * P;  // x-ring slot stride (slot-major ring)
+  float *rx = a.ring.x + ((size_t)b * sh.H + h) * P;
+  float *rdt = a.ring.dt + ((size_t)b * sh.H + h) * L;
+  float *rB = a.ring.Bm + ((size_t)b * sh.G + g) * 2 * L * N;
+  const float *xin = a.x + ((size_t)b * sh.H + h) * P;
+  const float *Bin = a.Bm + ((size_t)b * sh.G + g) * N;
+  const float *Cin = a.Cm + ((size_t)b * sh.G + g) * N;
 
+  // 1. Everything whose address needs no pointer, checkpoint first: its loads
+  //    are then in flight while the pointers arrive.  (Loads complete in issue
+  //    order, so nothing issued later can delay it.)
+  float4 s[RBW][NCH];
+  load_rows<NCH, RBW>(s, S, rb0, lane);
+  float4 cv[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) cv[c] = ld4(Cin + 16 * c + 4 * q);
+  const float dtrow = rdt[r16 < L ? r16 : 0];  // the head's whole dt ring, slot = r16
+  const float dt_in = a.dt[(size_t)b * sh.H + h];
+  const float Ah = a.A[h], Dh = a.D[h];
+
+  // 2. Pointers.
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
   const int count = pos - ck;
   if (count < 0 || count > L) {
-    if (h == 0 && t.tid == 0) {
+    if (h == 0 && threadIdx.x == 0) {
       atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
       a.ptr.pos_out[b] = pos;
       a.ptr.ckpt_out[b] = ck;
@@ -156,81 +314,81 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
     return;
   }
   const bool fold = count == L;
-  float *S = a.ckpt + ((size_t)b * sh.H + h) * P * N;
-  float4 s[RBW][NCH];
-  load_tile<NCH, RBW>(s, S, t);
+  const int s0 = fmod_(ck, sh.fL), s0b = fmod_(ck, sh.f2L);  // slots of window record 0
+  const int slot = wrap(s0, count, L), slotb = wrap(s0b, count, 2 * L);  // slots of this token
 
-  const float Ah = a.A[h];
-  float *rx = a.ring.x + ((size_t)b * sh.H + h) * L * P;
-  float *rdt = a.ring.dt + ((size_t)b * sh.H + h) * L;
-  float *rB = a.ring.Bm + ((size_t)b * sh.G + g) * 2 * L * N;
-  const float *xin = a.x + ((size_t)b * sh.H + h) * P;
-  const float *Bin = a.Bm + ((size_t)b * sh.G + g) * N;
-  const float *Cin = a.Cm + ((size_t)b * sh.G + g) * N;
-  const float dt_in = a.dt[(size_t)b * sh.H + h];
-
-  int base = ck;
-  if (fold) {
-    fold_tile<NCH, RBW>(s, sm, L, ck, Ah, rx, rdt, rB, L, P, t);
-    store_tile<NCH, RBW>(s, S, t);
-    base = pos;
-  }
-  const int m = pos - base + 1;  // window records including this token (1..L)
-
-  // dt of the window, record r in lane r; segment sums for the decays.
-  const float dtv = t.lane < m - 1 ? rdt[(base + t.lane) % L] : (t.lane == m - 1 ? dt_in : 0.f);
-  float total;
-  const float seg = suffix_sum16(dtv, t.lane, &total);
-
-  // B_r . C for every window record: 16 lanes per record, 4 records per wave pass.
-  for (int r0 = 4 * t.wave; r0 < m; r0 += 4 * (t.nthreads >> 6)) {
-    const int r = r0 + t.q;
-    float part = 0.f;
-    if (r < m) {
-      const float *Br = (r == m - 1) ? Bin : rB + (size_t)((base + r) % (2 * L)) * N;
+  float bdot = 0.f, dtv;
+  float xr[4][RBW];
+  int base;
+  if (!fold) {
+    // 3. Window records (ring slots known now).  Every load is unconditional on
+    //    a clamped record index, masked afterwards: no per-load branches.
+    base = ck;
+    const int m = count + 1;
+    float4 bj[NCH];
+    {
+      const int j = r16 < m ? r16 : m - 1;
+      const float *Bj = (j == m - 1) ? Bin : rB + wrap(s0b, j, 2 * L) * N;
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) part += Br[t.r16 + 16 * i] * Cin[t.r16 + 16 * i];
+      for (int c = 0; c < NCH; ++c) bj[c] = ld4(Bj + 16 * c + 4 * q);
     }
-    part = sum16(part);
-    if (t.r16 == 0 && r < m) sm.dot[r] = part;
-  }
-  lds_barrier();
-  const float w = t.lane < m ? __expf(Ah * seg) * dtv * sm.dot[t.lane] : 0.f;
-  const float scale = __expf(Ah * total);
-  const float Dh = a.D[h];
-
-  float4 cv[NCH];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) cv[c] = ld4(Cin + 16 * c + 4 * t.q);
-#pragma unroll
-  for (int k = 0; k < RBW; ++k) {
-    const int row = (t.wave * RBW + k) * 16 + t.r16;
-    float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) acc += dot4(s[k][c], cv[c]);
-    acc *= scale;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const int r = 4 * st + t.q;
-      const float wr = __shfl(w, r, kWave);
-      if (r < m) {
-        const float xv = (r == m - 1) ? xin[row] : rx[(size_t)((base + r) % L) * P + row];
-        acc += wr * xv;
+      const int j = 4 * st + q;
+      const int jc = j < m ? j : m - 1;
+      const float *xj = (jc == m - 1) ? xin : rx + wrap(s0, jc, L) * xs;
+#pragma unroll
+      for (int k = 0; k < RBW; ++k) {
+        const float v = xj[(rb0 + k) * 16 + r16];
+        xr[st][k] = j < m ? v : 0.f;
       }
     }
-    acc = sum_quarters(acc);
-    if (t.q == 0) a.y[((size_t)b * sh.H + h) * P + row] = acc + Dh * xin[row];
+    {
+      // dt of record `lane`, permuted out of the ring row loaded up front (after
+      // the loads above in program order, so it does not hold them back).
+      const float d = __shfl(dtrow, wrap(s0, r16 < m - 1 ? r16 : 0, L), kWave);
+      dtv = lane < m - 1 ? d : (lane == m - 1 ? dt_in : 0.f);
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) bdot += dot4(bj[c], cv[c]);
+    bdot = r16 < m ? bdot : 0.f;
+  } else {
+    // Fold the full window into the checkpoint, store it, and start the next
+    // window with this token as its only record.
+    FoldIn<NCH, RBW> fi;
+    fold_load<NCH, RBW>(fi, L, s0, s0b, rx, rdt, rB, L, xs, rb0, lane);
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      const float v = xin[(rb0 + k) * 16 + r16];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) xr[st][k] = (st == 0 && q == 0) ? v : 0.f;
+    }
+    dtv = lane == 0 ? dt_in : 0.f;
+    fold_apply<NCH, RBW>(s, fi, Ah, lane);
+    store_rows<NCH, RBW>(s, S, rb0, lane);
+    base = pos;
+    // This token's B . C after the fold: computing it earlier keeps more
+    // registers live across the fold and costs occupancy on every step.
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) bdot += dot4(ld4(Bin + 16 * c + 4 * q), cv[c]);
+    bdot = r16 == 0 ? bdot : 0.f;
   }
+  const int m = pos - base + 1;
+  const float out = replay_output<NCH, RBW>(s, cv, bdot, dtv, xr, m, Ah, lane);
 
-  // Append this token's record.  After a fold the slot of x / dt being written
-  // held the oldest folded record: wait until every wave has consumed it.
-  if (fold) __syncthreads();
-  const int slot = pos % L;
-  for (int i = t.tid; i < P; i += t.nthreads) rx[(size_t)slot * P + i] = xin[i];
-  if (t.tid == 0) rdt[slot] = dt_in;
-  if (h % hpg == 0)
-    for (int i = t.tid; i < N; i += t.nthreads) rB[(size_t)(pos % (2 * L)) * N + i] = Bin[i];
-  if (h == 0 && t.tid == 0) {
+  // 4. Append this token's record.  After a fold the dt slot being written
+  //    held a record that the other waves of a multi-wave head also read.
+  if (fold && nwaves > 1) __syncthreads();
+  if (q < RBW) {
+    const int row = (rb0 + q) * 16 + r16;
+    const float xv = xin[row];
+    a.y[((size_t)b * sh.H + h) * P + row] = out + Dh * xv;
+    rx[slot * xs + row] = xv;
+  }
+  if (threadIdx.x == 0) rdt[slot] = dt_in;
+  if (h - g * (sh.H / sh.G) == 0 && wave == 0)
+    for (int i = lane; i < N; i += kWave) rB[slotb * N + i] = Bin[i];
+  if (h == 0 && threadIdx.x == 0) {
     a.ptr.pos_out[b] = pos + 1;
     a.ptr.ckpt_out[b] = base;
   }
@@ -260,10 +418,11 @@ __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
   float *S = a.ckpt + ((size_t)b * sh.H + h) * P * N;
   float4 s[RBW][NCH];
   load_tile<NCH, RBW>(s, S, t);
-  const float *rx = a.ring.x + ((size_t)b * sh.H + h) * L * P;
+  const size_t xs = (size_t)sh.B * sh.H * P;
+  const float *rx = a.ring.x + ((size_t)b * sh.H + h) * P;
   const float *rdt = a.ring.dt + ((size_t)b * sh.H + h) * L;
   const float *rB = a.ring.Bm + ((size_t)b * sh.G + g) * 2 * L * N;
-  fold_tile<NCH, RBW>(s, sm, count, ck, a.A[h], rx, rdt, rB, L, P, t);
+  fold_tile<NCH, RBW>(s, sm, count, ck, a.A[h], rx, rdt, rB, L, xs, t);
   store_tile<NCH, RBW>(s, S, t);
 }
 
@@ -300,12 +459,13 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   float4 s[RBW][NCH];
   load_tile<NCH, RBW>(s, S, t);
   const float Ah = a.A[h];
-  float *rx = a.ring.x + ((size_t)b * H + h) * L * P;
+  const size_t xs = (size_t)sh.B * H * P;
+  float *rx = a.ring.x + ((size_t)b * H + h) * P;
   float *rdt = a.ring.dt + ((size_t)b * H + h) * L;
   float *rB = a.ring.Bm + ((size_t)b * G + g) * 2 * L * N;
   int base = ck;
   if (fold) {
-    fold_tile<NCH, RBW>(s, sm, count, ck, Ah, rx, rdt, rB, L, P, t);
+    fold_tile<NCH, RBW>(s, sm, count, ck, Ah, rx, rdt, rB, L, xs, t);
     store_tile<NCH, RBW>(s, S, t);
     base = pos;
   }
@@ -385,7 +545,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
       float4 o = make_float4(sc * acc[0], sc * acc[1], sc * acc[2], sc * acc[3]);
       for (int r = 0; r <= c + i; ++r) {
         const float cf = sm.coef[i][r];
-        const float4 xv = ld4(r < c ? rx + (size_t)((base + r) % L) * P + p0 : draft_x(r - c) + p0);
+        const float4 xv = ld4(r < c ? rx + (size_t)((base + r) % L) * xs + p0 : draft_x(r - c) + p0);
         o.x += cf * xv.x;
         o.y += cf * xv.y;
         o.z += cf * xv.z;
@@ -404,7 +564,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   __syncthreads();
   for (int e = t.tid; e < T * P; e += t.nthreads) {
     const int i = e / P, p = e - i * P;
-    rx[(size_t)((pos + i) % L) * P + p] = draft_x(i)[p];
+    rx[(size_t)((pos + i) % L) * xs + p] = draft_x(i)[p];
   }
   if (t.tid < T) rdt[(pos + t.tid) % L] = a.dt[((size_t)b * T + t.tid) * H + h];
   if (h % hpg == 0)
@@ -419,67 +579,76 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
 }
 
 // ---- baseline: conventional load-update-store step -------------------------
+// Same geometry and load order as the replay step: one wave per head, every
+// load issued before any arithmetic.
 template <int NCH, int RBW>
 __global__ __launch_bounds__(256) void m2_conv_step(M2ConvArgs a) {
   constexpr int N = 16 * NCH;
-  const TileCtx t = tile_ctx();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 4, r16 = lane & 15;
   const Shape &sh = a.s;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = tile / sh.H, h = tile - b * sh.H;
-  const int g = h / (sh.H / sh.G);
-  const int P = sh.P;
+  const int b = fdiv(tile, sh.fH), h = tile - b * sh.H;
+  const int g = fdiv(h, sh.fHpg);
+  const int P = sh.P, rb0 = wave * RBW;
   float *S = a.state + ((size_t)b * sh.H + h) * P * N;
   float4 s[RBW][NCH];
-  load_tile<NCH, RBW>(s, S, t);
-  const float dt = a.dt[(size_t)b * sh.H + h];
-  const float decay = __expf(dt * a.A[h]);
-  const float Dh = a.D[h];
-  const float *xin = a.x + ((size_t)b * sh.H + h) * P;
+  load_rows<NCH, RBW>(s, S, rb0, lane);
   const float *Bin = a.Bm + ((size_t)b * sh.G + g) * N;
   const float *Cin = a.Cm + ((size_t)b * sh.G + g) * N;
   float4 bv[NCH], cv[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    bv[c] = ld4(Bin + 16 * c + 4 * t.q);
-    cv[c] = ld4(Cin + 16 * c + 4 * t.q);
+    bv[c] = ld4(Bin + 16 * c + 4 * q);
+    cv[c] = ld4(Cin + 16 * c + 4 * q);
   }
+  const float *xin = a.x + ((size_t)b * sh.H + h) * P;
+  float xr[RBW];
+#pragma unroll
+  for (int k = 0; k < RBW; ++k) xr[k] = xin[(rb0 + k) * 16 + r16];
+  const float dt = a.dt[(size_t)b * sh.H + h];
+  const float decay = __expf(dt * a.A[h]);
+  const float Dh = a.D[h];
+  float acc[RBW];
 #pragma unroll
   for (int k = 0; k < RBW; ++k) {
-    const int row = (t.wave * RBW + k) * 16 + t.r16;
-    const float xv = xin[row];
-    const float dx = dt * xv;
-    float acc = 0.f;
+    const float dx = dt * xr[k];
+    float v = 0.f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      float4 &v = s[k][c];
-      v.x = decay * v.x + dx * bv[c].x;
-      v.y = decay * v.y + dx * bv[c].y;
-      v.z = decay * v.z + dx * bv[c].z;
-      v.w = decay * v.w + dx * bv[c].w;
-      acc += dot4(v, cv[c]);
+      float4 &e = s[k][c];
+      e.x = decay * e.x + dx * bv[c].x;
+      e.y = decay * e.y + dx * bv[c].y;
+      e.z = decay * e.z + dx * bv[c].z;
+      e.w = decay * e.w + dx * bv[c].w;
+      v += dot4(e, cv[c]);
     }
-    acc = sum_quarters(acc);
-    if (t.q == 0) a.y[((size_t)b * sh.H + h) * P + row] = acc + Dh * xv;
+    acc[k] = sum_quarters(v);
   }
-  store_tile<NCH, RBW>(s, S, t);
+  store_rows<NCH, RBW>(s, S, rb0, lane);
+  if (q < RBW) {
+    const int row = (rb0 + q) * 16 + r16;
+    a.y[((size_t)b * sh.H + h) * P + row] = pick<RBW>(acc, q) + Dh * xin[row];
+  }
 }
 
 // ---- baseline: snapshot-per-draft verify -----------------------------------
 template <int NCH, int RBW>
 __global__ __launch_bounds__(256) void m2_snapshot_verify(M2SnapArgs a) {
   constexpr int N = 16 * NCH;
-  const TileCtx t = tile_ctx();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 4, r16 = lane & 15;
   const Shape &sh = a.s;
-  const int T = a.T, H = sh.H, G = sh.G, P = sh.P;
+  const int T = a.T, H = sh.H, G = sh.G, P = sh.P, rb0 = wave * RBW;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = tile / H, h = tile - b * H;
-  const int g = h / (H / G);
+  const int b = fdiv(tile, sh.fH), h = tile - b * H;
+  const int g = fdiv(h, sh.fHpg);
   const int cur = a.cur[b];
   if (cur < 0 || cur >= a.nslots) return;  // never index outside the slot array
   const size_t head_elems = (size_t)P * N;
   auto slot_ptr = [&](int sl) { return a.slots + (((size_t)b * a.nslots + sl) * H + h) * head_elems; };
   float4 s[RBW][NCH];
-  load_tile<NCH, RBW>(s, slot_ptr(cur), t);
+  load_rows<NCH, RBW>(s, slot_ptr(cur), rb0, lane);
   const float Ah = a.A[h], Dh = a.D[h];
   for (int i = 0; i < T; ++i) {
     const float dt = a.dt[((size_t)b * T + i) * H + h];
@@ -490,52 +659,58 @@ __global__ __launch_bounds__(256) void m2_snapshot_verify(M2SnapArgs a) {
     float4 bv[NCH], cv[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      bv[c] = ld4(Bin + 16 * c + 4 * t.q);
-      cv[c] = ld4(Cin + 16 * c + 4 * t.q);
+      bv[c] = ld4(Bin + 16 * c + 4 * q);
+      cv[c] = ld4(Cin + 16 * c + 4 * q);
     }
+    float acc[RBW];
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
-      const int row = (t.wave * RBW + k) * 16 + t.r16;
-      const float xv = xin[row];
-      const float dx = dt * xv;
-      float acc = 0.f;
+      const float dx = dt * xin[(rb0 + k) * 16 + r16];
+      float v = 0.f;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        float4 &v = s[k][c];
-        v.x = decay * v.x + dx * bv[c].x;
-        v.y = decay * v.y + dx * bv[c].y;
-        v.z = decay * v.z + dx * bv[c].z;
-        v.w = decay * v.w + dx * bv[c].w;
-        acc += dot4(v, cv[c]);
+        float4 &e = s[k][c];
+        e.x = decay * e.x + dx * bv[c].x;
+        e.y = decay * e.y + dx * bv[c].y;
+        e.z = decay * e.z + dx * bv[c].z;
+        e.w = decay * e.w + dx * bv[c].w;
+        v += dot4(e, cv[c]);
       }
-      acc = sum_quarters(acc);
-      if (t.q == 0) a.y[(((size_t)b * T + i) * H + h) * P + row] = acc + Dh * xv;
+      acc[k] = sum_quarters(v);
     }
-    store_tile<NCH, RBW>(s, slot_ptr((cur + 1 + i) % a.nslots), t);
+    if (q < RBW) {
+      const int row = (rb0 + q) * 16 + r16;
+      a.y[(((size_t)b * T + i) * H + h) * P + row] = pick<RBW>(acc, q) + Dh * xin[row];
+    }
+    store_rows<NCH, RBW>(s, slot_ptr((cur + 1 + i) % a.nslots), rb0, lane);
   }
 }
 
 // ---- dispatch ---------------------------------------------------------------
+// Wave-per-head kernels: RBW = min(P / 16, 4) row blocks per wave, P / (16 RBW)
+// waves per head.  Workgroup kernels (flush, verify): one wave per row block, up
+// to 4 waves, RBW = 2 at P = 128.
 template <template <int, int> class K, typename Args>
-int dispatch(const Args &a, int N, int P, int B, int H, hipStream_t st) {
+int dispatch(const Args &a, int N, int P, int B, int H, bool wave_per_head, hipStream_t st) {
   int waves, rbw;
-  if (!tile_geometry(P, &waves, &rbw)) return (int)hipErrorInvalidValue;
+  if (!tile_geometry(P, wave_per_head, &waves, &rbw)) return (int)hipErrorInvalidValue;
   const dim3 grid((unsigned)((size_t)B * H)), block(64 * waves);
-#define RSSM_CASE(NCH_, RBW_)                                   \
-  if (N == 16 * NCH_ && rbw == RBW_) {                          \
+#define RSSM_CASE(NCH_, RBW_)                                       \
+  if (N == 16 * NCH_ && rbw == RBW_) {                              \
     hipLaunchKernelGGL((K<NCH_, RBW_>::fn), grid, block, 0, st, a); \
-    return (int)hipGetLastError();                              \
+    return (int)hipGetLastError();                                  \
   }
-  RSSM_CASE(1, 1) RSSM_CASE(2, 1) RSSM_CASE(4, 1) RSSM_CASE(8, 1)
-  RSSM_CASE(1, 2) RSSM_CASE(2, 2) RSSM_CASE(4, 2) RSSM_CASE(8, 2)
+#define RSSM_NCH(RBW_) RSSM_CASE(1, RBW_) RSSM_CASE(2, RBW_) RSSM_CASE(4, RBW_) RSSM_CASE(8, RBW_)
+  RSSM_NCH(1) RSSM_NCH(2)
+#undef RSSM_NCH
 #undef RSSM_CASE
   return (int)hipErrorInvalidValue;
 }
 
-#define RSSM_WRAP(name, kern)                          \
-  template <int NCH, int RBW>                          \
-  struct name {                                        \
-    static constexpr auto fn = kern<NCH, RBW>;         \
+#define RSSM_WRAP(name, kern)                  \
+  template <int NCH, int RBW>                  \
+  struct name {                                \
+    static constexpr auto fn = kern<NCH, RBW>; \
   };
 RSSM_WRAP(StepK, m2_replay_step)
 RSSM_WRAP(FlushK, m2_flush)
@@ -547,19 +722,19 @@ RSSM_WRAP(SnapK, m2_snapshot_verify)
 }  // namespace
 
 int launch_m2_step(const M2StepArgs &a, hipStream_t st) {
-  return dispatch<StepK>(a, a.s.N, a.s.P, a.s.B, a.s.H, st);
+  return dispatch<StepK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
 }
 int launch_m2_flush(const M2FlushArgs &a, hipStream_t st) {
-  return dispatch<FlushK>(a, a.s.N, a.s.P, a.s.B, a.s.H, st);
+  return dispatch<FlushK>(a, a.s.N, a.s.P, a.s.B, a.s.H, false, st);
 }
 int launch_m2_verify(const M2VerifyArgs &a, hipStream_t st) {
-  return dispatch<VerifyK>(a, a.s.N, a.s.P, a.s.B, a.s.H, st);
+  return dispatch<VerifyK>(a, a.s.N, a.s.P, a.s.B, a.s.H, false, st);
 }
 int launch_m2_conv(const M2ConvArgs &a, hipStream_t st) {
-  return dispatch<ConvK>(a, a.s.N, a.s.P, a.s.B, a.s.H, st);
+  return dispatch<ConvK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
 }
 int launch_m2_snapshot(const M2SnapArgs &a, hipStream_t st) {
-  return dispatch<SnapK>(a, a.s.N, a.s.P, a.s.B, a.s.H, st);
+  return dispatch<SnapK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
 }
 
 }  // namespace rssm

@@ -18,7 +18,7 @@ int check_cfg(const replay_config *c) {
   if (c->heads % c->groups) return REPLAY_EINVAL;
   if (c->kind == REPLAY_KIND_GDN && c->groups != c->heads) return REPLAY_EINVAL;
   int waves, rbw;
-  if (!tile_geometry(c->head_dim, &waves, &rbw)) return REPLAY_EINVAL;
+  if (!tile_geometry(c->head_dim, true, &waves, &rbw)) return REPLAY_EINVAL;
   if (c->state_dim != 16 && c->state_dim != 32 && c->state_dim != 64 && c->state_dim != 128) return REPLAY_EINVAL;
   if (c->window < 1 || c->window > REPLAY_MAX_WINDOW) return REPLAY_EINVAL;
   if (c->max_draft < 0 || c->max_draft > c->window) return REPLAY_EINVAL;
@@ -35,7 +35,7 @@ int check_ctx(const replay_ctx *ctx) {
 }
 
 Shape shape_of(const replay_config &c) {
-  return Shape{c.batch, c.heads, c.groups, c.head_dim, c.state_dim, c.window};
+  return make_shape(c.batch, c.heads, c.groups, c.head_dim, c.state_dim, c.window);
 }
 
 PtrHalves halves(const replay_ctx &ctx) {

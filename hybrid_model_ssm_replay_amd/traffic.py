@@ -1,0 +1,103 @@
+"""Algorithmic HBM bytes of each decode call: what the method itself must move.
+
+Counts one read of every input byte the call needs and one write of every byte
+it must leave behind; caching, re-reads and work the method avoids are not
+counted.  Float32 throughout (4 bytes).  Per sequence, for one layer:
+
+Mamba-2 (x per head, B and C per group, dt per head; a ring record holds x, B, dt):
+  record_in  = (H P + 2 G N + H) 4        new token's x, B, C, dt
+  ring_rec   = (H P + G N + H) 4          one buffered record (C is not kept)
+  state      = H P N 4
+  non-fold step at window position m:     read  state + (m - 1) ring_rec + record_in
+                                          write ring_rec + y (H P 4)
+  fold (lazy, at the step that finds L records):  read  + L ring_rec, write + state
+Gated DeltaNet (q, k, v, alpha, beta per head; a ring record holds k, v, alpha, beta):
+  record_in  = H (2 dk + dv + 2) 4, ring_rec = H (dk + dv + 2) 4, state = H dv dk 4
+  (same structure).
+Conventional step: read state + record_in, write state + y.
+Replay verify of T drafts after c committed records: read state + c ring_rec +
+T record_in, write T ring_rec + T y (+ fold-first: L' ring_rec read, state written).
+Snapshot verify: read state + T record_in, write T states + T y.
+
+The checkpoint stream is read once per step and written once per window, against
+once read and once written per step for the conventional kernel [P1,
+Interpretation 2; P3, Interpretation 2].
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+E = 4  # bytes per float32
+
+
+@dataclass(frozen=True)
+class Layer:
+    kind: str
+    batch: int
+    heads: int
+    head_dim: int
+    state_dim: int
+    groups: int
+    window: int
+
+    @property
+    def state(self) -> int:
+        return self.heads * self.head_dim * self.state_dim * E
+
+    @property
+    def record_in(self) -> int:
+        H, P, N, G = self.heads, self.head_dim, self.state_dim, self.groups
+        if self.kind == "mamba2":
+            return (H * P + 2 * G * N + H) * E
+        return H * (2 * N + P + 2) * E
+
+    @property
+    def ring_rec(self) -> int:
+        H, P, N, G = self.heads, self.head_dim, self.state_dim, self.groups
+        if self.kind == "mamba2":
+            return (H * P + G * N + H) * E
+        return H * (N + P + 2) * E
+
+    @property
+    def y(self) -> int:
+        return self.heads * self.head_dim * E
+
+
+def replay_step_bytes(l: Layer, m: int, fold: bool) -> tuple[int, int]:
+    """(read, write) bytes of one step for the whole batch; m = window records after the append."""
+    rd = l.state + (m - 1) * l.ring_rec + l.record_in
+    wr = l.ring_rec + l.y
+    if fold:
+        rd += l.window * l.ring_rec
+        wr += l.state
+    return rd * l.batch, wr * l.batch
+
+
+def replay_window_mean(l: Layer) -> tuple[float, float]:
+    """Mean (read, write) bytes per step over a steady-state window of L steps.
+
+    In steady state the step that finds the window full folds it and then
+    starts the next window with m = 1; the other L - 1 steps have m = 2..L.
+    """
+    rd = wr = 0
+    for m in range(1, l.window + 1):
+        r, w = replay_step_bytes(l, m, fold=(m == 1))
+        rd += r
+        wr += w
+    return rd / l.window, wr / l.window
+
+
+def conventional_step_bytes(l: Layer) -> tuple[int, int]:
+    return (l.state + l.record_in) * l.batch, (l.state + l.y) * l.batch
+
+
+def replay_verify_bytes(l: Layer, T: int, committed: int, fold_first: bool) -> tuple[int, int]:
+    rd = l.state + committed * l.ring_rec + T * l.record_in
+    wr = T * l.ring_rec + T * l.y
+    if fold_first:
+        wr += l.state
+    return rd * l.batch, wr * l.batch
+
+
+def snapshot_verify_bytes(l: Layer, T: int) -> tuple[int, int]:
+    return (l.state + T * l.record_in) * l.batch, (T * l.state + T * l.y) * l.batch
