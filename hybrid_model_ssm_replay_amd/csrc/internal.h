@@ -21,8 +21,8 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 struct RingLayout {
   // Mamba-2: f0 = x [L][B][H][P] (slot-major: one step's appends form one
   //          contiguous block), f1 = B [B][G][2L][N], f2 = dt [B][H][L].
-  // GDN:     f0 = k [B][H][L][dk], f1 = v [B][H][L][dv], f2 = alpha [B][H][L],
-  //          f3 = beta [B][H][L].
+  // GDN:     f0 = k [L][B][H][dk], f1 = v [L][B][H][dv] (slot-major),
+  //          f2 = alpha [B][H][L], f3 = beta [B][H][L].
   size_t off[4];
   size_t bytes;
 };
@@ -121,7 +121,66 @@ struct M2SnapArgs {
   float *y;
 };
 
+// Gated DeltaNet ---------------------------------------------------------
+struct GdnRing {
+  float *k;      // [L][B][H][dk] (slot-major)
+  float *v;      // [L][B][H][dv] (slot-major)
+  float *alpha;  // [B][H][L]
+  float *beta;   // [B][H][L]
+};
+
+struct GdnStepArgs {
+  Shape s;  // P = d_v, N = d_k
+  float *ckpt;
+  GdnRing ring;
+  PtrHalves ptr;
+  int32_t *status;
+  const float *q, *k, *v, *alpha, *beta;  // this token: [B][H][dk], [B][H][dk], [B][H][dv], [B][H], [B][H]
+  float *y;                               // [B][H][dv]
+};
+
+struct GdnVerifyArgs {
+  Shape s;
+  int T;
+  float *ckpt;
+  GdnRing ring;
+  PtrHalves ptr;
+  int32_t *status;
+  const float *q, *k, *v, *alpha, *beta;  // drafts: [B][T][H][...]
+  float *y;                               // [B][T][H][dv]
+};
+
+struct GdnFlushArgs {
+  Shape s;
+  float *ckpt;
+  GdnRing ring;
+  PtrHalves ptr;
+  int32_t *status;
+  const uint8_t *mask;
+};
+
+struct GdnConvArgs {
+  Shape s;
+  float *state;  // [B][H][dv][dk]
+  const float *q, *k, *v, *alpha, *beta;
+  float *y;
+};
+
+struct GdnSnapArgs {
+  Shape s;
+  int T, nslots;
+  float *slots;  // [B][nslots][H][dv][dk]
+  const int32_t *cur;
+  const float *q, *k, *v, *alpha, *beta;  // drafts
+  float *y;
+};
+
 // Launchers (return a hipError_t value).
+int launch_gdn_step(const GdnStepArgs &a, hipStream_t st);
+int launch_gdn_verify(const GdnVerifyArgs &a, hipStream_t st);
+int launch_gdn_flush(const GdnFlushArgs &a, hipStream_t st);
+int launch_gdn_conv(const GdnConvArgs &a, hipStream_t st);
+int launch_gdn_snapshot(const GdnSnapArgs &a, hipStream_t st);
 int launch_m2_step(const M2StepArgs &a, hipStream_t st);
 int launch_m2_verify(const M2VerifyArgs &a, hipStream_t st);
 int launch_m2_flush(const M2FlushArgs &a, hipStream_t st);

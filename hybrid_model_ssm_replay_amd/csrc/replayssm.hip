@@ -23,6 +23,11 @@ int check_cfg(const replay_config *c) {
   if (c->window < 1 || c->window > REPLAY_MAX_WINDOW) return REPLAY_EINVAL;
   if (c->max_draft < 0 || c->max_draft > c->window) return REPLAY_EINVAL;
   if ((int64_t)c->batch * c->heads > 0x7fffffffLL) return REPLAY_EINVAL;
+  if (c->kind == REPLAY_KIND_GDN) {
+    // Four waves of 16 d_v rows x RBW per head; keys at least 32 wide.
+    if (c->head_dim != 64 && c->head_dim != 128) return REPLAY_EINVAL;
+    if (c->state_dim < 32) return REPLAY_EINVAL;
+  }
   if (c->ckpt_fmt < REPLAY_FMT_F32 || c->ckpt_fmt > REPLAY_FMT_F4E2M1_B16) return REPLAY_EINVAL;
   if (c->read_fmt < REPLAY_FMT_F32 || c->read_fmt > REPLAY_FMT_F4E2M1_B16) return REPLAY_EINVAL;
   if (!(c->ckpt_fmt == REPLAY_FMT_F32 && c->read_fmt == REPLAY_FMT_F32)) return REPLAY_ENOTSUP;
@@ -49,6 +54,13 @@ M2Ring m2_ring(const replay_ctx &ctx) {
   const RingLayout lay = ring_layout(ctx.cfg);
   char *base = (char *)ctx.buf.ring;
   return M2Ring{(float *)(base + lay.off[0]), (float *)(base + lay.off[1]), (float *)(base + lay.off[2])};
+}
+
+GdnRing gdn_ring(const replay_ctx &ctx) {
+  const RingLayout lay = ring_layout(ctx.cfg);
+  char *base = (char *)ctx.buf.ring;
+  return GdnRing{(float *)(base + lay.off[0]), (float *)(base + lay.off[1]), (float *)(base + lay.off[2]),
+                 (float *)(base + lay.off[3])};
 }
 
 int hip_status(int e) { return e == 0 ? REPLAY_OK : REPLAY_EHIP; }
@@ -153,7 +165,19 @@ int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *strea
     a.y = y;
     e = launch_m2_step(a, (hipStream_t)stream);
   } else {
-    return REPLAY_ENOTSUP;
+    GdnStepArgs a{};
+    a.s = shape_of(c);
+    a.ckpt = (float *)ctx->buf.ckpt;
+    a.ring = gdn_ring(*ctx);
+    a.ptr = halves(*ctx);
+    a.status = ctx->buf.status;
+    a.q = rec->f0;
+    a.k = rec->f1;
+    a.v = rec->f2;
+    a.alpha = rec->f3;
+    a.beta = rec->f4;
+    a.y = y;
+    e = launch_gdn_step(a, (hipStream_t)stream);
   }
   if (e) return REPLAY_EHIP;
   ctx->parity ^= 1;
@@ -176,7 +200,14 @@ int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream) {
     a.mask = seq_mask;
     e = launch_m2_flush(a, (hipStream_t)stream);
   } else {
-    return REPLAY_ENOTSUP;
+    GdnFlushArgs a{};
+    a.s = shape_of(c);
+    a.ckpt = (float *)ctx->buf.ckpt;
+    a.ring = gdn_ring(*ctx);
+    a.ptr = halves(*ctx);
+    a.status = ctx->buf.status;
+    a.mask = seq_mask;
+    e = launch_gdn_flush(a, (hipStream_t)stream);
   }
   if (e) return REPLAY_EHIP;
   ctx->parity ^= 1;
@@ -206,7 +237,20 @@ int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float
     a.y = y;
     e = launch_m2_verify(a, (hipStream_t)stream);
   } else {
-    return REPLAY_ENOTSUP;
+    GdnVerifyArgs a{};
+    a.s = shape_of(c);
+    a.T = T;
+    a.ckpt = (float *)ctx->buf.ckpt;
+    a.ring = gdn_ring(*ctx);
+    a.ptr = halves(*ctx);
+    a.status = ctx->buf.status;
+    a.q = drafts->f0;
+    a.k = drafts->f1;
+    a.v = drafts->f2;
+    a.alpha = drafts->f3;
+    a.beta = drafts->f4;
+    a.y = y;
+    e = launch_gdn_verify(a, (hipStream_t)stream);
   }
   if (e) return REPLAY_EHIP;
   ctx->parity ^= 1;
@@ -243,7 +287,16 @@ int replay_conv_step(const replay_config *cfg, float *state, const float *A, con
     a.y = y;
     return hip_status(launch_m2_conv(a, (hipStream_t)stream));
   }
-  return REPLAY_ENOTSUP;
+  GdnConvArgs a{};
+  a.s = shape_of(*cfg);
+  a.state = state;
+  a.q = rec->f0;
+  a.k = rec->f1;
+  a.v = rec->f2;
+  a.alpha = rec->f3;
+  a.beta = rec->f4;
+  a.y = y;
+  return hip_status(launch_gdn_conv(a, (hipStream_t)stream));
 }
 
 int replay_snapshot_verify(const replay_config *cfg, float *slots, const int32_t *cur, int32_t T,
@@ -270,7 +323,19 @@ int replay_snapshot_verify(const replay_config *cfg, float *slots, const int32_t
     a.y = y;
     return hip_status(launch_m2_snapshot(a, (hipStream_t)stream));
   }
-  return REPLAY_ENOTSUP;
+  GdnSnapArgs a{};
+  a.s = shape_of(*cfg);
+  a.T = T;
+  a.nslots = cfg->max_draft + 1;
+  a.slots = slots;
+  a.cur = cur;
+  a.q = drafts->f0;
+  a.k = drafts->f1;
+  a.v = drafts->f2;
+  a.alpha = drafts->f3;
+  a.beta = drafts->f4;
+  a.y = y;
+  return hip_status(launch_gdn_snapshot(a, (hipStream_t)stream));
 }
 
 int replay_snapshot_commit(const replay_config *cfg, int32_t *cur, const int32_t *accepted, int32_t T,
