@@ -27,8 +27,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["hybrid_model_ssm_replay_amd/csrc/mamba2.hip", "hybrid_model_ssm_replay_amd/csrc/common.h",
-                  "hybrid_model_ssm_replay_amd/csrc/internal.h"]
+KERNEL_SOURCES = ["hybrid_model_ssm_replay_amd/csrc/mamba2.hip", "hybrid_model_ssm_replay_amd/csrc/gdn.hip",
+                  "hybrid_model_ssm_replay_amd/csrc/common.h", "hybrid_model_ssm_replay_amd/csrc/internal.h"]
 
 
 def log(*a):
@@ -234,6 +234,24 @@ def main(argv=None):
             v = extra[f"verify_b512_T{T}"]
             v["replay_over_standard_step"] = v["replay_verify_commit_us"] / us_std
             v["snapshot_over_standard_step"] = v["snapshot_verify_commit_us"] / us_std
+
+    if not args.no_extra:
+        gname = "gdn_b256_h32_d128_l16"
+        gshape = WORKLOADS[gname]
+        log("gdn replay step", gname)
+        us_g = bench_replay(torch, gshape, 2, args.steps, args.warmup)
+        glay = Layer("gdn", gshape.batch, gshape.heads, gshape.head_dim, gshape.state_dim, gshape.groups,
+                     gshape.window)
+        grd, gwr = replay_window_mean(glay)
+        log("gdn conventional step", gname)
+        us_gc = bench_conv(torch, gshape, 2, args.steps, args.warmup)
+        gcrd, gcwr = conventional_step_bytes(glay)
+        extra["gdn_b256"] = {"replay_step_us": us_g, "replay_gbs": (grd + gwr) / us_g / 1e3,
+                             "replay_frac_of_peak": (grd + gwr) / us_g / 1e3 / HBM_PEAK_GBS,
+                             "replay_model_bytes_per_step": grd + gwr, "conventional_step_us": us_gc,
+                             "conventional_gbs": (gcrd + gcwr) / us_gc / 1e3, "speedup_vs_conventional": us_gc / us_g,
+                             "tokens_per_s": gshape.batch / us_g * 1e6,
+                             "traffic_bytes_per_launch": stored_traffic("gdn_replay_step_b256_traffic.txt")}
 
     traffic = stored_traffic("m2_replay_step_b256_traffic.txt")
     roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,

@@ -1,0 +1,77 @@
+"""Summaries of rocprofv3 output for the replay kernels.
+
+    python -m hybrid_model_ssm_replay_amd.rocprof_summary trace <kernel_trace.csv>
+    python -m hybrid_model_ssm_replay_amd.rocprof_summary traffic <fetch_counter_collection.csv> \
+        <write_counter_collection.csv> <kernel-substring>
+
+``trace`` prints the mean, min and max duration per kernel.  ``traffic`` prints
+FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the named kernel, calibrated
+against the library's HBM probe copy kernel, whose bytes are known: it reads and
+writes exactly the same number of bytes, so factor_read = WRITE_SIZE / FETCH_SIZE
+of the probe and factor_write = 1 when the probe's WRITE_SIZE equals the bytes
+it copies.  The calibrated traffic per launch is
+FETCH_SIZE * 1024 * factor_read + WRITE_SIZE * 1024 * factor_write.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import sys
+
+PROBE_COPY = "probe_copy_k"
+
+
+def _by_kernel(path: str, value_field: str):
+    d = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if value_field == "duration":
+            d[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        else:
+            d[r["Kernel_Name"]].append(float(r[value_field]))
+    return d
+
+
+def _find(d, sub):
+    keys = [k for k in d if sub in k]
+    if len(keys) != 1:
+        raise KeyError(f"{sub!r} matches {len(keys)} kernels: {keys}")
+    return keys[0]
+
+
+def trace(path: str) -> str:
+    d = _by_kernel(path, "duration")
+    lines = ["| kernel | dispatches | mean us | min us | max us |", "|---|---|---|---|---|"]
+    for k, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k[:90]}` | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
+    return "\n".join(lines)
+
+
+def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int | None = None) -> dict:
+    fe = _by_kernel(fetch_csv, "Counter_Value")
+    wr = _by_kernel(write_csv, "Counter_Value")
+    pk_f, pk_w = _find(fe, PROBE_COPY), _find(wr, PROBE_COPY)
+    probe_fetch = sum(fe[pk_f]) / len(fe[pk_f])
+    probe_write = sum(wr[pk_w]) / len(wr[pk_w])
+    f_w = 1.0 if copy_bytes is None else copy_bytes / (probe_write * 1024)
+    f_r = probe_write * f_w / probe_fetch
+    k_f, k_w = _find(fe, kernel), _find(wr, kernel)
+    kf = sum(fe[k_f]) / len(fe[k_f])
+    kw = sum(wr[k_w]) / len(wr[k_w])
+    return {"kernel": k_f, "dispatches": len(fe[k_f]), "fetch_kib": kf, "write_kib": kw,
+            "probe_fetch_kib": probe_fetch, "probe_write_kib": probe_write, "factor_read": f_r,
+            "factor_write": f_w, "traffic_bytes_per_launch": kf * 1024 * f_r + kw * 1024 * f_w}
+
+
+def main(argv):
+    if argv[0] == "trace":
+        print(trace(argv[1]))
+    elif argv[0] == "traffic":
+        r = traffic(argv[1], argv[2], argv[3], int(argv[4]) if len(argv) > 4 else None)
+        for k, v in r.items():
+            print(f"{k}: {v}")
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
