@@ -63,6 +63,7 @@ _SIG = {
     "replay_abi_sizeof": (ctypes.c_size_t, [ctypes.c_int]),
     "replay_init": (ctypes.c_int, [ctypes.POINTER(replay_ctx), ctypes.POINTER(replay_config),
                                    ctypes.POINTER(replay_buffers), _P]),
+    "replay_set_state": (ctypes.c_int, [ctypes.POINTER(replay_ctx), _P, _P]),
     "replay_step": (ctypes.c_int, [ctypes.POINTER(replay_ctx), ctypes.POINTER(replay_record), _P, _P]),
     "replay_flush": (ctypes.c_int, [ctypes.POINTER(replay_ctx), _P, _P]),
     "replay_verify": (ctypes.c_int, [ctypes.POINTER(replay_ctx), ctypes.c_int32, ctypes.POINTER(replay_record),
@@ -154,6 +155,10 @@ def replay_pointer_words(cfg) -> int:
 def replay_init(ctx: replay_ctx, cfg: replay_config, buf: replay_buffers, stream: int) -> None:
     _check("replay_init", load_library().replay_init(ctypes.byref(ctx), ctypes.byref(cfg), ctypes.byref(buf),
                                                      stream or None))
+
+
+def replay_set_state(ctx, state: int, stream: int) -> None:
+    _check("replay_set_state", load_library().replay_set_state(ctypes.byref(ctx), state, stream or None))
 
 
 def replay_step(ctx, rec: replay_record, y: int, stream: int) -> None:

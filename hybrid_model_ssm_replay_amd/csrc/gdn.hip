@@ -13,10 +13,14 @@
 // fold [P1, Synopsis; P2, paragraph 3; P3, Interpretation 2].
 //
 // Tile = one (sequence, head); four waves, each holding 16 RBW rows (d_v
-// indices) of S0 in registers in the layout shared with the Mamba-2 kernels:
-//     s[k][c] = S[16 (rb0 + k) + (l % 16)][16 c + 4 (l / 16) + 0..3].
+// indices) of S0 in registers:
+//     s[k][c] = S[16 (rb0 + k) + (l % 16)][col(c, q) + 0..3],  col(c, q) = 4 NCH q + 4 c,
+// q = l / 16: each lane owns 4 NCH contiguous columns of its rows, so that the
+// low-precision copies load as contiguous bytes and every 16-column scale block
+// of the e2m1 format lies inside one lane.  The same column permutation is
+// applied to keys and queries, so every contraction over d_k is unchanged.
 // Per wave, with X = the window's keys in MFMA operand layout (lane (j, q)
-// holds k_j[16 c + 4 q + 0..3], j = l % 16):
+// holds k_j[col(c, q) + 0..3], j = l % 16):
 //   * W = S0 X^T (one v_mfma_f32_16x16x4f32 pass: M = row, N = record, K = d_k),
 //   * the Gram matrix X X^T from the same operand registers,
 //   * S0 q and k_j . q on the VALU (q has its own registers),
@@ -24,6 +28,7 @@
 //     m x m forward substitution for it with no cross-lane traffic,
 //   * a fold is the transposed MFMA rank-m update S^T += K^T U~^T whose output
 //     layout equals the register layout of S0.
+#include "codecs.h"
 #include "internal.h"
 
 namespace rssm {
@@ -60,6 +65,12 @@ __device__ __forceinline__ float prefix_sum16(float v, int lane) {
   return t;
 }
 
+// First column of chunk c held by lane quarter q.
+template <int NCH>
+__device__ __forceinline__ int colq(int c, int q) {
+  return 4 * NCH * q + 4 * c;
+}
+
 template <int NCH, int RBW>
 __device__ __forceinline__ void load_rows_g(float4 (&s)[RBW][NCH], const float *S, int rb0, int lane) {
   constexpr int DK = 16 * NCH;
@@ -68,7 +79,7 @@ __device__ __forceinline__ void load_rows_g(float4 (&s)[RBW][NCH], const float *
   for (int k = 0; k < RBW; ++k) {
     const int row = (rb0 + k) * 16 + r16;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) s[k][c] = ld4(S + (size_t)row * DK + 16 * c + 4 * q);
+    for (int c = 0; c < NCH; ++c) s[k][c] = ld4(S + (size_t)row * DK + colq<NCH>(c, q));
   }
 }
 
@@ -80,9 +91,231 @@ __device__ __forceinline__ void store_rows_g(const float4 (&s)[RBW][NCH], float 
   for (int k = 0; k < RBW; ++k) {
     const int row = (rb0 + k) * 16 + r16;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) st4(S + (size_t)row * DK + 16 * c + 4 * q, s[k][c]);
+    for (int c = 0; c < NCH; ++c) st4(S + (size_t)row * DK + colq<NCH>(c, q), s[k][c]);
   }
 }
+
+// A vector (key or query) in the lane's column order.
+template <int NCH>
+__device__ __forceinline__ void load_vec(float4 (&v)[NCH], const float *p, int lane) {
+  const int q = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) v[c] = ld4(p + colq<NCH>(c, q));
+}
+
+// ---- state storage formats ------------------------------------------------------
+// Where one head's state lives: element offset `head` of the head tile, the
+// data array and, for e2m1, the scale array (one byte per 16 elements).
+struct StateBuf {
+  void *data;
+  uint8_t *scales;
+};
+
+// Counter and key of the stochastic-rounding bits of one fold: element e of
+// the head takes word e % 4 of Philox(e / 4, h, b, ckpt_pos) under the seed.
+struct SRKey {
+  uint32_t k0, k1, h, b, ckpt;
+};
+
+template <int FMT, int NCH, int RBW>
+struct SIO;
+
+template <int NCH, int RBW>
+struct SIO<REPLAY_FMT_F32, NCH, RBW> {
+  struct Raw {
+    float4 v[RBW][NCH];
+  };
+  static __device__ __forceinline__ void load(Raw &r, const StateBuf &b, size_t head, int rb0, int lane) {
+    load_rows_g<NCH, RBW>(r.v, (const float *)b.data + head, rb0, lane);
+  }
+  static __device__ __forceinline__ void decode(float4 (&s)[RBW][NCH], const Raw &r) {
+#pragma unroll
+    for (int k = 0; k < RBW; ++k)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) s[k][c] = r.v[k][c];
+  }
+  static __device__ __forceinline__ void store(const float4 (&s)[RBW][NCH], const StateBuf &b, size_t head, int rb0,
+                                               int lane, const SRKey &) {
+    store_rows_g<NCH, RBW>(s, (float *)b.data + head, rb0, lane);
+  }
+};
+
+template <int NCH, int RBW>
+struct SIO<REPLAY_FMT_F16_SR, NCH, RBW> {
+  static constexpr int DK = 16 * NCH;
+  struct Raw {
+    uint2 v[RBW][NCH];  // four halves per chunk
+  };
+  static __device__ __forceinline__ void load(Raw &r, const StateBuf &b, size_t head, int rb0, int lane) {
+    const __half *S = (const __half *)b.data + head;
+    const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      const int row = (rb0 + k) * 16 + r16;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) r.v[k][c] = *reinterpret_cast<const uint2 *>(S + (size_t)row * DK + colq<NCH>(c, q));
+    }
+  }
+  static __device__ __forceinline__ float h2f(uint32_t bits16) {
+    return __half2float(__ushort_as_half((unsigned short)bits16));
+  }
+  static __device__ __forceinline__ void decode(float4 (&s)[RBW][NCH], const Raw &r) {
+#pragma unroll
+    for (int k = 0; k < RBW; ++k)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint2 w = r.v[k][c];
+        s[k][c] = make_float4(h2f(w.x & 0xFFFF), h2f(w.x >> 16), h2f(w.y & 0xFFFF), h2f(w.y >> 16));
+      }
+  }
+  static __device__ __forceinline__ void store(const float4 (&s)[RBW][NCH], const StateBuf &b, size_t head, int rb0,
+                                               int lane, const SRKey &key) {
+    __half *S = (__half *)b.data + head;
+    const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      const int row = (rb0 + k) * 16 + r16;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t e4 = (uint32_t)((row * DK + colq<NCH>(c, q)) >> 2);
+        const Philox4 r = philox4x32_10(e4, key.h, key.b, key.ckpt, key.k0, key.k1);
+        const float4 v = s[k][c];
+        const uint32_t h0 = __half_as_ushort(__float2half(f16_sr(v.x, r.x >> 8)));
+        const uint32_t h1 = __half_as_ushort(__float2half(f16_sr(v.y, r.y >> 8)));
+        const uint32_t h2 = __half_as_ushort(__float2half(f16_sr(v.z, r.z >> 8)));
+        const uint32_t h3 = __half_as_ushort(__float2half(f16_sr(v.w, r.w >> 8)));
+        *reinterpret_cast<uint2 *>(S + (size_t)row * DK + colq<NCH>(c, q)) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      }
+    }
+  }
+};
+
+template <int NCH, int RBW>
+struct SIO<REPLAY_FMT_F8E4M3, NCH, RBW> {
+  static constexpr int DK = 16 * NCH;
+  struct Raw {
+    uint32_t v[RBW][NCH];  // four codes per chunk
+  };
+  static __device__ __forceinline__ void load(Raw &r, const StateBuf &b, size_t head, int rb0, int lane) {
+    const uint8_t *S = (const uint8_t *)b.data + head;
+    const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      const int row = (rb0 + k) * 16 + r16;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) r.v[k][c] = *reinterpret_cast<const uint32_t *>(S + (size_t)row * DK + colq<NCH>(c, q));
+    }
+  }
+  static __device__ __forceinline__ void decode(float4 (&s)[RBW][NCH], const Raw &r) {
+#pragma unroll
+    for (int k = 0; k < RBW; ++k)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(r.v[k][c], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(r.v[k][c], true);
+        s[k][c] = make_float4(lo[0], lo[1], hi[0], hi[1]);
+      }
+  }
+  static __device__ __forceinline__ void store(const float4 (&s)[RBW][NCH], const StateBuf &b, size_t head, int rb0,
+                                               int lane, const SRKey &) {
+    uint8_t *S = (uint8_t *)b.data + head;
+    const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      const int row = (rb0 + k) * 16 + r16;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const float4 v = s[k][c];
+        const uint32_t w = e4m3_encode(v.x) | (e4m3_encode(v.y) << 8) | (e4m3_encode(v.z) << 16) |
+                           (e4m3_encode(v.w) << 24);
+        *reinterpret_cast<uint32_t *>(S + (size_t)row * DK + colq<NCH>(c, q)) = w;
+      }
+    }
+  }
+};
+
+// e2m1 + e4m3 scale per 16: a lane's 4 NCH columns of a row are NCH / 4 whole
+// blocks (NCH = 4 or 8); codes are 2 NCH contiguous bytes, scales NCH / 4.
+template <int NCH, int RBW>
+struct SIO<REPLAY_FMT_F4E2M1_B16, NCH, RBW> {
+  static_assert(NCH == 4 || NCH == 8, "e2m1 blocks must not straddle lanes");
+  static constexpr int DK = 16 * NCH;
+  struct Raw {
+    uint32_t codes[RBW][NCH / 2];  // 8 codes per word
+    uint32_t scales[RBW];          // NCH / 4 scale bytes
+  };
+  static __device__ __forceinline__ void load(Raw &r, const StateBuf &b, size_t head, int rb0, int lane) {
+    const uint8_t *C = (const uint8_t *)b.data + head / 2;
+    const uint8_t *SC = b.scales + head / 16;
+    const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      const int row = (rb0 + k) * 16 + r16;
+      const uint8_t *rowc = C + ((size_t)row * DK + colq<NCH>(0, q)) / 2;
+#pragma unroll
+      for (int p = 0; p < NCH / 2; ++p) r.codes[k][p] = *reinterpret_cast<const uint32_t *>(rowc + 4 * p);
+      const uint8_t *rows = SC + ((size_t)row * DK + colq<NCH>(0, q)) / 16;
+      if constexpr (NCH == 8)
+        r.scales[k] = *reinterpret_cast<const uint16_t *>(rows);
+      else
+        r.scales[k] = *rows;
+    }
+  }
+  static __device__ __forceinline__ void decode(float4 (&s)[RBW][NCH], const Raw &r) {
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+#pragma unroll
+      for (int p = 0; p < NCH / 2; ++p) {
+        const float sc = e4m3_decode((r.scales[k] >> (8 * ((2 * p) / 4))) & 0xFF);
+        const float2 a = e2m1_pair<0>(r.codes[k][p]), bb = e2m1_pair<1>(r.codes[k][p]);
+        const float2 c2 = e2m1_pair<2>(r.codes[k][p]), d = e2m1_pair<3>(r.codes[k][p]);
+        s[k][2 * p] = make_float4(a.x * sc, a.y * sc, bb.x * sc, bb.y * sc);
+        s[k][2 * p + 1] = make_float4(c2.x * sc, c2.y * sc, d.x * sc, d.y * sc);
+      }
+    }
+  }
+  static __device__ __forceinline__ void store(const float4 (&s)[RBW][NCH], const StateBuf &b, size_t head, int rb0,
+                                               int lane, const SRKey &) {
+    uint8_t *C = (uint8_t *)b.data + head / 2;
+    uint8_t *SC = b.scales + head / 16;
+    const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      const int row = (rb0 + k) * 16 + r16;
+      uint8_t *rowc = C + ((size_t)row * DK + colq<NCH>(0, q)) / 2;
+      uint32_t scw = 0;
+#pragma unroll
+      for (int blk = 0; blk < NCH / 4; ++blk) {
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 4 * blk; c < 4 * blk + 4; ++c)
+          amax = fmaxf(amax, fmaxf(fmaxf(fabsf(s[k][c].x), fabsf(s[k][c].y)), fmaxf(fabsf(s[k][c].z), fabsf(s[k][c].w))));
+        const uint32_t scode = e4m3_encode(__fdiv_rn(amax, 6.f));
+        const float sc = e4m3_decode(scode);
+        scw |= scode << (8 * blk);
+#pragma unroll
+        for (int p = 2 * blk; p < 2 * blk + 2; ++p) {
+          uint32_t w = 0;
+          if (sc > 0.f) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const float4 v = s[k][2 * p + h2];
+              w |= (e2m1_code(v.x, sc) | (e2m1_code(v.y, sc) << 4) | (e2m1_code(v.z, sc) << 8) |
+                    (e2m1_code(v.w, sc) << 12))
+                   << (16 * h2);
+            }
+          }
+          *reinterpret_cast<uint32_t *>(rowc + 4 * p) = w;
+        }
+      }
+      uint8_t *rows = SC + ((size_t)row * DK + colq<NCH>(0, q)) / 16;
+      if constexpr (NCH == 8)
+        *reinterpret_cast<uint16_t *>(rows) = (uint16_t)scw;
+      else
+        *rows = (uint8_t)scw;
+    }
+  }
+};
 
 // The window of one wave: records 0..m-1 (keys in X, lane j's alpha_j, beta_j
 // in al/be, this lane's row of v_t in vr[t] for lanes < 16 RBW).
@@ -188,8 +421,8 @@ __device__ __forceinline__ float gdn_window(const float4 (&s)[RBW][NCH], const f
 
 // s <- e^{g_{cnt-1}} s + sum_t e^{g_{cnt-1} - g_t} u_t k_t^T for the cnt window
 // records, with u_t and the weights already in sm.U and sm.us (gdn_window with
-// want_u).  The MFMA A operand k_{4 st + q}[16 c + r16] is read from the ring
-// (cache-resident).
+// want_u).  The MFMA A operand (M = column of chunk c, K = record) is read from
+// the ring (cache-resident).
 template <int NCH, int RBW>
 __device__ __forceinline__ void gdn_fold_apply(float4 (&s)[RBW][NCH], int cnt, int s0, const float *rk, size_t ks,
                                                int L, float escale, GdnLds<RBW> &sm, int lane) {
@@ -202,7 +435,7 @@ __device__ __forceinline__ void gdn_fold_apply(float4 (&s)[RBW][NCH], int cnt, i
     const float *kr = rk + (size_t)wrap(s0, r < cnt ? r : cnt - 1, L) * ks;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const float v = kr[16 * c + r16];
+      const float v = kr[colq<NCH>(c, r16 >> 2) + (r16 & 3)];  // M = r16 in chunk c
       aK[c][st] = r < cnt ? v : 0.f;
     }
   }
@@ -250,7 +483,7 @@ __device__ __forceinline__ void load_keys(float4 (&X)[NCH], int cnt, int last, c
   const float *kj = (j == last) ? kin : rp.rk + (size_t)wrap(s0, j, L) * rp.ks;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const float4 v = ld4(kj + 16 * c + 4 * q);
+    const float4 v = ld4(kj + colq<NCH>(c, q));
     X[c] = r16 < cnt ? v : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
@@ -269,29 +502,43 @@ __device__ __forceinline__ void load_vrows(float (&vr)[16], int cnt, int last, c
   }
 }
 
+// State buffers of one launch: the checkpoint (format CF) and the read copy
+// (format RF; the same buffer when RF == CF).
+struct GdnStateBufs {
+  StateBuf ck, rd;
+  uint32_t seed_lo, seed_hi;
+};
+
+template <int CF, int RF, int NCH, int RBW>
+__device__ __forceinline__ void store_both(const float4 (&s)[RBW][NCH], const GdnStateBufs &sb, size_t head, int rb0,
+                                           int lane, uint32_t h, uint32_t b, uint32_t ckpt) {
+  const SRKey key{sb.seed_lo, sb.seed_hi, h, b, ckpt};
+  SIO<CF, NCH, RBW>::store(s, sb.ck, head, rb0, lane, key);
+  if constexpr (RF != CF) SIO<RF, NCH, RBW>::store(s, sb.rd, head, rb0, lane, key);
+}
+
 // ---- replay step ------------------------------------------------------------
-template <int NCH, int RBW>
-__global__ __launch_bounds__(256) void gdn_replay_step(GdnStepArgs a) {
+template <int CF, int RF, int NCH, int RBW>
+__global__ __launch_bounds__(256) void gdn_replay_step(GdnStepArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
   __shared__ GdnLds<RBW> lds_all[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  const int q = lane >> 4, r16 = lane & 15;
+  const int r16 = lane & 15;
   GdnLds<RBW> &sm = lds_all[wave];
   const Shape &sh = a.s;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int b = fdiv(tile, sh.fH), h = tile - b * sh.H;
   const int DV = sh.P, L = sh.L, rb0 = wave * RBW;
   const size_t bh = (size_t)b * sh.H + h;
-  float *S = a.ckpt + bh * DV * DK;
+  const size_t head = bh * DV * DK;
   const GdnRingPtrs rp = gdn_ring_ptrs(a.ring, sh, b, h);
   const float *qin = a.q + bh * DK, *kin = a.k + bh * DK, *vin = a.v + bh * DV;
 
-  // 1. Checkpoint rows first, then what needs no pointer.
-  float4 s[RBW][NCH];
-  load_rows_g<NCH, RBW>(s, S, rb0, lane);
+  // 1. The read copy first (a non-fold step reads only it), then what needs no pointer.
+  typename SIO<RF, NCH, RBW>::Raw raw;
+  SIO<RF, NCH, RBW>::load(raw, sb.rd, head, rb0, lane);
   float4 qv[NCH];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) qv[c] = ld4(qin + 16 * c + 4 * q);
+  load_vec<NCH>(qv, qin, lane);
   const float al_row = rp.ral[r16 < L ? r16 : 0], be_row = rp.rbe[r16 < L ? r16 : 0];
   const float al_in = a.alpha[bh], be_in = a.beta[bh];
 
@@ -309,28 +556,38 @@ __global__ __launch_bounds__(256) void gdn_replay_step(GdnStepArgs a) {
   const bool fold = count == L;
   const int s0 = fmod_(ck, sh.fL);
   const int slot = wrap(s0, count, L);  // this token's slot
-  int base = ck, sb = s0;
+  int base = ck, sb0 = s0;
+  float4 s[RBW][NCH];
   float4 X[NCH];
   float vr[16];
   if (fold) {
-    // Fold the full window (all records in the ring), store, restart the window.
+    // Fold the full window from the recurrence checkpoint, store both copies,
+    // and restart the window; this step's output comes from the fresh fp32 fold.
+    if constexpr (RF == CF) {
+      SIO<RF, NCH, RBW>::decode(s, raw);
+    } else {
+      typename SIO<CF, NCH, RBW>::Raw rc;
+      SIO<CF, NCH, RBW>::load(rc, sb.ck, head, rb0, lane);
+      SIO<CF, NCH, RBW>::decode(s, rc);
+    }
     load_keys<NCH>(X, L, -1, kin, rp, s0, L, lane);
     load_vrows<RBW>(vr, L, -1, vin, rp, s0, L, rb0, lane);
     const float al = __shfl(al_row, wrap(s0, r16, L), kWave), be = __shfl(be_row, wrap(s0, r16, L), kWave);
     gdn_window<NCH, RBW>(s, X, qv, L, al, be, vr, false, true, sm, lane);
-    float gl = sm.g[L - 1];
+    const float gl = sm.g[L - 1];
     gdn_fold_apply<NCH, RBW>(s, L, s0, rp.rk, rp.ks, L, __expf(gl), sm, lane);
-    store_rows_g<NCH, RBW>(s, S, rb0, lane);
+    store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
-    sb = slot;
+    sb0 = slot;
   }
   const int m = pos - base + 1;
-  load_keys<NCH>(X, m, m - 1, kin, rp, sb, L, lane);
-  load_vrows<RBW>(vr, m, m - 1, vin, rp, sb, L, rb0, lane);
+  load_keys<NCH>(X, m, m - 1, kin, rp, sb0, L, lane);
+  load_vrows<RBW>(vr, m, m - 1, vin, rp, sb0, L, rb0, lane);
+  if (!fold) SIO<RF, NCH, RBW>::decode(s, raw);  // after the ring loads in program order
   float al, be;
   {
     const int j = r16 < m - 1 ? r16 : 0;
-    const float a1 = __shfl(al_row, wrap(sb, j, L), kWave), b1 = __shfl(be_row, wrap(sb, j, L), kWave);
+    const float a1 = __shfl(al_row, wrap(sb0, j, L), kWave), b1 = __shfl(be_row, wrap(sb0, j, L), kWave);
     al = r16 < m - 1 ? a1 : (r16 == m - 1 ? al_in : 1.f);
     be = r16 < m - 1 ? b1 : (r16 == m - 1 ? be_in : 0.f);
   }
@@ -356,8 +613,8 @@ __global__ __launch_bounds__(256) void gdn_replay_step(GdnStepArgs a) {
 }
 
 // ---- explicit flush -------------------------------------------------------------
-template <int NCH, int RBW>
-__global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a) {
+template <int CF, int RF, int NCH, int RBW>
+__global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
   __shared__ GdnLds<RBW> lds_all[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -368,6 +625,7 @@ __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a) {
   const int b = fdiv(tile, sh.fH), h = tile - b * sh.H;
   const int DV = sh.P, L = sh.L, rb0 = wave * RBW;
   const size_t bh = (size_t)b * sh.H + h;
+  const size_t head = bh * DV * DK;
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
   const int count = pos - ck;
   const bool bad = count < 0 || count > L;
@@ -378,10 +636,13 @@ __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a) {
     a.ptr.ckpt_out[b] = fold ? pos : ck;
   }
   if (!fold) return;
-  float *S = a.ckpt + bh * DV * DK;
   const GdnRingPtrs rp = gdn_ring_ptrs(a.ring, sh, b, h);
   float4 s[RBW][NCH];
-  load_rows_g<NCH, RBW>(s, S, rb0, lane);
+  {
+    typename SIO<CF, NCH, RBW>::Raw rc;
+    SIO<CF, NCH, RBW>::load(rc, sb.ck, head, rb0, lane);
+    SIO<CF, NCH, RBW>::decode(s, rc);
+  }
   const int s0 = fmod_(ck, sh.fL);
   float4 X[NCH], qv[NCH];
 #pragma unroll
@@ -394,7 +655,7 @@ __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a) {
   gdn_window<NCH, RBW>(s, X, qv, count, al, be, vr, false, true, sm, lane);
   const float gl = sm.g[count - 1];
   gdn_fold_apply<NCH, RBW>(s, count, s0, rp.rk, rp.ks, L, __expf(gl), sm, lane);
-  store_rows_g<NCH, RBW>(s, S, rb0, lane);
+  store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
 }
 
 // ---- speculative verify ---------------------------------------------------------
@@ -402,9 +663,9 @@ __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a) {
 // forward substitution over all c + T records; draft i's output is
 //   o_i = e^{g_{c+i}} S0 q_i + sum_{j <= c+i} e^{g_{c+i} - g_j} (k_j . q_i) u_j.
 // S0 q_i is a second MFMA pass over the queries, k_j . q_i an MFMA of the key
-// and query operand registers.
-template <int NCH, int RBW>
-__global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a) {
+// and query operand registers.  Without a fold-first, S0 is the read copy.
+template <int CF, int RF, int NCH, int RBW>
+__global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
   __shared__ GdnLds<RBW> lds_all[4];
   __shared__ float SQ_all[4][16 * RBW][17];  // [row][draft]: S0 q_i
@@ -420,15 +681,15 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a) {
   const int b = fdiv(tile, sh.fH), h = tile - b * sh.H;
   const int DV = sh.P, L = sh.L, rb0 = wave * RBW, H = sh.H;
   const size_t bh = (size_t)b * H + h;
-  float *S = a.ckpt + bh * DV * DK;
+  const size_t head = bh * DV * DK;
   const GdnRingPtrs rp = gdn_ring_ptrs(a.ring, sh, b, h);
   auto dq_ = [&](int i) { return a.q + (((size_t)b * T + i) * H + h) * DK; };
   auto dk_ = [&](int i) { return a.k + (((size_t)b * T + i) * H + h) * DK; };
   auto dv_ = [&](int i) { return a.v + (((size_t)b * T + i) * H + h) * DV; };
   auto dsc = [&](const float *f, int i) { return f[((size_t)b * T + i) * H + h]; };
 
-  float4 s[RBW][NCH];
-  load_rows_g<NCH, RBW>(s, S, rb0, lane);
+  typename SIO<RF, NCH, RBW>::Raw raw;
+  SIO<RF, NCH, RBW>::load(raw, sb.rd, head, rb0, lane);
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
   const int count = pos - ck;
   if (count < 0 || count > L) {
@@ -441,12 +702,20 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a) {
   }
   const bool fold = count + T > L;  // implies count >= 1 because T <= L
   const int s0 = fmod_(ck, sh.fL);
-  int base = ck, sb = s0;
+  int base = ck, sb0 = s0;
+  float4 s[RBW][NCH];
   float4 X[NCH], Q[NCH];
   float vr[16];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) Q[c] = make_float4(0.f, 0.f, 0.f, 0.f);
   if (fold) {
+    if constexpr (RF == CF) {
+      SIO<RF, NCH, RBW>::decode(s, raw);
+    } else {
+      typename SIO<CF, NCH, RBW>::Raw rc;
+      SIO<CF, NCH, RBW>::load(rc, sb.ck, head, rb0, lane);
+      SIO<CF, NCH, RBW>::decode(s, rc);
+    }
     load_keys<NCH>(X, count, -1, nullptr, rp, s0, L, lane);
     load_vrows<RBW>(vr, count, -1, nullptr, rp, s0, L, rb0, lane);
     const int j = r16 < count ? r16 : 0;
@@ -454,24 +723,24 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a) {
     gdn_window<NCH, RBW>(s, X, Q, count, al, be, vr, false, true, sm, lane);
     const float gl = sm.g[count - 1];
     gdn_fold_apply<NCH, RBW>(s, count, s0, rp.rk, rp.ks, L, __expf(gl), sm, lane);
-    store_rows_g<NCH, RBW>(s, S, rb0, lane);
+    store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
-    sb = wrap(s0, count, L);
+    sb0 = wrap(s0, count, L);
   }
   const int c = pos - base, nrec = c + T;
   // Keys: committed records from the ring, drafts from the input.
   {
     const int j = r16 < nrec ? r16 : nrec - 1;
-    const float *kj = j < c ? rp.rk + (size_t)wrap(sb, j, L) * rp.ks : dk_(j - c);
+    const float *kj = j < c ? rp.rk + (size_t)wrap(sb0, j, L) * rp.ks : dk_(j - c);
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
-      const float4 v = ld4(kj + 16 * cc + 4 * q);
+      const float4 v = ld4(kj + colq<NCH>(cc, q));
       X[cc] = r16 < nrec ? v : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const int i = r16 < T ? r16 : T - 1;
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
-      const float4 v = ld4(dq_(i) + 16 * cc + 4 * q);
+      const float4 v = ld4(dq_(i) + colq<NCH>(cc, q));
       Q[cc] = r16 < T ? v : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
@@ -480,18 +749,19 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int tc = t < nrec ? t : nrec - 1;
-      const float v = tc < c ? rp.rv[(size_t)wrap(sb, tc, L) * rp.vs + row] : dv_(tc - c)[row];
+      const float v = tc < c ? rp.rv[(size_t)wrap(sb0, tc, L) * rp.vs + row] : dv_(tc - c)[row];
       vr[t] = t < nrec ? v : 0.f;
     }
   }
   float al, be;
   {
     const int j = r16 < nrec ? r16 : nrec - 1;
-    const float a1 = j < c ? rp.ral[wrap(sb, j, L)] : dsc(a.alpha, j - c);
-    const float b1 = j < c ? rp.rbe[wrap(sb, j, L)] : dsc(a.beta, j - c);
+    const float a1 = j < c ? rp.ral[wrap(sb0, j, L)] : dsc(a.alpha, j - c);
+    const float b1 = j < c ? rp.rbe[wrap(sb0, j, L)] : dsc(a.beta, j - c);
     al = r16 < nrec ? a1 : 1.f;
     be = r16 < nrec ? b1 : 0.f;
   }
+  if (!fold) SIO<RF, NCH, RBW>::decode(s, raw);
   // S0 Q^T and K Q^T on the MFMA, into per-wave LDS.
 #pragma unroll
   for (int k = 0; k < RBW; ++k) {
@@ -538,12 +808,12 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a) {
   // Stage the drafts in the ring after every wave is done with folded slots.
   __syncthreads();
   for (int i = 0; i < T; ++i) {
-    const int sl = wrap(sb, c + i, L);
+    const int sl = wrap(sb0, c + i, L);
     if (lane < 16 * RBW) rp.rv[(size_t)sl * rp.vs + rb0 * 16 + lane] = dv_(i)[rb0 * 16 + lane];
     for (int e = threadIdx.x; e < DK; e += 256) rp.rk[(size_t)sl * rp.ks + e] = dk_(i)[e];
   }
   if (threadIdx.x < T) {
-    const int sl = wrap(sb, c + threadIdx.x, L);
+    const int sl = wrap(sb0, c + threadIdx.x, L);
     rp.ral[sl] = dsc(a.alpha, threadIdx.x);
     rp.rbe[sl] = dsc(a.beta, threadIdx.x);
   }
@@ -551,6 +821,25 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a) {
     a.ptr.pos_out[b] = pos;
     a.ptr.ckpt_out[b] = base;
   }
+}
+
+// ---- state encode: a float32 state into both stored copies -------------------------
+// The stochastic-rounding counter uses each sequence's current ckpt_pos.
+template <int CF, int RF, int NCH, int RBW>
+__global__ __launch_bounds__(256) void gdn_encode_state(GdnEncodeArgs a, GdnStateBufs sb) {
+  constexpr int DK = 16 * NCH;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const Shape &sh = a.s;
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = fdiv(tile, sh.fH), h = tile - b * sh.H;
+  const int DV = sh.P, rb0 = wave * RBW;
+  const size_t head = ((size_t)b * sh.H + h) * DV * DK;
+  float4 s[RBW][NCH];
+  load_rows_g<NCH, RBW>(s, a.src + head, rb0, lane);
+  const uint32_t ckpt = (uint32_t)a.ckpt_pos[b];
+  const SRKey key{sb.seed_lo, sb.seed_hi, (uint32_t)h, (uint32_t)b, ckpt};
+  if (a.write_ckpt) SIO<CF, NCH, RBW>::store(s, sb.ck, head, rb0, lane, key);
+  if constexpr (RF != CF) SIO<RF, NCH, RBW>::store(s, sb.rd, head, rb0, lane, key);
 }
 
 // ---- baselines: conventional step and snapshot-per-draft verify ----------------
@@ -564,8 +853,8 @@ __device__ __forceinline__ void gdn_update_rows(float4 (&s)[RBW][NCH], const flo
   float4 kv[NCH], qv[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    kv[c] = ld4(kin + 16 * c + 4 * q);
-    qv[c] = ld4(qin + 16 * c + 4 * q);
+    kv[c] = ld4(kin + colq<NCH>(c, q));
+    qv[c] = ld4(qin + colq<NCH>(c, q));
   }
   float acc[RBW];
 #pragma unroll
@@ -635,10 +924,40 @@ __global__ __launch_bounds__(256) void gdn_snapshot_verify(GdnSnapArgs a) {
 }
 
 // ---- dispatch -----------------------------------------------------------------
-// All GDN kernels use the wave-per-row-block geometry with four waves per head:
-// RBW = d_v / 64 row blocks per wave (d_v in {64, 128}).
+// Four waves per head, RBW = d_v / 64 row blocks per wave (d_v in {64, 128}).
+// Format pairs (checkpoint, read copy): (f32, f32) for every d_k in {32, 64,
+// 128}; the low-precision pairs at d_k = 128.
+#define RSSM_FMT_PAIRS(X)                                                                           \
+  X(REPLAY_FMT_F32, REPLAY_FMT_F4E2M1_B16)                                                          \
+  X(REPLAY_FMT_F16_SR, REPLAY_FMT_F4E2M1_B16)                                                       \
+  X(REPLAY_FMT_F8E4M3, REPLAY_FMT_F4E2M1_B16)                                                       \
+  X(REPLAY_FMT_F4E2M1_B16, REPLAY_FMT_F4E2M1_B16)                                                   \
+  X(REPLAY_FMT_F16_SR, REPLAY_FMT_F16_SR)                                                           \
+  X(REPLAY_FMT_F8E4M3, REPLAY_FMT_F8E4M3)
+
+template <template <int, int, int, int> class K, typename Args>
+int gdn_dispatch(const Args &a, const GdnStateBufs &sb, int cf, int rf, hipStream_t st) {
+  const int DK = a.s.N, DV = a.s.P;
+  if (DV != 64 && DV != 128) return (int)hipErrorInvalidValue;
+  const int rbw = DV / 64;
+  const dim3 grid((unsigned)((size_t)a.s.B * a.s.H)), block(256);
+#define RSSM_CASE(CF_, RF_, NCH_, RBW_)                                             \
+  if (cf == CF_ && rf == RF_ && DK == 16 * NCH_ && rbw == RBW_) {                   \
+    hipLaunchKernelGGL((K<CF_, RF_, NCH_, RBW_>::fn), grid, block, 0, st, a, sb); \
+    return (int)hipGetLastError();                                                  \
+  }
+#define RSSM_F32(NCH_) RSSM_CASE(REPLAY_FMT_F32, REPLAY_FMT_F32, NCH_, 1) RSSM_CASE(REPLAY_FMT_F32, REPLAY_FMT_F32, NCH_, 2)
+  RSSM_F32(2) RSSM_F32(4) RSSM_F32(8)
+#define RSSM_Q(CF_, RF_) RSSM_CASE(CF_, RF_, 8, 1) RSSM_CASE(CF_, RF_, 8, 2)
+  RSSM_FMT_PAIRS(RSSM_Q)
+#undef RSSM_Q
+#undef RSSM_F32
+#undef RSSM_CASE
+  return (int)hipErrorInvalidValue;
+}
+
 template <template <int, int> class K, typename Args>
-int gdn_dispatch(const Args &a, hipStream_t st) {
+int gdn_dispatch_f32(const Args &a, hipStream_t st) {
   const int DK = a.s.N, DV = a.s.P;
   if (DV != 64 && DV != 128) return (int)hipErrorInvalidValue;
   const int rbw = DV / 64;
@@ -653,24 +972,49 @@ int gdn_dispatch(const Args &a, hipStream_t st) {
   return (int)hipErrorInvalidValue;
 }
 
+#define RSSM_WRAP4(name, kern)                           \
+  template <int CF, int RF, int NCH, int RBW>            \
+  struct name {                                          \
+    static constexpr auto fn = kern<CF, RF, NCH, RBW>;   \
+  };
+RSSM_WRAP4(GStepK, gdn_replay_step)
+RSSM_WRAP4(GFlushK, gdn_flush)
+RSSM_WRAP4(GVerifyK, gdn_replay_verify)
+RSSM_WRAP4(GEncodeK, gdn_encode_state)
+#undef RSSM_WRAP4
 #define RSSM_WRAP(name, kern)                  \
   template <int NCH, int RBW>                  \
   struct name {                                \
     static constexpr auto fn = kern<NCH, RBW>; \
   };
-RSSM_WRAP(GStepK, gdn_replay_step)
-RSSM_WRAP(GFlushK, gdn_flush)
-RSSM_WRAP(GVerifyK, gdn_replay_verify)
 RSSM_WRAP(GConvK, gdn_conv_step)
 RSSM_WRAP(GSnapK, gdn_snapshot_verify)
 #undef RSSM_WRAP
 
+GdnStateBufs state_bufs(const GdnFormatBufs &f) {
+  GdnStateBufs sb;
+  sb.ck = StateBuf{f.ckpt, f.ckpt_scales};
+  sb.rd = StateBuf{f.read, f.read_scales};
+  sb.seed_lo = (uint32_t)(f.seed & 0xFFFFFFFFu);
+  sb.seed_hi = (uint32_t)(f.seed >> 32);
+  return sb;
+}
+
 }  // namespace
 
-int launch_gdn_step(const GdnStepArgs &a, hipStream_t st) { return gdn_dispatch<GStepK>(a, st); }
-int launch_gdn_flush(const GdnFlushArgs &a, hipStream_t st) { return gdn_dispatch<GFlushK>(a, st); }
-int launch_gdn_verify(const GdnVerifyArgs &a, hipStream_t st) { return gdn_dispatch<GVerifyK>(a, st); }
-int launch_gdn_conv(const GdnConvArgs &a, hipStream_t st) { return gdn_dispatch<GConvK>(a, st); }
-int launch_gdn_snapshot(const GdnSnapArgs &a, hipStream_t st) { return gdn_dispatch<GSnapK>(a, st); }
+int launch_gdn_step(const GdnStepArgs &a, const GdnFormatBufs &f, hipStream_t st) {
+  return gdn_dispatch<GStepK>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
+}
+int launch_gdn_flush(const GdnFlushArgs &a, const GdnFormatBufs &f, hipStream_t st) {
+  return gdn_dispatch<GFlushK>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
+}
+int launch_gdn_verify(const GdnVerifyArgs &a, const GdnFormatBufs &f, hipStream_t st) {
+  return gdn_dispatch<GVerifyK>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
+}
+int launch_gdn_encode(const GdnEncodeArgs &a, const GdnFormatBufs &f, hipStream_t st) {
+  return gdn_dispatch<GEncodeK>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
+}
+int launch_gdn_conv(const GdnConvArgs &a, hipStream_t st) { return gdn_dispatch_f32<GConvK>(a, st); }
+int launch_gdn_snapshot(const GdnSnapArgs &a, hipStream_t st) { return gdn_dispatch_f32<GSnapK>(a, st); }
 
 }  // namespace rssm

@@ -131,7 +131,6 @@ struct GdnRing {
 
 struct GdnStepArgs {
   Shape s;  // P = d_v, N = d_k
-  float *ckpt;
   GdnRing ring;
   PtrHalves ptr;
   int32_t *status;
@@ -142,7 +141,6 @@ struct GdnStepArgs {
 struct GdnVerifyArgs {
   Shape s;
   int T;
-  float *ckpt;
   GdnRing ring;
   PtrHalves ptr;
   int32_t *status;
@@ -152,7 +150,6 @@ struct GdnVerifyArgs {
 
 struct GdnFlushArgs {
   Shape s;
-  float *ckpt;
   GdnRing ring;
   PtrHalves ptr;
   int32_t *status;
@@ -175,10 +172,41 @@ struct GdnSnapArgs {
   float *y;
 };
 
+// Stored copies of the GDN state: the checkpoint that carries the recurrence
+// (ckpt_fmt) and the copy non-fold steps read (read_fmt; the same storage when
+// the formats are equal).  e2m1 copies keep their scales after the codes.
+struct GdnFormatBufs {
+  int ckpt_fmt, read_fmt;
+  void *ckpt;
+  uint8_t *ckpt_scales;
+  void *read;
+  uint8_t *read_scales;
+  uint64_t seed;
+};
+
+struct GdnEncodeArgs {
+  Shape s;
+  const float *src;         // [B][H][dv][dk] float32 state
+  const int32_t *ckpt_pos;  // current ckpt_pos[B] (stochastic-rounding counter)
+  int write_ckpt;           // 0: write only the read copy
+};
+
+// Bytes of one stored copy of n elements, and where an e2m1 copy's scales start.
+inline size_t state_bytes(int fmt, size_t n) {
+  switch (fmt) {
+    case REPLAY_FMT_F32: return 4 * n;
+    case REPLAY_FMT_F16_SR: return 2 * n;
+    case REPLAY_FMT_F8E4M3: return n;
+    default: return align256(n / 2) + n / 16;
+  }
+}
+inline size_t e2m1_scale_offset(size_t n) { return align256(n / 2); }
+
 // Launchers (return a hipError_t value).
-int launch_gdn_step(const GdnStepArgs &a, hipStream_t st);
-int launch_gdn_verify(const GdnVerifyArgs &a, hipStream_t st);
-int launch_gdn_flush(const GdnFlushArgs &a, hipStream_t st);
+int launch_gdn_step(const GdnStepArgs &a, const GdnFormatBufs &f, hipStream_t st);
+int launch_gdn_verify(const GdnVerifyArgs &a, const GdnFormatBufs &f, hipStream_t st);
+int launch_gdn_flush(const GdnFlushArgs &a, const GdnFormatBufs &f, hipStream_t st);
+int launch_gdn_encode(const GdnEncodeArgs &a, const GdnFormatBufs &f, hipStream_t st);
 int launch_gdn_conv(const GdnConvArgs &a, hipStream_t st);
 int launch_gdn_snapshot(const GdnSnapArgs &a, hipStream_t st);
 int launch_m2_step(const M2StepArgs &a, hipStream_t st);

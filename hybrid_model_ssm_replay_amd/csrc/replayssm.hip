@@ -11,6 +11,8 @@ namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+size_t state_elems(const replay_config &c) { return (size_t)c.batch * c.heads * c.head_dim * c.state_dim; }
+
 int check_cfg(const replay_config *c) {
   if (!c) return REPLAY_EINVAL;
   if (c->kind != REPLAY_KIND_MAMBA2 && c->kind != REPLAY_KIND_GDN) return REPLAY_EINVAL;
@@ -30,7 +32,12 @@ int check_cfg(const replay_config *c) {
   }
   if (c->ckpt_fmt < REPLAY_FMT_F32 || c->ckpt_fmt > REPLAY_FMT_F4E2M1_B16) return REPLAY_EINVAL;
   if (c->read_fmt < REPLAY_FMT_F32 || c->read_fmt > REPLAY_FMT_F4E2M1_B16) return REPLAY_EINVAL;
-  if (!(c->ckpt_fmt == REPLAY_FMT_F32 && c->read_fmt == REPLAY_FMT_F32)) return REPLAY_ENOTSUP;
+  if (c->ckpt_fmt == REPLAY_FMT_F32 && c->read_fmt == REPLAY_FMT_F32) return REPLAY_OK;
+  // Low-precision copies: Gated DeltaNet with d_k = 128; the read copy is e2m1
+  // (split precision) or the checkpoint itself (one shared copy); an f32 read
+  // copy next to a lower-precision checkpoint is not a supported pair.
+  if (c->kind != REPLAY_KIND_GDN || c->state_dim != 128) return REPLAY_ENOTSUP;
+  if (c->read_fmt != c->ckpt_fmt && c->read_fmt != REPLAY_FMT_F4E2M1_B16) return REPLAY_ENOTSUP;
   return REPLAY_OK;
 }
 
@@ -63,6 +70,25 @@ GdnRing gdn_ring(const replay_ctx &ctx) {
                  (float *)(base + lay.off[3])};
 }
 
+GdnFormatBufs gdn_formats(const replay_ctx &ctx) {
+  const replay_config &c = ctx.cfg;
+  const size_t n = state_elems(c);
+  GdnFormatBufs f{};
+  f.ckpt_fmt = c.ckpt_fmt;
+  f.read_fmt = c.read_fmt;
+  f.seed = c.seed;
+  f.ckpt = ctx.buf.ckpt;
+  f.ckpt_scales = c.ckpt_fmt == REPLAY_FMT_F4E2M1_B16 ? (uint8_t *)ctx.buf.ckpt + e2m1_scale_offset(n) : nullptr;
+  if (c.read_fmt == c.ckpt_fmt) {
+    f.read = f.ckpt;
+    f.read_scales = f.ckpt_scales;
+  } else {
+    f.read = ctx.buf.read_copy;
+    f.read_scales = c.read_fmt == REPLAY_FMT_F4E2M1_B16 ? (uint8_t *)ctx.buf.read_copy + e2m1_scale_offset(n) : nullptr;
+  }
+  return f;
+}
+
 int hip_status(int e) { return e == 0 ? REPLAY_OK : REPLAY_EHIP; }
 
 bool rec_ok(const replay_record *r, int kind) {
@@ -79,12 +105,12 @@ int replay_validate_config(const replay_config *cfg) { return check_cfg(cfg); }
 
 size_t replay_ckpt_bytes(const replay_config *c) {
   if (check_cfg(c) != REPLAY_OK) return 0;
-  return (size_t)c->batch * c->heads * c->head_dim * c->state_dim * sizeof(float);
+  return state_bytes(c->ckpt_fmt, state_elems(*c));
 }
 
 size_t replay_read_copy_bytes(const replay_config *c) {
   if (check_cfg(c) != REPLAY_OK) return 0;
-  return 0;  // single F32 copy
+  return c->read_fmt == c->ckpt_fmt ? 0 : state_bytes(c->read_fmt, state_elems(*c));
 }
 
 size_t replay_ring_bytes(const replay_config *c) {
@@ -125,15 +151,43 @@ int replay_init(replay_ctx *ctx, const replay_config *cfg, const replay_buffers 
   if (!aligned16(buf->ckpt) || !aligned16(buf->ring) || ((uintptr_t)buf->ring & 255u)) return REPLAY_EINVAL;
   if (!aligned16(buf->pointers)) return REPLAY_EINVAL;
   if (cfg->kind == REPLAY_KIND_MAMBA2 && (!buf->A || !buf->D)) return REPLAY_EINVAL;
+  if (cfg->read_fmt != cfg->ckpt_fmt && (!buf->read_copy || ((uintptr_t)buf->read_copy & 255u))) return REPLAY_EINVAL;
+  if (((uintptr_t)buf->ckpt & 255u) && cfg->ckpt_fmt != REPLAY_FMT_F32) return REPLAY_EINVAL;
   memset(ctx, 0, sizeof(*ctx));
   ctx->cfg = *cfg;
   ctx->buf = *buf;
   ctx->parity = 0;
   ctx->t_pending = 0;
-  const int e = launch_init_pointers(buf->pointers, (int)replay_pointer_words(cfg), buf->status, (hipStream_t)stream);
+  int e = launch_init_pointers(buf->pointers, (int)replay_pointer_words(cfg), buf->status, (hipStream_t)stream);
   if (e) return REPLAY_EHIP;
+  if (cfg->kind == REPLAY_KIND_GDN && cfg->ckpt_fmt == REPLAY_FMT_F32 && cfg->read_fmt != REPLAY_FMT_F32) {
+    // The read copy starts as the encoding of the initial float32 checkpoint.
+    GdnEncodeArgs a{};
+    a.s = shape_of(*cfg);
+    a.src = (const float *)buf->ckpt;
+    a.ckpt_pos = buf->pointers;  // half 0: all zero after the init kernel
+    a.write_ckpt = 0;
+    e = launch_gdn_encode(a, gdn_formats(*ctx), (hipStream_t)stream);
+    if (e) return REPLAY_EHIP;
+  }
   ctx->magic = kCtxMagic;
   return REPLAY_OK;
+}
+
+int replay_set_state(replay_ctx *ctx, const float *state, void *stream) {
+  if (check_ctx(ctx) != REPLAY_OK || !state || !aligned16(state)) return REPLAY_EINVAL;
+  const replay_config &c = ctx->cfg;
+  if (c.kind == REPLAY_KIND_MAMBA2) {
+    const hipError_t e = hipMemcpyAsync(ctx->buf.ckpt, state, state_elems(c) * sizeof(float),
+                                        hipMemcpyDeviceToDevice, (hipStream_t)stream);
+    return e == hipSuccess ? REPLAY_OK : REPLAY_EHIP;
+  }
+  GdnEncodeArgs a{};
+  a.s = shape_of(c);
+  a.src = state;
+  a.ckpt_pos = halves(*ctx).ckpt_in;
+  a.write_ckpt = 1;
+  return hip_status(launch_gdn_encode(a, gdn_formats(*ctx), (hipStream_t)stream));
 }
 
 int replay_current_pointers(const replay_ctx *ctx, const int32_t **pos, const int32_t **ckpt_pos) {
@@ -167,7 +221,6 @@ int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *strea
   } else {
     GdnStepArgs a{};
     a.s = shape_of(c);
-    a.ckpt = (float *)ctx->buf.ckpt;
     a.ring = gdn_ring(*ctx);
     a.ptr = halves(*ctx);
     a.status = ctx->buf.status;
@@ -177,7 +230,7 @@ int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *strea
     a.alpha = rec->f3;
     a.beta = rec->f4;
     a.y = y;
-    e = launch_gdn_step(a, (hipStream_t)stream);
+    e = launch_gdn_step(a, gdn_formats(*ctx), (hipStream_t)stream);
   }
   if (e) return REPLAY_EHIP;
   ctx->parity ^= 1;
@@ -202,12 +255,11 @@ int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream) {
   } else {
     GdnFlushArgs a{};
     a.s = shape_of(c);
-    a.ckpt = (float *)ctx->buf.ckpt;
     a.ring = gdn_ring(*ctx);
     a.ptr = halves(*ctx);
     a.status = ctx->buf.status;
     a.mask = seq_mask;
-    e = launch_gdn_flush(a, (hipStream_t)stream);
+    e = launch_gdn_flush(a, gdn_formats(*ctx), (hipStream_t)stream);
   }
   if (e) return REPLAY_EHIP;
   ctx->parity ^= 1;
@@ -240,7 +292,6 @@ int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float
     GdnVerifyArgs a{};
     a.s = shape_of(c);
     a.T = T;
-    a.ckpt = (float *)ctx->buf.ckpt;
     a.ring = gdn_ring(*ctx);
     a.ptr = halves(*ctx);
     a.status = ctx->buf.status;
@@ -250,7 +301,7 @@ int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float
     a.alpha = drafts->f3;
     a.beta = drafts->f4;
     a.y = y;
-    e = launch_gdn_verify(a, (hipStream_t)stream);
+    e = launch_gdn_verify(a, gdn_formats(*ctx), (hipStream_t)stream);
   }
   if (e) return REPLAY_EHIP;
   ctx->parity ^= 1;

@@ -69,7 +69,7 @@ class ReplayLayer:
             raise B.ReplayError("replay_validate_config", rc)
         dev = torch.device(device)
         self.ckpt = torch.zeros(B.replay_ckpt_bytes(self.cfg), dtype=torch.uint8, device=dev)
-        if ckpt0 is not None:
+        if ckpt0 is not None and ckpt_fmt == B.FMT_F32:
             self.ckpt.view(torch.float32).copy_(torch.as_tensor(ckpt0, dtype=torch.float32).reshape(-1))
         rc_bytes = B.replay_read_copy_bytes(self.cfg)
         self.read_copy = torch.zeros(max(rc_bytes, 16), dtype=torch.uint8, device=dev) if rc_bytes else None
@@ -91,12 +91,26 @@ class ReplayLayer:
                                     self.D.data_ptr() if self.D is not None else None)
         self.ctx = B.replay_ctx()
         B.replay_init(self.ctx, self.cfg, self.buf, _stream())
+        if ckpt0 is not None and ckpt_fmt != B.FMT_F32:
+            self.set_state(torch.as_tensor(ckpt0, dtype=torch.float32).to(dev))
 
     # -- views ---------------------------------------------------------------
     @property
     def checkpoint(self) -> torch.Tensor:
+        """The float32 checkpoint (F32 checkpoint format only)."""
+        if self.cfg.ckpt_fmt != B.FMT_F32:
+            raise ValueError("the checkpoint is stored in a low-precision format; see stored_copies()")
         s = self.shapes
         return self.ckpt.view(torch.float32).view(s.batch, s.heads, s.head_dim, s.state_dim)
+
+    def stored_copies(self):
+        """Raw device bytes of (checkpoint, read copy or None), in their formats."""
+        return self.ckpt, self.read_copy
+
+    def set_state(self, state: torch.Tensor) -> None:
+        s = self.shapes
+        st = _dev_f32(state.contiguous(), (s.batch, s.heads, s.head_dim, s.state_dim), "state")
+        B.replay_set_state(self.ctx, st.data_ptr(), _stream())
 
     def pointers(self) -> tuple[torch.Tensor, torch.Tensor]:
         """(pos, ckpt_pos) device views of the current pointer half."""

@@ -80,8 +80,26 @@ extern "C" {
  *   ckpt_fmt    format of the checkpoint that carries the recurrence.
  *   read_fmt    format of the copy non-fold steps read; equal to ckpt_fmt
  *               means a single copy [P1, Interpretation 4; P3, Interpretation 3].
- *   seed        key of the stochastic-rounding generator.
- * Supported format pairs in this version: (F32, F32).
+ *   seed        key of the stochastic-rounding generator (Philox-4x32-10; the
+ *               fold that sets ckpt_pos of sequence b draws element e of head h
+ *               from word e % 4 of Philox(counter (e / 4, h, b, ckpt_pos),
+ *               key (seed low 32 bits, seed high 32 bits)), top 24 bits).
+ * Supported format pairs (ckpt_fmt, read_fmt): (F32, F32) for both families;
+ * for Gated DeltaNet with state_dim = 128 also (F32 | F16_SR | F8E4M3, F4E2M1_B16)
+ * (split precision) and (F16_SR, F16_SR), (F8E4M3, F8E4M3), (F4E2M1_B16,
+ * F4E2M1_B16) (one shared low-precision copy).  Other pairs: REPLAY_ENOTSUP.
+ *
+ * Storage formats, per element of [batch][heads][head_dim][state_dim]:
+ *   F32         float32.
+ *   F16_SR      IEEE binary16, written with stochastic rounding
+ *               RTZ16(x + sign(x) (r / 2^24) ulp16(|x|)), saturating at +-65504.
+ *   F8E4M3      OCP e4m3fn, round to nearest even, saturating at +-448.
+ *   F4E2M1_B16  4-bit e2m1 codes (two per byte, the even element in the low
+ *               nibble) followed, at the next 256-byte boundary, by one e4m3
+ *               scale byte per 16 consecutive state_dim elements:
+ *               s = e4m3(amax / 6); element codes round x / s to
+ *               {0, .5, 1, 1.5, 2, 3, 4, 6} (ties to the even code, clamped).
+ * An all-zero buffer is the zero state in every format.
  */
 typedef struct replay_config {
   int32_t kind;
@@ -99,10 +117,11 @@ typedef struct replay_config {
 
 /*
  * Device buffers of one layer, all allocated by the caller.
- *   ckpt       replay_ckpt_bytes(cfg) bytes.  F32 layout [batch][heads][head_dim][state_dim]
- *              (state_dim contiguous).  Its contents at replay_init are the
- *              initial state; afterwards it changes only at a fold.
- *   read_copy  replay_read_copy_bytes(cfg) bytes, or NULL when that is 0.
+ *   ckpt       replay_ckpt_bytes(cfg) bytes, layout [batch][heads][head_dim][state_dim]
+ *              (state_dim contiguous) in ckpt_fmt; 256-byte aligned unless F32.
+ *              It changes only at a fold (and replay_set_state).
+ *   read_copy  replay_read_copy_bytes(cfg) bytes (256-byte aligned), or NULL
+ *              when that is 0 (read_fmt == ckpt_fmt).
  *   ring       replay_ring_bytes(cfg) bytes; layout private to the library.
  *   pointers   replay_pointer_words(cfg) int32 words: two halves, each
  *              {pos[batch], ckpt_pos[batch]}; see replay_current_pointers().
@@ -167,8 +186,18 @@ size_t replay_abi_sizeof(int which);
 /* ---- the decode calls -------------------------------------------------- */
 
 /* Fill *ctx from cfg and buf, and enqueue: pos = ckpt_pos = 0 for every
- * sequence, status = 0.  The checkpoint buffer already holds the initial state. */
+ * sequence, status = 0.  The checkpoint buffer already holds the initial state
+ * in ckpt_fmt; with an F32 checkpoint and a separate read copy, the read copy
+ * is written from it here.  (For other formats load the state with
+ * replay_set_state, or start from all-zero buffers.) */
 int replay_init(replay_ctx *ctx, const replay_config *cfg, const replay_buffers *buf, void *stream);
+
+/* Replace the state of every sequence with the float32 `state`
+ * ([batch][heads][head_dim][state_dim], device), encoding it into the
+ * checkpoint and the read copy in their formats.  Pointers are unchanged: the
+ * state becomes the checkpoint at each sequence's ckpt_pos (call it with empty
+ * windows, e.g. right after replay_init or a full replay_flush). */
+int replay_set_state(replay_ctx *ctx, const float *state, void *stream);
 
 /* One decode token for every sequence [P1, Interpretation 2; P3, Interpretation 2]:
  * if a sequence's window is full (L records) it is first folded into the

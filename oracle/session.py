@@ -143,3 +143,120 @@ class ReplaySession:
         for b in np.nonzero(m & (self.ptr.count > 0))[0]:
             self._fold(b)
         return self.ptr.flush(m)
+
+
+# ---- split-precision state ---------------------------------------------------------
+FMT_F32, FMT_F16_SR, FMT_F8E4M3, FMT_F4E2M1_B16 = 0, 1, 2, 3
+
+
+def encode_state(S32, fmt, seed=0, b=0, ckpt_pos=0):
+    """Stored form of one sequence's float32 state [H, P, N] in `fmt`."""
+    from . import quant
+    S32 = np.asarray(S32, np.float32)
+    if fmt == FMT_F32:
+        return S32.copy()
+    if fmt == FMT_F16_SR:
+        H = S32.shape[0]
+        out = np.empty(S32.shape, np.float16)
+        for h in range(H):
+            r = quant.sr_bits(seed, b, h, ckpt_pos, S32[h].size).reshape(S32[h].shape)
+            out[h] = quant.fp16_sr(S32[h], r)
+        return out
+    if fmt == FMT_F8E4M3:
+        return quant.e4m3_encode(S32)
+    if fmt == FMT_F4E2M1_B16:
+        return quant.e2m1_block_encode(S32)
+    raise ValueError(fmt)
+
+
+def decode_state(stored, fmt):
+    from . import quant
+    if fmt == FMT_F32:
+        return np.asarray(stored, np.float64)
+    if fmt == FMT_F16_SR:
+        return np.asarray(stored, np.float64)
+    if fmt == FMT_F8E4M3:
+        return quant.e4m3_decode(stored).astype(np.float64)
+    return quant.e2m1_block_decode(*stored).astype(np.float64)
+
+
+class SplitReplaySession(ReplaySession):
+    """Replay with the checkpoint stored in ckpt_fmt (it carries the recurrence)
+    and a read copy in read_fmt (non-fold outputs read it); read_fmt == ckpt_fmt
+    is one shared copy.  The pages separate the two precisions so that the read
+    copy's rounding never re-enters the recurrence [P1, Interpretation 4; P3,
+    Interpretation 3].  Readings: a fold starts from the decoded recurrence copy,
+    folds in full precision, rounds to float32 and encodes both copies from that
+    float32 state; the output of a step or verify that folded first comes from
+    the fresh fold result, every other output from the decoded read copy plus
+    the buffered records (which are exact)."""
+
+    def __init__(self, kind, state0, window, params=None, ckpt_fmt=FMT_F32, read_fmt=FMT_F32, seed=0):
+        super().__init__(kind, state0, window, params)
+        self.cf, self.rf, self.seed = ckpt_fmt, read_fmt, seed
+        S32 = np.asarray(state0, np.float32)
+        B = S32.shape[0]
+        self.R = [encode_state(S32[b], ckpt_fmt, seed, b, 0) for b in range(B)]
+        self.Q = self.R if read_fmt == ckpt_fmt else [encode_state(S32[b], read_fmt, seed, b, 0) for b in range(B)]
+        self.fresh = {}                                  # sequence -> float64 fold result of this call
+
+    def read_state(self, b):
+        return decode_state(self.Q[b], self.rf)
+
+    def recurrence_state(self, b):
+        return decode_state(self.R[b], self.cf)
+
+    def _fold(self, b):
+        pos = int(self.ptr.pos[b])
+        S = self.k.fold(self.recurrence_state(b), self._window(b, pos))
+        S32 = S.astype(np.float32)
+        self.R[b] = encode_state(S32, self.cf, self.seed, b, pos)
+        if self.Q is not self.R:
+            self.Q[b] = encode_state(S32, self.rf, self.seed, b, pos)
+        self.fresh[b] = S
+        for p in [p for p in self.recs[b] if p < pos]:
+            del self.recs[b][p]
+
+    def _source(self, b):
+        return self.fresh[b] if b in self.fresh else self.read_state(b)
+
+    def step(self, rec):
+        self.fresh = {}
+        will_fold = self.ptr.count == self.ptr.L
+        for b in np.nonzero(will_fold)[0]:
+            self._fold(b)
+        pos_before = self.ptr.pos.copy()
+        self.ptr.step()
+        ys = []
+        for b in range(self.batch):
+            self.recs[b][int(pos_before[b])] = _rec_b(rec, b)
+            ys.append(self.k.output(self._source(b), self._window(b, int(self.ptr.pos[b]))))
+        self.fresh = {}
+        return np.stack(ys)
+
+    def verify(self, drafts):
+        self.fresh = {}
+        T = next(iter(drafts.values())).shape[1]
+        will_fold = self.ptr.count + T > self.ptr.L
+        for b in np.nonzero(will_fold)[0]:
+            self._fold(b)
+        self.ptr.verify(T)
+        out = []
+        for b in range(self.batch):
+            p0 = int(self.ptr.pos[b])
+            for i in range(T):
+                self.recs[b][p0 + i] = _draft_b(drafts, b, i)
+            committed = self._window(b, p0)
+            S0 = self._source(b)
+            out.append(np.stack([self.k.output(S0, committed + [self.recs[b][p0 + j] for j in range(i + 1)])
+                                 for i in range(T)]))
+        self.fresh = {}
+        return np.stack(out)
+
+    def flush(self, mask=None):
+        self.fresh = {}
+        m = np.ones(self.batch, bool) if mask is None else np.asarray(mask, bool)
+        for b in np.nonzero(m & (self.ptr.count > 0))[0]:
+            self._fold(b)
+        self.fresh = {}
+        return self.ptr.flush(m)
