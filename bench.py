@@ -156,6 +156,43 @@ def bench_probe(torch, nbytes=2 << 30):
     return nbytes / us_read / 1e3, 2 * half / us_copy / 1e3
 
 
+SPLIT_PAIRS = ((0, 0), (0, 3), (1, 3), (2, 3), (3, 3))
+FMT_NAMES = {0: "f32", 1: "f16sr", 2: "e4m3", 3: "e2m1"}
+
+
+def bench_split(torch, seed=5, layers=8, steps=64, warmup=32):
+    """Split-precision Gated DeltaNet layer (32 heads, d = 128, L = 16, batch 64).
+
+    `layers` independent layer instances are stepped in rotation, so that the
+    state is not served from the 256 MB Infinity Cache; reported per format pair
+    (checkpoint / read copy): microseconds per layer step and algorithmic GB/s
+    from the format-aware byte model.  (The accuracy of the same pairs against
+    the float64 oracle over 32768 steps is a GPU test, tests/test_gpu_split.py.)
+    """
+    from hybrid_model_ssm_replay_amd.layer import ReplayLayer
+    from hybrid_model_ssm_replay_amd.traffic import Layer, split_window_mean
+    from synth import WORKLOADS, InputStream
+    name = "gdn_b64_h32_d128_l16"
+    shape = WORKLOADS[name]
+    lm = Layer("gdn", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.groups, shape.window)
+    recs = dev_records(torch, InputStream(shape, seed), 16)
+    y = torch.empty((shape.batch, shape.heads, shape.head_dim), device="cuda")
+    out = {"workload": name, "layers_rotated": layers, "pairs": {}}
+    tm = Timer(torch)
+    for cf, rf in SPLIT_PAIRS:
+        lays = [ReplayLayer("gdn", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
+                            ckpt_fmt=cf, read_fmt=rf, seed=seed) for _ in range(layers)]
+        tm.run(lambda i: lays[i % layers].step(recs[(i // layers) % 16], y), warmup * layers)
+        us = tm.run(lambda i: lays[i % layers].step(recs[(i // layers) % 16], y), steps * layers)
+        rd, wr = split_window_mean(lm, cf, rf)
+        out["pairs"][f"{FMT_NAMES[cf]}/{FMT_NAMES[rf]}"] = {"us_per_step": us, "model_bytes_per_step": rd + wr,
+                                                          "gbs": (rd + wr) / us / 1e3,
+                                                          "frac_of_peak": (rd + wr) / us / 1e3 / HBM_PEAK_GBS}
+        del lays
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(shape, seed, budget_s=12.0):
     """The float64 stepwise oracle on a bounded sample of sequences, scaled to the full batch."""
     import numpy as np
@@ -252,6 +289,10 @@ def main(argv=None):
                              "conventional_gbs": (gcrd + gcwr) / us_gc / 1e3, "speedup_vs_conventional": us_gc / us_g,
                              "tokens_per_s": gshape.batch / us_g * 1e6,
                              "traffic_bytes_per_launch": stored_traffic("gdn_replay_step_b256_traffic.txt")}
+
+    if not args.no_extra:
+        log("split precision")
+        extra["gdn_split_b64"] = bench_split(torch)
 
     traffic = stored_traffic("m2_replay_step_b256_traffic.txt")
     roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,

@@ -29,6 +29,9 @@ from dataclasses import dataclass
 
 E = 4  # bytes per float32
 
+# Bytes per state element of each storage format (F32, F16_SR, F8E4M3, F4E2M1_B16).
+FORMAT_BYTES = {0: 4.0, 1: 2.0, 2: 1.0, 3: 0.5 + 1.0 / 16}
+
 
 @dataclass(frozen=True)
 class Layer:
@@ -85,6 +88,25 @@ def replay_window_mean(l: Layer) -> tuple[float, float]:
         rd += r
         wr += w
     return rd / l.window, wr / l.window
+
+
+def split_window_mean(l: Layer, ckpt_fmt: int, read_fmt: int) -> tuple[float, float]:
+    """Window-mean (read, write) bytes per step with a stored checkpoint in ckpt_fmt
+    and a read copy in read_fmt (the same copy when equal): non-fold steps read the
+    read copy; a fold reads the checkpoint and writes both copies."""
+    elems = l.heads * l.head_dim * l.state_dim
+    ck, rd = FORMAT_BYTES[ckpt_fmt] * elems, FORMAT_BYTES[read_fmt] * elems
+    rd_sum = wr_sum = 0.0
+    for m in range(1, l.window + 1):
+        fold = m == 1
+        r = (ck if fold else rd) + (m - 1) * l.ring_rec + l.record_in
+        w = l.ring_rec + l.y
+        if fold:
+            r += l.window * l.ring_rec
+            w += ck + (rd if read_fmt != ckpt_fmt else 0.0)
+        rd_sum += r * l.batch
+        wr_sum += w * l.batch
+    return rd_sum / l.window, wr_sum / l.window
 
 
 def conventional_step_bytes(l: Layer) -> tuple[int, int]:

@@ -149,3 +149,37 @@ class InputStream:
 def take_batch(rec: dict[str, np.ndarray], idx) -> dict[str, np.ndarray]:
     """Rows ``idx`` of every field (the sequences an oracle check samples)."""
     return {n: np.ascontiguousarray(a[idx]) for n, a in rec.items()}
+
+
+class DeviceInputStream:
+    """Seeded decode records generated on the GPU with torch, for long runs
+    (tens of thousands of steps) where host-side arrays would be too large.
+
+    Same distributions as InputStream; the random numbers come from a seeded
+    torch generator on the device, so the stream is reproducible but is not
+    the same stream as InputStream's.  Only Gated DeltaNet layers.
+    """
+
+    def __init__(self, shape: LayerShape, seed: int, device="cuda"):
+        import torch
+        if shape.kind != GDN:
+            raise ValueError("DeviceInputStream generates Gated DeltaNet records")
+        self.torch = torch
+        self.shape = shape
+        self.gen = torch.Generator(device=device)
+        self.gen.manual_seed(seed)
+        self.device = device
+
+    def record(self):
+        t, s = self.torch, self.shape
+        lead = (s.batch, s.heads)
+        n = lambda *shp: t.randn(*shp, generator=self.gen, device=self.device, dtype=t.float32)  # noqa: E731
+        q = n(*lead, s.state_dim)
+        k = n(*lead, s.state_dim)
+        q = q / t.linalg.vector_norm(q, dim=-1, keepdim=True)
+        k = k / t.linalg.vector_norm(k, dim=-1, keepdim=True)
+        v = n(*lead, s.head_dim)
+        alpha = t.exp(-0.1 * t.nn.functional.softplus(n(*lead)))
+        beta = t.sigmoid(n(*lead))
+        return {"q": q.contiguous(), "k": k.contiguous(), "v": v.contiguous(), "alpha": alpha.contiguous(),
+                "beta": beta.contiguous()}
