@@ -14,11 +14,12 @@
 //
 // Tile = one (sequence, head); four waves, each holding 16 RBW rows (d_v
 // indices) of S0 in registers:
-//     s[k][c] = S[16 (rb0 + k) + (l % 16)][col(c, q) + 0..3],  col(c, q) = 4 NCH q + 4 c,
-// q = l / 16: each lane owns 4 NCH contiguous columns of its rows, so that the
-// low-precision copies load as contiguous bytes and every 16-column scale block
-// of the e2m1 format lies inside one lane.  The same column permutation is
-// applied to keys and queries, so every contraction over d_k is unchanged.
+//     s[k][c] = S[16 (rb0 + k) + (l % 16)][col(c, q) + 0..3],  q = l / 16.
+// The column map col is a compile-time choice (colq below): interleaved
+// (16 c + 4 q) when the copies are float32, contiguous per lane (4 NCH q + 4 c)
+// when a low-precision copy is read, so that its bytes load wide and every
+// 16-column e2m1 scale block lies inside one lane.  Keys and queries use the
+// same map, so every contraction over d_k is unchanged.
 // Per wave, with X = the window's keys in MFMA operand layout (lane (j, q)
 // holds k_j[col(c, q) + 0..3], j = l % 16):
 //   * W = S0 X^T (one v_mfma_f32_16x16x4f32 pass: M = row, N = record, K = d_k),
@@ -65,13 +66,27 @@ __device__ __forceinline__ float prefix_sum16(float v, int lane) {
   return t;
 }
 
-// First column of chunk c held by lane quarter q.
-template <int NCH>
-__device__ __forceinline__ int colq(int c, int q) {
-  return 4 * NCH * q + 4 * c;
+// Column maps: which d_k columns lane quarter q holds in chunk c.
+//   kColIlv:    16 c + 4 q     (a chunk is 16 contiguous columns across the
+//                               quarters: each float32 load instruction covers
+//                               16 rows x 64 contiguous bytes);
+//   kColContig: 4 NCH q + 4 c  (a lane owns 4 NCH contiguous columns, so that
+//                               low-precision copies load as wide contiguous
+//                               bytes and e2m1 blocks of 16 lie inside a lane).
+constexpr int kColIlv = 0, kColContig = 1;
+
+// Interleaved when both stored copies are float32, contiguous otherwise.
+constexpr int col_map(int cf, int rf) {
+  return (cf == REPLAY_FMT_F32 && rf == REPLAY_FMT_F32) ? kColIlv : kColContig;
 }
 
-template <int NCH, int RBW>
+// First column of chunk c held by lane quarter q.
+template <int NCH, int CM>
+__device__ __forceinline__ int colq(int c, int q) {
+  return CM == kColContig ? 4 * NCH * q + 4 * c : 16 * c + 4 * q;
+}
+
+template <int NCH, int RBW, int CM>
 __device__ __forceinline__ void load_rows_g(float4 (&s)[RBW][NCH], const float *S, int rb0, int lane) {
   constexpr int DK = 16 * NCH;
   const int q = lane >> 4, r16 = lane & 15;
@@ -79,11 +94,11 @@ __device__ __forceinline__ void load_rows_g(float4 (&s)[RBW][NCH], const float *
   for (int k = 0; k < RBW; ++k) {
     const int row = (rb0 + k) * 16 + r16;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) s[k][c] = ld4(S + (size_t)row * DK + colq<NCH>(c, q));
+    for (int c = 0; c < NCH; ++c) s[k][c] = ld4(S + (size_t)row * DK + colq<NCH, CM>(c, q));
   }
 }
 
-template <int NCH, int RBW>
+template <int NCH, int RBW, int CM>
 __device__ __forceinline__ void store_rows_g(const float4 (&s)[RBW][NCH], float *S, int rb0, int lane) {
   constexpr int DK = 16 * NCH;
   const int q = lane >> 4, r16 = lane & 15;
@@ -91,16 +106,16 @@ __device__ __forceinline__ void store_rows_g(const float4 (&s)[RBW][NCH], float 
   for (int k = 0; k < RBW; ++k) {
     const int row = (rb0 + k) * 16 + r16;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) st4(S + (size_t)row * DK + colq<NCH>(c, q), s[k][c]);
+    for (int c = 0; c < NCH; ++c) st4(S + (size_t)row * DK + colq<NCH, CM>(c, q), s[k][c]);
   }
 }
 
 // A vector (key or query) in the lane's column order.
-template <int NCH>
+template <int NCH, int CM>
 __device__ __forceinline__ void load_vec(float4 (&v)[NCH], const float *p, int lane) {
   const int q = lane >> 4;
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) v[c] = ld4(p + colq<NCH>(c, q));
+  for (int c = 0; c < NCH; ++c) v[c] = ld4(p + colq<NCH, CM>(c, q));
 }
 
 // ---- state storage formats ------------------------------------------------------
@@ -117,16 +132,16 @@ struct SRKey {
   uint32_t k0, k1, h, b, ckpt;
 };
 
-template <int FMT, int NCH, int RBW>
+template <int FMT, int NCH, int RBW, int CM>
 struct SIO;
 
-template <int NCH, int RBW>
-struct SIO<REPLAY_FMT_F32, NCH, RBW> {
+template <int NCH, int RBW, int CM>
+struct SIO<REPLAY_FMT_F32, NCH, RBW, CM> {
   struct Raw {
     float4 v[RBW][NCH];
   };
   static __device__ __forceinline__ void load(Raw &r, const StateBuf &b, size_t head, int rb0, int lane) {
-    load_rows_g<NCH, RBW>(r.v, (const float *)b.data + head, rb0, lane);
+    load_rows_g<NCH, RBW, CM>(r.v, (const float *)b.data + head, rb0, lane);
   }
   static __device__ __forceinline__ void decode(float4 (&s)[RBW][NCH], const Raw &r) {
 #pragma unroll
@@ -136,12 +151,12 @@ struct SIO<REPLAY_FMT_F32, NCH, RBW> {
   }
   static __device__ __forceinline__ void store(const float4 (&s)[RBW][NCH], const StateBuf &b, size_t head, int rb0,
                                                int lane, const SRKey &) {
-    store_rows_g<NCH, RBW>(s, (float *)b.data + head, rb0, lane);
+    store_rows_g<NCH, RBW, CM>(s, (float *)b.data + head, rb0, lane);
   }
 };
 
-template <int NCH, int RBW>
-struct SIO<REPLAY_FMT_F16_SR, NCH, RBW> {
+template <int NCH, int RBW, int CM>
+struct SIO<REPLAY_FMT_F16_SR, NCH, RBW, CM> {
   static constexpr int DK = 16 * NCH;
   struct Raw {
     uint2 v[RBW][NCH];  // four halves per chunk
@@ -152,8 +167,19 @@ struct SIO<REPLAY_FMT_F16_SR, NCH, RBW> {
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
       const int row = (rb0 + k) * 16 + r16;
+      if constexpr (CM == kColContig && NCH % 2 == 0) {  // 8 NCH contiguous bytes: 16-byte loads
+        const uint4 *src = reinterpret_cast<const uint4 *>(S + (size_t)row * DK + colq<NCH, CM>(0, q));
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) r.v[k][c] = *reinterpret_cast<const uint2 *>(S + (size_t)row * DK + colq<NCH>(c, q));
+        for (int p = 0; p < NCH / 2; ++p) {
+          const uint4 w = src[p];
+          r.v[k][2 * p] = make_uint2(w.x, w.y);
+          r.v[k][2 * p + 1] = make_uint2(w.z, w.w);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          r.v[k][c] = *reinterpret_cast<const uint2 *>(S + (size_t)row * DK + colq<NCH, CM>(c, q));
+      }
     }
   }
   static __device__ __forceinline__ float h2f(uint32_t bits16) {
@@ -177,21 +203,21 @@ struct SIO<REPLAY_FMT_F16_SR, NCH, RBW> {
       const int row = (rb0 + k) * 16 + r16;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const uint32_t e4 = (uint32_t)((row * DK + colq<NCH>(c, q)) >> 2);
+        const uint32_t e4 = (uint32_t)((row * DK + colq<NCH, CM>(c, q)) >> 2);
         const Philox4 r = philox4x32_10(e4, key.h, key.b, key.ckpt, key.k0, key.k1);
         const float4 v = s[k][c];
         const uint32_t h0 = __half_as_ushort(__float2half(f16_sr(v.x, r.x >> 8)));
         const uint32_t h1 = __half_as_ushort(__float2half(f16_sr(v.y, r.y >> 8)));
         const uint32_t h2 = __half_as_ushort(__float2half(f16_sr(v.z, r.z >> 8)));
         const uint32_t h3 = __half_as_ushort(__float2half(f16_sr(v.w, r.w >> 8)));
-        *reinterpret_cast<uint2 *>(S + (size_t)row * DK + colq<NCH>(c, q)) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        *reinterpret_cast<uint2 *>(S + (size_t)row * DK + colq<NCH, CM>(c, q)) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
       }
     }
   }
 };
 
-template <int NCH, int RBW>
-struct SIO<REPLAY_FMT_F8E4M3, NCH, RBW> {
+template <int NCH, int RBW, int CM>
+struct SIO<REPLAY_FMT_F8E4M3, NCH, RBW, CM> {
   static constexpr int DK = 16 * NCH;
   struct Raw {
     uint32_t v[RBW][NCH];  // four codes per chunk
@@ -202,8 +228,21 @@ struct SIO<REPLAY_FMT_F8E4M3, NCH, RBW> {
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
       const int row = (rb0 + k) * 16 + r16;
+      if constexpr (CM == kColContig && NCH % 4 == 0) {  // 4 NCH contiguous bytes: 16-byte loads
+        const uint4 *src = reinterpret_cast<const uint4 *>(S + (size_t)row * DK + colq<NCH, CM>(0, q));
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) r.v[k][c] = *reinterpret_cast<const uint32_t *>(S + (size_t)row * DK + colq<NCH>(c, q));
+        for (int p = 0; p < NCH / 4; ++p) {
+          const uint4 w = src[p];
+          r.v[k][4 * p] = w.x;
+          r.v[k][4 * p + 1] = w.y;
+          r.v[k][4 * p + 2] = w.z;
+          r.v[k][4 * p + 3] = w.w;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          r.v[k][c] = *reinterpret_cast<const uint32_t *>(S + (size_t)row * DK + colq<NCH, CM>(c, q));
+      }
     }
   }
   static __device__ __forceinline__ void decode(float4 (&s)[RBW][NCH], const Raw &r) {
@@ -228,7 +267,7 @@ struct SIO<REPLAY_FMT_F8E4M3, NCH, RBW> {
         const float4 v = s[k][c];
         const uint32_t w = e4m3_encode(v.x) | (e4m3_encode(v.y) << 8) | (e4m3_encode(v.z) << 16) |
                            (e4m3_encode(v.w) << 24);
-        *reinterpret_cast<uint32_t *>(S + (size_t)row * DK + colq<NCH>(c, q)) = w;
+        *reinterpret_cast<uint32_t *>(S + (size_t)row * DK + colq<NCH, CM>(c, q)) = w;
       }
     }
   }
@@ -236,9 +275,10 @@ struct SIO<REPLAY_FMT_F8E4M3, NCH, RBW> {
 
 // e2m1 + e4m3 scale per 16: a lane's 4 NCH columns of a row are NCH / 4 whole
 // blocks (NCH = 4 or 8); codes are 2 NCH contiguous bytes, scales NCH / 4.
-template <int NCH, int RBW>
-struct SIO<REPLAY_FMT_F4E2M1_B16, NCH, RBW> {
+template <int NCH, int RBW, int CM>
+struct SIO<REPLAY_FMT_F4E2M1_B16, NCH, RBW, CM> {
   static_assert(NCH == 4 || NCH == 8, "e2m1 blocks must not straddle lanes");
+  static_assert(CM == kColContig, "e2m1 needs the contiguous column map");
   static constexpr int DK = 16 * NCH;
   struct Raw {
     uint32_t codes[RBW][NCH / 2];  // 8 codes per word
@@ -251,10 +291,19 @@ struct SIO<REPLAY_FMT_F4E2M1_B16, NCH, RBW> {
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
       const int row = (rb0 + k) * 16 + r16;
-      const uint8_t *rowc = C + ((size_t)row * DK + colq<NCH>(0, q)) / 2;
-#pragma unroll
-      for (int p = 0; p < NCH / 2; ++p) r.codes[k][p] = *reinterpret_cast<const uint32_t *>(rowc + 4 * p);
-      const uint8_t *rows = SC + ((size_t)row * DK + colq<NCH>(0, q)) / 16;
+      const uint8_t *rowc = C + ((size_t)row * DK + colq<NCH, CM>(0, q)) / 2;
+      if constexpr (NCH == 8) {  // 16 contiguous bytes of codes
+        const uint4 w = *reinterpret_cast<const uint4 *>(rowc);
+        r.codes[k][0] = w.x;
+        r.codes[k][1] = w.y;
+        r.codes[k][2] = w.z;
+        r.codes[k][3] = w.w;
+      } else {
+        const uint2 w = *reinterpret_cast<const uint2 *>(rowc);
+        r.codes[k][0] = w.x;
+        r.codes[k][1] = w.y;
+      }
+      const uint8_t *rows = SC + ((size_t)row * DK + colq<NCH, CM>(0, q)) / 16;
       if constexpr (NCH == 8)
         r.scales[k] = *reinterpret_cast<const uint16_t *>(rows);
       else
@@ -282,7 +331,7 @@ struct SIO<REPLAY_FMT_F4E2M1_B16, NCH, RBW> {
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
       const int row = (rb0 + k) * 16 + r16;
-      uint8_t *rowc = C + ((size_t)row * DK + colq<NCH>(0, q)) / 2;
+      uint8_t *rowc = C + ((size_t)row * DK + colq<NCH, CM>(0, q)) / 2;
       uint32_t scw = 0;
 #pragma unroll
       for (int blk = 0; blk < NCH / 4; ++blk) {
@@ -308,7 +357,7 @@ struct SIO<REPLAY_FMT_F4E2M1_B16, NCH, RBW> {
           *reinterpret_cast<uint32_t *>(rowc + 4 * p) = w;
         }
       }
-      uint8_t *rows = SC + ((size_t)row * DK + colq<NCH>(0, q)) / 16;
+      uint8_t *rows = SC + ((size_t)row * DK + colq<NCH, CM>(0, q)) / 16;
       if constexpr (NCH == 8)
         *reinterpret_cast<uint16_t *>(rows) = (uint16_t)scw;
       else
@@ -423,7 +472,7 @@ __device__ __forceinline__ float gdn_window(const float4 (&s)[RBW][NCH], const f
 // records, with u_t and the weights already in sm.U and sm.us (gdn_window with
 // want_u).  The MFMA A operand (M = column of chunk c, K = record) is read from
 // the ring (cache-resident).
-template <int NCH, int RBW>
+template <int NCH, int RBW, int CM>
 __device__ __forceinline__ void gdn_fold_apply(float4 (&s)[RBW][NCH], int cnt, int s0, const float *rk, size_t ks,
                                                int L, float escale, GdnLds<RBW> &sm, int lane) {
   const int q = lane >> 4, r16 = lane & 15;
@@ -435,7 +484,7 @@ __device__ __forceinline__ void gdn_fold_apply(float4 (&s)[RBW][NCH], int cnt, i
     const float *kr = rk + (size_t)wrap(s0, r < cnt ? r : cnt - 1, L) * ks;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const float v = kr[colq<NCH>(c, r16 >> 2) + (r16 & 3)];  // M = r16 in chunk c
+      const float v = kr[colq<NCH, CM>(c, r16 >> 2) + (r16 & 3)];  // M = r16 in chunk c
       aK[c][st] = r < cnt ? v : 0.f;
     }
   }
@@ -475,7 +524,7 @@ __device__ __forceinline__ GdnRingPtrs gdn_ring_ptrs(const GdnRing &r, const Sha
 // Keys of window records 0..cnt-1 at ring positions starting at slot s0, in
 // operand layout (zeros beyond cnt); the record at index `last` (if >= 0) is
 // taken from kin instead of the ring.
-template <int NCH>
+template <int NCH, int CM>
 __device__ __forceinline__ void load_keys(float4 (&X)[NCH], int cnt, int last, const float *kin, const GdnRingPtrs &rp,
                                           int s0, int L, int lane) {
   const int q = lane >> 4, r16 = lane & 15;
@@ -483,7 +532,7 @@ __device__ __forceinline__ void load_keys(float4 (&X)[NCH], int cnt, int last, c
   const float *kj = (j == last) ? kin : rp.rk + (size_t)wrap(s0, j, L) * rp.ks;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const float4 v = ld4(kj + colq<NCH>(c, q));
+    const float4 v = ld4(kj + colq<NCH, CM>(c, q));
     X[c] = r16 < cnt ? v : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
@@ -512,15 +561,17 @@ struct GdnStateBufs {
 template <int CF, int RF, int NCH, int RBW>
 __device__ __forceinline__ void store_both(const float4 (&s)[RBW][NCH], const GdnStateBufs &sb, size_t head, int rb0,
                                            int lane, uint32_t h, uint32_t b, uint32_t ckpt) {
+  constexpr int CM = col_map(CF, RF);
   const SRKey key{sb.seed_lo, sb.seed_hi, h, b, ckpt};
-  SIO<CF, NCH, RBW>::store(s, sb.ck, head, rb0, lane, key);
-  if constexpr (RF != CF) SIO<RF, NCH, RBW>::store(s, sb.rd, head, rb0, lane, key);
+  SIO<CF, NCH, RBW, CM>::store(s, sb.ck, head, rb0, lane, key);
+  if constexpr (RF != CF) SIO<RF, NCH, RBW, CM>::store(s, sb.rd, head, rb0, lane, key);
 }
 
 // ---- replay step ------------------------------------------------------------
 template <int CF, int RF, int NCH, int RBW>
 __global__ __launch_bounds__(256) void gdn_replay_step(GdnStepArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
+  constexpr int CM = col_map(CF, RF);
   __shared__ GdnLds<RBW> lds_all[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int r16 = lane & 15;
@@ -535,10 +586,10 @@ __global__ __launch_bounds__(256) void gdn_replay_step(GdnStepArgs a, GdnStateBu
   const float *qin = a.q + bh * DK, *kin = a.k + bh * DK, *vin = a.v + bh * DV;
 
   // 1. The read copy first (a non-fold step reads only it), then what needs no pointer.
-  typename SIO<RF, NCH, RBW>::Raw raw;
-  SIO<RF, NCH, RBW>::load(raw, sb.rd, head, rb0, lane);
+  typename SIO<RF, NCH, RBW, CM>::Raw raw;
+  SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
   float4 qv[NCH];
-  load_vec<NCH>(qv, qin, lane);
+  load_vec<NCH, CM>(qv, qin, lane);
   const float al_row = rp.ral[r16 < L ? r16 : 0], be_row = rp.rbe[r16 < L ? r16 : 0];
   const float al_in = a.alpha[bh], be_in = a.beta[bh];
 
@@ -564,26 +615,26 @@ __global__ __launch_bounds__(256) void gdn_replay_step(GdnStepArgs a, GdnStateBu
     // Fold the full window from the recurrence checkpoint, store both copies,
     // and restart the window; this step's output comes from the fresh fp32 fold.
     if constexpr (RF == CF) {
-      SIO<RF, NCH, RBW>::decode(s, raw);
+      SIO<RF, NCH, RBW, CM>::decode(s, raw);
     } else {
-      typename SIO<CF, NCH, RBW>::Raw rc;
-      SIO<CF, NCH, RBW>::load(rc, sb.ck, head, rb0, lane);
-      SIO<CF, NCH, RBW>::decode(s, rc);
+      typename SIO<CF, NCH, RBW, CM>::Raw rc;
+      SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
+      SIO<CF, NCH, RBW, CM>::decode(s, rc);
     }
-    load_keys<NCH>(X, L, -1, kin, rp, s0, L, lane);
+    load_keys<NCH, CM>(X, L, -1, kin, rp, s0, L, lane);
     load_vrows<RBW>(vr, L, -1, vin, rp, s0, L, rb0, lane);
     const float al = __shfl(al_row, wrap(s0, r16, L), kWave), be = __shfl(be_row, wrap(s0, r16, L), kWave);
     gdn_window<NCH, RBW>(s, X, qv, L, al, be, vr, false, true, sm, lane);
     const float gl = sm.g[L - 1];
-    gdn_fold_apply<NCH, RBW>(s, L, s0, rp.rk, rp.ks, L, __expf(gl), sm, lane);
+    gdn_fold_apply<NCH, RBW, CM>(s, L, s0, rp.rk, rp.ks, L, __expf(gl), sm, lane);
     store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
     sb0 = slot;
   }
   const int m = pos - base + 1;
-  load_keys<NCH>(X, m, m - 1, kin, rp, sb0, L, lane);
+  load_keys<NCH, CM>(X, m, m - 1, kin, rp, sb0, L, lane);
   load_vrows<RBW>(vr, m, m - 1, vin, rp, sb0, L, rb0, lane);
-  if (!fold) SIO<RF, NCH, RBW>::decode(s, raw);  // after the ring loads in program order
+  if (!fold) SIO<RF, NCH, RBW, CM>::decode(s, raw);  // after the ring loads in program order
   float al, be;
   {
     const int j = r16 < m - 1 ? r16 : 0;
@@ -616,6 +667,7 @@ __global__ __launch_bounds__(256) void gdn_replay_step(GdnStepArgs a, GdnStateBu
 template <int CF, int RF, int NCH, int RBW>
 __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
+  constexpr int CM = col_map(CF, RF);
   __shared__ GdnLds<RBW> lds_all[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
@@ -639,22 +691,22 @@ __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a, GdnStateBufs sb
   const GdnRingPtrs rp = gdn_ring_ptrs(a.ring, sh, b, h);
   float4 s[RBW][NCH];
   {
-    typename SIO<CF, NCH, RBW>::Raw rc;
-    SIO<CF, NCH, RBW>::load(rc, sb.ck, head, rb0, lane);
-    SIO<CF, NCH, RBW>::decode(s, rc);
+    typename SIO<CF, NCH, RBW, CM>::Raw rc;
+    SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
+    SIO<CF, NCH, RBW, CM>::decode(s, rc);
   }
   const int s0 = fmod_(ck, sh.fL);
   float4 X[NCH], qv[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) qv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
   float vr[16];
-  load_keys<NCH>(X, count, -1, nullptr, rp, s0, L, lane);
+  load_keys<NCH, CM>(X, count, -1, nullptr, rp, s0, L, lane);
   load_vrows<RBW>(vr, count, -1, nullptr, rp, s0, L, rb0, lane);
   const int j = r16 < count ? r16 : 0;
   const float al = rp.ral[wrap(s0, j, L)], be = rp.rbe[wrap(s0, j, L)];
   gdn_window<NCH, RBW>(s, X, qv, count, al, be, vr, false, true, sm, lane);
   const float gl = sm.g[count - 1];
-  gdn_fold_apply<NCH, RBW>(s, count, s0, rp.rk, rp.ks, L, __expf(gl), sm, lane);
+  gdn_fold_apply<NCH, RBW, CM>(s, count, s0, rp.rk, rp.ks, L, __expf(gl), sm, lane);
   store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
 }
 
@@ -667,6 +719,7 @@ __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a, GdnStateBufs sb
 template <int CF, int RF, int NCH, int RBW>
 __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
+  constexpr int CM = col_map(CF, RF);
   __shared__ GdnLds<RBW> lds_all[4];
   __shared__ float SQ_all[4][16 * RBW][17];  // [row][draft]: S0 q_i
   __shared__ float KQ_all[4][16][17];        // [record][draft]: k_j . q_i
@@ -688,8 +741,8 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
   auto dv_ = [&](int i) { return a.v + (((size_t)b * T + i) * H + h) * DV; };
   auto dsc = [&](const float *f, int i) { return f[((size_t)b * T + i) * H + h]; };
 
-  typename SIO<RF, NCH, RBW>::Raw raw;
-  SIO<RF, NCH, RBW>::load(raw, sb.rd, head, rb0, lane);
+  typename SIO<RF, NCH, RBW, CM>::Raw raw;
+  SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
   const int count = pos - ck;
   if (count < 0 || count > L) {
@@ -710,19 +763,19 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
   for (int c = 0; c < NCH; ++c) Q[c] = make_float4(0.f, 0.f, 0.f, 0.f);
   if (fold) {
     if constexpr (RF == CF) {
-      SIO<RF, NCH, RBW>::decode(s, raw);
+      SIO<RF, NCH, RBW, CM>::decode(s, raw);
     } else {
-      typename SIO<CF, NCH, RBW>::Raw rc;
-      SIO<CF, NCH, RBW>::load(rc, sb.ck, head, rb0, lane);
-      SIO<CF, NCH, RBW>::decode(s, rc);
+      typename SIO<CF, NCH, RBW, CM>::Raw rc;
+      SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
+      SIO<CF, NCH, RBW, CM>::decode(s, rc);
     }
-    load_keys<NCH>(X, count, -1, nullptr, rp, s0, L, lane);
+    load_keys<NCH, CM>(X, count, -1, nullptr, rp, s0, L, lane);
     load_vrows<RBW>(vr, count, -1, nullptr, rp, s0, L, rb0, lane);
     const int j = r16 < count ? r16 : 0;
     const float al = rp.ral[wrap(s0, j, L)], be = rp.rbe[wrap(s0, j, L)];
     gdn_window<NCH, RBW>(s, X, Q, count, al, be, vr, false, true, sm, lane);
     const float gl = sm.g[count - 1];
-    gdn_fold_apply<NCH, RBW>(s, count, s0, rp.rk, rp.ks, L, __expf(gl), sm, lane);
+    gdn_fold_apply<NCH, RBW, CM>(s, count, s0, rp.rk, rp.ks, L, __expf(gl), sm, lane);
     store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
     sb0 = wrap(s0, count, L);
@@ -734,13 +787,13 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
     const float *kj = j < c ? rp.rk + (size_t)wrap(sb0, j, L) * rp.ks : dk_(j - c);
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
-      const float4 v = ld4(kj + colq<NCH>(cc, q));
+      const float4 v = ld4(kj + colq<NCH, CM>(cc, q));
       X[cc] = r16 < nrec ? v : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const int i = r16 < T ? r16 : T - 1;
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
-      const float4 v = ld4(dq_(i) + colq<NCH>(cc, q));
+      const float4 v = ld4(dq_(i) + colq<NCH, CM>(cc, q));
       Q[cc] = r16 < T ? v : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
@@ -761,7 +814,7 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
     al = r16 < nrec ? a1 : 1.f;
     be = r16 < nrec ? b1 : 0.f;
   }
-  if (!fold) SIO<RF, NCH, RBW>::decode(s, raw);
+  if (!fold) SIO<RF, NCH, RBW, CM>::decode(s, raw);
   // S0 Q^T and K Q^T on the MFMA, into per-wave LDS.
 #pragma unroll
   for (int k = 0; k < RBW; ++k) {
@@ -828,6 +881,7 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
 template <int CF, int RF, int NCH, int RBW>
 __global__ __launch_bounds__(256) void gdn_encode_state(GdnEncodeArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
+  constexpr int CM = col_map(CF, RF);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const Shape &sh = a.s;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -835,11 +889,11 @@ __global__ __launch_bounds__(256) void gdn_encode_state(GdnEncodeArgs a, GdnStat
   const int DV = sh.P, rb0 = wave * RBW;
   const size_t head = ((size_t)b * sh.H + h) * DV * DK;
   float4 s[RBW][NCH];
-  load_rows_g<NCH, RBW>(s, a.src + head, rb0, lane);
+  load_rows_g<NCH, RBW, CM>(s, a.src + head, rb0, lane);
   const uint32_t ckpt = (uint32_t)a.ckpt_pos[b];
   const SRKey key{sb.seed_lo, sb.seed_hi, (uint32_t)h, (uint32_t)b, ckpt};
-  if (a.write_ckpt) SIO<CF, NCH, RBW>::store(s, sb.ck, head, rb0, lane, key);
-  if constexpr (RF != CF) SIO<RF, NCH, RBW>::store(s, sb.rd, head, rb0, lane, key);
+  if (a.write_ckpt) SIO<CF, NCH, RBW, CM>::store(s, sb.ck, head, rb0, lane, key);
+  if constexpr (RF != CF) SIO<RF, NCH, RBW, CM>::store(s, sb.rd, head, rb0, lane, key);
 }
 
 // ---- baselines: conventional step and snapshot-per-draft verify ----------------
@@ -849,12 +903,13 @@ template <int NCH, int RBW>
 __device__ __forceinline__ void gdn_update_rows(float4 (&s)[RBW][NCH], const float *qin, const float *kin,
                                                 const float *vin, float alpha, float beta, int rb0, int lane,
                                                 float *o_rows /* nullptr: no store */) {
+  constexpr int CM = kColIlv;
   const int q = lane >> 4, r16 = lane & 15;
   float4 kv[NCH], qv[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    kv[c] = ld4(kin + colq<NCH>(c, q));
-    qv[c] = ld4(qin + colq<NCH>(c, q));
+    kv[c] = ld4(kin + colq<NCH, CM>(c, q));
+    qv[c] = ld4(qin + colq<NCH, CM>(c, q));
   }
   float acc[RBW];
 #pragma unroll
@@ -896,10 +951,10 @@ __global__ __launch_bounds__(256) void gdn_conv_step(GdnConvArgs a) {
   const size_t bh = (size_t)b * sh.H + h;
   float *S = a.state + bh * DV * DK;
   float4 s[RBW][NCH];
-  load_rows_g<NCH, RBW>(s, S, rb0, lane);
+  load_rows_g<NCH, RBW, kColIlv>(s, S, rb0, lane);
   gdn_update_rows<NCH, RBW>(s, a.q + bh * DK, a.k + bh * DK, a.v + bh * DV, a.alpha[bh], a.beta[bh], rb0, lane,
                             a.y + bh * DV);
-  store_rows_g<NCH, RBW>(s, S, rb0, lane);
+  store_rows_g<NCH, RBW, kColIlv>(s, S, rb0, lane);
 }
 
 template <int NCH, int RBW>
@@ -914,12 +969,12 @@ __global__ __launch_bounds__(256) void gdn_snapshot_verify(GdnSnapArgs a) {
   if (cur < 0 || cur >= a.nslots) return;  // never index outside the slot array
   auto slot_ptr = [&](int sl) { return a.slots + (((size_t)b * a.nslots + sl) * H + h) * (size_t)DV * DK; };
   float4 s[RBW][NCH];
-  load_rows_g<NCH, RBW>(s, slot_ptr(cur), rb0, lane);
+  load_rows_g<NCH, RBW, kColIlv>(s, slot_ptr(cur), rb0, lane);
   for (int i = 0; i < T; ++i) {
     const size_t d = ((size_t)b * T + i) * H + h;
     gdn_update_rows<NCH, RBW>(s, a.q + d * DK, a.k + d * DK, a.v + d * DV, a.alpha[d], a.beta[d], rb0, lane,
                               a.y + d * DV);
-    store_rows_g<NCH, RBW>(s, slot_ptr((cur + 1 + i) % a.nslots), rb0, lane);
+    store_rows_g<NCH, RBW, kColIlv>(s, slot_ptr((cur + 1 + i) % a.nslots), rb0, lane);
   }
 }
 
