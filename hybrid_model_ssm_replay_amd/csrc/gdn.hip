@@ -12,6 +12,14 @@
 // One read of S0 serves the whole window; the checkpoint is written only by a
 // fold [P1, Synopsis; P2, paragraph 3; P3, Interpretation 2].
 //
+// The system is triangular, so u_t never changes once record t is appended:
+// the ring keeps u_t (next to k_t, alpha_t, beta_t) and a step solves one new
+// row.  A non-fold step is then a streaming pass over S0 for S0 k_m and S0 q_m
+// on the VALU.  A fold is the MFMA rank-m update S^T += K^T U~^T.  With a
+// separate read copy the cached u_t come from the read copy, so a fold
+// re-solves them from the checkpoint and the buffered values v_t (kept in the
+// ring for that purpose) with the full-window solve below.
+//
 // Tile = one (sequence, head); four waves, each holding 16 RBW rows (d_v
 // indices) of S0 in registers:
 //     s[k][c] = S[16 (rb0 + k) + (l % 16)][col(c, q) + 0..3],  q = l / 16.
@@ -20,15 +28,14 @@
 // when a low-precision copy is read, so that its bytes load wide and every
 // 16-column e2m1 scale block lies inside one lane.  Keys and queries use the
 // same map, so every contraction over d_k is unchanged.
-// Per wave, with X = the window's keys in MFMA operand layout (lane (j, q)
-// holds k_j[col(c, q) + 0..3], j = l % 16):
+// The full-window solve (verify, re-solving folds), per wave, with X = the
+// window's keys in MFMA operand layout (lane (j, q) holds k_j[col(c, q) + 0..3],
+// j = l % 16):
 //   * W = S0 X^T (one v_mfma_f32_16x16x4f32 pass: M = row, N = record, K = d_k),
 //   * the Gram matrix X X^T from the same operand registers,
-//   * S0 q and k_j . q on the VALU (q has its own registers),
 //   * W goes through per-wave LDS so that each lane owns one row and runs the
 //     m x m forward substitution for it with no cross-lane traffic,
-//   * a fold is the transposed MFMA rank-m update S^T += K^T U~^T whose output
-//     layout equals the register layout of S0.
+//   * the fold's MFMA output layout equals the register layout of S0.
 #include "codecs.h"
 #include "internal.h"
 
@@ -37,15 +44,13 @@ namespace {
 
 template <int RBW>
 struct GdnLds {
-  float W[16 * RBW][20];      // [row][record]: S0 k_j; column 16: S0 q
+  float W[16 * RBW][17];      // [row][record]: S0 k_j
   float gram[16][17];         // k_t . k_j
   float A[16][17];            // beta_t e^{g_t - g_j} (k_t . k_j) for j < t, else 0
   float c1[16], c2[16];       // beta_t, beta_t e^{g_t}
-  float dq[16];               // e^{g_m - g_j} (k_j . q)
   float us[16];               // e^{g_m - g_j}: pseudo-value weight in a fold
-  float kq[16];               // k_j . q
   float g[16], beta[16];
-  float U[16][16 * RBW + 4];  // pseudo-values u_t [record][row] (want_u)
+  float U[16][16 * RBW + 4];  // pseudo-values u_t [record][row]
 };
 
 // Program-order fence for LDS traffic between lanes of one wave.
@@ -132,6 +137,11 @@ struct SRKey {
   uint32_t k0, k1, h, b, ckpt;
 };
 
+// SIO<FMT, ...>: one wave's rows of one head in a storage format.
+//   Raw          the stored bits of the wave's rows, in registers;
+//   load/write   Raw <-> memory;
+//   decode       Raw -> float32 register tile (exact);
+//   encode       float32 register tile -> Raw (the format's rounding).
 template <int FMT, int NCH, int RBW, int CM>
 struct SIO;
 
@@ -149,15 +159,21 @@ struct SIO<REPLAY_FMT_F32, NCH, RBW, CM> {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) s[k][c] = r.v[k][c];
   }
-  static __device__ __forceinline__ void store(const float4 (&s)[RBW][NCH], const StateBuf &b, size_t head, int rb0,
-                                               int lane, const SRKey &) {
-    store_rows_g<NCH, RBW, CM>(s, (float *)b.data + head, rb0, lane);
+  static __device__ __forceinline__ void encode(Raw &r, const float4 (&s)[RBW][NCH], int, int, const SRKey &) {
+#pragma unroll
+    for (int k = 0; k < RBW; ++k)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) r.v[k][c] = s[k][c];
+  }
+  static __device__ __forceinline__ void write(const Raw &r, const StateBuf &b, size_t head, int rb0, int lane) {
+    store_rows_g<NCH, RBW, CM>(r.v, (float *)b.data + head, rb0, lane);
   }
 };
 
 template <int NCH, int RBW, int CM>
 struct SIO<REPLAY_FMT_F16_SR, NCH, RBW, CM> {
   static constexpr int DK = 16 * NCH;
+  static constexpr bool kWide = CM == kColContig && NCH % 2 == 0;  // 8 NCH contiguous bytes: 16-byte accesses
   struct Raw {
     uint2 v[RBW][NCH];  // four halves per chunk
   };
@@ -167,7 +183,7 @@ struct SIO<REPLAY_FMT_F16_SR, NCH, RBW, CM> {
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
       const int row = (rb0 + k) * 16 + r16;
-      if constexpr (CM == kColContig && NCH % 2 == 0) {  // 8 NCH contiguous bytes: 16-byte loads
+      if constexpr (kWide) {
         const uint4 *src = reinterpret_cast<const uint4 *>(S + (size_t)row * DK + colq<NCH, CM>(0, q));
 #pragma unroll
         for (int p = 0; p < NCH / 2; ++p) {
@@ -194,9 +210,8 @@ struct SIO<REPLAY_FMT_F16_SR, NCH, RBW, CM> {
         s[k][c] = make_float4(h2f(w.x & 0xFFFF), h2f(w.x >> 16), h2f(w.y & 0xFFFF), h2f(w.y >> 16));
       }
   }
-  static __device__ __forceinline__ void store(const float4 (&s)[RBW][NCH], const StateBuf &b, size_t head, int rb0,
-                                               int lane, const SRKey &key) {
-    __half *S = (__half *)b.data + head;
+  static __device__ __forceinline__ void encode(Raw &r, const float4 (&s)[RBW][NCH], int rb0, int lane,
+                                                const SRKey &key) {
     const int q = lane >> 4, r16 = lane & 15;
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
@@ -204,13 +219,30 @@ struct SIO<REPLAY_FMT_F16_SR, NCH, RBW, CM> {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const uint32_t e4 = (uint32_t)((row * DK + colq<NCH, CM>(c, q)) >> 2);
-        const Philox4 r = philox4x32_10(e4, key.h, key.b, key.ckpt, key.k0, key.k1);
+        const Philox4 rr = philox4x32_10(e4, key.h, key.b, key.ckpt, key.k0, key.k1);
         const float4 v = s[k][c];
-        const uint32_t h0 = __half_as_ushort(__float2half(f16_sr(v.x, r.x >> 8)));
-        const uint32_t h1 = __half_as_ushort(__float2half(f16_sr(v.y, r.y >> 8)));
-        const uint32_t h2 = __half_as_ushort(__float2half(f16_sr(v.z, r.z >> 8)));
-        const uint32_t h3 = __half_as_ushort(__float2half(f16_sr(v.w, r.w >> 8)));
-        *reinterpret_cast<uint2 *>(S + (size_t)row * DK + colq<NCH, CM>(c, q)) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        const uint32_t h0 = __half_as_ushort(__float2half(f16_sr(v.x, rr.x >> 8)));
+        const uint32_t h1 = __half_as_ushort(__float2half(f16_sr(v.y, rr.y >> 8)));
+        const uint32_t h2 = __half_as_ushort(__float2half(f16_sr(v.z, rr.z >> 8)));
+        const uint32_t h3 = __half_as_ushort(__float2half(f16_sr(v.w, rr.w >> 8)));
+        r.v[k][c] = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      }
+    }
+  }
+  static __device__ __forceinline__ void write(const Raw &r, const StateBuf &b, size_t head, int rb0, int lane) {
+    __half *S = (__half *)b.data + head;
+    const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      const int row = (rb0 + k) * 16 + r16;
+      if constexpr (kWide) {
+        uint4 *dst = reinterpret_cast<uint4 *>(S + (size_t)row * DK + colq<NCH, CM>(0, q));
+#pragma unroll
+        for (int p = 0; p < NCH / 2; ++p)
+          dst[p] = make_uint4(r.v[k][2 * p].x, r.v[k][2 * p].y, r.v[k][2 * p + 1].x, r.v[k][2 * p + 1].y);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) *reinterpret_cast<uint2 *>(S + (size_t)row * DK + colq<NCH, CM>(c, q)) = r.v[k][c];
       }
     }
   }
@@ -219,6 +251,7 @@ struct SIO<REPLAY_FMT_F16_SR, NCH, RBW, CM> {
 template <int NCH, int RBW, int CM>
 struct SIO<REPLAY_FMT_F8E4M3, NCH, RBW, CM> {
   static constexpr int DK = 16 * NCH;
+  static constexpr bool kWide = CM == kColContig && NCH % 4 == 0;  // 4 NCH contiguous bytes: 16-byte accesses
   struct Raw {
     uint32_t v[RBW][NCH];  // four codes per chunk
   };
@@ -228,7 +261,7 @@ struct SIO<REPLAY_FMT_F8E4M3, NCH, RBW, CM> {
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
       const int row = (rb0 + k) * 16 + r16;
-      if constexpr (CM == kColContig && NCH % 4 == 0) {  // 4 NCH contiguous bytes: 16-byte loads
+      if constexpr (kWide) {
         const uint4 *src = reinterpret_cast<const uint4 *>(S + (size_t)row * DK + colq<NCH, CM>(0, q));
 #pragma unroll
         for (int p = 0; p < NCH / 4; ++p) {
@@ -255,19 +288,29 @@ struct SIO<REPLAY_FMT_F8E4M3, NCH, RBW, CM> {
         s[k][c] = make_float4(lo[0], lo[1], hi[0], hi[1]);
       }
   }
-  static __device__ __forceinline__ void store(const float4 (&s)[RBW][NCH], const StateBuf &b, size_t head, int rb0,
-                                               int lane, const SRKey &) {
+  static __device__ __forceinline__ void encode(Raw &r, const float4 (&s)[RBW][NCH], int, int, const SRKey &) {
+#pragma unroll
+    for (int k = 0; k < RBW; ++k)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const float4 v = s[k][c];
+        r.v[k][c] = e4m3_encode(v.x) | (e4m3_encode(v.y) << 8) | (e4m3_encode(v.z) << 16) | (e4m3_encode(v.w) << 24);
+      }
+  }
+  static __device__ __forceinline__ void write(const Raw &r, const StateBuf &b, size_t head, int rb0, int lane) {
     uint8_t *S = (uint8_t *)b.data + head;
     const int q = lane >> 4, r16 = lane & 15;
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
       const int row = (rb0 + k) * 16 + r16;
+      if constexpr (kWide) {
+        uint4 *dst = reinterpret_cast<uint4 *>(S + (size_t)row * DK + colq<NCH, CM>(0, q));
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const float4 v = s[k][c];
-        const uint32_t w = e4m3_encode(v.x) | (e4m3_encode(v.y) << 8) | (e4m3_encode(v.z) << 16) |
-                           (e4m3_encode(v.w) << 24);
-        *reinterpret_cast<uint32_t *>(S + (size_t)row * DK + colq<NCH, CM>(c, q)) = w;
+        for (int p = 0; p < NCH / 4; ++p)
+          dst[p] = make_uint4(r.v[k][4 * p], r.v[k][4 * p + 1], r.v[k][4 * p + 2], r.v[k][4 * p + 3]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) *reinterpret_cast<uint32_t *>(S + (size_t)row * DK + colq<NCH, CM>(c, q)) = r.v[k][c];
       }
     }
   }
@@ -284,30 +327,28 @@ struct SIO<REPLAY_FMT_F4E2M1_B16, NCH, RBW, CM> {
     uint32_t codes[RBW][NCH / 2];  // 8 codes per word
     uint32_t scales[RBW];          // NCH / 4 scale bytes
   };
+  static __device__ __forceinline__ size_t row_elem(int rb0, int k, int lane) {
+    return (size_t)((rb0 + k) * 16 + (lane & 15)) * DK + colq<NCH, CM>(0, lane >> 4);
+  }
   static __device__ __forceinline__ void load(Raw &r, const StateBuf &b, size_t head, int rb0, int lane) {
     const uint8_t *C = (const uint8_t *)b.data + head / 2;
     const uint8_t *SC = b.scales + head / 16;
-    const int q = lane >> 4, r16 = lane & 15;
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
-      const int row = (rb0 + k) * 16 + r16;
-      const uint8_t *rowc = C + ((size_t)row * DK + colq<NCH, CM>(0, q)) / 2;
+      const size_t e = row_elem(rb0, k, lane);
       if constexpr (NCH == 8) {  // 16 contiguous bytes of codes
-        const uint4 w = *reinterpret_cast<const uint4 *>(rowc);
+        const uint4 w = *reinterpret_cast<const uint4 *>(C + e / 2);
         r.codes[k][0] = w.x;
         r.codes[k][1] = w.y;
         r.codes[k][2] = w.z;
         r.codes[k][3] = w.w;
+        r.scales[k] = *reinterpret_cast<const uint16_t *>(SC + e / 16);
       } else {
-        const uint2 w = *reinterpret_cast<const uint2 *>(rowc);
+        const uint2 w = *reinterpret_cast<const uint2 *>(C + e / 2);
         r.codes[k][0] = w.x;
         r.codes[k][1] = w.y;
+        r.scales[k] = SC[e / 16];
       }
-      const uint8_t *rows = SC + ((size_t)row * DK + colq<NCH, CM>(0, q)) / 16;
-      if constexpr (NCH == 8)
-        r.scales[k] = *reinterpret_cast<const uint16_t *>(rows);
-      else
-        r.scales[k] = *rows;
     }
   }
   static __device__ __forceinline__ void decode(float4 (&s)[RBW][NCH], const Raw &r) {
@@ -323,15 +364,9 @@ struct SIO<REPLAY_FMT_F4E2M1_B16, NCH, RBW, CM> {
       }
     }
   }
-  static __device__ __forceinline__ void store(const float4 (&s)[RBW][NCH], const StateBuf &b, size_t head, int rb0,
-                                               int lane, const SRKey &) {
-    uint8_t *C = (uint8_t *)b.data + head / 2;
-    uint8_t *SC = b.scales + head / 16;
-    const int q = lane >> 4, r16 = lane & 15;
+  static __device__ __forceinline__ void encode(Raw &r, const float4 (&s)[RBW][NCH], int, int, const SRKey &) {
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
-      const int row = (rb0 + k) * 16 + r16;
-      uint8_t *rowc = C + ((size_t)row * DK + colq<NCH, CM>(0, q)) / 2;
       uint32_t scw = 0;
 #pragma unroll
       for (int blk = 0; blk < NCH / 4; ++blk) {
@@ -354,31 +389,67 @@ struct SIO<REPLAY_FMT_F4E2M1_B16, NCH, RBW, CM> {
                    << (16 * h2);
             }
           }
-          *reinterpret_cast<uint32_t *>(rowc + 4 * p) = w;
+          r.codes[k][p] = w;
         }
       }
-      uint8_t *rows = SC + ((size_t)row * DK + colq<NCH, CM>(0, q)) / 16;
-      if constexpr (NCH == 8)
-        *reinterpret_cast<uint16_t *>(rows) = (uint16_t)scw;
-      else
-        *rows = (uint8_t)scw;
+      r.scales[k] = scw;
+    }
+  }
+  static __device__ __forceinline__ void write(const Raw &r, const StateBuf &b, size_t head, int rb0, int lane) {
+    uint8_t *C = (uint8_t *)b.data + head / 2;
+    uint8_t *SC = b.scales + head / 16;
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      const size_t e = row_elem(rb0, k, lane);
+      if constexpr (NCH == 8) {
+        *reinterpret_cast<uint4 *>(C + e / 2) = make_uint4(r.codes[k][0], r.codes[k][1], r.codes[k][2], r.codes[k][3]);
+        *reinterpret_cast<uint16_t *>(SC + e / 16) = (uint16_t)r.scales[k];
+      } else {
+        *reinterpret_cast<uint2 *>(C + e / 2) = make_uint2(r.codes[k][0], r.codes[k][1]);
+        SC[e / 16] = (uint8_t)r.scales[k];
+      }
     }
   }
 };
 
+// State buffers of one launch: the checkpoint (format CF) and the read copy
+// (format RF; the same buffer when RF == CF).
+struct GdnStateBufs {
+  StateBuf ck, rd;
+  uint32_t seed_lo, seed_hi;
+};
+
+// Encode the tile s into the checkpoint and (if separate) the read copy, and
+// leave in s what the read copy now holds, decoded: the S0 of the window that
+// starts here.
+template <int CF, int RF, int NCH, int RBW>
+__device__ __forceinline__ void store_both(float4 (&s)[RBW][NCH], const GdnStateBufs &sb, size_t head, int rb0,
+                                           int lane, uint32_t h, uint32_t b, uint32_t ckpt) {
+  constexpr int CM = col_map(CF, RF);
+  const SRKey key{sb.seed_lo, sb.seed_hi, h, b, ckpt};
+  typename SIO<CF, NCH, RBW, CM>::Raw rc;
+  SIO<CF, NCH, RBW, CM>::encode(rc, s, rb0, lane, key);
+  SIO<CF, NCH, RBW, CM>::write(rc, sb.ck, head, rb0, lane);
+  if constexpr (RF != CF) {
+    typename SIO<RF, NCH, RBW, CM>::Raw rr;
+    SIO<RF, NCH, RBW, CM>::encode(rr, s, rb0, lane, key);
+    SIO<RF, NCH, RBW, CM>::write(rr, sb.rd, head, rb0, lane);
+    SIO<RF, NCH, RBW, CM>::decode(s, rr);
+  } else if constexpr (CF != REPLAY_FMT_F32) {
+    SIO<CF, NCH, RBW, CM>::decode(s, rc);
+  }
+}
+
 // The window of one wave: records 0..m-1 (keys in X, lane j's alpha_j, beta_j
-// in al/be, this lane's row of v_t in vr[t] for lanes < 16 RBW).
-// Computes the pseudo-values of every record for the wave's rows, and
-//   want_o: the newest output o_{m-1} for row `lane` (lanes < 16 RBW), using q (qv);
-//   want_u: the pseudo-values u_t in sm.U[t][row] (their fold weights in sm.us).
-// Returns the output (or 0).
+// in al/be).  For t < known, vr[t] is this lane's row of the already known
+// pseudo-value u_t; for known <= t < m it is the row of v_t (lanes < 16 RBW).
+// Solves for the remaining pseudo-values and leaves every u_t in sm.U[t][row],
+// the decay prefix g in sm.g and the fold weights e^{g_{m-1} - g_t} in sm.us.
 template <int NCH, int RBW>
-__device__ __forceinline__ float gdn_window(const float4 (&s)[RBW][NCH], const float4 (&X)[NCH],
-                                            const float4 (&qv)[NCH], int m, float al, float be,
-                                            const float (&vr)[16], bool want_o, bool want_u, GdnLds<RBW> &sm,
-                                            int lane) {
+__device__ __forceinline__ void gdn_window(const float4 (&s)[RBW][NCH], const float4 (&X)[NCH], int m, int known,
+                                           float al, float be, const float (&vr)[16], GdnLds<RBW> &sm, int lane) {
   const int q = lane >> 4, r16 = lane & 15;
-  // W = S0 X^T and the Gram matrix, both MFMA; S0 q and k . q on the VALU.
+  // W = S0 X^T and the Gram matrix X X^T on the MFMA.
   floatx4 acc[RBW];
 #pragma unroll
   for (int k = 0; k < RBW; ++k) {
@@ -405,21 +476,6 @@ __device__ __forceinline__ float gdn_window(const float4 (&s)[RBW][NCH], const f
     for (int i = 0; i < 4; ++i) sm.W[16 * k + 4 * q + i][r16] = acc[k][i];
 #pragma unroll
   for (int i = 0; i < 4; ++i) sm.gram[4 * q + i][r16] = gacc[i];
-  float kq = 0.f;
-  if (want_o) {
-#pragma unroll
-    for (int k = 0; k < RBW; ++k) {
-      float v = 0.f;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) v += dot4(s[k][c], qv[c]);
-      v = sum_quarters(v);
-      if (q == 0) sm.W[16 * k + r16][16] = v;
-    }
-    float p = 0.f;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) p += dot4(X[c], qv[c]);
-    kq = sum_quarters(p);  // lane (j, .): k_j . q
-  }
   // Per-record scalars, record j in lane j (lanes 0..15).
   const float la = lane < m ? __logf(al) : 0.f;
   const float g = prefix_sum16(la, lane);
@@ -429,7 +485,6 @@ __device__ __forceinline__ float gdn_window(const float4 (&s)[RBW][NCH], const f
     sm.beta[lane] = lane < m ? be : 0.f;
     sm.c1[lane] = lane < m ? be : 0.f;
     sm.c2[lane] = lane < m ? be * __expf(g) : 0.f;
-    sm.dq[lane] = lane < m ? __expf(gm - g) * kq : 0.f;
     sm.us[lane] = lane < m ? __expf(gm - g) : 0.f;
   }
   wave_lds_sync();
@@ -440,73 +495,67 @@ __device__ __forceinline__ float gdn_window(const float4 (&s)[RBW][NCH], const f
     sm.A[t][j] = (j < t && t < m) ? sm.beta[t] * __expf(sm.g[t] - sm.g[j]) * sm.gram[t][j] : 0.f;
   }
   wave_lds_sync();
-  float o = 0.f;
   if (lane < 16 * RBW) {
     // Forward substitution for this lane's row; u[t] kept in registers.
     float u[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       float v = 0.f;
-      if (t < m) {
+      if (t < known) {
+        v = vr[t];
+      } else if (t < m) {
         v = sm.c1[t] * vr[t] - sm.c2[t] * sm.W[lane][t];
 #pragma unroll
         for (int j = 0; j < t; ++j) v -= sm.A[t][j] * u[j];
       }
       u[t] = v;
     }
-    if (want_o) {
-      o = __expf(gm) * sm.W[lane][16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) o += sm.dq[j] * u[j];
-    }
-    if (want_u) {
-#pragma unroll
-      for (int t = 0; t < 16; ++t) sm.U[t][lane] = u[t];
-    }
+    for (int t = 0; t < 16; ++t) sm.U[t][lane] = u[t];
   }
   wave_lds_sync();
-  return o;
 }
 
-// s <- e^{g_{cnt-1}} s + sum_t e^{g_{cnt-1} - g_t} u_t k_t^T for the cnt window
-// records, with u_t and the weights already in sm.U and sm.us (gdn_window with
-// want_u).  The MFMA A operand (M = column of chunk c, K = record) is read from
-// the ring (cache-resident).
+// s <- escale s + K^T Ub: the MFMA rank-cnt update of a fold, with the A
+// operand (M = column of chunk c, K = record) read from the key ring (cache
+// resident) and the B operand ub[k][st] = weight x u of record 4 st + q at row
+// 16 (rb0 + k) + (lane % 16), supplied by the caller.  The tile accumulates in
+// place, four records at a time, so that only one group of keys is live.
 template <int NCH, int RBW, int CM>
-__device__ __forceinline__ void gdn_fold_apply(float4 (&s)[RBW][NCH], int cnt, int s0, const float *rk, size_t ks,
-                                               int L, float escale, GdnLds<RBW> &sm, int lane) {
+__device__ __forceinline__ void fold_rank(float4 (&s)[RBW][NCH], int cnt, int s0, const float *rk, size_t ks, int L,
+                                          float escale, const float (&ub)[RBW][4], int lane) {
   const int q = lane >> 4, r16 = lane & 15;
   const int nsteps = (cnt + 3) >> 2;
-  float aK[NCH][4];
+#pragma unroll
+  for (int k = 0; k < RBW; ++k)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      s[k][c] = make_float4(s[k][c].x * escale, s[k][c].y * escale, s[k][c].z * escale, s[k][c].w * escale);
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
-    const int r = 4 * st + q;
-    const float *kr = rk + (size_t)wrap(s0, r < cnt ? r : cnt - 1, L) * ks;
+    if (st < nsteps) {
+      const int r = 4 * st + q;
+      const float *kr = rk + (size_t)wrap(s0, r < cnt ? r : cnt - 1, L) * ks;
+      float aK[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const float v = kr[colq<NCH, CM>(c, r16 >> 2) + (r16 & 3)];  // M = r16 in chunk c
-      aK[c][st] = r < cnt ? v : 0.f;
-    }
-  }
+      for (int c = 0; c < NCH; ++c) {
+        const float v = kr[colq<NCH, CM>(c, r16 >> 2) + (r16 & 3)];  // M = r16 in chunk c
+        aK[c] = r < cnt ? v : 0.f;
+      }
 #pragma unroll
-  for (int k = 0; k < RBW; ++k) {
-    float ub[4];
+      for (int k = 0; k < RBW; ++k)
 #pragma unroll
-    for (int st = 0; st < 4; ++st) ub[st] = sm.us[4 * st + q] * sm.U[4 * st + q][16 * k + r16];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      floatx4 acc = {s[k][c].x * escale, s[k][c].y * escale, s[k][c].z * escale, s[k][c].w * escale};
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        if (st < nsteps) acc = mfma_16x16x4(aK[c][st], ub[st], acc);
-      s[k][c] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        for (int c = 0; c < NCH; ++c) {
+          const floatx4 acc = mfma_16x16x4(aK[c], ub[k][st], floatx4{s[k][c].x, s[k][c].y, s[k][c].z, s[k][c].w});
+          s[k][c] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
     }
   }
 }
 
 struct GdnRingPtrs {
-  float *rk, *rv, *ral, *rbe;  // head bases: k, v slot-major; alpha, beta per head row
-  size_t ks, vs;               // slot strides of the k and v rings
+  float *rk, *ru, *rv, *ral, *rbe;  // head bases: k, u, v slot-major (v: re-solving folds only); alpha, beta rows
+  size_t ks, vs;                    // slot strides of the k ring and of the u and v rings
 };
 
 __device__ __forceinline__ GdnRingPtrs gdn_ring_ptrs(const GdnRing &r, const Shape &sh, int b, int h) {
@@ -515,21 +564,20 @@ __device__ __forceinline__ GdnRingPtrs gdn_ring_ptrs(const GdnRing &r, const Sha
   p.ks = (size_t)sh.B * sh.H * sh.N;
   p.vs = (size_t)sh.B * sh.H * sh.P;
   p.rk = r.k + bh * sh.N;
-  p.rv = r.v + bh * sh.P;
+  p.ru = r.u + bh * sh.P;
+  p.rv = r.v ? r.v + bh * sh.P : nullptr;
   p.ral = r.alpha + bh * sh.L;
   p.rbe = r.beta + bh * sh.L;
   return p;
 }
 
 // Keys of window records 0..cnt-1 at ring positions starting at slot s0, in
-// operand layout (zeros beyond cnt); the record at index `last` (if >= 0) is
-// taken from kin instead of the ring.
+// operand layout (zeros beyond cnt).
 template <int NCH, int CM>
-__device__ __forceinline__ void load_keys(float4 (&X)[NCH], int cnt, int last, const float *kin, const GdnRingPtrs &rp,
-                                          int s0, int L, int lane) {
+__device__ __forceinline__ void load_keys(float4 (&X)[NCH], int cnt, const GdnRingPtrs &rp, int s0, int L, int lane) {
   const int q = lane >> 4, r16 = lane & 15;
   const int j = r16 < cnt ? r16 : cnt - 1;
-  const float *kj = (j == last) ? kin : rp.rk + (size_t)wrap(s0, j, L) * rp.ks;
+  const float *kj = rp.rk + (size_t)wrap(s0, j, L) * rp.ks;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const float4 v = ld4(kj + colq<NCH, CM>(c, q));
@@ -537,45 +585,109 @@ __device__ __forceinline__ void load_keys(float4 (&X)[NCH], int cnt, int last, c
   }
 }
 
-// This lane's row of v_t for t < cnt (lanes < 16 RBW), record `last` from vin.
-template <int RBW>
-__device__ __forceinline__ void load_vrows(float (&vr)[16], int cnt, int last, const float *vin, const GdnRingPtrs &rp,
-                                           int s0, int L, int rb0, int lane) {
-  const int row = rb0 * 16 + (lane < 16 * RBW ? lane : 0);
+// Row `row` of ring field f (u or v) for window records 0..cnt-1 from slot s0.
+__device__ __forceinline__ void load_ring_rows(float (&vr)[16], int cnt, const float *f, size_t vs, int s0, int L,
+                                               int row) {
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
-    const int tc = t < cnt ? t : cnt - 1;
-    const float *vt = (tc == last) ? vin : rp.rv + (size_t)wrap(s0, tc, L) * rp.vs;
-    const float v = vt[row];
+    const int tc = t < cnt ? t : (cnt > 0 ? cnt - 1 : 0);
+    const float v = f[(size_t)wrap(s0, tc, L) * vs + row];
     vr[t] = t < cnt ? v : 0.f;
   }
 }
 
-// State buffers of one launch: the checkpoint (format CF) and the read copy
-// (format RF; the same buffer when RF == CF).
-struct GdnStateBufs {
-  StateBuf ck, rd;
-  uint32_t seed_lo, seed_hi;
-};
-
+// Fold the cnt (>= 1) committed records that start at slot s0 into the tile s,
+// which holds the decoded checkpoint:
+//     S <- e^{g_cnt} S + sum_t e^{g_cnt - g_t} u_t k_t^T.
+// With one stored copy (CF == RF) the cached pseudo-values are those of this
+// checkpoint and are folded as they are.  With a separate read copy they were
+// computed from the read copy, so the fold re-solves them from the checkpoint
+// and the values v (a full-window solve through sm), and the read copy's
+// rounding never enters the recurrence.
 template <int CF, int RF, int NCH, int RBW>
-__device__ __forceinline__ void store_both(const float4 (&s)[RBW][NCH], const GdnStateBufs &sb, size_t head, int rb0,
-                                           int lane, uint32_t h, uint32_t b, uint32_t ckpt) {
+__device__ __forceinline__ void gdn_fold(float4 (&s)[RBW][NCH], int cnt, int s0, const GdnRingPtrs &rp, int L,
+                                         int rb0, int lane, GdnLds<RBW> *sm) {
   constexpr int CM = col_map(CF, RF);
-  const SRKey key{sb.seed_lo, sb.seed_hi, h, b, ckpt};
-  SIO<CF, NCH, RBW, CM>::store(s, sb.ck, head, rb0, lane, key);
-  if constexpr (RF != CF) SIO<RF, NCH, RBW, CM>::store(s, sb.rd, head, rb0, lane, key);
+  const int q = lane >> 4, r16 = lane & 15;
+  const int j = r16 < cnt ? r16 : cnt - 1;
+  const float al = rp.ral[wrap(s0, j, L)];
+  float ub[RBW][4];
+  float escale;
+  if constexpr (CF != RF) {
+    float4 X[NCH];
+    float vr[16];
+    load_keys<NCH, CM>(X, cnt, rp, s0, L, lane);
+    load_ring_rows(vr, cnt, rp.rv, rp.vs, s0, L, rb0 * 16 + (lane < 16 * RBW ? lane : 0));
+    const float be = rp.rbe[wrap(s0, j, L)];
+    gdn_window<NCH, RBW>(s, X, cnt, 0, al, be, vr, *sm, lane);
+    escale = __expf(sm->g[cnt - 1]);
+#pragma unroll
+    for (int k = 0; k < RBW; ++k)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) ub[k][st] = sm->us[4 * st + q] * sm->U[4 * st + q][16 * k + r16];
+  } else {
+    const float la = lane < cnt ? __logf(al) : 0.f;
+    const float g = prefix_sum16(la, lane);
+    const float gl = __shfl(g, cnt - 1, kWave);
+    const float us = lane < cnt ? __expf(gl - g) : 0.f;  // lane t: weight of record t
+    escale = __expf(gl);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int r = 4 * st + q;
+      const float w = __shfl(us, r, kWave);
+      const float *ur = rp.ru + (size_t)wrap(s0, r < cnt ? r : cnt - 1, L) * rp.vs;
+#pragma unroll
+      for (int k = 0; k < RBW; ++k) ub[k][st] = w * ur[(rb0 + k) * 16 + r16];
+    }
+  }
+  fold_rank<NCH, RBW, CM>(s, cnt, s0, rp.rk, rp.ks, L, escale, ub, lane);
 }
 
 // ---- replay step ------------------------------------------------------------
+// The ring caches each record's pseudo-value u_t, computed when the record was
+// appended from the S0 every output of the window reads (the decoded read
+// copy).  A step that appends record m of its window then needs one read of S0
+// for S0 k_m and S0 q_m, plus the older records' keys and pseudo-values:
+//     u_m = beta_m (v_m - e^{g_m} S0 k_m - sum_{j<m} e^{g_m - g_j} (k_j . k_m) u_j)
+//     o_m = e^{g_m} S0 q_m + sum_{j<=m} e^{g_m - g_j} (k_j . q_m) u_j.
+// Lane (r, q) of a wave: S0 rows 16 (rb0 + k) + r, columns colq(c, q); the
+// per-row recurrence runs in the lanes with q < RBW for row 16 (rb0 + q) + r.
+// The key dot products are spread over the tile: thread group j (16 threads)
+// takes k_j . k_m and k_j . q_m over NCH columns each (group 15: k_m . q_m),
+// and k_m, q_m reach every wave through LDS, so no lane holds them whole.
+// A step that finds the window full folds it first, stores both copies and
+// starts the next window from what the read copy now holds.
+template <int NCH>
+__device__ __forceinline__ void load_cols(float (&v)[NCH], const float *p) {
+  if constexpr (NCH % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NCH / 4; ++i) {
+      const float4 t = ld4(p + 4 * i);
+      v[4 * i] = t.x;
+      v[4 * i + 1] = t.y;
+      v[4 * i + 2] = t.z;
+      v[4 * i + 3] = t.w;
+    }
+  } else {
+    static_assert(NCH == 2, "NCH is 2, 4 or 8");
+    const float2 t = *reinterpret_cast<const float2 *>(p);
+    v[0] = t.x;
+    v[1] = t.y;
+  }
+}
+
+// Float32 copies: held to 128 VGPRs (four waves per SIMD), which fits without spills.
 template <int CF, int RF, int NCH, int RBW>
-__global__ __launch_bounds__(256) void gdn_replay_step(GdnStepArgs a, GdnStateBufs sb) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32 ? 4 : 1))) void gdn_replay_step(GdnStepArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
   constexpr int CM = col_map(CF, RF);
-  __shared__ GdnLds<RBW> lds_all[4];
+  constexpr int kMaxOld = 15;            // older records of a window (L <= 16)
+  __shared__ float4 kq_s[2][DK / 4];     // k_m, q_m in natural column order
+  __shared__ float dot_s[2][16];         // [0][j] = k_j . k_m, [1][j] = k_j . q_m; [1][15] = k_m . q_m
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  const int r16 = lane & 15;
-  GdnLds<RBW> &sm = lds_all[wave];
+  const int q = lane >> 4, r16 = lane & 15;
+  const int grp = threadIdx.x >> 4;      // record of this thread's key dot products
   const Shape &sh = a.s;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int b = fdiv(tile, sh.fH), h = tile - b * sh.H;
@@ -584,14 +696,17 @@ __global__ __launch_bounds__(256) void gdn_replay_step(GdnStepArgs a, GdnStateBu
   const size_t head = bh * DV * DK;
   const GdnRingPtrs rp = gdn_ring_ptrs(a.ring, sh, b, h);
   const float *qin = a.q + bh * DK, *kin = a.k + bh * DK, *vin = a.v + bh * DV;
+  const int orow = (rb0 + (q < RBW ? q : 0)) * 16 + r16;  // this lane's output row (q < RBW)
 
   // 1. The read copy first (a non-fold step reads only it), then what needs no pointer.
   typename SIO<RF, NCH, RBW, CM>::Raw raw;
   SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
-  float4 qv[NCH];
-  load_vec<NCH, CM>(qv, qin, lane);
+  float km[NCH], qm[NCH];  // columns NCH r16 .. of k_m and q_m
+  load_cols<NCH>(km, kin + NCH * r16);
+  load_cols<NCH>(qm, qin + NCH * r16);
   const float al_row = rp.ral[r16 < L ? r16 : 0], be_row = rp.rbe[r16 < L ? r16 : 0];
   const float al_in = a.alpha[bh], be_in = a.beta[bh];
+  const float v_in = vin[orow];
 
   // 2. Pointers.
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
@@ -609,48 +724,117 @@ __global__ __launch_bounds__(256) void gdn_replay_step(GdnStepArgs a, GdnStateBu
   const int slot = wrap(s0, count, L);  // this token's slot
   int base = ck, sb0 = s0;
   float4 s[RBW][NCH];
-  float4 X[NCH];
-  float vr[16];
+  float kj[NCH];         // this thread's slice of key grp (an older record)
+  float uo[kMaxOld];     // older pseudo-values of this lane's row
   if (fold) {
-    // Fold the full window from the recurrence checkpoint, store both copies,
-    // and restart the window; this step's output comes from the fresh fp32 fold.
     if constexpr (RF == CF) {
       SIO<RF, NCH, RBW, CM>::decode(s, raw);
+      gdn_fold<CF, RF, NCH, RBW>(s, L, s0, rp, L, rb0, lane, nullptr);
     } else {
+      __shared__ GdnLds<RBW> lds_all[4];
       typename SIO<CF, NCH, RBW, CM>::Raw rc;
       SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
       SIO<CF, NCH, RBW, CM>::decode(s, rc);
+      gdn_fold<CF, RF, NCH, RBW>(s, L, s0, rp, L, rb0, lane, &lds_all[wave]);
     }
-    load_keys<NCH, CM>(X, L, -1, kin, rp, s0, L, lane);
-    load_vrows<RBW>(vr, L, -1, vin, rp, s0, L, rb0, lane);
-    const float al = __shfl(al_row, wrap(s0, r16, L), kWave), be = __shfl(be_row, wrap(s0, r16, L), kWave);
-    gdn_window<NCH, RBW>(s, X, qv, L, al, be, vr, false, true, sm, lane);
-    const float gl = sm.g[L - 1];
-    gdn_fold_apply<NCH, RBW, CM>(s, L, s0, rp.rk, rp.ks, L, __expf(gl), sm, lane);
     store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
     sb0 = slot;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) kj[i] = 0.f;
+#pragma unroll
+    for (int t = 0; t < kMaxOld; ++t) uo[t] = 0.f;
+  } else {
+    // The count older records, then the read copy (after the ring loads in program order).
+    const int j = grp < count ? grp : 0;
+    load_cols<NCH>(kj, rp.rk + (size_t)wrap(s0, j, L) * rp.ks + NCH * r16);
+#pragma unroll
+    for (int t = 0; t < kMaxOld; ++t) {
+      const int tc = t < count ? t : 0;
+      const float v = rp.ru[(size_t)wrap(s0, tc, L) * rp.vs + orow];
+      uo[t] = t < count ? v : 0.f;
+    }
+    SIO<RF, NCH, RBW, CM>::decode(s, raw);
   }
-  const int m = pos - base + 1;
-  load_keys<NCH, CM>(X, m, m - 1, kin, rp, sb0, L, lane);
-  load_vrows<RBW>(vr, m, m - 1, vin, rp, sb0, L, rb0, lane);
-  if (!fold) SIO<RF, NCH, RBW, CM>::decode(s, raw);  // after the ring loads in program order
-  float al, be;
-  {
-    const int j = r16 < m - 1 ? r16 : 0;
-    const float a1 = __shfl(al_row, wrap(sb0, j, L), kWave), b1 = __shfl(be_row, wrap(sb0, j, L), kWave);
-    al = r16 < m - 1 ? a1 : (r16 == m - 1 ? al_in : 1.f);
-    be = r16 < m - 1 ? b1 : (r16 == m - 1 ? be_in : 0.f);
-  }
-  const float o = gdn_window<NCH, RBW>(s, X, qv, m, al, be, vr, true, false, sm, lane);
+  const int nold = pos - base;  // older records in this window
 
-  // 3. Output and append.  After a fold the slot being written held the
-  //    oldest folded record, which every wave of the tile read.
-  if (fold) __syncthreads();
-  if (lane < 16 * RBW) {
-    const int row = rb0 * 16 + lane;
-    a.y[bh * DV + row] = o;
-    rp.rv[(size_t)slot * rp.vs + row] = vin[row];
+  // Key dot products (group grp), and k_m, q_m into LDS (group 0).
+  {
+    float dk = 0.f, dq = 0.f;
+    if (grp == 15) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) dq += km[i] * qm[i];
+    } else if (grp < nold) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        dk += kj[i] * km[i];
+        dq += kj[i] * qm[i];
+      }
+    }
+    dk = sum16(dk);
+    dq = sum16(dq);
+    if (r16 == 0) {
+      dot_s[0][grp] = dk;
+      dot_s[1][grp] = dq;
+    }
+    if (grp == 0) {
+      float *kd = reinterpret_cast<float *>(kq_s[0]), *qd = reinterpret_cast<float *>(kq_s[1]);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        kd[NCH * r16 + i] = km[i];
+        qd[NCH * r16 + i] = qm[i];
+      }
+    }
+  }
+  // Also orders every wave's fold reads of the ring before the append below.
+  __syncthreads();
+
+  // Per-record decay prefix, record j in lane j: older records from the ring, then this token.
+  float al;
+  {
+    const int j = r16 < nold ? r16 : 0;
+    const float a1 = __shfl(al_row, wrap(sb0, j, L), kWave);
+    al = r16 < nold ? a1 : (r16 == nold ? al_in : 1.f);
+  }
+  const float g = prefix_sum16(lane < 16 ? __logf(al) : 0.f, lane);
+  const float gm = __shfl(g, nold, kWave);
+  const float egm = __expf(gm);
+  const float dec = __expf(gm - g);
+  const float wk = r16 < nold ? dec * dot_s[0][r16] : 0.f;
+  const float wq = r16 < nold ? dec * dot_s[1][r16] : 0.f;
+  const float kmq = dot_s[1][15];
+  // S0 k_m and S0 q_m for the rows of this lane, then this lane's output row.
+  float skr = 0.f, sqr = 0.f;
+#pragma unroll
+  for (int k = 0; k < RBW; ++k) {
+    float ak = 0.f, aq = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int c4 = colq<NCH, CM>(c, q) >> 2;
+      ak += dot4(s[k][c], kq_s[0][c4]);
+      aq += dot4(s[k][c], kq_s[1][c4]);
+    }
+    ak = sum_quarters(ak);
+    aq = sum_quarters(aq);
+    if (q == k) {
+      skr = ak;
+      sqr = aq;
+    }
+  }
+  float acc_k = 0.f, acc_q = 0.f;
+#pragma unroll
+  for (int t = 0; t < kMaxOld; ++t) {
+    acc_k += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), t)) * uo[t];
+    acc_q += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), t)) * uo[t];
+  }
+  const float um = be_in * (v_in - egm * skr - acc_k);
+  const float o = egm * sqr + acc_q + kmq * um;
+
+  // 3. Output and append.
+  if (q < RBW) {
+    a.y[bh * DV + orow] = o;
+    rp.ru[(size_t)slot * rp.vs + orow] = um;
+    if constexpr (RF != CF) rp.rv[(size_t)slot * rp.vs + orow] = v_in;
   }
   for (int i = threadIdx.x; i < DK; i += 64 * nwaves) rp.rk[(size_t)slot * rp.ks + i] = kin[i];
   if (threadIdx.x == 0) {
@@ -668,10 +852,8 @@ template <int CF, int RF, int NCH, int RBW>
 __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
   constexpr int CM = col_map(CF, RF);
-  __shared__ GdnLds<RBW> lds_all[4];
+  __shared__ GdnLds<RBW> lds_all[RF != CF ? 4 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r16 = lane & 15;
-  GdnLds<RBW> &sm = lds_all[wave];
   const Shape &sh = a.s;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int b = fdiv(tile, sh.fH), h = tile - b * sh.H;
@@ -695,27 +877,19 @@ __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a, GdnStateBufs sb
     SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
     SIO<CF, NCH, RBW, CM>::decode(s, rc);
   }
-  const int s0 = fmod_(ck, sh.fL);
-  float4 X[NCH], qv[NCH];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) qv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-  float vr[16];
-  load_keys<NCH, CM>(X, count, -1, nullptr, rp, s0, L, lane);
-  load_vrows<RBW>(vr, count, -1, nullptr, rp, s0, L, rb0, lane);
-  const int j = r16 < count ? r16 : 0;
-  const float al = rp.ral[wrap(s0, j, L)], be = rp.rbe[wrap(s0, j, L)];
-  gdn_window<NCH, RBW>(s, X, qv, count, al, be, vr, false, true, sm, lane);
-  const float gl = sm.g[count - 1];
-  gdn_fold_apply<NCH, RBW, CM>(s, count, s0, rp.rk, rp.ks, L, __expf(gl), sm, lane);
+  gdn_fold<CF, RF, NCH, RBW>(s, count, fmod_(ck, sh.fL), rp, L, rb0, lane, &lds_all[RF != CF ? wave : 0]);
   store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
 }
 
 // ---- speculative verify ---------------------------------------------------------
-// c committed records then T drafts (c + T <= L after a fold-first).  One
-// forward substitution over all c + T records; draft i's output is
+// c committed records (pseudo-values cached in the ring) then T drafts
+// (c + T <= L after a fold-first).  One forward substitution solves the drafts'
+// pseudo-values; draft i's output is
 //   o_i = e^{g_{c+i}} S0 q_i + sum_{j <= c+i} e^{g_{c+i} - g_j} (k_j . q_i) u_j.
 // S0 q_i is a second MFMA pass over the queries, k_j . q_i an MFMA of the key
-// and query operand registers.  Without a fold-first, S0 is the read copy.
+// and query operand registers.  S0 is the read copy as it stands after a
+// fold-first.  The drafts' keys, pseudo-values and scalars are staged in the
+// ring, so that a commit is only a pointer move.
 template <int CF, int RF, int NCH, int RBW>
 __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
@@ -736,6 +910,7 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
   const size_t bh = (size_t)b * H + h;
   const size_t head = bh * DV * DK;
   const GdnRingPtrs rp = gdn_ring_ptrs(a.ring, sh, b, h);
+  const int row = rb0 * 16 + (lane < 16 * RBW ? lane : 0);  // this lane's row in the substitution
   auto dq_ = [&](int i) { return a.q + (((size_t)b * T + i) * H + h) * DK; };
   auto dk_ = [&](int i) { return a.k + (((size_t)b * T + i) * H + h) * DK; };
   auto dv_ = [&](int i) { return a.v + (((size_t)b * T + i) * H + h) * DV; };
@@ -757,10 +932,6 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
   const int s0 = fmod_(ck, sh.fL);
   int base = ck, sb0 = s0;
   float4 s[RBW][NCH];
-  float4 X[NCH], Q[NCH];
-  float vr[16];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) Q[c] = make_float4(0.f, 0.f, 0.f, 0.f);
   if (fold) {
     if constexpr (RF == CF) {
       SIO<RF, NCH, RBW, CM>::decode(s, raw);
@@ -769,19 +940,14 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
       SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
       SIO<CF, NCH, RBW, CM>::decode(s, rc);
     }
-    load_keys<NCH, CM>(X, count, -1, nullptr, rp, s0, L, lane);
-    load_vrows<RBW>(vr, count, -1, nullptr, rp, s0, L, rb0, lane);
-    const int j = r16 < count ? r16 : 0;
-    const float al = rp.ral[wrap(s0, j, L)], be = rp.rbe[wrap(s0, j, L)];
-    gdn_window<NCH, RBW>(s, X, Q, count, al, be, vr, false, true, sm, lane);
-    const float gl = sm.g[count - 1];
-    gdn_fold_apply<NCH, RBW, CM>(s, count, s0, rp.rk, rp.ks, L, __expf(gl), sm, lane);
+    gdn_fold<CF, RF, NCH, RBW>(s, count, s0, rp, L, rb0, lane, &sm);
     store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
     sb0 = wrap(s0, count, L);
   }
   const int c = pos - base, nrec = c + T;
-  // Keys: committed records from the ring, drafts from the input.
+  // Keys: committed records from the ring, drafts from the input; draft queries.
+  float4 X[NCH], Q[NCH];
   {
     const int j = r16 < nrec ? r16 : nrec - 1;
     const float *kj = j < c ? rp.rk + (size_t)wrap(sb0, j, L) * rp.ks : dk_(j - c);
@@ -797,14 +963,13 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
       Q[cc] = r16 < T ? v : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
-  {
-    const int row = rb0 * 16 + (lane < 16 * RBW ? lane : 0);
+  // This lane's row: cached u_t of the committed records, v of the drafts.
+  float vr[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int tc = t < nrec ? t : nrec - 1;
-      const float v = tc < c ? rp.rv[(size_t)wrap(sb0, tc, L) * rp.vs + row] : dv_(tc - c)[row];
-      vr[t] = t < nrec ? v : 0.f;
-    }
+  for (int t = 0; t < 16; ++t) {
+    const int tc = t < nrec ? t : nrec - 1;
+    const float v = tc < c ? rp.ru[(size_t)wrap(sb0, tc, L) * rp.vs + row] : dv_(tc - c)[row];
+    vr[t] = t < nrec ? v : 0.f;
   }
   float al, be;
   {
@@ -841,10 +1006,9 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
 #pragma unroll
     for (int i = 0; i < 4; ++i) KQ[4 * q + i][r16] = acc[i];
   }
-  // Pseudo-values of all nrec records.
-  gdn_window<NCH, RBW>(s, X, Q, nrec, al, be, vr, false, true, sm, lane);
+  // Pseudo-values of the drafts (the committed ones are known).
+  gdn_window<NCH, RBW>(s, X, nrec, c, al, be, vr, sm, lane);
   if (lane < 16 * RBW) {
-    const int row = rb0 * 16 + lane;
     float u[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) u[t] = t < nrec ? sm.U[t][lane] : 0.f;
@@ -862,7 +1026,10 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
   __syncthreads();
   for (int i = 0; i < T; ++i) {
     const int sl = wrap(sb0, c + i, L);
-    if (lane < 16 * RBW) rp.rv[(size_t)sl * rp.vs + rb0 * 16 + lane] = dv_(i)[rb0 * 16 + lane];
+    if (lane < 16 * RBW) {
+      rp.ru[(size_t)sl * rp.vs + row] = sm.U[c + i][lane];
+      if constexpr (RF != CF) rp.rv[(size_t)sl * rp.vs + row] = dv_(i)[row];
+    }
     for (int e = threadIdx.x; e < DK; e += 256) rp.rk[(size_t)sl * rp.ks + e] = dk_(i)[e];
   }
   if (threadIdx.x < T) {
@@ -890,10 +1057,17 @@ __global__ __launch_bounds__(256) void gdn_encode_state(GdnEncodeArgs a, GdnStat
   const size_t head = ((size_t)b * sh.H + h) * DV * DK;
   float4 s[RBW][NCH];
   load_rows_g<NCH, RBW, CM>(s, a.src + head, rb0, lane);
-  const uint32_t ckpt = (uint32_t)a.ckpt_pos[b];
-  const SRKey key{sb.seed_lo, sb.seed_hi, (uint32_t)h, (uint32_t)b, ckpt};
-  if (a.write_ckpt) SIO<CF, NCH, RBW, CM>::store(s, sb.ck, head, rb0, lane, key);
-  if constexpr (RF != CF) SIO<RF, NCH, RBW, CM>::store(s, sb.rd, head, rb0, lane, key);
+  const SRKey key{sb.seed_lo, sb.seed_hi, (uint32_t)h, (uint32_t)b, (uint32_t)a.ckpt_pos[b]};
+  if (a.write_ckpt) {
+    typename SIO<CF, NCH, RBW, CM>::Raw rc;
+    SIO<CF, NCH, RBW, CM>::encode(rc, s, rb0, lane, key);
+    SIO<CF, NCH, RBW, CM>::write(rc, sb.ck, head, rb0, lane);
+  }
+  if constexpr (RF != CF) {
+    typename SIO<RF, NCH, RBW, CM>::Raw rr;
+    SIO<RF, NCH, RBW, CM>::encode(rr, s, rb0, lane, key);
+    SIO<RF, NCH, RBW, CM>::write(rr, sb.rd, head, rb0, lane);
+  }
 }
 
 // ---- baselines: conventional step and snapshot-per-draft verify ----------------

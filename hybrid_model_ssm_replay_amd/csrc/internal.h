@@ -21,29 +21,36 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 struct RingLayout {
   // Mamba-2: f0 = x [L][B][H][P] (slot-major: one step's appends form one
   //          contiguous block), f1 = B [B][G][2L][N], f2 = dt [B][H][L].
-  // GDN:     f0 = k [L][B][H][dk], f1 = v [L][B][H][dv] (slot-major),
-  //          f2 = alpha [B][H][L], f3 = beta [B][H][L].
-  size_t off[4];
+  // GDN:     f0 = k [L][B][H][dk], f1 = u [L][B][H][dv] (pseudo-values,
+  //          slot-major), f2 = alpha [B][H][L], f3 = beta [B][H][L], and with
+  //          a separate read copy (ckpt_fmt != read_fmt) f4 = v [L][B][H][dv]:
+  //          the fold then re-solves the pseudo-values from the checkpoint.
+  size_t off[5];
   size_t bytes;
 };
+
+// Whether a GDN fold re-solves the window from the checkpoint and the values v
+// (a separate read copy: the cached pseudo-values were computed from the read
+// copy and must not enter the recurrence), or folds the cached pseudo-values.
+inline bool gdn_refold(const replay_config &c) { return c.ckpt_fmt != c.read_fmt; }
 
 inline RingLayout ring_layout(const replay_config &c) {
   RingLayout r{};
   const size_t B = c.batch, H = c.heads, G = c.groups, L = c.window, P = c.head_dim, N = c.state_dim;
-  size_t sz[4];
+  size_t sz[5] = {0, 0, 0, 0, 0};
   if (c.kind == REPLAY_KIND_MAMBA2) {
     sz[0] = B * H * L * P;
     sz[1] = B * G * 2 * L * N;
     sz[2] = B * H * L;
-    sz[3] = 0;
   } else {
     sz[0] = B * H * L * N;
     sz[1] = B * H * L * P;
     sz[2] = B * H * L;
     sz[3] = B * H * L;
+    sz[4] = gdn_refold(c) ? B * H * L * P : 0;
   }
   size_t o = 0;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 5; ++i) {
     r.off[i] = o;
     o += align256(sz[i] * sizeof(float));
   }
@@ -124,9 +131,10 @@ struct M2SnapArgs {
 // Gated DeltaNet ---------------------------------------------------------
 struct GdnRing {
   float *k;      // [L][B][H][dk] (slot-major)
-  float *v;      // [L][B][H][dv] (slot-major)
+  float *u;      // [L][B][H][dv] (slot-major): pseudo-values
   float *alpha;  // [B][H][L]
   float *beta;   // [B][H][L]
+  float *v;      // [L][B][H][dv] (slot-major), separate read copy only; else NULL
 };
 
 struct GdnStepArgs {

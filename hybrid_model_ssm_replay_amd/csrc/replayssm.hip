@@ -67,7 +67,7 @@ GdnRing gdn_ring(const replay_ctx &ctx) {
   const RingLayout lay = ring_layout(ctx.cfg);
   char *base = (char *)ctx.buf.ring;
   return GdnRing{(float *)(base + lay.off[0]), (float *)(base + lay.off[1]), (float *)(base + lay.off[2]),
-                 (float *)(base + lay.off[3])};
+                 (float *)(base + lay.off[3]), gdn_refold(ctx.cfg) ? (float *)(base + lay.off[4]) : nullptr};
 }
 
 GdnFormatBufs gdn_formats(const replay_ctx &ctx) {

@@ -11,9 +11,12 @@ Mamba-2 (x per head, B and C per group, dt per head; a ring record holds x, B, d
   non-fold step at window position m:     read  state + (m - 1) ring_rec + record_in
                                           write ring_rec + y (H P 4)
   fold (lazy, at the step that finds L records):  read  + L ring_rec, write + state
-Gated DeltaNet (q, k, v, alpha, beta per head; a ring record holds k, v, alpha, beta):
+Gated DeltaNet (q, k, v, alpha, beta per head; a ring record holds k, the
+pseudo-value u (d_v), alpha, beta):
   record_in  = H (2 dk + dv + 2) 4, ring_rec = H (dk + dv + 2) 4, state = H dv dk 4
-  (same structure).
+  (same structure).  With a separate read copy the ring also keeps v (H dv 4
+  per record): written by every step, read back by the fold, which re-solves
+  the pseudo-values from the checkpoint.
 Conventional step: read state + record_in, write state + y.
 Replay verify of T drafts after c committed records: read state + c ring_rec +
 T record_in, write T ring_rec + T y (+ fold-first: L' ring_rec read, state written).
@@ -93,16 +96,18 @@ def replay_window_mean(l: Layer) -> tuple[float, float]:
 def split_window_mean(l: Layer, ckpt_fmt: int, read_fmt: int) -> tuple[float, float]:
     """Window-mean (read, write) bytes per step with a stored checkpoint in ckpt_fmt
     and a read copy in read_fmt (the same copy when equal): non-fold steps read the
-    read copy; a fold reads the checkpoint and writes both copies."""
+    read copy; a fold reads the checkpoint and writes both copies (Gated DeltaNet;
+    a separate read copy adds the buffered values v)."""
     elems = l.heads * l.head_dim * l.state_dim
     ck, rd = FORMAT_BYTES[ckpt_fmt] * elems, FORMAT_BYTES[read_fmt] * elems
+    vrec = l.heads * l.head_dim * E if read_fmt != ckpt_fmt else 0
     rd_sum = wr_sum = 0.0
     for m in range(1, l.window + 1):
         fold = m == 1
         r = (ck if fold else rd) + (m - 1) * l.ring_rec + l.record_in
-        w = l.ring_rec + l.y
+        w = l.ring_rec + vrec + l.y
         if fold:
-            r += l.window * l.ring_rec
+            r += l.window * (l.ring_rec + vrec)
             w += ck + (rd if read_fmt != ckpt_fmt else 0.0)
         rd_sum += r * l.batch
         wr_sum += w * l.batch

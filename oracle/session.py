@@ -187,9 +187,11 @@ class SplitReplaySession(ReplaySession):
     copy's rounding never re-enters the recurrence [P1, Interpretation 4; P3,
     Interpretation 3].  Readings: a fold starts from the decoded recurrence copy,
     folds in full precision, rounds to float32 and encodes both copies from that
-    float32 state; the output of a step or verify that folded first comes from
-    the fresh fold result, every other output from the decoded read copy plus
-    the buffered records (which are exact)."""
+    float32 state; every output, including that of a step or verify that folded
+    first, comes from the decoded read copy as it stands after the call's fold
+    plus the buffered records (which are exact).  The pages fix only that
+    non-fold outputs read the approximate copy; reading it for the fold step's
+    output too makes all outputs of a window one recurrence from one S0."""
 
     def __init__(self, kind, state0, window, params=None, ckpt_fmt=FMT_F32, read_fmt=FMT_F32, seed=0):
         super().__init__(kind, state0, window, params)
@@ -198,7 +200,6 @@ class SplitReplaySession(ReplaySession):
         B = S32.shape[0]
         self.R = [encode_state(S32[b], ckpt_fmt, seed, b, 0) for b in range(B)]
         self.Q = self.R if read_fmt == ckpt_fmt else [encode_state(S32[b], read_fmt, seed, b, 0) for b in range(B)]
-        self.fresh = {}                                  # sequence -> float64 fold result of this call
 
     def read_state(self, b):
         return decode_state(self.Q[b], self.rf)
@@ -213,15 +214,10 @@ class SplitReplaySession(ReplaySession):
         self.R[b] = encode_state(S32, self.cf, self.seed, b, pos)
         if self.Q is not self.R:
             self.Q[b] = encode_state(S32, self.rf, self.seed, b, pos)
-        self.fresh[b] = S
         for p in [p for p in self.recs[b] if p < pos]:
             del self.recs[b][p]
 
-    def _source(self, b):
-        return self.fresh[b] if b in self.fresh else self.read_state(b)
-
     def step(self, rec):
-        self.fresh = {}
         will_fold = self.ptr.count == self.ptr.L
         for b in np.nonzero(will_fold)[0]:
             self._fold(b)
@@ -230,12 +226,10 @@ class SplitReplaySession(ReplaySession):
         ys = []
         for b in range(self.batch):
             self.recs[b][int(pos_before[b])] = _rec_b(rec, b)
-            ys.append(self.k.output(self._source(b), self._window(b, int(self.ptr.pos[b]))))
-        self.fresh = {}
+            ys.append(self.k.output(self.read_state(b), self._window(b, int(self.ptr.pos[b]))))
         return np.stack(ys)
 
     def verify(self, drafts):
-        self.fresh = {}
         T = next(iter(drafts.values())).shape[1]
         will_fold = self.ptr.count + T > self.ptr.L
         for b in np.nonzero(will_fold)[0]:
@@ -247,16 +241,13 @@ class SplitReplaySession(ReplaySession):
             for i in range(T):
                 self.recs[b][p0 + i] = _draft_b(drafts, b, i)
             committed = self._window(b, p0)
-            S0 = self._source(b)
+            S0 = self.read_state(b)
             out.append(np.stack([self.k.output(S0, committed + [self.recs[b][p0 + j] for j in range(i + 1)])
                                  for i in range(T)]))
-        self.fresh = {}
         return np.stack(out)
 
     def flush(self, mask=None):
-        self.fresh = {}
         m = np.ones(self.batch, bool) if mask is None else np.asarray(mask, bool)
         for b in np.nonzero(m & (self.ptr.count > 0))[0]:
             self._fold(b)
-        self.fresh = {}
         return self.ptr.flush(m)
