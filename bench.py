@@ -27,22 +27,25 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["hybrid_model_ssm_replay_amd/csrc/mamba2.hip", "hybrid_model_ssm_replay_amd/csrc/gdn.hip",
-                  "hybrid_model_ssm_replay_amd/csrc/common.h", "hybrid_model_ssm_replay_amd/csrc/internal.h"]
+_CSRC = "hybrid_model_ssm_replay_amd/csrc/"
+# Sources each kernel family is built from: a stored counter summary is used only
+# while the hash of these files matches the one it records.
+KERNEL_SOURCES = {"m2": [_CSRC + f for f in ("mamba2.hip", "common.h", "internal.h")],
+                  "gdn": [_CSRC + f for f in ("gdn.hip", "codecs.h", "common.h", "internal.h")]}
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(family: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[family]:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(name: str):
+def stored_traffic(name: str, family: str):
     """Per-launch HBM bytes from a committed counter summary, if it matches the current kernel source."""
     path = os.path.join(PROFILE_DIR, name)
     if not os.path.exists(path):
@@ -50,7 +53,7 @@ def stored_traffic(name: str):
     txt = open(path).read()
     m = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m or not t or m.group(1) != kernel_source_hash():
+    if not m or not t or m.group(1) != kernel_source_hash(family):
         return None
     return float(t.group(1))
 
@@ -288,15 +291,15 @@ def main(argv=None):
                              "replay_model_bytes_per_step": grd + gwr, "conventional_step_us": us_gc,
                              "conventional_gbs": (gcrd + gcwr) / us_gc / 1e3, "speedup_vs_conventional": us_gc / us_g,
                              "tokens_per_s": gshape.batch / us_g * 1e6,
-                             "traffic_bytes_per_launch": stored_traffic("gdn_replay_step_b256_traffic.txt")}
+                             "traffic_bytes_per_launch": stored_traffic("gdn_replay_step_b256_traffic.txt", "gdn")}
 
     if not args.no_extra:
         log("split precision")
         extra["gdn_split_b64"] = bench_split(torch)
 
-    traffic = stored_traffic("m2_replay_step_b256_traffic.txt")
+    traffic = stored_traffic("m2_replay_step_b256_traffic.txt", "m2")
     roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-            "traffic": traffic, "kernel": "m2_replay_step<8,1>",
+            "traffic": traffic, "kernel": "m2_replay_step<8, 2>",
             "bytes_per_launch": rd + wr}
     cpu = None if args.no_cpu else cpu_baseline(shape, 1)
     out = {

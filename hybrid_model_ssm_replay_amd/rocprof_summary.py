@@ -2,10 +2,12 @@
 
     python -m hybrid_model_ssm_replay_amd.rocprof_summary trace <kernel_trace.csv>
     python -m hybrid_model_ssm_replay_amd.rocprof_summary traffic <fetch_counter_collection.csv> \
-        <write_counter_collection.csv> <kernel-substring>
+        <write_counter_collection.csv> <kernel-substring> <probe-copy-bytes> [grid-size]
 
-``trace`` prints the mean, min and max duration per kernel.  ``traffic`` prints
-FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the named kernel, calibrated
+``trace`` prints the mean, min and max duration per kernel and launch size
+(grid size in work-items).  ``traffic`` prints FETCH_SIZE and WRITE_SIZE (KiB
+per dispatch) of the named kernel (only its launches of the given grid size,
+when one is given), calibrated
 against the library's HBM probe copy kernel, whose bytes are known: it reads and
 writes exactly the same number of bytes, so factor_read = WRITE_SIZE / FETCH_SIZE
 of the probe and factor_write = 1 when the probe's WRITE_SIZE equals the bytes
@@ -21,13 +23,23 @@ import sys
 PROBE_COPY = "probe_copy_k"
 
 
-def _by_kernel(path: str, value_field: str):
+def _grid(r) -> int:
+    if "Grid_Size" in r:
+        return int(r["Grid_Size"])
+    return int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1) * int(r.get("Grid_Size_Z", 1) or 1)
+
+
+def _by_kernel(path: str, value_field: str, grid: int | None = None, with_grid: bool = False):
     d = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
+        g = _grid(r)
+        if grid is not None and g != grid and PROBE_COPY not in r["Kernel_Name"]:
+            continue
+        key = (r["Kernel_Name"], g) if with_grid else r["Kernel_Name"]
         if value_field == "duration":
-            d[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            d[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         else:
-            d[r["Kernel_Name"]].append(float(r[value_field]))
+            d[key].append(float(r[value_field]))
     return d
 
 
@@ -39,16 +51,17 @@ def _find(d, sub):
 
 
 def trace(path: str) -> str:
-    d = _by_kernel(path, "duration")
-    lines = ["| kernel | dispatches | mean us | min us | max us |", "|---|---|---|---|---|"]
-    for k, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"| `{k[:90]}` | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
+    d = _by_kernel(path, "duration", with_grid=True)
+    lines = ["| kernel | grid (work-items) | dispatches | mean us | min us | max us |", "|---|---|---|---|---|---|"]
+    for (k, g), v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k[:90]}` | {g} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
     return "\n".join(lines)
 
 
-def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int | None = None) -> dict:
-    fe = _by_kernel(fetch_csv, "Counter_Value")
-    wr = _by_kernel(write_csv, "Counter_Value")
+def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int | None = None,
+            grid: int | None = None) -> dict:
+    fe = _by_kernel(fetch_csv, "Counter_Value", grid)
+    wr = _by_kernel(write_csv, "Counter_Value", grid)
     pk_f, pk_w = _find(fe, PROBE_COPY), _find(wr, PROBE_COPY)
     probe_fetch = sum(fe[pk_f]) / len(fe[pk_f])
     probe_write = sum(wr[pk_w]) / len(wr[pk_w])
@@ -66,7 +79,8 @@ def main(argv):
     if argv[0] == "trace":
         print(trace(argv[1]))
     elif argv[0] == "traffic":
-        r = traffic(argv[1], argv[2], argv[3], int(argv[4]) if len(argv) > 4 else None)
+        r = traffic(argv[1], argv[2], argv[3], int(argv[4]) if len(argv) > 4 else None,
+                    int(argv[5]) if len(argv) > 5 else None)
         for k, v in r.items():
             print(f"{k}: {v}")
     else:

@@ -78,8 +78,13 @@ extern "C" {
  *               only once it is full [P2, paragraph 3; P3, Interpretation 2].
  *   max_draft   largest T a verify call will use, 0..L (sizes the ring).
  *   ckpt_fmt    format of the checkpoint that carries the recurrence.
- *   read_fmt    format of the copy non-fold steps read; equal to ckpt_fmt
+ *   read_fmt    format of the copy the outputs read; equal to ckpt_fmt
  *               means a single copy [P1, Interpretation 4; P3, Interpretation 3].
+ *               Every output (also that of a step or verify that folds first)
+ *               reads the read copy as it stands after the call's fold, plus
+ *               the buffered records in float32; a fold starts from the
+ *               checkpoint, so the read copy's rounding never enters the
+ *               recurrence.
  *   seed        key of the stochastic-rounding generator (Philox-4x32-10; the
  *               fold that sets ckpt_pos of sequence b draws element e of head h
  *               from word e % 4 of Philox(counter (e / 4, h, b, ckpt_pos),
