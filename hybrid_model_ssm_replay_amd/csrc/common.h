@@ -70,6 +70,13 @@ __device__ __forceinline__ float sum16(float v) {
   v += __shfl_xor(v, 1, kWave);
   return v;
 }
+// Program-order fence for LDS traffic between lanes of one wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Sum over the four lanes l, l^16, l^32, l^48 (the four k-quarters of an MFMA row).
 __device__ __forceinline__ float sum_quarters(float v) {
   v += __shfl_xor(v, 16, kWave);

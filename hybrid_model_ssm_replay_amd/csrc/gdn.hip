@@ -53,13 +53,6 @@ struct GdnLds {
   float U[16][16 * RBW + 4];  // pseudo-values u_t [record][row]
 };
 
-// Program-order fence for LDS traffic between lanes of one wave.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Inclusive prefix sum over lanes 0..15 (lanes >= 16 must pass 0).
 __device__ __forceinline__ float prefix_sum16(float v, int lane) {
   float t = v;

@@ -430,149 +430,225 @@ __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
 // T drafts follow the c committed window records.  Outputs for draft i
 // (window record c + i):
 //   y_i = exp(A s_{1..c+i}) S0 C_i + sum_{r <= c+i} exp(A s_{r+1..c+i}) dt_r (B_r . C_i) x_r + D x_{c+i}
-// S0 . [C_0 .. C_{T-1}] and the B_r . C_i table are MFMA products; no state
-// is written except by a fold-first when c + T > L.
+// Geometry as the step: each wave owns RBW row blocks of the head.  Drafts go
+// in passes of four through v_mfma_f32_4x4x1_16b_f32 (16 blocks of 4 x 4 x 1;
+// lane l feeds block l / 4, row / column l % 4, and gets rows 0..3 of column
+// l % 4 of its block), so no MFMA work is spent on absent drafts.  With lane
+// l = r + 16 q, g = r / 4, m = r % 4, draft n = 4 p + m in pass p:
+//   * S0 . C_n: block (g, q) takes rows 16 rb + 4 g + 0..3 over the columns of
+//     quarter q of the register tile; a sum over q completes the products;
+//   * B_r . C_n the same way, with record r in place of the row; a per-wave
+//     LDS transpose then gives lane (r, q) the records 4 st + q it feeds;
+//   * the record sum X~ . Coef^T (K = record 4 st + q) is accumulated onto the
+//     scaled partial products before the sum over q.
+// The drafts' C and the records' B reach LDS by direct global-to-LDS loads
+// (global_load_lds_dwordx4: lane l of a load writes 16 bytes at base + 16 l),
+// laid out so that every read is linear in the lane (no bank conflicts) and
+// no VGPR holds them while the checkpoint stream is in flight.  Loads that
+// need no pointer (checkpoint, drafts' C and x) are issued first; the drafts
+// are staged in the ring from registers and LDS; no state is written except
+// by a fold-first when c + T > L.
+__device__ __forceinline__ floatx4 mfma_4x4x1(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
+
+// One 16-byte global-to-LDS load per lane: lane l's 16 bytes go to lds[l].
+__device__ __forceinline__ void dma16(const float *src, float4 *lds) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src), (lds_void *)(lds), 16, 0, 0);
+}
+
 template <int NCH, int RBW>
 __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   constexpr int N = 16 * NCH;
-  __shared__ M2Smem<NCH> sm;
-  const TileCtx t = tile_ctx();
+  constexpr int kPass = kMaxL / 4;
+  __shared__ float4 ldsB[NCH][64];          // [chunk cc][r + 16 q]: B_r[16 cc + 4 q .. + 3]
+  __shared__ float4 ldsC[kPass * NCH * 16];  // [(p NCH + cc) 16 + 4 m + q]: C_{4 p + m}[16 cc + 4 q .. + 3]
+  __shared__ float dots_all[4][kMaxL][4];    // per wave: [record][draft of the pass] B_r . C_n
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int q = lane >> 4, r16 = lane & 15, gq = r16 >> 2, m4 = r16 & 3;
   const Shape &sh = a.s;
   const int T = a.T;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = tile / sh.H, h = tile - b * sh.H;
-  const int hpg = sh.H / sh.G, g = h / hpg;
+  const int b = fdiv(tile, sh.fH), h = tile - b * sh.H;
+  const int g = fdiv(h, sh.fHpg);
   const int P = sh.P, L = sh.L, H = sh.H, G = sh.G;
-
-  const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
-  const int count = pos - ck;
-  if (count < 0 || count > L) {
-    if (h == 0 && t.tid == 0) {
-      atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
-      a.ptr.pos_out[b] = pos;
-      a.ptr.ckpt_out[b] = ck;
-    }
-    return;
-  }
-  const bool fold = count + T > L;  // implies count >= 1 because T <= L
+  const int rb0 = wave * RBW;
   float *S = a.ckpt + ((size_t)b * H + h) * P * N;
-  float4 s[RBW][NCH];
-  load_tile<NCH, RBW>(s, S, t);
-  const float Ah = a.A[h];
   const size_t xs = (size_t)sh.B * H * P;
   float *rx = a.ring.x + ((size_t)b * H + h) * P;
   float *rdt = a.ring.dt + ((size_t)b * H + h) * L;
   float *rB = a.ring.Bm + ((size_t)b * G + g) * 2 * L * N;
+  auto draft_x = [&](int i) { return a.x + (((size_t)b * T + i) * H + h) * P; };
+  auto draft_B = [&](int i) { return a.Bm + (((size_t)b * T + i) * G + g) * N; };
+  auto draft_C = [&](int i) { return a.Cm + (((size_t)b * T + i) * G + g) * N; };
+  const int npass = (T + 3) >> 2;
+
+  // 1. The checkpoint stream, then the drafts' C into LDS (load j of the
+  //    tile by wave j % nwaves), then the pointers.
+  float4 s[RBW][NCH];
+  load_rows<NCH, RBW>(s, S, rb0, lane);
+  {
+    const int nload = (npass * NCH * 16 + 63) >> 6;
+    for (int j = wave; j < nload; j += nwaves) {
+      const int slot = 64 * j + lane;
+      const int q2 = slot & 3, m2 = (slot >> 2) & 3, pc = slot >> 4;  // pc = p NCH + cc
+      const int p2 = pc / NCH, cc = pc - p2 * NCH;
+      const int n = 4 * p2 + m2;
+      dma16(draft_C(n < T ? n : T - 1) + 16 * cc + 4 * q2, &ldsC[64 * j]);
+    }
+  }
+  const float Ah = a.A[h], Dh = a.D[h];
+
+  // 2. Pointers; fold-first when the window cannot take T more records.
+  const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
+  const int count = pos - ck;
+  if (count < 0 || count > L) {
+    if (h == 0 && threadIdx.x == 0) {
+      atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
+      a.ptr.pos_out[b] = pos;
+      a.ptr.ckpt_out[b] = ck;
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // no global-to-LDS load outlives the workgroup
+    return;
+  }
+  const bool fold = count + T > L;  // implies count >= 1 because T <= L
   int base = ck;
   if (fold) {
-    fold_tile<NCH, RBW>(s, sm, count, ck, Ah, rx, rdt, rB, L, xs, t);
-    store_tile<NCH, RBW>(s, S, t);
+    FoldIn<NCH, RBW> fi;
+    fold_load<NCH, RBW>(fi, count, fmod_(ck, sh.fL), fmod_(ck, sh.f2L), rx, rdt, rB, L, xs, rb0, lane);
+    fold_apply<NCH, RBW>(s, fi, Ah, lane);
+    store_rows<NCH, RBW>(s, S, rb0, lane);
     base = pos;
   }
   const int c = pos - base;  // committed records in the window
   const int nrec = c + T;    // <= L
+  const int sb = fmod_(base, sh.fL), sbb = fmod_(base, sh.f2L);
 
-  auto draft_x = [&](int i) { return a.x + (((size_t)b * T + i) * H + h) * P; };
-  auto draft_B = [&](int i) { return a.Bm + (((size_t)b * T + i) * G + g) * N; };
-  auto draft_C = [&](int i) { return a.Cm + (((size_t)b * T + i) * G + g) * N; };
-  auto rec_B = [&](int r) -> const float * {
-    return r < c ? rB + (size_t)((base + r) % (2 * L)) * N : draft_B(r - c);
-  };
-
-  // C of draft r16 at this lane's columns (zero for lanes without a draft).
-  float4 cd[NCH];
-#pragma unroll
-  for (int cc = 0; cc < NCH; ++cc)
-    cd[cc] = t.r16 < T ? ld4(draft_C(t.r16) + 16 * cc + 4 * t.q) : make_float4(0.f, 0.f, 0.f, 0.f);
-
-  if (t.wave == 0) {
-    // dt of the window records.
-    if (t.lane < nrec)
-      sm.dt[t.lane] = t.lane < c ? rdt[(base + t.lane) % L] : a.dt[((size_t)b * T + (t.lane - c)) * H + h];
-    // dots[r][i] = B_r . C_i: M = record, N = draft, K = state column.
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    const float *Br = t.r16 < nrec ? rec_B(t.r16) : nullptr;
-#pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-      const float4 bv = Br ? ld4(Br + 16 * cc + 4 * t.q) : make_float4(0.f, 0.f, 0.f, 0.f);
-      acc = mfma_16x16x4(bv.x, cd[cc].x, acc);
-      acc = mfma_16x16x4(bv.y, cd[cc].y, acc);
-      acc = mfma_16x16x4(bv.z, cd[cc].z, acc);
-      acc = mfma_16x16x4(bv.w, cd[cc].w, acc);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm.dots[4 * t.q + i][t.r16] = acc[i];
-  }
-  lds_barrier();
+  // 3. Window records.  B of record r16 at the tile columns into LDS (chunk cc
+  //    by wave cc % nwaves); x of record 4 st + q at this lane's rows
+  //    (record-sum A operand); dt of record r16.
   {
-    // coef[i][r] for draft i = tid / 16, record r = tid % 16.
-    const int i = t.tid >> 4, r = t.tid & 15;
-    if (i < T) {
-      const int last = c + i;
-      float cf = 0.f;
-      if (r <= last) {
-        float sg = 0.f;
-        for (int j = r + 1; j <= last; ++j) sg += sm.dt[j];
-        cf = __expf(Ah * sg) * sm.dt[r] * sm.dots[r][i];
-      }
-      sm.coef[i][r] = cf;
-      if (r == 0) {
-        float tot = 0.f;
-        for (int j = 0; j <= last; ++j) tot += sm.dt[j];
-        sm.scale[i] = __expf(Ah * tot);
-      }
-    }
+    const int rc = r16 < nrec ? r16 : nrec - 1;
+    const float *Br = rc < c ? rB + (size_t)wrap(sbb, rc, 2 * L) * N : draft_B(rc - c);
+    for (int cc = wave; cc < NCH; cc += nwaves) dma16(Br + 16 * cc + 4 * q, &ldsB[cc][0]);
   }
-  lds_barrier();
-
-  const float Dh = a.D[h];
+  float xa[RBW][4];
 #pragma unroll
-  for (int k = 0; k < RBW; ++k) {
-    const int rb = t.wave * RBW + k;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int st = 0; st < 4; ++st) {
+    const int r = 4 * st + q;
+    const int rc = r < nrec ? r : nrec - 1;
+    const float *xr = rc < c ? rx + (size_t)wrap(sb, rc, L) * xs : draft_x(rc - c);
 #pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-      acc = mfma_16x16x4(s[k][cc].x, cd[cc].x, acc);
-      acc = mfma_16x16x4(s[k][cc].y, cd[cc].y, acc);
-      acc = mfma_16x16x4(s[k][cc].z, cd[cc].z, acc);
-      acc = mfma_16x16x4(s[k][cc].w, cd[cc].w, acc);
+    for (int k = 0; k < RBW; ++k) {
+      const float v = xr[(rb0 + k) * 16 + r16];
+      xa[k][st] = r < nrec ? v : 0.f;
     }
-    // Lane holds rows p0 .. p0+3 of draft i.
-    const int i = t.r16;
-    if (i < T) {
-      const int p0 = rb * 16 + 4 * t.q;
-      const float sc = sm.scale[i];
-      float4 o = make_float4(sc * acc[0], sc * acc[1], sc * acc[2], sc * acc[3]);
-      for (int r = 0; r <= c + i; ++r) {
-        const float cf = sm.coef[i][r];
-        const float4 xv = ld4(r < c ? rx + (size_t)((base + r) % L) * xs + p0 : draft_x(r - c) + p0);
-        o.x += cf * xv.x;
-        o.y += cf * xv.y;
-        o.z += cf * xv.z;
-        o.w += cf * xv.w;
+  }
+  float dtl;
+  {
+    const int rc = r16 < nrec ? r16 : nrec - 1;
+    const float v = rc < c ? rdt[wrap(sb, rc, L)] : a.dt[((size_t)b * T + (rc - c)) * H + h];
+    dtl = r16 < nrec ? v : 0.f;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's global-to-LDS loads have landed
+  __syncthreads();                // and every other wave's
+
+  // 4. Passes of four drafts.
+  const int nsteps = (nrec + 3) >> 2;
+  for (int p = 0; p < npass; ++p) {
+    const int n = 4 * p + m4;  // this lane's draft
+    const int nc = n < T ? n : T - 1;
+    float4 xl[RBW];  // x_n at rows 16 rb + 4 g + 0..3 (the D x term)
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) xl[k] = ld4(draft_x(nc) + (rb0 + k) * 16 + 4 * gq);
+    const float4 *cdp = &ldsC[(p * NCH * 4 + m4) * 4 + q];  // C_n at tile chunk cc: cdp[16 cc]
+
+    // dots[4 g + v][n] (register v, summed over q), transposed through LDS.
+    {
+      floatx4 dacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) {
+        const float4 bq = ldsB[cc][lane], cv = cdp[16 * cc];
+        dacc = mfma_4x4x1(bq.x, cv.x, dacc);
+        dacc = mfma_4x4x1(bq.y, cv.y, dacc);
+        dacc = mfma_4x4x1(bq.z, cv.z, dacc);
+        dacc = mfma_4x4x1(bq.w, cv.w, dacc);
       }
-      const float4 xl = ld4(draft_x(i) + p0);
-      o.x += Dh * xl.x;
-      o.y += Dh * xl.y;
-      o.z += Dh * xl.z;
-      o.w += Dh * xl.w;
-      st4(a.y + (((size_t)b * T + i) * H + h) * P + p0, o);
+      float dsum[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dsum[v] = sum_quarters(dacc[v]);  // every lane takes part
+      if (p) wave_lds_sync();  // the previous pass has read the table
+      if (q == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dots_all[wave][4 * gq + v][m4] = dsum[v];
+      }
+      wave_lds_sync();
+    }
+    // Record-sum operand: coef[n][r], r = 4 st + q, with each segment sum
+    // accumulated directly from the newest record down; and the S0 weight.
+    const int last = n < T ? c + n : -1;
+    float seg[4] = {0.f, 0.f, 0.f, 0.f};
+    float tot = 0.f;
+#pragma unroll
+    for (int j = kMaxL - 1; j >= 0; --j) {
+      if (j <= last) tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dtl), j));
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        if (j == 4 * st + q + 1) seg[st] = tot;
+    }
+    const float sc = __expf(Ah * tot);
+    float cb[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int r = 4 * st + q;
+      const float dtr = __shfl(dtl, r, kWave);
+      cb[st] = r <= last ? __expf(Ah * seg[st]) * dtr * dots_all[wave][r][m4] : 0.f;
+    }
+
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) {
+        const float4 cv = cdp[16 * cc];
+        acc = mfma_4x4x1(s[k][cc].x, cv.x, acc);
+        acc = mfma_4x4x1(s[k][cc].y, cv.y, acc);
+        acc = mfma_4x4x1(s[k][cc].z, cv.z, acc);
+        acc = mfma_4x4x1(s[k][cc].w, cv.w, acc);
+      }
+      acc = floatx4{sc * acc[0], sc * acc[1], sc * acc[2], sc * acc[3]};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        if (st < nsteps) acc = mfma_4x4x1(xa[k][st], cb[st], acc);
+      float4 o = make_float4(sum_quarters(acc[0]), sum_quarters(acc[1]), sum_quarters(acc[2]),
+                             sum_quarters(acc[3]));
+      o.x += Dh * xl[k].x;
+      o.y += Dh * xl[k].y;
+      o.z += Dh * xl[k].z;
+      o.w += Dh * xl[k].w;
+      if (q == 0 && n < T) st4(a.y + (((size_t)b * T + n) * H + h) * P + (rb0 + k) * 16 + 4 * gq, o);
     }
   }
 
-  // Stage the drafts in the ring (after every wave is done with the folded slots).
-  __syncthreads();
-  for (int e = t.tid; e < T * P; e += t.nthreads) {
-    const int i = e / P, p = e - i * P;
-    rx[(size_t)((pos + i) % L) * xs + p] = draft_x(i)[p];
-  }
-  if (t.tid < T) rdt[(pos + t.tid) % L] = a.dt[((size_t)b * T + t.tid) * H + h];
-  if (h % hpg == 0)
-    for (int e = t.tid; e < T * N; e += t.nthreads) {
-      const int i = e / N, n = e - i * N;
-      rB[(size_t)((pos + i) % (2 * L)) * N + n] = draft_B(i)[n];
+  // 5. Stage the drafts (records c .. nrec-1) in the ring.  The workgroup
+  //    barrier above already ordered every wave's fold reads before this.
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int r = 4 * st + q;
+    if (r >= c && r < nrec) {
+#pragma unroll
+      for (int k = 0; k < RBW; ++k) rx[(size_t)wrap(sb, r, L) * xs + (rb0 + k) * 16 + r16] = xa[k][st];
     }
-  if (h == 0 && t.tid == 0) {
+  }
+  if (wave == 0) {
+    if (lane >= c && lane < nrec) rdt[wrap(sb, lane, L)] = dtl;
+    if (h - g * (H / G) == 0 && r16 >= c && r16 < nrec) {
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) st4(rB + (size_t)wrap(sbb, r16, 2 * L) * N + 16 * cc + 4 * q, ldsB[cc][lane]);
+    }
+  }
+  if (h == 0 && threadIdx.x == 0) {
     a.ptr.pos_out[b] = pos;
     a.ptr.ckpt_out[b] = base;
   }
@@ -728,7 +804,7 @@ int launch_m2_flush(const M2FlushArgs &a, hipStream_t st) {
   return dispatch<FlushK>(a, a.s.N, a.s.P, a.s.B, a.s.H, false, st);
 }
 int launch_m2_verify(const M2VerifyArgs &a, hipStream_t st) {
-  return dispatch<VerifyK>(a, a.s.N, a.s.P, a.s.B, a.s.H, false, st);
+  return dispatch<VerifyK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
 }
 int launch_m2_conv(const M2ConvArgs &a, hipStream_t st) {
   return dispatch<ConvK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);

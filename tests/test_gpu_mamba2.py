@@ -108,6 +108,7 @@ def _spec_run(shape, seed, ops, T_max):
     (LayerShape("mamba2", 4, 4, 32, 64, 2, 6), 6),
     (LayerShape("mamba2", 3, 8, 64, 128, 8, 16), 8),
     (LayerShape("mamba2", 2, 2, 16, 16, 1, 3), 3),
+    (LayerShape("mamba2", 2, 2, 16, 32, 1, 12), 12),  # one wave per head, more drafts than 64 / 16
 ])
 def test_speculative_sequence(shape, T_max):
     _spec_run(shape, seed=5, ops=60, T_max=T_max)
