@@ -70,6 +70,14 @@ __device__ __forceinline__ float sum16(float v) {
   v += __shfl_xor(v, 1, kWave);
   return v;
 }
+// One 16-byte global-to-LDS load per lane (global_load_lds_dwordx4): lane l's
+// 16 bytes from src go to lds[l]; lds must be the same for the whole wave.
+// Completion is counted by vmcnt like any load.
+__device__ __forceinline__ void dma16(const float *src, float4 *lds) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src), (lds_void *)(lds), 16, 0, 0);
+}
+
 // Program-order fence for LDS traffic between lanes of one wave.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

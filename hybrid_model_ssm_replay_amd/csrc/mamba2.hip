@@ -452,12 +452,6 @@ __device__ __forceinline__ floatx4 mfma_4x4x1(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
 
-// One 16-byte global-to-LDS load per lane: lane l's 16 bytes go to lds[l].
-__device__ __forceinline__ void dma16(const float *src, float4 *lds) {
-  typedef __attribute__((address_space(3))) void lds_void;
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src), (lds_void *)(lds), 16, 0, 0);
-}
-
 template <int NCH, int RBW>
 __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   constexpr int N = 16 * NCH;
@@ -484,10 +478,14 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   auto draft_C = [&](int i) { return a.Cm + (((size_t)b * T + i) * G + g) * N; };
   const int npass = (T + 3) >> 2;
 
-  // 1. The checkpoint stream, then the drafts' C into LDS (load j of the
-  //    tile by wave j % nwaves), then the pointers.
+  // 1. The checkpoint stream, the pointers, then the drafts' C into LDS (load
+  //    j of the tile by wave j % nwaves).
+  //    The pointer words are read before any global-to-LDS load: the compiler
+  //    keeps loads that follow such a load off the scalar unit.
   float4 s[RBW][NCH];
   load_rows<NCH, RBW>(s, S, rb0, lane);
+  const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
+  const float Ah = a.A[h], Dh = a.D[h];
   {
     const int nload = (npass * NCH * 16 + 63) >> 6;
     for (int j = wave; j < nload; j += nwaves) {
@@ -498,10 +496,8 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
       dma16(draft_C(n < T ? n : T - 1) + 16 * cc + 4 * q2, &ldsC[64 * j]);
     }
   }
-  const float Ah = a.A[h], Dh = a.D[h];
 
   // 2. Pointers; fold-first when the window cannot take T more records.
-  const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
   const int count = pos - ck;
   if (count < 0 || count > L) {
     if (h == 0 && threadIdx.x == 0) {
