@@ -111,14 +111,15 @@ def bench_conv(torch, shape, seed, steps, warmup, pool=32):
 
 
 def bench_verify(torch, shape, T, seed, reps=16):
-    """Replay verify + commit vs snapshot verify + commit vs one conventional step, batch as in shape."""
+    """Replay verify + commit vs snapshot verify + commit, batch as in shape (accepted counts uniform in 0..T)."""
     from hybrid_model_ssm_replay_amd.layer import ReplayLayer, SnapshotLayer
     from synth import InputStream
     ins = InputStream(shape, seed)
     drafts = [{k: torch.from_numpy(v).cuda() for k, v in ins.drafts(T).items()} for _ in range(4)]
     accs = [torch.from_numpy(ins.accepted(T)).cuda() for _ in range(4)]
-    lay = ReplayLayer("mamba2", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
-                      groups=shape.groups, max_draft=T, A=ins.params["A"], D=ins.params["D"])
+    kw = dict(A=ins.params["A"], D=ins.params["D"]) if shape.kind == "mamba2" else {}
+    lay = ReplayLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
+                      groups=shape.groups, max_draft=T, **kw)
     y = torch.empty((shape.batch, T, shape.heads, shape.head_dim), device="cuda")
     tm = Timer(torch)
 
@@ -129,8 +130,8 @@ def bench_verify(torch, shape, T, seed, reps=16):
     tm.run(rv, 8)
     us_replay = tm.run(rv, reps)
     del lay
-    snap = SnapshotLayer("mamba2", shape.batch, shape.heads, shape.head_dim, shape.state_dim, T, groups=shape.groups,
-                         A=ins.params["A"], D=ins.params["D"])
+    snap = SnapshotLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, T,
+                         groups=shape.groups, **kw)
 
     def sv(i):
         snap.verify(drafts[i % 4], y)
@@ -157,6 +158,32 @@ def bench_probe(torch, nbytes=2 << 30):
     del src, dst
     torch.cuda.empty_cache()
     return nbytes / us_read / 1e3, 2 * half / us_copy / 1e3
+
+
+def bench_sweeps(torch, steps=64, warmup=16):
+    """Mamba-2 replay step against the conventional step over the batch (L = 16)
+    and over the window length L (batch 256), on the 128-head layer: the pages
+    report no gain at batch 1, a gain that grows with the batch, and the lowest
+    amortised cost at the full window.  steps and warmup are whole windows for
+    every L swept."""
+    import dataclasses
+
+    from synth import WORKLOADS
+    base = WORKLOADS["mamba2_b256_h128_p64_n128_g8_l16"]
+    out = {"batch": [], "window": []}
+    for B in (1, 4, 16, 64, 256):
+        shp = dataclasses.replace(base, batch=B)
+        r = bench_replay(torch, shp, 7, steps, warmup)
+        c = bench_conv(torch, shp, 7, steps, warmup)
+        out["batch"].append({"batch": B, "replay_us": r, "conventional_us": c, "speedup": c / r})
+        torch.cuda.empty_cache()
+    conv = out["batch"][-1]["conventional_us"]
+    for L in (1, 2, 4, 8, 16):
+        shp = dataclasses.replace(base, window=L)
+        r = bench_replay(torch, shp, 7, steps, warmup)
+        out["window"].append({"window": L, "replay_us": r, "speedup_vs_conventional": conv / r})
+        torch.cuda.empty_cache()
+    return out
 
 
 SPLIT_PAIRS = ((0, 0), (0, 3), (1, 3), (2, 3), (3, 3))
@@ -293,9 +320,18 @@ def main(argv=None):
                              "tokens_per_s": gshape.batch / us_g * 1e6,
                              "traffic_bytes_per_launch": stored_traffic("gdn_replay_step_b256_traffic.txt", "gdn")}
 
+        for T in (4, 8):
+            log("gdn verify T", T)
+            us_rv, us_sv = bench_verify(torch, gshape, T, 2)
+            extra["gdn_b256"][f"verify_T{T}"] = {"replay_verify_commit_us": us_rv, "snapshot_verify_commit_us": us_sv,
+                                                 "replay_over_conventional_step": us_rv / us_gc,
+                                                 "snapshot_over_conventional_step": us_sv / us_gc}
+
     if not args.no_extra:
         log("split precision")
         extra["gdn_split_b64"] = bench_split(torch)
+        log("batch and window sweeps")
+        extra["mamba2_sweeps"] = bench_sweeps(torch)
 
     traffic = stored_traffic("m2_replay_step_b256_traffic.txt", "m2")
     roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
