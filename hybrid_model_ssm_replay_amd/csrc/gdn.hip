@@ -287,7 +287,7 @@ struct SIO<REPLAY_FMT_F8E4M3, NCH, RBW, CM> {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const float4 v = s[k][c];
-        r.v[k][c] = e4m3_encode(v.x) | (e4m3_encode(v.y) << 8) | (e4m3_encode(v.z) << 16) | (e4m3_encode(v.w) << 24);
+        r.v[k][c] = e4m3_encode4(v.x, v.y, v.z, v.w);
       }
   }
   static __device__ __forceinline__ void write(const Raw &r, const StateBuf &b, size_t head, int rb0, int lane) {
@@ -369,20 +369,19 @@ struct SIO<REPLAY_FMT_F4E2M1_B16, NCH, RBW, CM> {
           amax = fmaxf(amax, fmaxf(fmaxf(fabsf(s[k][c].x), fabsf(s[k][c].y)), fmaxf(fabsf(s[k][c].z), fabsf(s[k][c].w))));
         const uint32_t scode = e4m3_encode(__fdiv_rn(amax, 6.f));
         const float sc = e4m3_decode(scode);
+        const E2m1Thr th = e2m1_thresholds(sc);
         scw |= scode << (8 * blk);
 #pragma unroll
         for (int p = 2 * blk; p < 2 * blk + 2; ++p) {
           uint32_t w = 0;
-          if (sc > 0.f) {
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              const float4 v = s[k][2 * p + h2];
-              w |= (e2m1_code(v.x, sc) | (e2m1_code(v.y, sc) << 4) | (e2m1_code(v.z, sc) << 8) |
-                    (e2m1_code(v.w, sc) << 12))
-                   << (16 * h2);
-            }
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const float4 v = s[k][2 * p + h2];
+            w |= (e2m1_code(v.x, th) | (e2m1_code(v.y, th) << 4) | (e2m1_code(v.z, th) << 8) |
+                  (e2m1_code(v.w, th) << 12))
+                 << (16 * h2);
           }
-          r.codes[k][p] = w;
+          r.codes[k][p] = sc > 0.f ? w : 0u;  // a zero scale makes the block zero
         }
       }
       r.scales[k] = scw;
