@@ -2,12 +2,13 @@
 
     python -m hybrid_model_ssm_replay_amd.rocprof_summary trace <kernel_trace.csv>
     python -m hybrid_model_ssm_replay_amd.rocprof_summary traffic <fetch_counter_collection.csv> \
-        <write_counter_collection.csv> <kernel-substring> <probe-copy-bytes> [grid-size]
+        <write_counter_collection.csv> <kernel-substring> <probe-copy-bytes> [grid-size [first-n]]
 
 ``trace`` prints the mean, min and max duration per kernel and launch size
 (grid size in work-items).  ``traffic`` prints FETCH_SIZE and WRITE_SIZE (KiB
 per dispatch) of the named kernel (only its launches of the given grid size,
-when one is given), calibrated
+when one is given, and only the first n of those in dispatch order, when n is
+given), calibrated
 against the library's HBM probe copy kernel, whose bytes are known: it reads and
 writes exactly the same number of bytes, so factor_read = WRITE_SIZE / FETCH_SIZE
 of the probe and factor_write = 1 when the probe's WRITE_SIZE equals the bytes
@@ -29,13 +30,23 @@ def _grid(r) -> int:
     return int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1) * int(r.get("Grid_Size_Z", 1) or 1)
 
 
-def _by_kernel(path: str, value_field: str, grid: int | None = None, with_grid: bool = False):
+def _order(r) -> int:
+    for f in ("Dispatch_Id", "Correlation_Id"):
+        if r.get(f):
+            return int(r[f])
+    return 0
+
+
+def _by_kernel(path: str, value_field: str, grid: int | None = None, with_grid: bool = False,
+               first: int | None = None):
     d = collections.defaultdict(list)
-    for r in csv.DictReader(open(path)):
+    for r in sorted(csv.DictReader(open(path)), key=_order):
         g = _grid(r)
         if grid is not None and g != grid and PROBE_COPY not in r["Kernel_Name"]:
             continue
         key = (r["Kernel_Name"], g) if with_grid else r["Kernel_Name"]
+        if first is not None and PROBE_COPY not in r["Kernel_Name"] and len(d[key]) >= first:
+            continue
         if value_field == "duration":
             d[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         else:
@@ -59,9 +70,9 @@ def trace(path: str) -> str:
 
 
 def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int | None = None,
-            grid: int | None = None) -> dict:
-    fe = _by_kernel(fetch_csv, "Counter_Value", grid)
-    wr = _by_kernel(write_csv, "Counter_Value", grid)
+            grid: int | None = None, first: int | None = None) -> dict:
+    fe = _by_kernel(fetch_csv, "Counter_Value", grid, first=first)
+    wr = _by_kernel(write_csv, "Counter_Value", grid, first=first)
     pk_f, pk_w = _find(fe, PROBE_COPY), _find(wr, PROBE_COPY)
     probe_fetch = sum(fe[pk_f]) / len(fe[pk_f])
     probe_write = sum(wr[pk_w]) / len(wr[pk_w])
@@ -80,7 +91,7 @@ def main(argv):
         print(trace(argv[1]))
     elif argv[0] == "traffic":
         r = traffic(argv[1], argv[2], argv[3], int(argv[4]) if len(argv) > 4 else None,
-                    int(argv[5]) if len(argv) > 5 else None)
+                    int(argv[5]) if len(argv) > 5 else None, int(argv[6]) if len(argv) > 6 else None)
         for k, v in r.items():
             print(f"{k}: {v}")
     else:
