@@ -873,27 +873,53 @@ __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a, GdnStateBufs sb
   store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
 }
 
+__device__ __forceinline__ floatx4 mfma_4x4x1(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
+
 // ---- speculative verify ---------------------------------------------------------
 // c committed records (pseudo-values cached in the ring) then T drafts
-// (c + T <= L after a fold-first).  One forward substitution solves the drafts'
-// pseudo-values; draft i's output is
-//   o_i = e^{g_{c+i}} S0 q_i + sum_{j <= c+i} e^{g_{c+i} - g_j} (k_j . q_i) u_j.
-// S0 q_i is a second MFMA pass over the queries, k_j . q_i an MFMA of the key
-// and query operand registers.  S0 is the read copy as it stands after a
-// fold-first.  The drafts' keys, pseudo-values and scalars are staged in the
-// ring, so that a commit is only a pointer move.
+// (c + T <= L after a fold-first).  Draft d is window record t = c + d:
+//   u_t = beta_t v_t - beta_t e^{g_t} S0 k_t - sum_{j<t} beta_t e^{g_t - g_j} (k_j . k_t) u_j
+//   o_d = e^{g_t} S0 q_d + sum_{j<=t} e^{g_t - g_j} (k_j . q_d) u_j.
+// The products run in passes of four drafts on v_mfma_f32_4x4x1_16b_f32 (16
+// blocks of 4 x 4 x 1; lane l feeds row / column l % 4 of block l / 4 and gets
+// rows 0..3 of column l % 4): with lane l = r + 16 q of the register tile,
+// g = r / 4, m = r % 4, block (g, q) takes rows 16 rb + 4 g + 0..3 (S0 k_d,
+// S0 q_d) or records 4 g + 0..3 (k_j . k_d, k_j . q_d) over the columns of
+// quarter q, and a sum over the quarters completes them, so absent drafts
+// cost no MFMA work.  The drafts' keys and queries and the window's keys
+// reach LDS by direct global-to-LDS loads in the lane-linear operand layout.
+// The draft rows of the triangular system are then solved per state row (one
+// lane per row) with the committed rows known.  The drafts' keys, pseudo-
+// values and scalars are staged in the ring, so that a commit is only a
+// pointer move.
+template <int RBW>
+struct GdnVerifyLds {
+  float W[16 * RBW][17];   // [row][draft]: S0 k_d
+  float SQ[16 * RBW][17];  // [row][draft]: S0 q_d
+  float A[16][17];         // [draft][record]: beta_t e^{g_t - g_j} (k_j . k_t) for j < t, else 0
+  float Bq[16][17];        // [draft][record]: e^{g_t - g_j} (k_j . q_d) for j <= t, else 0
+  float g[16], beta[16];   // record j: decay prefix, beta
+};
+
+template <int RBW>
+union GdnWaveLds {
+  GdnLds<RBW> fold;          // a re-solving fold-first
+  GdnVerifyLds<RBW> verify;  // the drafts (after the fold)
+};
+
 template <int CF, int RF, int NCH, int RBW>
 __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
   constexpr int CM = col_map(CF, RF);
-  __shared__ GdnLds<RBW> lds_all[4];
-  __shared__ float SQ_all[4][16 * RBW][17];  // [row][draft]: S0 q_i
-  __shared__ float KQ_all[4][16][17];        // [record][draft]: k_j . q_i
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int q = lane >> 4, r16 = lane & 15;
-  GdnLds<RBW> &sm = lds_all[wave];
-  float(&SQ)[16 * RBW][17] = SQ_all[wave];
-  float(&KQ)[16][17] = KQ_all[wave];
+  constexpr int kPass = kMaxL / 4;
+  __shared__ float4 ldsK[NCH][64];                 // [chunk cc][record j + 16 q]: k_j at colq(cc, q)
+  __shared__ float4 ldsD[kPass * 2 * NCH * 16];    // [((p 2 + w) NCH + cc) 16 + 4 m + q]: w = 0: k, 1: q of draft 4 p + m
+  __shared__ GdnWaveLds<RBW> lds_all[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int q = lane >> 4, r16 = lane & 15, gq = r16 >> 2, m4 = r16 & 3;
+  GdnVerifyLds<RBW> &sv = lds_all[wave].verify;
   const Shape &sh = a.s;
   const int T = a.T;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -902,15 +928,36 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
   const size_t bh = (size_t)b * H + h;
   const size_t head = bh * DV * DK;
   const GdnRingPtrs rp = gdn_ring_ptrs(a.ring, sh, b, h);
-  const int row = rb0 * 16 + (lane < 16 * RBW ? lane : 0);  // this lane's row in the substitution
+  const int row = rb0 * 16 + (lane < 16 * RBW ? lane : 0);  // this lane's row in the solve
   auto dq_ = [&](int i) { return a.q + (((size_t)b * T + i) * H + h) * DK; };
   auto dk_ = [&](int i) { return a.k + (((size_t)b * T + i) * H + h) * DK; };
   auto dv_ = [&](int i) { return a.v + (((size_t)b * T + i) * H + h) * DV; };
   auto dsc = [&](const float *f, int i) { return f[((size_t)b * T + i) * H + h]; };
+  const int npass = (T + 3) >> 2;
 
+  // 1. The read copy first, the pointer words (before any global-to-LDS load:
+  //    the compiler keeps loads that follow such a load off the scalar unit),
+  //    the drafts' keys and queries into LDS (load j of the tile by wave
+  //    j % nwaves) and this lane's row of the drafts' values.
   typename SIO<RF, NCH, RBW, CM>::Raw raw;
   SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
+  {
+    const int nload = (npass * 2 * NCH * 16) >> 6;
+    for (int j = wave; j < nload; j += nwaves) {
+      const int slot = 64 * j + lane;
+      const int q2 = slot & 3, m2 = (slot >> 2) & 3, pwc = slot >> 4;  // pwc = (p 2 + w) NCH + cc
+      const int cc = pwc % NCH, pw = pwc / NCH;
+      const int n = 4 * (pw >> 1) + m2;
+      const float *src = (pw & 1) ? dq_(n < T ? n : T - 1) : dk_(n < T ? n : T - 1);
+      dma16(src + colq<NCH, CM>(cc, q2), &ldsD[64 * j]);
+    }
+  }
+  float vrow[kMaxL];
+#pragma unroll
+  for (int d = 0; d < kMaxL; ++d) vrow[d] = dv_(d < T ? d : T - 1)[row];
+
+  // 2. Pointers; fold-first when the window cannot take T more records.
   const int count = pos - ck;
   if (count < 0 || count > L) {
     if (h == 0 && threadIdx.x == 0) {
@@ -918,6 +965,7 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
       a.ptr.pos_out[b] = pos;
       a.ptr.ckpt_out[b] = ck;
     }
+    __builtin_amdgcn_s_waitcnt(0);  // no global-to-LDS load outlives the workgroup
     return;
   }
   const bool fold = count + T > L;  // implies count >= 1 because T <= L
@@ -932,36 +980,27 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
       SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
       SIO<CF, NCH, RBW, CM>::decode(s, rc);
     }
-    gdn_fold<CF, RF, NCH, RBW>(s, count, s0, rp, L, rb0, lane, &sm);
+    gdn_fold<CF, RF, NCH, RBW>(s, count, s0, rp, L, rb0, lane, &lds_all[wave].fold);
     store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
     sb0 = wrap(s0, count, L);
   }
   const int c = pos - base, nrec = c + T;
-  // Keys: committed records from the ring, drafts from the input; draft queries.
-  float4 X[NCH], Q[NCH];
+
+  // 3. Window records: every key into LDS (committed from the ring, drafts from
+  //    the input; chunk cc by wave cc % nwaves), this lane's row of the
+  //    committed pseudo-values, and alpha, beta of record r16.
   {
     const int j = r16 < nrec ? r16 : nrec - 1;
     const float *kj = j < c ? rp.rk + (size_t)wrap(sb0, j, L) * rp.ks : dk_(j - c);
-#pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-      const float4 v = ld4(kj + colq<NCH, CM>(cc, q));
-      X[cc] = r16 < nrec ? v : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    const int i = r16 < T ? r16 : T - 1;
-#pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-      const float4 v = ld4(dq_(i) + colq<NCH, CM>(cc, q));
-      Q[cc] = r16 < T ? v : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int cc = wave; cc < NCH; cc += nwaves) dma16(kj + colq<NCH, CM>(cc, q), &ldsK[cc][0]);
   }
-  // This lane's row: cached u_t of the committed records, v of the drafts.
-  float vr[16];
+  float uc[kMaxL - 1];
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int tc = t < nrec ? t : nrec - 1;
-    const float v = tc < c ? rp.ru[(size_t)wrap(sb0, tc, L) * rp.vs + row] : dv_(tc - c)[row];
-    vr[t] = t < nrec ? v : 0.f;
+  for (int j = 0; j < kMaxL - 1; ++j) {
+    const int jc = j < c ? j : 0;
+    const float v = rp.ru[(size_t)wrap(sb0, jc, L) * rp.vs + row];
+    uc[j] = j < c ? v : 0.f;
   }
   float al, be;
   {
@@ -972,57 +1011,114 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
     be = r16 < nrec ? b1 : 0.f;
   }
   if (!fold) SIO<RF, NCH, RBW, CM>::decode(s, raw);
-  // S0 Q^T and K Q^T on the MFMA, into per-wave LDS.
-#pragma unroll
-  for (int k = 0; k < RBW; ++k) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-      acc = mfma_16x16x4(s[k][cc].x, Q[cc].x, acc);
-      acc = mfma_16x16x4(s[k][cc].y, Q[cc].y, acc);
-      acc = mfma_16x16x4(s[k][cc].z, Q[cc].z, acc);
-      acc = mfma_16x16x4(s[k][cc].w, Q[cc].w, acc);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) SQ[16 * k + 4 * q + i][r16] = acc[i];
-  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's global-to-LDS loads have landed
+  __syncthreads();                // and every other wave's; all ring reads are done
+
+  // 4. Record scalars (record j in lane j), then the passes.
   {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    const float gj = prefix_sum16(lane < 16 ? __logf(al) : 0.f, lane);
+    if (lane < 16) {
+      sv.g[lane] = gj;
+      sv.beta[lane] = be;
+    }
+  }
+  wave_lds_sync();
+  for (int p = 0; p < npass; ++p) {
+    const int d = 4 * p + m4;  // this lane's draft
+    const float4 *kd = &ldsD[(p * 2 * NCH) * 16 + 4 * m4 + q];        // k_d at chunk cc: kd[16 cc]
+    const float4 *qd = &ldsD[((p * 2 + 1) * NCH) * 16 + 4 * m4 + q];  // q_d at chunk cc: qd[16 cc]
+    {
+      floatx4 dk = {0.f, 0.f, 0.f, 0.f}, dqq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-      acc = mfma_16x16x4(X[cc].x, Q[cc].x, acc);
-      acc = mfma_16x16x4(X[cc].y, Q[cc].y, acc);
-      acc = mfma_16x16x4(X[cc].z, Q[cc].z, acc);
-      acc = mfma_16x16x4(X[cc].w, Q[cc].w, acc);
+      for (int cc = 0; cc < NCH; ++cc) {
+        const float4 kj = ldsK[cc][lane], kv = kd[16 * cc], qv = qd[16 * cc];
+        dk = mfma_4x4x1(kj.x, kv.x, dk);
+        dk = mfma_4x4x1(kj.y, kv.y, dk);
+        dk = mfma_4x4x1(kj.z, kv.z, dk);
+        dk = mfma_4x4x1(kj.w, kv.w, dk);
+        dqq = mfma_4x4x1(kj.x, qv.x, dqq);
+        dqq = mfma_4x4x1(kj.y, qv.y, dqq);
+        dqq = mfma_4x4x1(kj.z, qv.z, dqq);
+        dqq = mfma_4x4x1(kj.w, qv.w, dqq);
+      }
+      float kk[4], kq[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        kk[v] = sum_quarters(dk[v]);
+        kq[v] = sum_quarters(dqq[v]);
+      }
+      if (q == 0) {
+        const int t = c + d;
+        const float gt = sv.g[t < kMaxL ? t : kMaxL - 1], bt = sv.beta[t < kMaxL ? t : kMaxL - 1];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int j = 4 * gq + v;  // record
+          const float e = __expf(gt - sv.g[j]);
+          sv.A[d][j] = (d < T && j < t) ? bt * e * kk[v] : 0.f;
+          sv.Bq[d][j] = (d < T && j <= t) ? e * kq[v] : 0.f;
+        }
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) KQ[4 * q + i][r16] = acc[i];
+    for (int k = 0; k < RBW; ++k) {
+      floatx4 w = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) {
+        const float4 kv = kd[16 * cc], qv = qd[16 * cc];
+        w = mfma_4x4x1(s[k][cc].x, kv.x, w);
+        w = mfma_4x4x1(s[k][cc].y, kv.y, w);
+        w = mfma_4x4x1(s[k][cc].z, kv.z, w);
+        w = mfma_4x4x1(s[k][cc].w, kv.w, w);
+        sq = mfma_4x4x1(s[k][cc].x, qv.x, sq);
+        sq = mfma_4x4x1(s[k][cc].y, qv.y, sq);
+        sq = mfma_4x4x1(s[k][cc].z, qv.z, sq);
+        sq = mfma_4x4x1(s[k][cc].w, qv.w, sq);
+      }
+      float wv[4], sqv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        wv[v] = sum_quarters(w[v]);
+        sqv[v] = sum_quarters(sq[v]);
+      }
+      if (q == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          sv.W[16 * k + 4 * gq + v][d] = wv[v];
+          sv.SQ[16 * k + 4 * gq + v][d] = sqv[v];
+        }
+      }
+    }
   }
-  // Pseudo-values of the drafts (the committed ones are known).
-  gdn_window<NCH, RBW>(s, X, nrec, c, al, be, vr, sm, lane);
+  wave_lds_sync();
+
+  // 5. The drafts' rows of the system and their outputs, one lane per state row.
   if (lane < 16 * RBW) {
-    float u[16];
+    float u[kMaxL];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) u[t] = t < nrec ? sm.U[t][lane] : 0.f;
-    for (int i = 0; i < T; ++i) {
-      const int last = c + i;
-      const float gi = sm.g[last];
-      float o = __expf(gi) * SQ[lane][i];
+    for (int j = 0; j < kMaxL; ++j) u[j] = j < kMaxL - 1 ? uc[j] : 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j <= last) o += __expf(gi - sm.g[j]) * KQ[j][i] * u[j];
-      a.y[(((size_t)b * T + i) * H + h) * DV + row] = o;
+    for (int t = 0; t < kMaxL; ++t) {
+      if (t >= c && t < nrec) {
+        const int d = t - c;
+        const float bt = sv.beta[t], et = __expf(sv.g[t]);
+        float v = bt * vrow[d] - bt * et * sv.W[lane][d];
+#pragma unroll
+        for (int j = 0; j < t; ++j) v -= sv.A[d][j] * u[j];
+        u[t] = v;
+        float o = et * sv.SQ[lane][d];
+#pragma unroll
+        for (int j = 0; j <= t; ++j) o += sv.Bq[d][j] * u[j];
+        a.y[(((size_t)b * T + d) * H + h) * DV + row] = o;
+        rp.ru[(size_t)wrap(sb0, t, L) * rp.vs + row] = v;  // stage the pseudo-value
+        if constexpr (RF != CF) rp.rv[(size_t)wrap(sb0, t, L) * rp.vs + row] = vrow[d];
+      }
     }
   }
-  // Stage the drafts in the ring after every wave is done with folded slots.
-  __syncthreads();
+  // 6. Stage the drafts' keys and scalars.  The workgroup barrier above already
+  //    ordered every wave's reads of the folded slots before these writes.
   for (int i = 0; i < T; ++i) {
     const int sl = wrap(sb0, c + i, L);
-    if (lane < 16 * RBW) {
-      rp.ru[(size_t)sl * rp.vs + row] = sm.U[c + i][lane];
-      if constexpr (RF != CF) rp.rv[(size_t)sl * rp.vs + row] = dv_(i)[row];
-    }
-    for (int e = threadIdx.x; e < DK; e += 256) rp.rk[(size_t)sl * rp.ks + e] = dk_(i)[e];
+    for (int e = threadIdx.x; e < DK; e += 64 * nwaves) rp.rk[(size_t)sl * rp.ks + e] = dk_(i)[e];
   }
   if (threadIdx.x < T) {
     const int sl = wrap(sb0, c + threadIdx.x, L);
