@@ -97,6 +97,9 @@ def _spec_run(shape, seed, ops, T_max):
 @pytest.mark.parametrize("shape,T_max", [
     (LayerShape("gdn", 4, 3, 64, 32, 3, 6), 6),
     (LayerShape("gdn", 3, 4, 128, 128, 4, 16), 8),
+    (LayerShape("gdn", 2, 3, 128, 128, 3, 16), 16),  # T = L: four passes of drafts, a fold before most verifies
+    (LayerShape("gdn", 3, 2, 64, 128, 2, 12), 11),   # one row block per wave, three passes, L not a power of 2
+    (LayerShape("gdn", 2, 3, 128, 32, 3, 8), 8),     # d_k = 32
 ])
 def test_speculative_sequence(shape, T_max):
     _spec_run(shape, seed=13, ops=60, T_max=T_max)

@@ -109,6 +109,7 @@ def _spec_run(shape, seed, ops, T_max):
     (LayerShape("mamba2", 3, 8, 64, 128, 8, 16), 8),
     (LayerShape("mamba2", 2, 2, 16, 16, 1, 3), 3),
     (LayerShape("mamba2", 2, 2, 16, 32, 1, 12), 12),  # one wave per head, more drafts than 64 / 16
+    (LayerShape("mamba2", 2, 4, 64, 128, 2, 16), 16),  # T = L: four passes of drafts
 ])
 def test_speculative_sequence(shape, T_max):
     _spec_run(shape, seed=5, ops=60, T_max=T_max)

@@ -134,6 +134,49 @@ def test_steps_and_folds_match_oracle(cf, rf):
     assert worst_post <= POST_FOLD_TOL[rf], worst_post
 
 
+@pytest.mark.parametrize("cf,rf", [(FMT_F32, FMT_F4E2M1_B16), (FMT_F4E2M1_B16, FMT_F4E2M1_B16),
+                                   (FMT_F8E4M3, FMT_F8E4M3)])
+def test_speculative_with_many_drafts(cf, rf):
+    """Verify / commit / step sequences with up to 12 drafts (three passes) on a
+    16-record window, against SplitReplaySession; the same bars as above."""
+    import torch
+    from oracle.pointers import PointerMachine
+    shape = LayerShape("gdn", 2, 3, 128, 128, 3, 16)
+    announce("split speculative", shape, cf, rf)
+    ins = InputStream(shape, 21)
+    S0 = ins.initial_state(zeros=False, scale=0.3)
+    lay = _layer(shape, cf, rf, S0, max_draft=12)
+    sess = SplitReplaySession("gdn", S0, shape.window, None, cf, rf, seed=SEED)
+    pm = PointerMachine(shape.batch, shape.window)
+    rng = np.random.default_rng(21)
+    worst_pre, worst_post = 0.0, 0.0
+    for it in range(40):
+        folded = bool(np.any(pm.ckpt_pos > 0))
+        if rng.random() < 0.5:
+            T = int(rng.integers(1, 13))
+            d = ins.drafts(T)
+            e = max_rel_err(host(lay.verify(to_dev(d))), sess.verify(d))
+            pm.verify(T)
+            acc = ins.accepted(T)
+            lay.commit(torch.from_numpy(acc).cuda())
+            sess.commit(acc)
+            pm.commit(acc)
+        else:
+            r = ins.record()
+            e = max_rel_err(host(lay.step(to_dev(r))), sess.step(r))
+            pm.step()
+        folded = folded or bool(np.any(pm.ckpt_pos > 0))
+        if folded:
+            worst_post = max(worst_post, e)
+        else:
+            worst_pre = max(worst_pre, e)
+    pos, ck = (host(t) for t in lay.pointers())
+    assert np.array_equal(pos, pm.pos) and np.array_equal(ck, pm.ckpt_pos)
+    print(f"[split spec] cf={cf} rf={rf} pre-fold {worst_pre:.2e} post-fold {worst_post:.2e}")
+    assert worst_pre <= 1e-4, worst_pre
+    assert worst_post <= POST_FOLD_TOL[rf], worst_post
+
+
 def test_error_curves_over_32768_steps():
     """Per-step error of each format pair against the float64 stepwise oracle on the
     split-precision workload (Gated DeltaNet, 32 heads, d = 128, L = 16, batch 64),
