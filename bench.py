@@ -80,14 +80,14 @@ def dev_records(torch, ins, n):
     return [{k: torch.from_numpy(v).cuda() for k, v in ins.record().items()} for _ in range(n)]
 
 
-def bench_replay(torch, shape, seed, steps, warmup, pool=32):
+def bench_replay(torch, shape, seed, steps, warmup, pool=32, flags=0):
     from hybrid_model_ssm_replay_amd.layer import ReplayLayer
     from synth import InputStream
     ins = InputStream(shape, seed)
     recs = dev_records(torch, ins, pool)
     kw = dict(A=ins.params["A"], D=ins.params["D"]) if shape.kind == "mamba2" else {}
     lay = ReplayLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
-                      groups=shape.groups, **kw)
+                      groups=shape.groups, flags=flags, **kw)
     y = torch.empty((shape.batch, shape.heads, shape.head_dim), device="cuda")
     tm = Timer(torch)
     tm.run(lambda i: lay.step(recs[i % pool], y), warmup)
@@ -290,6 +290,12 @@ def main(argv=None):
         crd, cwr = conventional_step_bytes(lay)
         extra.update({"conventional_step_us": us_c, "conventional_gbs": (crd + cwr) / us_c / 1e3,
                       "speedup_vs_conventional": us_c / us})
+        from hybrid_model_ssm_replay_amd.binding import FLAG_DECAY_SKIP
+        log("replay step with the decay skip", name)
+        us_s = bench_replay(torch, shape, 1, args.steps, args.warmup, flags=FLAG_DECAY_SKIP)
+        extra["decay_skip"] = {"replay_step_us": us_s, "speedup_vs_exact_replay": us / us_s,
+                               "speedup_vs_conventional": us_c / us_s,
+                               "rule": "checkpoint term dropped where exp(A s) < 2^-24 (an approximation)"}
         vshape = WORKLOADS["mamba2_b512_h128_p64_n128_g8_l16"]
         for T in (4, 8):
             log("verify T", T)

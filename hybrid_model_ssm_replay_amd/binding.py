@@ -12,6 +12,7 @@ import os
 KIND_MAMBA2, KIND_GDN = 0, 1
 FMT_F32, FMT_F16_SR, FMT_F8E4M3, FMT_F4E2M1_B16 = 0, 1, 2, 3
 STATUS_ACCEPT_CLAMPED, STATUS_BAD_POINTERS = 0x1, 0x2
+FLAG_DECAY_SKIP = 0x1
 OK, EINVAL, EHIP, ENOTSUP = 0, -1, -2, -3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +32,8 @@ class replay_config(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("groups", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("state_dim", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("max_draft", ctypes.c_int32), ("ckpt_fmt", ctypes.c_int32),
-                ("read_fmt", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("read_fmt", ctypes.c_int32), ("seed", ctypes.c_uint64), ("flags", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
 
 
 class replay_buffers(ctypes.Structure):
@@ -121,9 +123,9 @@ def _check(fn: str, rc: int) -> None:
 
 
 def make_config(kind, batch, heads, groups, head_dim, state_dim, window, max_draft=0,
-                ckpt_fmt=FMT_F32, read_fmt=FMT_F32, seed=0) -> replay_config:
+                ckpt_fmt=FMT_F32, read_fmt=FMT_F32, seed=0, flags=0) -> replay_config:
     return replay_config(kind, batch, heads, groups, head_dim, state_dim, window, max_draft, ckpt_fmt,
-                         read_fmt, seed)
+                         read_fmt, seed, flags, 0)
 
 
 def make_record(*fields) -> replay_record:

@@ -79,6 +79,7 @@ struct M2Ring {
 
 struct M2StepArgs {
   Shape s;
+  int decay_skip;  // REPLAY_FLAG_DECAY_SKIP set
   float *ckpt;
   M2Ring ring;
   PtrHalves ptr;
@@ -90,6 +91,7 @@ struct M2StepArgs {
 
 struct M2VerifyArgs {
   Shape s;
+  int decay_skip;
   int T;
   float *ckpt;
   M2Ring ring;
@@ -102,6 +104,7 @@ struct M2VerifyArgs {
 
 struct M2FlushArgs {
   Shape s;
+  int decay_skip;
   float *ckpt;
   M2Ring ring;
   PtrHalves ptr;

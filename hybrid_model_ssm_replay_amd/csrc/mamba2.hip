@@ -25,6 +25,19 @@
 namespace rssm {
 namespace {
 
+// Decay skip (REPLAY_FLAG_DECAY_SKIP): a head whose window decay exp(A s) is
+// below 2^-24 drops the checkpoint term, in outputs and folds alike, and a step
+// does not read its checkpoint; its fold is then a pure write of the folded
+// records [P3, Perspective, paragraph 1].  The comparison is A s < ln 2^-24 in
+// float32, with s the dt summed over the window records the computation uses.
+constexpr float kDecaySkipLog = -16.635532333438686f;  // ln 2^-24
+
+// exp(A s), or 0 when the decay skip drops it.
+template <bool SKIP>
+__device__ __forceinline__ float s0_weight(float As) {
+  return (SKIP && As < kDecaySkipLog) ? 0.f : __expf(As);
+}
+
 template <int NCH>
 struct M2Smem {
   float Bs[kMaxL][16 * NCH + 16];  // fold: B records (rows padded: conflict-free MFMA operand reads)
@@ -89,7 +102,7 @@ __device__ __forceinline__ float suffix_sum16(float v, int lane, float *total) {
 // Fold the cnt (1..L) committed records at positions base .. base+cnt-1 into
 // the register tile: s <- exp(A s_{1..cnt}) s + sum_r exp(A s_{r+1..cnt}) dt_r x_r B_r^T.
 // Ends with a barrier; sm.Bs is free again afterwards.
-template <int NCH, int RBW>
+template <int NCH, int RBW, bool SKIP>
 __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm, int cnt, int base,
                                           float Ah, const float *rx, const float *rdt, const float *rB,
                                           int L, size_t xs, const TileCtx &t) {
@@ -107,7 +120,7 @@ __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm
   float total;
   const float seg = suffix_sum16(dtv, t.lane, &total);
   const float f = __expf(Ah * seg) * dtv;
-  const float scale = __expf(Ah * total);
+  const float scale = s0_weight<SKIP>(Ah * total);
   lds_barrier();
   const int nsteps = rows4 >> 2;
 #pragma unroll
@@ -185,14 +198,14 @@ __device__ __forceinline__ void fold_load(FoldIn<NCH, RBW> &fi, int cnt, int s0,
   }
 }
 
-template <int NCH, int RBW>
+template <int NCH, int RBW, bool SKIP>
 __device__ __forceinline__ void fold_apply(float4 (&s)[RBW][NCH], FoldIn<NCH, RBW> &fi, float Ah, int lane) {
   const int q = lane >> 4;
   const float dtv = fi.f;
   float total;
   const float seg = suffix_sum16(dtv, lane, &total);
   const float f = __expf(Ah * seg) * dtv;
-  const float scale = __expf(Ah * total);
+  const float scale = s0_weight<SKIP>(Ah * total);
 #pragma unroll
   for (int k = 0; k < RBW; ++k) {
     float xb[4];  // MFMA B operand: f_r x_r[row], r = 4 st + q  (K = record, N = row)
@@ -247,7 +260,7 @@ __device__ __forceinline__ float pick(const float (&acc)[RBW], int sel) {
 // columns), bdot (the lane's partial B_{r16} . C), dtv (dt of record `lane`,
 // lanes 0..15), xr[st][k] (x of record 4 st + q at row block k).  Returns the
 // finished output of row 16 (rb0 + q) + r16 (lanes with q < RBW).
-template <int NCH, int RBW>
+template <int NCH, int RBW, bool SKIP>
 __device__ __forceinline__ float replay_output(const float4 (&s)[RBW][NCH], const float4 (&cv)[NCH], float bdot,
                                                float dtv, const float (&xr)[4][RBW], int m, float Ah, int lane) {
   const int q = lane >> 4;
@@ -255,7 +268,7 @@ __device__ __forceinline__ float replay_output(const float4 (&s)[RBW][NCH], cons
   float total;
   const float seg = suffix_sum16(dtv, lane, &total);
   const float w = lane < m ? __expf(Ah * seg) * dtv * dot : 0.f;
-  const float scale = __expf(Ah * total);
+  const float scale = s0_weight<SKIP>(Ah * total);
   float acc[RBW];
 #pragma unroll
   for (int k = 0; k < RBW; ++k) {
@@ -270,7 +283,7 @@ __device__ __forceinline__ float replay_output(const float4 (&s)[RBW][NCH], cons
   return pick<RBW>(acc, q);
 }
 
-template <int NCH, int RBW>
+template <int NCH, int RBW, bool SKIP>
 __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   constexpr int N = 16 * NCH;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
@@ -293,8 +306,10 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   // 1. Everything whose address needs no pointer, checkpoint first: its loads
   //    are then in flight while the pointers arrive.  (Loads complete in issue
   //    order, so nothing issued later can delay it.)
+  //    With the decay skip the checkpoint stream waits for the decision, which
+  //    needs the pointers and the head's dt ring row.
   float4 s[RBW][NCH];
-  load_rows<NCH, RBW>(s, S, rb0, lane);
+  if constexpr (!SKIP) load_rows<NCH, RBW>(s, S, rb0, lane);
   float4 cv[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) cv[c] = ld4(Cin + 16 * c + 4 * q);
@@ -316,6 +331,22 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   const bool fold = count == L;
   const int s0 = fmod_(ck, sh.fL), s0b = fmod_(ck, sh.f2L);  // slots of window record 0
   const int slot = wrap(s0, count, L), slotb = wrap(s0b, count, 2 * L);  // slots of this token
+  if constexpr (SKIP) {
+    // The checkpoint term this call uses: the fold's (L records) or this
+    // token's output (count + 1 records).  Read the checkpoint only if it stays.
+    const int n = fold ? L : count + 1;
+    const int j = r16 < n ? r16 : 0;
+    const float d = __shfl(dtrow, wrap(s0, j < count ? j : 0, L), kWave);
+    const float tot = sum16(r16 < n ? ((!fold && r16 == count) ? dt_in : d) : 0.f);
+    if (Ah * tot < kDecaySkipLog) {
+#pragma unroll
+      for (int k = 0; k < RBW; ++k)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) s[k][c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      load_rows<NCH, RBW>(s, S, rb0, lane);
+    }
+  }
 
   float bdot = 0.f, dtv;
   float xr[4][RBW];
@@ -364,7 +395,7 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
       for (int st = 0; st < 4; ++st) xr[st][k] = (st == 0 && q == 0) ? v : 0.f;
     }
     dtv = lane == 0 ? dt_in : 0.f;
-    fold_apply<NCH, RBW>(s, fi, Ah, lane);
+    fold_apply<NCH, RBW, SKIP>(s, fi, Ah, lane);
     store_rows<NCH, RBW>(s, S, rb0, lane);
     base = pos;
     // This token's B . C after the fold: computing it earlier keeps more
@@ -374,7 +405,7 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
     bdot = r16 == 0 ? bdot : 0.f;
   }
   const int m = pos - base + 1;
-  const float out = replay_output<NCH, RBW>(s, cv, bdot, dtv, xr, m, Ah, lane);
+  const float out = replay_output<NCH, RBW, SKIP>(s, cv, bdot, dtv, xr, m, Ah, lane);
 
   // 4. Append this token's record.  After a fold the dt slot being written
   //    held a record that the other waves of a multi-wave head also read.
@@ -395,7 +426,7 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
 }
 
 // ---- explicit flush ---------------------------------------------------------
-template <int NCH, int RBW>
+template <int NCH, int RBW, bool SKIP>
 __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
   constexpr int N = 16 * NCH;
   __shared__ M2Smem<NCH> sm;
@@ -416,13 +447,25 @@ __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
   }
   if (!fold) return;
   float *S = a.ckpt + ((size_t)b * sh.H + h) * P * N;
-  float4 s[RBW][NCH];
-  load_tile<NCH, RBW>(s, S, t);
   const size_t xs = (size_t)sh.B * sh.H * P;
   const float *rx = a.ring.x + ((size_t)b * sh.H + h) * P;
   const float *rdt = a.ring.dt + ((size_t)b * sh.H + h) * L;
   const float *rB = a.ring.Bm + ((size_t)b * sh.G + g) * 2 * L * N;
-  fold_tile<NCH, RBW>(s, sm, count, ck, a.A[h], rx, rdt, rB, L, xs, t);
+  float4 s[RBW][NCH];
+  bool keep = true;  // the checkpoint term survives the decay skip
+  if constexpr (SKIP) {
+    const float d = rdt[(ck + (t.r16 < count ? t.r16 : 0)) % L];
+    keep = !(a.A[h] * sum16(t.r16 < count ? d : 0.f) < kDecaySkipLog);
+  }
+  if (keep) {
+    load_tile<NCH, RBW>(s, S, t);
+  } else {
+#pragma unroll
+    for (int k = 0; k < RBW; ++k)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) s[k][c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  fold_tile<NCH, RBW, SKIP>(s, sm, count, ck, a.A[h], rx, rdt, rB, L, xs, t);
   store_tile<NCH, RBW>(s, S, t);
 }
 
@@ -452,7 +495,7 @@ __device__ __forceinline__ floatx4 mfma_4x4x1(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
 
-template <int NCH, int RBW>
+template <int NCH, int RBW, bool SKIP>
 __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   constexpr int N = 16 * NCH;
   constexpr int kPass = kMaxL / 4;
@@ -513,7 +556,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   if (fold) {
     FoldIn<NCH, RBW> fi;
     fold_load<NCH, RBW>(fi, count, fmod_(ck, sh.fL), fmod_(ck, sh.f2L), rx, rdt, rB, L, xs, rb0, lane);
-    fold_apply<NCH, RBW>(s, fi, Ah, lane);
+    fold_apply<NCH, RBW, SKIP>(s, fi, Ah, lane);
     store_rows<NCH, RBW>(s, S, rb0, lane);
     base = pos;
   }
@@ -593,7 +636,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
       for (int st = 0; st < 4; ++st)
         if (j == 4 * st + q + 1) seg[st] = tot;
     }
-    const float sc = __expf(Ah * tot);
+    const float sc = s0_weight<SKIP>(Ah * tot);
     float cb[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -784,23 +827,35 @@ int dispatch(const Args &a, int N, int P, int B, int H, bool wave_per_head, hipS
   struct name {                                \
     static constexpr auto fn = kern<NCH, RBW>; \
   };
-RSSM_WRAP(StepK, m2_replay_step)
-RSSM_WRAP(FlushK, m2_flush)
-RSSM_WRAP(VerifyK, m2_replay_verify)
+#define RSSM_WRAP_SKIP(name, kern, SKIP_)             \
+  template <int NCH, int RBW>                         \
+  struct name {                                       \
+    static constexpr auto fn = kern<NCH, RBW, SKIP_>; \
+  };
+RSSM_WRAP_SKIP(StepK, m2_replay_step, false)
+RSSM_WRAP_SKIP(StepSkipK, m2_replay_step, true)
+RSSM_WRAP_SKIP(FlushK, m2_flush, false)
+RSSM_WRAP_SKIP(FlushSkipK, m2_flush, true)
+RSSM_WRAP_SKIP(VerifyK, m2_replay_verify, false)
+RSSM_WRAP_SKIP(VerifySkipK, m2_replay_verify, true)
 RSSM_WRAP(ConvK, m2_conv_step)
 RSSM_WRAP(SnapK, m2_snapshot_verify)
+#undef RSSM_WRAP_SKIP
 #undef RSSM_WRAP
 
 }  // namespace
 
 int launch_m2_step(const M2StepArgs &a, hipStream_t st) {
-  return dispatch<StepK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
+  return a.decay_skip ? dispatch<StepSkipK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st)
+                      : dispatch<StepK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
 }
 int launch_m2_flush(const M2FlushArgs &a, hipStream_t st) {
-  return dispatch<FlushK>(a, a.s.N, a.s.P, a.s.B, a.s.H, false, st);
+  return a.decay_skip ? dispatch<FlushSkipK>(a, a.s.N, a.s.P, a.s.B, a.s.H, false, st)
+                      : dispatch<FlushK>(a, a.s.N, a.s.P, a.s.B, a.s.H, false, st);
 }
 int launch_m2_verify(const M2VerifyArgs &a, hipStream_t st) {
-  return dispatch<VerifyK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
+  return a.decay_skip ? dispatch<VerifySkipK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st)
+                      : dispatch<VerifyK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
 }
 int launch_m2_conv(const M2ConvArgs &a, hipStream_t st) {
   return dispatch<ConvK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);

@@ -30,6 +30,8 @@ int check_cfg(const replay_config *c) {
     if (c->head_dim != 64 && c->head_dim != 128) return REPLAY_EINVAL;
     if (c->state_dim < 32) return REPLAY_EINVAL;
   }
+  if ((c->flags & ~REPLAY_FLAG_DECAY_SKIP) || c->reserved) return REPLAY_EINVAL;
+  if ((c->flags & REPLAY_FLAG_DECAY_SKIP) && c->kind != REPLAY_KIND_MAMBA2) return REPLAY_ENOTSUP;
   if (c->ckpt_fmt < REPLAY_FMT_F32 || c->ckpt_fmt > REPLAY_FMT_F4E2M1_B16) return REPLAY_EINVAL;
   if (c->read_fmt < REPLAY_FMT_F32 || c->read_fmt > REPLAY_FMT_F4E2M1_B16) return REPLAY_EINVAL;
   if (c->ckpt_fmt == REPLAY_FMT_F32 && c->read_fmt == REPLAY_FMT_F32) return REPLAY_OK;
@@ -206,6 +208,7 @@ int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *strea
   if (c.kind == REPLAY_KIND_MAMBA2) {
     M2StepArgs a{};
     a.s = shape_of(c);
+    a.decay_skip = (c.flags & REPLAY_FLAG_DECAY_SKIP) ? 1 : 0;
     a.ckpt = (float *)ctx->buf.ckpt;
     a.ring = m2_ring(*ctx);
     a.ptr = halves(*ctx);
@@ -245,6 +248,7 @@ int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream) {
   if (c.kind == REPLAY_KIND_MAMBA2) {
     M2FlushArgs a{};
     a.s = shape_of(c);
+    a.decay_skip = (c.flags & REPLAY_FLAG_DECAY_SKIP) ? 1 : 0;
     a.ckpt = (float *)ctx->buf.ckpt;
     a.ring = m2_ring(*ctx);
     a.ptr = halves(*ctx);
@@ -275,6 +279,7 @@ int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float
   if (c.kind == REPLAY_KIND_MAMBA2) {
     M2VerifyArgs a{};
     a.s = shape_of(c);
+    a.decay_skip = (c.flags & REPLAY_FLAG_DECAY_SKIP) ? 1 : 0;
     a.T = T;
     a.ckpt = (float *)ctx->buf.ckpt;
     a.ring = m2_ring(*ctx);

@@ -57,13 +57,14 @@ class ReplayLayer:
     """One layer's replay state on the current CUDA (HIP) device."""
 
     def __init__(self, kind, batch, heads, head_dim, state_dim, window, groups=None, max_draft=0,
-                 ckpt_fmt=B.FMT_F32, read_fmt=B.FMT_F32, seed=0, A=None, D=None, ckpt0=None, device="cuda"):
+                 ckpt_fmt=B.FMT_F32, read_fmt=B.FMT_F32, seed=0, A=None, D=None, ckpt0=None, device="cuda",
+                 flags=0):
         B.load_library()
         k = _kind(kind)
         groups = heads if groups is None else groups
         self.shapes = _Shapes(k, batch, heads, groups, head_dim, state_dim)
         self.cfg = B.make_config(k, batch, heads, groups, head_dim, state_dim, window, max_draft, ckpt_fmt,
-                                 read_fmt, seed)
+                                 read_fmt, seed, flags)
         rc = B.replay_validate_config(self.cfg)
         if rc != B.OK:
             raise B.ReplayError("replay_validate_config", rc)

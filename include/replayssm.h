@@ -55,6 +55,9 @@ extern "C" {
 #define REPLAY_FMT_F8E4M3 2     /* OCP FP8 e4m3fn, round to nearest even, saturating */
 #define REPLAY_FMT_F4E2M1_B16 3 /* 4-bit e2m1 values, one e4m3 scale per 16 */
 
+/* Option flags (replay_config.flags). */
+#define REPLAY_FLAG_DECAY_SKIP 0x1u /* Mamba-2: drop the checkpoint term of heads whose decay is below 2^-24 */
+
 /* Return codes. */
 #define REPLAY_OK 0
 #define REPLAY_EINVAL (-1)
@@ -89,6 +92,15 @@ extern "C" {
  *               fold that sets ckpt_pos of sequence b draws element e of head h
  *               from word e % 4 of Philox(counter (e / 4, h, b, ckpt_pos),
  *               key (seed low 32 bits, seed high 32 bits)), top 24 bits).
+ *   flags       0 or REPLAY_FLAG_DECAY_SKIP (Mamba-2 only, else REPLAY_ENOTSUP):
+ *               a head whose window decay exp(A s) (s = the dt summed over the
+ *               window records a computation uses) is below 2^-24 drops the
+ *               checkpoint term: a step then does not read that head's
+ *               checkpoint, and its fold is a pure write of the folded records
+ *               [P3, Perspective, paragraph 1].  An approximation: each output
+ *               moves by at most 2^-24 |S0 C|.  Verify applies the same rule to
+ *               its outputs and fold-first but always reads the checkpoint.
+ *   reserved    must be 0.
  * Supported format pairs (ckpt_fmt, read_fmt): (F32, F32) for both families;
  * for Gated DeltaNet with state_dim = 128 also (F32 | F16_SR | F8E4M3, F4E2M1_B16)
  * (split precision) and (F16_SR, F16_SR), (F8E4M3, F8E4M3), (F4E2M1_B16,
@@ -118,6 +130,8 @@ typedef struct replay_config {
   int32_t ckpt_fmt;
   int32_t read_fmt;
   uint64_t seed;
+  uint32_t flags;
+  uint32_t reserved;
 } replay_config;
 
 /*

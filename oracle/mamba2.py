@@ -28,6 +28,14 @@ so the newest output needs one read of S0 and the buffered records:
 Decay factors are always formed from segment sums s_m - s_j, never as a ratio
 of two cumulative decays, which would underflow to 0/0 for strongly decaying
 heads.
+
+Decay skip (optional).  The pages name as a next direction letting heads whose
+decay has become negligible skip the checkpoint read on non-fold steps and
+turning their fold into a pure write [P3, Perspective, paragraph 1], without a
+threshold.  Reading taken: the checkpoint term of a head is dropped when
+A s_m < ln 2^-24 (the decay exp(A s_m) is below float32's unit roundoff), in
+outputs and in folds alike: replay_output and fold take skip_below = that
+logarithm.
 """
 from __future__ import annotations
 
@@ -68,7 +76,16 @@ def _cumsum_dt(recs):
     return np.cumsum(np.stack([np.asarray(r["dt"], np.float64) for r in recs]), axis=0)  # [m, H]
 
 
-def replay_output(S0, recs, A, D):
+DECAY_SKIP_LOG = -24.0 * np.log(2.0)  # ln 2^-24
+
+
+def _s0_weight(A, s_m, skip_below):
+    """exp(A s_m), or 0 for heads whose decay is below the skip threshold."""
+    w = np.exp(A * s_m)
+    return w if skip_below is None else np.where(A * s_m < skip_below, 0.0, w)
+
+
+def replay_output(S0, recs, A, D, skip_below=None):
     """Output of the newest record, from checkpoint S0 and the buffered records.
 
     One sequence.  S0 [H, P, N]; recs: records 1..m since the checkpoint,
@@ -81,7 +98,7 @@ def replay_output(S0, recs, A, D):
     s = _cumsum_dt(recs)
     newest = recs[-1]
     Cm = np.asarray(newest["C"], np.float64)[g]          # [H, N]
-    y = np.exp(A * s[-1])[:, None] * np.einsum("hpn,hn->hp", S0, Cm)
+    y = _s0_weight(A, s[-1], skip_below)[:, None] * np.einsum("hpn,hn->hp", S0, Cm)
     for j, r in enumerate(recs):
         seg = s[-1] - s[j]                              # dt summed over records j+1..m
         Bj = np.asarray(r["B"], np.float64)[g]
@@ -90,7 +107,7 @@ def replay_output(S0, recs, A, D):
     return y + np.asarray(D, np.float64)[:, None] * np.asarray(newest["x"], np.float64)
 
 
-def fold(S0, recs, A):
+def fold(S0, recs, A, skip_below=None):
     """New checkpoint after folding records 1..m into S0 (one sequence)."""
     S0 = np.asarray(S0, np.float64)
     A = np.asarray(A, np.float64)
@@ -99,7 +116,7 @@ def fold(S0, recs, A):
     H, G = S0.shape[0], recs[0]["B"].shape[0]
     g = head_group(H, G)
     s = _cumsum_dt(recs)
-    S = np.exp(A * s[-1])[:, None, None] * S0
+    S = _s0_weight(A, s[-1], skip_below)[:, None, None] * S0
     for j, r in enumerate(recs):
         coef = np.exp(A * (s[-1] - s[j])) * np.asarray(r["dt"], np.float64)          # [H]
         xj = np.asarray(r["x"], np.float64)

@@ -44,14 +44,14 @@ class _Kind:
             return mamba2.step(S, r["x"], r["B"], r["C"], r["dt"], self.params["A"], self.params["D"])
         return gdn.step(S, r["q"], r["k"], r["v"], r["alpha"], r["beta"])
 
-    def output(self, S0, recs):
+    def output(self, S0, recs, skip_below=None):
         if self.kind == "mamba2":
-            return mamba2.replay_output(S0, recs, self.params["A"], self.params["D"])
+            return mamba2.replay_output(S0, recs, self.params["A"], self.params["D"], skip_below)
         return gdn.replay_output(S0, recs, recs[-1]["q"])
 
-    def fold(self, S0, recs):
+    def fold(self, S0, recs, skip_below=None):
         if self.kind == "mamba2":
-            return mamba2.fold(S0, recs, self.params["A"])
+            return mamba2.fold(S0, recs, self.params["A"], skip_below)
         return gdn.fold(S0, recs)
 
 
@@ -88,8 +88,13 @@ class StepwiseSession:
 
 
 class ReplaySession:
-    def __init__(self, kind: str, state0, window: int, params: dict | None = None):
+    """The method: checkpoint + ring of the last L records, lazy folds.  With
+    decay_skip (Mamba-2), heads whose window decay is below 2^-24 drop the
+    checkpoint term in outputs and folds (see oracle/mamba2.py)."""
+
+    def __init__(self, kind: str, state0, window: int, params: dict | None = None, decay_skip: bool = False):
         self.k = _Kind(kind, params or {})
+        self.skip = mamba2.DECAY_SKIP_LOG if decay_skip else None
         self.ckpt = np.array(state0, np.float64)        # [batch, H, P, N]
         self.ptr = PointerMachine(self.ckpt.shape[0], window)
         self.recs = [dict() for _ in range(self.ckpt.shape[0])]   # position -> record
@@ -103,7 +108,7 @@ class ReplaySession:
 
     def _fold(self, b):
         pos = int(self.ptr.pos[b])
-        self.ckpt[b] = self.k.fold(self.ckpt[b], self._window(b, pos))
+        self.ckpt[b] = self.k.fold(self.ckpt[b], self._window(b, pos), self.skip)
         for p in [p for p in self.recs[b] if p < pos]:
             del self.recs[b][p]                          # folded records leave the window
 
@@ -116,7 +121,7 @@ class ReplaySession:
         ys = []
         for b in range(self.batch):
             self.recs[b][int(pos_before[b])] = _rec_b(rec, b)
-            ys.append(self.k.output(self.ckpt[b], self._window(b, int(self.ptr.pos[b]))))
+            ys.append(self.k.output(self.ckpt[b], self._window(b, int(self.ptr.pos[b])), self.skip))
         return np.stack(ys)
 
     def verify(self, drafts):
@@ -131,7 +136,8 @@ class ReplaySession:
             for i in range(T):
                 self.recs[b][p0 + i] = _draft_b(drafts, b, i)
             committed = self._window(b, p0)
-            out.append(np.stack([self.k.output(self.ckpt[b], committed + [self.recs[b][p0 + j] for j in range(i + 1)])
+            out.append(np.stack([self.k.output(self.ckpt[b], committed + [self.recs[b][p0 + j] for j in range(i + 1)],
+                                               self.skip)
                                  for i in range(T)]))
         return np.stack(out)
 

@@ -242,3 +242,52 @@ def test_snapshot_baseline():
         snap.commit(torch.from_numpy(acc).cuda())
         ref.commit(acc)
         assert ckpt_rel_err(host(snap.state()), ref.state) <= TOL
+
+
+def test_decay_skip_matches_oracle():
+    """REPLAY_FLAG_DECAY_SKIP: steps, verifies, commits and a flush against the
+    oracle session with the same rule (heads whose window decay is below 2^-24
+    drop the checkpoint term), and against the exact method (the dropped terms
+    are below float32 rounding)."""
+    import torch
+    from hybrid_model_ssm_replay_amd import binding as B
+    from hybrid_model_ssm_replay_amd.layer import ReplayLayer
+    shape = LayerShape("mamba2", 3, 8, 64, 128, 2, 16)
+    announce("mamba2 decay skip", shape)
+    ins = InputStream(shape, 9)
+    params = {"A": ins.params["A"].copy(), "D": ins.params["D"]}
+    params["A"][:3] = np.array([-80.0, -40.0, -25.0], np.float32)  # heads that skip within a window
+    S0 = ins.initial_state(zeros=False, scale=0.5)
+    lay = ReplayLayer("mamba2", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
+                      groups=shape.groups, max_draft=6, A=params["A"], D=params["D"], ckpt0=S0,
+                      flags=B.FLAG_DECAY_SKIP)
+    skip = ReplaySession("mamba2", S0, shape.window, params, decay_skip=True)
+    exact = ReplaySession("mamba2", S0, shape.window, params)
+    rng = np.random.default_rng(9)
+    worst_skip = worst_exact = 0.0
+    skipped_any = False
+    for it in range(50):
+        if it % 7 == 6:
+            T = int(rng.integers(1, 7))
+            d = ins.drafts(T)
+            y = host(lay.verify(to_dev(d)))
+            ys, ye = skip.verify(d), exact.verify(d)
+            acc = ins.accepted(T)
+            lay.commit(torch.from_numpy(acc).cuda())
+            skip.commit(acc)
+            exact.commit(acc)
+        else:
+            r = ins.record()
+            y = host(lay.step(to_dev(r)))
+            ys, ye = skip.step(r), exact.step(r)
+        worst_skip = max(worst_skip, max_rel_err(y, ys))
+        worst_exact = max(worst_exact, max_rel_err(y, ye))
+        skipped_any = skipped_any or not np.allclose(ys, ye, rtol=0, atol=0)
+    lay.flush()
+    skip.flush()
+    torch.cuda.synchronize()
+    assert skipped_any  # the rule did drop terms in this run
+    assert worst_skip <= TOL, worst_skip
+    assert worst_exact <= TOL, worst_exact
+    assert ckpt_rel_err(host(lay.checkpoint), skip.ckpt) <= TOL
+    assert lay.status == 0

@@ -151,3 +151,41 @@ def test_replay_session_equals_stepwise(L):
             # L = 1 is conventional decoding: every step folds the previous token,
             # so the checkpoint is the full state before this token.
             np.testing.assert_allclose(rep.ckpt, state_before, rtol=1e-12, atol=1e-12)
+
+
+def test_decay_skip_drops_exactly_the_checkpoint_term():
+    """With the decay skip, a head whose window decay A s_m is below ln 2^-24
+    gives exactly the output (and fold) of a zero checkpoint, and every other
+    head exactly the full replay form; the dropped term is below 2^-24 of
+    |S0 C| [P3, Perspective, paragraph 1]."""
+    rng = np.random.default_rng(4)
+    H, P, N, G, m = 4, 3, 5, 2, 9
+    A = np.array([-400.0, -0.01, -20.0, -1.0])
+    D = rng.standard_normal(H)
+    S0 = rng.standard_normal((H, P, N))
+    recs = [{"x": rng.standard_normal((H, P)), "B": rng.standard_normal((G, N)), "C": rng.standard_normal((G, N)),
+             "dt": rng.uniform(0.05, 0.3, H)} for _ in range(m)]
+    thr = mamba2.DECAY_SKIP_LOG
+    assert abs(thr - np.log(2.0 ** -24)) < 1e-12
+    zero = np.zeros_like(S0)
+    for k in range(1, m + 1):
+        window = recs[:k]
+        s = np.sum([r["dt"] for r in window], axis=0)
+        skipped = A * s < thr
+        y_skip = mamba2.replay_output(S0, window, A, D, skip_below=thr)
+        y_full = mamba2.replay_output(S0, window, A, D)
+        y_zero = mamba2.replay_output(zero, window, A, D)
+        f_skip = mamba2.fold(S0, window, A, skip_below=thr)
+        f_full, f_zero = mamba2.fold(S0, window, A), mamba2.fold(zero, window, A)
+        for h in range(H):
+            want_y, want_f = (y_zero[h], f_zero[h]) if skipped[h] else (y_full[h], f_full[h])
+            np.testing.assert_allclose(y_skip[h], want_y, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(f_skip[h], want_f, rtol=0, atol=1e-12)
+            if skipped[h]:
+                g = h // (H // G)
+                bound = 2.0 ** -24 * np.abs(S0[h] @ window[-1]["C"][g]).max()
+                assert np.abs(y_skip[h] - y_full[h]).max() <= bound
+    # head 0 skips from the first record on, head 1 never, head 2 from some record within the window
+    assert A[0] * recs[0]["dt"][0] < thr and A[1] * np.sum([r["dt"][1] for r in recs]) > thr
+    s2 = np.cumsum([r["dt"][2] for r in recs])
+    assert A[2] * s2[0] > thr and A[2] * s2[-1] < thr
