@@ -20,6 +20,15 @@ CPU and the GPU side, so that every rounding decision is bit-identical):
   0.75, 1.25, 1.75, 2.5, 3.5, 5; every t s is exact in float32); a zero
   magnitude carries no sign.  Two codes per byte, the even element in the low
   nibble.
+* two-axis e2m1 (a reading of the pages' suggestion of separate scales along
+  the state and channel dimensions for the read copy [P1, Perspective 2]):
+  the block scales above run along the state axis inside one
+  channel row; in addition every state column n of a head has a power-of-two
+  scale 2^e[n] (one signed byte), e = max(floor(log2 amax_n) - 5, -126) from
+  the column's largest magnitude over the head's channels (-126 for a zero
+  column).  The element codes and block scales are the block format of
+  S[p, n] / 2^e[n] (an exact division unless the quotient is subnormal), and
+  the decoded value is e2m1 x block scale x 2^e[n].
 * fp16 with stochastic rounding: SR(x, r) = RTZ_fp16(x + sign(x) (r / 2^24)
   ulp16(|x|)) for a 24-bit random integer r, saturating at +-65504, where
   ulp16 is the binary16 spacing at |x| (2^-24 below 2^-14).
@@ -118,6 +127,34 @@ def e2m1_block_decode(packed, scales) -> np.ndarray:
     s = e4m3_decode(scales)
     n = vals.shape[-1]
     return (vals.reshape(vals.shape[:-1] + (n // 16, 16)) * s[..., None]).reshape(vals.shape).astype(np.float32)
+
+
+# ---- e2m1 with block scales along the state axis and a scale per state column ----------
+def column_exponents(S) -> np.ndarray:
+    """S [..., P, N] float32 -> int8 e[..., N]: column n of each head takes the scale 2^e[n],
+    e = max(floor(log2 amax_n) - 5, -126) with amax_n = max_p |S[p, n]| (e = -126 for an
+    all-zero column), so that the column's largest magnitude divided by 2^e lies in [32, 64)."""
+    S = np.asarray(S, np.float32)
+    amax = np.max(np.abs(S), axis=-2).astype(np.float64)
+    _, ex = np.frexp(amax)                       # amax = f 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
+    e = np.where(amax > 0, ex - 1 - 5, -126)
+    return np.maximum(e, -126).astype(np.int8)
+
+
+def e2m1_cs_encode(S):
+    """S [..., P, N] float32 -> (packed codes [..., P, N/2], block scales [..., P, N/16],
+    column exponents [..., N] int8): the e2m1 block format of S[p, n] / 2^e[n]."""
+    S = np.asarray(S, np.float32)
+    e = column_exponents(S)
+    y = (S.astype(np.float64) * np.exp2(-e.astype(np.float64))[..., None, :]).astype(np.float32)
+    packed, scales = e2m1_block_encode(y)
+    return packed, scales, e
+
+
+def e2m1_cs_decode(packed, scales, e) -> np.ndarray:
+    """Float64 value of each element: e2m1 value x block scale x 2^e[column] (exact)."""
+    y = e2m1_block_decode(packed, scales).astype(np.float64)
+    return y * np.exp2(np.asarray(e, np.float64))[..., None, :]
 
 
 # ---- fp16 with stochastic rounding ------------------------------------------------------

@@ -152,7 +152,7 @@ class ReplaySession:
 
 
 # ---- split-precision state ---------------------------------------------------------
-FMT_F32, FMT_F16_SR, FMT_F8E4M3, FMT_F4E2M1_B16 = 0, 1, 2, 3
+FMT_F32, FMT_F16_SR, FMT_F8E4M3, FMT_F4E2M1_B16, FMT_F4E2M1_CS = 0, 1, 2, 3, 4
 
 
 def encode_state(S32, fmt, seed=0, b=0, ckpt_pos=0):
@@ -172,6 +172,8 @@ def encode_state(S32, fmt, seed=0, b=0, ckpt_pos=0):
         return quant.e4m3_encode(S32)
     if fmt == FMT_F4E2M1_B16:
         return quant.e2m1_block_encode(S32)
+    if fmt == FMT_F4E2M1_CS:
+        return quant.e2m1_cs_encode(S32)
     raise ValueError(fmt)
 
 
@@ -183,6 +185,8 @@ def decode_state(stored, fmt):
         return np.asarray(stored, np.float64)
     if fmt == FMT_F8E4M3:
         return quant.e4m3_decode(stored).astype(np.float64)
+    if fmt == FMT_F4E2M1_CS:
+        return quant.e2m1_cs_decode(*stored)
     return quant.e2m1_block_decode(*stored).astype(np.float64)
 
 

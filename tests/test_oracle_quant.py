@@ -114,3 +114,60 @@ def test_fp16_sr_zero_bits_truncate_and_mean_is_unbiased():
         vals = quant.fp16_sr(np.full(r.shape, xi, np.float32), r).astype(np.float64)
         step = np.spacing(np.float16(abs(xi))).astype(np.float64)
         assert abs(vals.mean() - float(xi)) <= 5 * step / 2 / np.sqrt(len(r)) + 1e-30
+
+
+# ---- two-axis e2m1 (block scales along the state axis, a power-of-two scale per column) ----
+def test_column_exponents_rule():
+    """e = floor(log2 amax) - 5 (so amax / 2^e is in [32, 64)), clamped at -126; zero columns -126."""
+    S = np.zeros((3, 6), np.float32)
+    S[1] = [1.0, -0.75, 64.0, 2.0 ** -130, 0.0, 3e38]
+    S[2, 0] = -0.5                                   # smaller than the column maximum: no effect
+    e = quant.column_exponents(S)
+    assert e.dtype == np.int8
+    assert e.tolist() == [-5, -6, 1, -126, -126, 122]
+    rng = np.random.default_rng(7)
+    X = (rng.standard_normal((4, 8, 32)) * 2.0 ** rng.integers(-30, 30, (4, 1, 32))).astype(np.float32)
+    e = quant.column_exponents(X).astype(np.float64)
+    ratio = np.max(np.abs(X), axis=-2) / 2.0 ** e
+    assert np.all((ratio >= 32) & (ratio < 64))
+
+
+def test_two_axis_column_scaling_is_equivariant():
+    """Scaling a column by 2^k moves only its exponent: codes, block scales and the rest stay."""
+    rng = np.random.default_rng(8)
+    S = rng.standard_normal((2, 16, 32)).astype(np.float32)
+    p0, s0, e0 = quant.e2m1_cs_encode(S)
+    T = S.copy()
+    T[:, :, 5] *= 2.0 ** 9
+    T[:, :, 20] *= 2.0 ** -7
+    p1, s1, e1 = quant.e2m1_cs_encode(T)
+    assert np.array_equal(p0, p1) and np.array_equal(s0, s1)
+    de = e1.astype(int) - e0.astype(int)
+    assert np.all(de[:, 5] == 9) and np.all(de[:, 20] == -7) and np.count_nonzero(de) == 4
+    D0, D1 = quant.e2m1_cs_decode(p0, s0, e0), quant.e2m1_cs_decode(p1, s1, e1)
+    assert np.array_equal(D1[:, :, 5], D0[:, :, 5] * 2.0 ** 9)
+    assert np.array_equal(D1[:, :, 20], D0[:, :, 20] * 2.0 ** -7)
+    # the block format alone is not equivariant: a 2^9 column takes over its blocks
+    b0 = quant.e2m1_block_decode(*quant.e2m1_block_encode(S))
+    b1 = quant.e2m1_block_decode(*quant.e2m1_block_encode(T))
+    assert not np.array_equal(b1[:, :, 4], b0[:, :, 4])
+
+
+def test_two_axis_grid_and_error_bound():
+    """Each decoded element / 2^e lies on its block's e2m1 grid, within half the largest step."""
+    rng = np.random.default_rng(9)
+    S = (rng.standard_normal((3, 16, 64)) * np.exp(2 * rng.standard_normal((3, 1, 64)))).astype(np.float32)
+    S[0, :, 3] = 0.0                                 # an all-zero column
+    p, sc, e = quant.e2m1_cs_encode(S)
+    D = quant.e2m1_cs_decode(p, sc, e)
+    assert np.all(D[0, :, 3] == 0)
+    y = D / 2.0 ** e.astype(np.float64)[:, None, :]
+    s = quant.e4m3_decode(sc).astype(np.float64)                       # [3, 16, 4]
+    blk = y.reshape(3, 16, 4, 16) / np.where(s > 0, s, 1.0)[..., None]
+    assert np.all(np.isin(np.abs(blk), quant.E2M1_GRID.astype(np.float64)))
+    x = (S.astype(np.float64) / 2.0 ** e.astype(np.float64)[:, None, :]).reshape(3, 16, 4, 16)
+    clamp = np.maximum(np.abs(x) - 6 * s[..., None], 0)
+    assert np.all(np.abs(y.reshape(3, 16, 4, 16) - x) <= s[..., None] + clamp + 1e-12)
+    # a block of equal magnitudes on one grid point is reproduced exactly
+    Z = np.full((1, 16, 16), 3.0, np.float32) * np.array([1, -1] * 8, np.float32)
+    assert np.array_equal(quant.e2m1_cs_decode(*quant.e2m1_cs_encode(Z)), Z.astype(np.float64))
