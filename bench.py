@@ -186,8 +186,8 @@ def bench_sweeps(torch, steps=64, warmup=16):
     return out
 
 
-SPLIT_PAIRS = ((0, 0), (0, 3), (1, 3), (2, 3), (3, 3))
-FMT_NAMES = {0: "f32", 1: "f16sr", 2: "e4m3", 3: "e2m1"}
+SPLIT_PAIRS = ((0, 0), (0, 3), (1, 3), (2, 3), (3, 3), (0, 4), (1, 4))
+FMT_NAMES = {0: "f32", 1: "f16sr", 2: "e4m3", 3: "e2m1", 4: "e2m1cs"}
 
 
 def bench_split(torch, seed=5, layers=8, steps=64, warmup=32):
@@ -218,6 +218,38 @@ def bench_split(torch, seed=5, layers=8, steps=64, warmup=32):
         out["pairs"][f"{FMT_NAMES[cf]}/{FMT_NAMES[rf]}"] = {"us_per_step": us, "model_bytes_per_step": rd + wr,
                                                           "gbs": (rd + wr) / us / 1e3,
                                                           "frac_of_peak": (rd + wr) / us / 1e3 / HBM_PEAK_GBS}
+        del lays
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_read_copy_error(torch, seed=6, steps=512, skip=64):
+    """Output error of the e2m1 read copies (block scales only, and two-axis)
+    against the float32 path of the same library, on the split-precision layer
+    (Gated DeltaNet, 32 heads, d = 128, L = 16, batch 64) with a float32
+    checkpoint, for isotropic keys and for keys whose dimensions have log-normal
+    magnitude weights (spread 1 and 2): mean over steps skip.. of
+    ||y - y_f32|| / ||y_f32||, all heads and sequences."""
+    from hybrid_model_ssm_replay_amd.layer import ReplayLayer
+    from synth import WORKLOADS, DeviceInputStream
+    shape = WORKLOADS["gdn_b64_h32_d128_l16"]
+    out = {}
+    for spread in (0.0, 1.0, 2.0):
+        ins = DeviceInputStream(shape, seed, key_spread=spread)
+        lays = {rf: ReplayLayer("gdn", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
+                                read_fmt=rf, seed=seed) for rf in (0, 3, 4)}
+        ys = {rf: torch.empty((shape.batch, shape.heads, shape.head_dim), device="cuda") for rf in lays}
+        err = {3: torch.zeros((), device="cuda", dtype=torch.float64), 4: torch.zeros((), device="cuda", dtype=torch.float64)}
+        for t in range(steps):
+            r = ins.record()
+            for rf, lay in lays.items():
+                lay.step(r, ys[rf])
+            if t >= skip:
+                nref = torch.linalg.vector_norm(ys[0])
+                for rf in (3, 4):
+                    err[rf] += (torch.linalg.vector_norm(ys[rf] - ys[0]) / nref).double()
+        e3, e4 = (float(err[rf]) / (steps - skip) for rf in (3, 4))
+        out[f"key_spread_{spread:g}"] = {"e2m1": e3, "e2m1cs": e4, "e2m1_over_e2m1cs": e3 / e4}
         del lays
         torch.cuda.empty_cache()
     return out
@@ -336,12 +368,14 @@ def main(argv=None):
     if not args.no_extra:
         log("split precision")
         extra["gdn_split_b64"] = bench_split(torch)
+        log("read copy error")
+        extra["gdn_split_b64"]["read_copy_error"] = bench_read_copy_error(torch)
         log("batch and window sweeps")
         extra["mamba2_sweeps"] = bench_sweeps(torch)
 
     traffic = stored_traffic("m2_replay_step_b256_traffic.txt", "m2")
     roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-            "traffic": traffic, "kernel": "m2_replay_step<8, 2>",
+            "traffic": traffic, "kernel": "m2_replay_step<8, 2, false>",
             "bytes_per_launch": rd + wr}
     cpu = None if args.no_cpu else cpu_baseline(shape, 1)
     out = {

@@ -9,8 +9,8 @@ device buffers with PyTorch and passes their addresses and the current stream.
 Importing the package does not load the library; the first call does, and it
 raises if ``libreplayssm.so`` has not been built -- there is no fallback path.
 """
-from .binding import (KIND_GDN, KIND_MAMBA2, FMT_F32, FMT_F16_SR, FMT_F8E4M3, FMT_F4E2M1_B16,
+from .binding import (KIND_GDN, KIND_MAMBA2, FMT_F32, FMT_F16_SR, FMT_F8E4M3, FMT_F4E2M1_B16, FMT_F4E2M1_CS,
                       STATUS_ACCEPT_CLAMPED, STATUS_BAD_POINTERS, ReplayError, lib_path, load_library)
 
-__all__ = ["KIND_GDN", "KIND_MAMBA2", "FMT_F32", "FMT_F16_SR", "FMT_F8E4M3", "FMT_F4E2M1_B16",
+__all__ = ["KIND_GDN", "KIND_MAMBA2", "FMT_F32", "FMT_F16_SR", "FMT_F8E4M3", "FMT_F4E2M1_B16", "FMT_F4E2M1_CS",
            "STATUS_ACCEPT_CLAMPED", "STATUS_BAD_POINTERS", "ReplayError", "lib_path", "load_library"]

@@ -70,6 +70,21 @@ __device__ __forceinline__ float sum16(float v) {
   v += __shfl_xor(v, 1, kWave);
   return v;
 }
+// Maximum over the 16 lanes of a row, by DPP within the row: the quad swaps
+// [1,0,3,2] and [2,3,0,1], then the half-row mirror (quads 0 <-> 1, 2 <-> 3)
+// and the row mirror (halves 0 <-> 1).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+
 // One 16-byte global-to-LDS load per lane (global_load_lds_dwordx4): lane l's
 // 16 bytes from src go to lds[l]; lds must be the same for the whole wave.
 // Completion is counted by vmcnt like any load.

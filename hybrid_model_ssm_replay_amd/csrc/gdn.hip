@@ -122,6 +122,7 @@ __device__ __forceinline__ void load_vec(float4 (&v)[NCH], const float *p, int l
 struct StateBuf {
   void *data;
   uint8_t *scales;
+  int8_t *cols;  // two-axis e2m1: column exponents [B][H][d_k]
 };
 
 // Counter and key of the stochastic-rounding bits of one fold: element e of
@@ -404,6 +405,101 @@ struct SIO<REPLAY_FMT_F4E2M1_B16, NCH, RBW, CM> {
   }
 };
 
+// Two-axis e2m1 (read copy only): the block format above of x / 2^e[n], with
+// one signed exponent byte e[n] per d_k column of the head,
+//     e[n] = max(floor(log2 amax_n) - 5, -126)   (amax_n over the head's rows),
+// read from the biased exponent field of amax_n.  A lane's 4 NCH columns are
+// contiguous, so their exponents are NCH words (word c: chunk c).  prepare()
+// finds the column maxima over the four waves (DPP within a wave, LDS across
+// waves: it contains a workgroup barrier, so every wave of the workgroup must
+// call it) and divides the tile by 2^e in place; encode() is then the block
+// encoder; decode() multiplies by 2^e again.  Division and multiplication by
+// 2^e are exact (ldexp) unless a quotient is subnormal, which only happens for
+// values that quantise to zero.
+template <int NCH, int RBW, int CM>
+struct SIO<REPLAY_FMT_F4E2M1_CS, NCH, RBW, CM> {
+  using Base = SIO<REPLAY_FMT_F4E2M1_B16, NCH, RBW, CM>;
+  static_assert(NCH % 4 == 0, "the exponent words load as 16-byte vectors");
+  static constexpr int DK = 16 * NCH, DV = 64 * RBW;
+  struct Raw {
+    typename Base::Raw base;
+    uint32_t ex[NCH];  // byte i of word c: exponent of column colq(c, q) + i
+  };
+  // This lane's exponents: column offset of the head (head / DV = (b H + h) d_k) plus its first column.
+  static __device__ __forceinline__ int8_t *col_ptr(const StateBuf &b, size_t head, int lane) {
+    return b.cols + head / DV + colq<NCH, CM>(0, lane >> 4);
+  }
+  static __device__ __forceinline__ int exp_of(uint32_t w, int i) { return (int)(int8_t)((w >> (8 * i)) & 0xFF); }
+  static __device__ __forceinline__ void scale(float4 (&s)[RBW][NCH], const uint32_t (&ex)[NCH], int sign) {
+#pragma unroll
+    for (int k = 0; k < RBW; ++k)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t w = ex[c];
+        float4 &v = s[k][c];
+        v = make_float4(__builtin_amdgcn_ldexpf(v.x, sign * exp_of(w, 0)), __builtin_amdgcn_ldexpf(v.y, sign * exp_of(w, 1)),
+                        __builtin_amdgcn_ldexpf(v.z, sign * exp_of(w, 2)), __builtin_amdgcn_ldexpf(v.w, sign * exp_of(w, 3)));
+      }
+  }
+  static __device__ __forceinline__ void load(Raw &r, const StateBuf &b, size_t head, int rb0, int lane) {
+    Base::load(r.base, b, head, rb0, lane);
+    const uint4 *src = reinterpret_cast<const uint4 *>(col_ptr(b, head, lane));
+#pragma unroll
+    for (int p = 0; p < NCH / 4; ++p) {
+      const uint4 w = src[p];
+      r.ex[4 * p] = w.x;
+      r.ex[4 * p + 1] = w.y;
+      r.ex[4 * p + 2] = w.z;
+      r.ex[4 * p + 3] = w.w;
+    }
+  }
+  static __device__ __forceinline__ void decode(float4 (&s)[RBW][NCH], const Raw &r) {
+    Base::decode(s, r.base);
+    scale(s, r.ex, 1);
+  }
+  static __device__ __forceinline__ void prepare(Raw &r, float4 (&s)[RBW][NCH], int lane, int wave) {
+    __shared__ float4 cmax[4][DK / 4];  // per wave: the maxima of its rows, natural column order
+    const int q = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      float4 m = make_float4(fabsf(s[0][c].x), fabsf(s[0][c].y), fabsf(s[0][c].z), fabsf(s[0][c].w));
+#pragma unroll
+      for (int k = 1; k < RBW; ++k)
+        m = make_float4(fmaxf(m.x, fabsf(s[k][c].x)), fmaxf(m.y, fabsf(s[k][c].y)), fmaxf(m.z, fabsf(s[k][c].z)),
+                        fmaxf(m.w, fabsf(s[k][c].w)));
+      m = make_float4(max16(m.x), max16(m.y), max16(m.z), max16(m.w));
+      if ((lane & 15) == 0) cmax[wave][(colq<NCH, CM>(c, q)) >> 2] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int c4 = colq<NCH, CM>(c, q) >> 2;
+      float4 m = cmax[0][c4];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const float4 t = cmax[w][c4];
+        m = make_float4(fmaxf(m.x, t.x), fmaxf(m.y, t.y), fmaxf(m.z, t.z), fmaxf(m.w, t.w));
+      }
+      // e = max(biased exponent - 132, -126): floor(log2 amax) - 5, and -126 for zero or subnormal maxima.
+      auto ex = [](float a) { return (uint32_t)max((int)(__float_as_uint(a) >> 23) - 132, -126) & 0xFFu; };
+      r.ex[c] = ex(m.x) | (ex(m.y) << 8) | (ex(m.z) << 16) | (ex(m.w) << 24);
+    }
+    scale(s, r.ex, -1);
+  }
+  static __device__ __forceinline__ void encode(Raw &r, const float4 (&s)[RBW][NCH], int rb0, int lane,
+                                                const SRKey &key) {
+    Base::encode(r.base, s, rb0, lane, key);  // s was divided by 2^e in prepare()
+  }
+  static __device__ __forceinline__ void write(const Raw &r, const StateBuf &b, size_t head, int rb0, int lane) {
+    Base::write(r.base, b, head, rb0, lane);
+    if (rb0 == 0 && (lane & 15) == 0) {  // every wave holds the same exponents: wave 0 writes them
+      uint4 *dst = reinterpret_cast<uint4 *>(col_ptr(b, head, lane));
+#pragma unroll
+      for (int p = 0; p < NCH / 4; ++p) dst[p] = make_uint4(r.ex[4 * p], r.ex[4 * p + 1], r.ex[4 * p + 2], r.ex[4 * p + 3]);
+    }
+  }
+};
+
 // State buffers of one launch: the checkpoint (format CF) and the read copy
 // (format RF; the same buffer when RF == CF).
 struct GdnStateBufs {
@@ -413,7 +509,9 @@ struct GdnStateBufs {
 
 // Encode the tile s into the checkpoint and (if separate) the read copy, and
 // leave in s what the read copy now holds, decoded: the S0 of the window that
-// starts here.
+// starts here.  A two-axis read copy makes this a workgroup-wide step (column
+// maxima over all rows): the callers decide per sequence, and a workgroup is
+// one (sequence, head), so all four waves arrive together.
 template <int CF, int RF, int NCH, int RBW>
 __device__ __forceinline__ void store_both(float4 (&s)[RBW][NCH], const GdnStateBufs &sb, size_t head, int rb0,
                                            int lane, uint32_t h, uint32_t b, uint32_t ckpt) {
@@ -424,6 +522,7 @@ __device__ __forceinline__ void store_both(float4 (&s)[RBW][NCH], const GdnState
   SIO<CF, NCH, RBW, CM>::write(rc, sb.ck, head, rb0, lane);
   if constexpr (RF != CF) {
     typename SIO<RF, NCH, RBW, CM>::Raw rr;
+    if constexpr (RF == REPLAY_FMT_F4E2M1_CS) SIO<RF, NCH, RBW, CM>::prepare(rr, s, lane, rb0 / RBW);
     SIO<RF, NCH, RBW, CM>::encode(rr, s, rb0, lane, key);
     SIO<RF, NCH, RBW, CM>::write(rr, sb.rd, head, rb0, lane);
     SIO<RF, NCH, RBW, CM>::decode(s, rr);
@@ -696,7 +795,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   float km[NCH], qm[NCH];  // columns NCH r16 .. of k_m and q_m
   load_cols<NCH>(km, kin + NCH * r16);
   load_cols<NCH>(qm, qin + NCH * r16);
-  const float al_row = rp.ral[r16 < L ? r16 : 0], be_row = rp.rbe[r16 < L ? r16 : 0];
+  const float al_row = rp.ral[r16 < L ? r16 : 0];
   const float al_in = a.alpha[bh], be_in = a.beta[bh];
   const float v_in = vin[orow];
 
@@ -1153,6 +1252,7 @@ __global__ __launch_bounds__(256) void gdn_encode_state(GdnEncodeArgs a, GdnStat
   }
   if constexpr (RF != CF) {
     typename SIO<RF, NCH, RBW, CM>::Raw rr;
+    if constexpr (RF == REPLAY_FMT_F4E2M1_CS) SIO<RF, NCH, RBW, CM>::prepare(rr, s, lane, wave);
     SIO<RF, NCH, RBW, CM>::encode(rr, s, rb0, lane, key);
     SIO<RF, NCH, RBW, CM>::write(rr, sb.rd, head, rb0, lane);
   }
@@ -1248,6 +1348,9 @@ __global__ __launch_bounds__(256) void gdn_snapshot_verify(GdnSnapArgs a) {
   X(REPLAY_FMT_F32, REPLAY_FMT_F4E2M1_B16)                                                          \
   X(REPLAY_FMT_F16_SR, REPLAY_FMT_F4E2M1_B16)                                                       \
   X(REPLAY_FMT_F8E4M3, REPLAY_FMT_F4E2M1_B16)                                                       \
+  X(REPLAY_FMT_F32, REPLAY_FMT_F4E2M1_CS)                                                           \
+  X(REPLAY_FMT_F16_SR, REPLAY_FMT_F4E2M1_CS)                                                        \
+  X(REPLAY_FMT_F8E4M3, REPLAY_FMT_F4E2M1_CS)                                                        \
   X(REPLAY_FMT_F4E2M1_B16, REPLAY_FMT_F4E2M1_B16)                                                   \
   X(REPLAY_FMT_F16_SR, REPLAY_FMT_F16_SR)                                                           \
   X(REPLAY_FMT_F8E4M3, REPLAY_FMT_F8E4M3)
@@ -1310,8 +1413,8 @@ RSSM_WRAP(GSnapK, gdn_snapshot_verify)
 
 GdnStateBufs state_bufs(const GdnFormatBufs &f) {
   GdnStateBufs sb;
-  sb.ck = StateBuf{f.ckpt, f.ckpt_scales};
-  sb.rd = StateBuf{f.read, f.read_scales};
+  sb.ck = StateBuf{f.ckpt, f.ckpt_scales, nullptr};
+  sb.rd = StateBuf{f.read, f.read_scales, f.read_cols};
   sb.seed_lo = (uint32_t)(f.seed & 0xFFFFFFFFu);
   sb.seed_hi = (uint32_t)(f.seed >> 32);
   return sb;

@@ -192,6 +192,7 @@ struct GdnFormatBufs {
   uint8_t *ckpt_scales;
   void *read;
   uint8_t *read_scales;
+  int8_t *read_cols;  // two-axis e2m1 read copy: column exponents [B][H][dk]
   uint64_t seed;
 };
 
@@ -202,16 +203,20 @@ struct GdnEncodeArgs {
   int write_ckpt;           // 0: write only the read copy
 };
 
-// Bytes of one stored copy of n elements, and where an e2m1 copy's scales start.
-inline size_t state_bytes(int fmt, size_t n) {
+// Bytes of one stored copy of n elements with ncols state columns in all
+// (batch x heads x state_dim), where an e2m1 copy's block scales start, and
+// where a two-axis copy's column exponents start.
+inline size_t e2m1_scale_offset(size_t n) { return align256(n / 2); }
+inline size_t e2m1_cols_offset(size_t n) { return align256(e2m1_scale_offset(n) + n / 16); }
+inline size_t state_bytes(int fmt, size_t n, size_t ncols) {
   switch (fmt) {
     case REPLAY_FMT_F32: return 4 * n;
     case REPLAY_FMT_F16_SR: return 2 * n;
     case REPLAY_FMT_F8E4M3: return n;
-    default: return align256(n / 2) + n / 16;
+    case REPLAY_FMT_F4E2M1_CS: return e2m1_cols_offset(n) + ncols;
+    default: return e2m1_scale_offset(n) + n / 16;
   }
 }
-inline size_t e2m1_scale_offset(size_t n) { return align256(n / 2); }
 
 // Launchers (return a hipError_t value).
 int launch_gdn_step(const GdnStepArgs &a, const GdnFormatBufs &f, hipStream_t st);

@@ -12,6 +12,7 @@ namespace {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t state_elems(const replay_config &c) { return (size_t)c.batch * c.heads * c.head_dim * c.state_dim; }
+size_t state_cols(const replay_config &c) { return (size_t)c.batch * c.heads * c.state_dim; }
 
 int check_cfg(const replay_config *c) {
   if (!c) return REPLAY_EINVAL;
@@ -32,14 +33,17 @@ int check_cfg(const replay_config *c) {
   }
   if ((c->flags & ~REPLAY_FLAG_DECAY_SKIP) || c->reserved) return REPLAY_EINVAL;
   if ((c->flags & REPLAY_FLAG_DECAY_SKIP) && c->kind != REPLAY_KIND_MAMBA2) return REPLAY_ENOTSUP;
-  if (c->ckpt_fmt < REPLAY_FMT_F32 || c->ckpt_fmt > REPLAY_FMT_F4E2M1_B16) return REPLAY_EINVAL;
-  if (c->read_fmt < REPLAY_FMT_F32 || c->read_fmt > REPLAY_FMT_F4E2M1_B16) return REPLAY_EINVAL;
+  if (c->ckpt_fmt < REPLAY_FMT_F32 || c->ckpt_fmt > REPLAY_FMT_F4E2M1_CS) return REPLAY_EINVAL;
+  if (c->read_fmt < REPLAY_FMT_F32 || c->read_fmt > REPLAY_FMT_F4E2M1_CS) return REPLAY_EINVAL;
   if (c->ckpt_fmt == REPLAY_FMT_F32 && c->read_fmt == REPLAY_FMT_F32) return REPLAY_OK;
   // Low-precision copies: Gated DeltaNet with d_k = 128; the read copy is e2m1
   // (split precision) or the checkpoint itself (one shared copy); an f32 read
   // copy next to a lower-precision checkpoint is not a supported pair.
   if (c->kind != REPLAY_KIND_GDN || c->state_dim != 128) return REPLAY_ENOTSUP;
-  if (c->read_fmt != c->ckpt_fmt && c->read_fmt != REPLAY_FMT_F4E2M1_B16) return REPLAY_ENOTSUP;
+  if (c->read_fmt != c->ckpt_fmt && c->read_fmt != REPLAY_FMT_F4E2M1_B16 && c->read_fmt != REPLAY_FMT_F4E2M1_CS)
+    return REPLAY_ENOTSUP;
+  // The two-axis copy is a read copy only: it never carries the recurrence.
+  if (c->ckpt_fmt == REPLAY_FMT_F4E2M1_CS) return REPLAY_ENOTSUP;
   return REPLAY_OK;
 }
 
@@ -86,7 +90,9 @@ GdnFormatBufs gdn_formats(const replay_ctx &ctx) {
     f.read_scales = f.ckpt_scales;
   } else {
     f.read = ctx.buf.read_copy;
-    f.read_scales = c.read_fmt == REPLAY_FMT_F4E2M1_B16 ? (uint8_t *)ctx.buf.read_copy + e2m1_scale_offset(n) : nullptr;
+    const bool e2m1 = c.read_fmt == REPLAY_FMT_F4E2M1_B16 || c.read_fmt == REPLAY_FMT_F4E2M1_CS;
+    f.read_scales = e2m1 ? (uint8_t *)ctx.buf.read_copy + e2m1_scale_offset(n) : nullptr;
+    f.read_cols = c.read_fmt == REPLAY_FMT_F4E2M1_CS ? (int8_t *)ctx.buf.read_copy + e2m1_cols_offset(n) : nullptr;
   }
   return f;
 }
@@ -107,12 +113,12 @@ int replay_validate_config(const replay_config *cfg) { return check_cfg(cfg); }
 
 size_t replay_ckpt_bytes(const replay_config *c) {
   if (check_cfg(c) != REPLAY_OK) return 0;
-  return state_bytes(c->ckpt_fmt, state_elems(*c));
+  return state_bytes(c->ckpt_fmt, state_elems(*c), state_cols(*c));
 }
 
 size_t replay_read_copy_bytes(const replay_config *c) {
   if (check_cfg(c) != REPLAY_OK) return 0;
-  return c->read_fmt == c->ckpt_fmt ? 0 : state_bytes(c->read_fmt, state_elems(*c));
+  return c->read_fmt == c->ckpt_fmt ? 0 : state_bytes(c->read_fmt, state_elems(*c), state_cols(*c));
 }
 
 size_t replay_ring_bytes(const replay_config *c) {

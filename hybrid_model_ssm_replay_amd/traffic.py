@@ -32,8 +32,15 @@ from dataclasses import dataclass
 
 E = 4  # bytes per float32
 
-# Bytes per state element of each storage format (F32, F16_SR, F8E4M3, F4E2M1_B16).
-FORMAT_BYTES = {0: 4.0, 1: 2.0, 2: 1.0, 3: 0.5 + 1.0 / 16}
+# Bytes per state element of each storage format (F32, F16_SR, F8E4M3, F4E2M1_B16,
+# F4E2M1_CS); the two-axis copy adds one exponent byte per state column.
+FORMAT_BYTES = {0: 4.0, 1: 2.0, 2: 1.0, 3: 0.5 + 1.0 / 16, 4: 0.5 + 1.0 / 16}
+
+
+def stored_state_bytes(l: "Layer", fmt: int) -> float:
+    """Bytes of one sequence's stored state in `fmt`."""
+    b = FORMAT_BYTES[fmt] * l.heads * l.head_dim * l.state_dim
+    return b + (l.heads * l.state_dim if fmt == 4 else 0)
 
 
 @dataclass(frozen=True)
@@ -98,8 +105,7 @@ def split_window_mean(l: Layer, ckpt_fmt: int, read_fmt: int) -> tuple[float, fl
     and a read copy in read_fmt (the same copy when equal): non-fold steps read the
     read copy; a fold reads the checkpoint and writes both copies (Gated DeltaNet;
     a separate read copy adds the buffered values v)."""
-    elems = l.heads * l.head_dim * l.state_dim
-    ck, rd = FORMAT_BYTES[ckpt_fmt] * elems, FORMAT_BYTES[read_fmt] * elems
+    ck, rd = stored_state_bytes(l, ckpt_fmt), stored_state_bytes(l, read_fmt)
     vrec = l.heads * l.head_dim * E if read_fmt != ckpt_fmt else 0
     rd_sum = wr_sum = 0.0
     for m in range(1, l.window + 1):

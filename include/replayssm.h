@@ -54,6 +54,7 @@ extern "C" {
 #define REPLAY_FMT_F16_SR 1     /* IEEE binary16, written with stochastic rounding */
 #define REPLAY_FMT_F8E4M3 2     /* OCP FP8 e4m3fn, round to nearest even, saturating */
 #define REPLAY_FMT_F4E2M1_B16 3 /* 4-bit e2m1 values, one e4m3 scale per 16 */
+#define REPLAY_FMT_F4E2M1_CS 4  /* F4E2M1_B16 plus a power-of-two scale per state column (read copy only) */
 
 /* Option flags (replay_config.flags). */
 #define REPLAY_FLAG_DECAY_SKIP 0x1u /* Mamba-2: drop the checkpoint term of heads whose decay is below 2^-24 */
@@ -103,7 +104,8 @@ extern "C" {
  *   reserved    must be 0.
  * Supported format pairs (ckpt_fmt, read_fmt): (F32, F32) for both families;
  * for Gated DeltaNet with state_dim = 128 also (F32 | F16_SR | F8E4M3, F4E2M1_B16)
- * (split precision) and (F16_SR, F16_SR), (F8E4M3, F8E4M3), (F4E2M1_B16,
+ * (split precision), (F32 | F16_SR | F8E4M3, F4E2M1_CS) (split precision with
+ * the two-axis read copy) and (F16_SR, F16_SR), (F8E4M3, F8E4M3), (F4E2M1_B16,
  * F4E2M1_B16) (one shared low-precision copy).  Other pairs: REPLAY_ENOTSUP.
  *
  * Storage formats, per element of [batch][heads][head_dim][state_dim]:
@@ -116,6 +118,17 @@ extern "C" {
  *               scale byte per 16 consecutive state_dim elements:
  *               s = e4m3(amax / 6); element codes round x / s to
  *               {0, .5, 1, 1.5, 2, 3, 4, 6} (ties to the even code, clamped).
+ *   F4E2M1_CS   scales along both axes of each head's [head_dim][state_dim]
+ *               state (the pages suggest separate state and channel scales for
+ *               the read copy [P1, Perspective, paragraph 2]): the F4E2M1_B16
+ *               codes and block scales (blocks along state_dim, inside one
+ *               head_dim channel) of x / 2^e[n], followed, at the next 256-byte
+ *               boundary after the block scales, by one signed byte e[n] per
+ *               state column [batch][heads][state_dim]:
+ *               e[n] = max(floor(log2 amax_n) - 5, -126), amax_n the largest
+ *               |x| of column n over the head's channels (-126 when zero), so
+ *               that amax_n / 2^e[n] lies in [32, 64).  Decoded value:
+ *               e2m1 x block scale x 2^e[n].
  * An all-zero buffer is the zero state in every format.
  */
 typedef struct replay_config {

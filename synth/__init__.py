@@ -160,7 +160,11 @@ class DeviceInputStream:
     the same stream as InputStream's.  Only Gated DeltaNet layers.
     """
 
-    def __init__(self, shape: LayerShape, seed: int, device="cuda"):
+    def __init__(self, shape: LayerShape, seed: int, device="cuda", key_spread: float = 0.0):
+        """key_spread > 0 gives every (head, key dimension) of q and of k a fixed
+        magnitude weight exp(key_spread N(0, 1)) (drawn once, before the first
+        record) applied before the L2 normalisation: key dimensions of uneven
+        size, hence state columns of uneven magnitude."""
         import torch
         if shape.kind != GDN:
             raise ValueError("DeviceInputStream generates Gated DeltaNet records")
@@ -169,6 +173,11 @@ class DeviceInputStream:
         self.gen = torch.Generator(device=device)
         self.gen.manual_seed(seed)
         self.device = device
+        self.wq = self.wk = None
+        if key_spread > 0:
+            w = lambda: torch.exp(key_spread * torch.randn(shape.heads, shape.state_dim, generator=self.gen,  # noqa: E731
+                                                           device=device, dtype=torch.float32))
+            self.wq, self.wk = w(), w()
 
     def record(self):
         t, s = self.torch, self.shape
@@ -176,6 +185,8 @@ class DeviceInputStream:
         n = lambda *shp: t.randn(*shp, generator=self.gen, device=self.device, dtype=t.float32)  # noqa: E731
         q = n(*lead, s.state_dim)
         k = n(*lead, s.state_dim)
+        if self.wq is not None:
+            q, k = q * self.wq, k * self.wk
         q = q / t.linalg.vector_norm(q, dim=-1, keepdim=True)
         k = k / t.linalg.vector_norm(k, dim=-1, keepdim=True)
         v = n(*lead, s.head_dim)

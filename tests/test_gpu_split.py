@@ -18,15 +18,19 @@ import pytest
 
 from _gpu import announce, host, to_dev
 from _metrics import max_rel_err
-from oracle.session import FMT_F16_SR, FMT_F32, FMT_F4E2M1_B16, FMT_F8E4M3, SplitReplaySession, encode_state
+from oracle.session import (FMT_F16_SR, FMT_F32, FMT_F4E2M1_B16, FMT_F4E2M1_CS, FMT_F8E4M3, SplitReplaySession,
+                            encode_state)
 from synth import InputStream, LayerShape
 
 pytestmark = pytest.mark.gpu
 
 PAIRS = [(FMT_F32, FMT_F4E2M1_B16), (FMT_F16_SR, FMT_F4E2M1_B16), (FMT_F8E4M3, FMT_F4E2M1_B16),
-         (FMT_F4E2M1_B16, FMT_F4E2M1_B16), (FMT_F16_SR, FMT_F16_SR), (FMT_F8E4M3, FMT_F8E4M3)]
+         (FMT_F4E2M1_B16, FMT_F4E2M1_B16), (FMT_F16_SR, FMT_F16_SR), (FMT_F8E4M3, FMT_F8E4M3),
+         (FMT_F32, FMT_F4E2M1_CS), (FMT_F16_SR, FMT_F4E2M1_CS), (FMT_F8E4M3, FMT_F4E2M1_CS)]
 SEED = 0x1234_5678_9ABC
-POST_FOLD_TOL = {FMT_F4E2M1_B16: 2e-2, FMT_F16_SR: 2.0 ** -8, FMT_F8E4M3: 2.0 ** -3, FMT_F32: 1e-4}
+POST_FOLD_TOL = {FMT_F4E2M1_B16: 2e-2, FMT_F4E2M1_CS: 2e-2, FMT_F16_SR: 2.0 ** -8, FMT_F8E4M3: 2.0 ** -3,
+                 FMT_F32: 1e-4}
+E2M1 = (FMT_F4E2M1_B16, FMT_F4E2M1_CS)
 
 
 def _state_for_codecs(shape, seed):
@@ -46,17 +50,22 @@ def _bytes_of(stored, fmt):
         return np.concatenate([s.view(np.uint8).reshape(-1) for s in stored])
     if fmt == FMT_F8E4M3:
         return np.concatenate([s.reshape(-1) for s in stored])
-    codes = np.concatenate([s[0].reshape(-1) for s in stored])
-    scales = np.concatenate([s[1].reshape(-1) for s in stored])
-    return codes, scales
+    return tuple(np.concatenate([s[i].reshape(-1).view(np.uint8) for s in stored]) for i in range(len(stored[0])))
 
 
-def _split_gpu(buf, fmt, n):
+def _split_gpu(buf, fmt, n, ncols):
+    """Sections of a device copy: codes, block scales (at the next 256 bytes) and,
+    for the two-axis format, the column exponents (at the next 256 bytes after that)."""
     raw = host(buf)
-    if fmt != FMT_F4E2M1_B16:
+    if fmt not in E2M1:
         return raw
-    off = (n // 2 + 255) // 256 * 256
-    return raw[: n // 2], raw[off: off + n // 16]
+    a256 = lambda x: (x + 255) // 256 * 256
+    off = a256(n // 2)
+    parts = (raw[: n // 2], raw[off: off + n // 16])
+    if fmt == FMT_F4E2M1_CS:
+        off2 = a256(off + n // 16)
+        parts += (raw[off2: off2 + ncols],)
+    return parts
 
 
 def _layer(shape, cf, rf, ckpt0, max_draft=0):
@@ -68,6 +77,7 @@ def _layer(shape, cf, rf, ckpt0, max_draft=0):
 def _check_copies(lay, sess, shape, cf, rf, exact=True):
     """Stored bytes vs the oracle's stored copies; returns the fraction of differing bytes."""
     n = shape.batch * shape.heads * shape.head_dim * shape.state_dim
+    ncols = shape.batch * shape.heads * shape.state_dim
     ck, rd = lay.stored_copies()
     fracs = []
     for buf, stored, fmt in ((ck, sess.R, cf), (rd, sess.Q, rf)):
@@ -80,9 +90,9 @@ def _check_copies(lay, sess, shape, cf, rf, exact=True):
             rel = np.max(np.abs(got - want), axis=-1) / np.maximum(np.max(np.abs(want), axis=-1), 1e-30)
             assert np.max(rel) <= 1e-5, np.max(rel)
             continue
-        got, want = _split_gpu(buf, fmt, n), _bytes_of(stored, fmt)
-        if fmt == FMT_F4E2M1_B16:
-            diff = (np.count_nonzero(got[0] != want[0]) + np.count_nonzero(got[1] != want[1])) / (got[0].size + got[1].size)
+        got, want = _split_gpu(buf, fmt, n, ncols), _bytes_of(stored, fmt)
+        if fmt in E2M1:
+            diff = sum(np.count_nonzero(g != w) for g, w in zip(got, want)) / sum(g.size for g in got)
         else:
             diff = np.count_nonzero(got[: want.size] != want) / want.size
         fracs.append(diff)
@@ -135,7 +145,7 @@ def test_steps_and_folds_match_oracle(cf, rf):
 
 
 @pytest.mark.parametrize("cf,rf", [(FMT_F32, FMT_F4E2M1_B16), (FMT_F4E2M1_B16, FMT_F4E2M1_B16),
-                                   (FMT_F8E4M3, FMT_F8E4M3)])
+                                   (FMT_F8E4M3, FMT_F8E4M3), (FMT_F32, FMT_F4E2M1_CS)])
 def test_speculative_with_many_drafts(cf, rf):
     """Verify / commit / step sequences with up to 12 drafts (three passes) on a
     16-record window, against SplitReplaySession; the same bars as above."""
