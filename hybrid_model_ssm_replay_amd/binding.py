@@ -13,6 +13,7 @@ KIND_MAMBA2, KIND_GDN = 0, 1
 FMT_F32, FMT_F16_SR, FMT_F8E4M3, FMT_F4E2M1_B16, FMT_F4E2M1_CS = 0, 1, 2, 3, 4
 STATUS_ACCEPT_CLAMPED, STATUS_BAD_POINTERS = 0x1, 0x2
 FLAG_DECAY_SKIP = 0x1
+FLAG_BF16_RECORDS = 0x2
 OK, EINVAL, EHIP, ENOTSUP = 0, -1, -2, -3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -70,6 +70,60 @@ __device__ __forceinline__ float sum16(float v) {
   v += __shfl_xor(v, 1, kWave);
   return v;
 }
+// ---- record element types ---------------------------------------------------
+// Record vector fields are float32, or bf16 (REPLAY_FLAG_BF16_RECORDS) stored
+// as the upper half of a float32 bit pattern: widening is an exact shift, and
+// a value read from a bf16 field is stored back exactly by truncation.
+typedef uint16_t bf16_t;
+
+template <typename R>
+__device__ __forceinline__ float ldr(const R *p);
+template <>
+__device__ __forceinline__ float ldr<float>(const float *p) {
+  return *p;
+}
+template <>
+__device__ __forceinline__ float ldr<bf16_t>(const bf16_t *p) {
+  return __uint_as_float((uint32_t)*p << 16);
+}
+
+// Four consecutive elements (16-byte aligned for float32, 8-byte for bf16).
+template <typename R>
+__device__ __forceinline__ float4 ldr4(const R *p);
+template <>
+__device__ __forceinline__ float4 ldr4<float>(const float *p) {
+  return ld4(p);
+}
+template <>
+__device__ __forceinline__ float4 ldr4<bf16_t>(const bf16_t *p) {
+  const uint2 w = *reinterpret_cast<const uint2 *>(p);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xFFFF0000u));
+}
+
+// Stores of values the field holds exactly (values read from such a field).
+template <typename R>
+__device__ __forceinline__ void str(R *p, float v);
+template <>
+__device__ __forceinline__ void str<float>(float *p, float v) {
+  *p = v;
+}
+template <>
+__device__ __forceinline__ void str<bf16_t>(bf16_t *p, float v) {
+  *p = (bf16_t)(__float_as_uint(v) >> 16);
+}
+template <typename R>
+__device__ __forceinline__ void str4(R *p, float4 v);
+template <>
+__device__ __forceinline__ void str4<float>(float *p, float4 v) {
+  st4(p, v);
+}
+template <>
+__device__ __forceinline__ void str4<bf16_t>(bf16_t *p, float4 v) {
+  *reinterpret_cast<uint2 *>(p) = make_uint2((__float_as_uint(v.x) >> 16) | (__float_as_uint(v.y) & 0xFFFF0000u),
+                                             (__float_as_uint(v.z) >> 16) | (__float_as_uint(v.w) & 0xFFFF0000u));
+}
+
 // Maximum over the 16 lanes of a row, by DPP within the row: the quad swaps
 // [1,0,3,2] and [2,3,0,1], then the half-row mirror (quads 0 <-> 1, 2 <-> 3)
 // and the row mirror (halves 0 <-> 1).
@@ -91,6 +145,21 @@ __device__ __forceinline__ float max16(float v) {
 __device__ __forceinline__ void dma16(const float *src, float4 *lds) {
   typedef __attribute__((address_space(3))) void lds_void;
   __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src), (lds_void *)(lds), 16, 0, 0);
+}
+
+// Four elements per lane into LDS as float32, lane l's at lds[l] (lds the same
+// for the whole wave): a direct global-to-LDS load for float32 fields, a load,
+// exact widening and LDS store for bf16 fields.  Either way the data is in
+// place after s_waitcnt(0) and a barrier.
+template <typename R>
+__device__ __forceinline__ void stage4(const R *src, float4 *lds, int lane);
+template <>
+__device__ __forceinline__ void stage4<float>(const float *src, float4 *lds, int) {
+  dma16(src, lds);
+}
+template <>
+__device__ __forceinline__ void stage4<bf16_t>(const bf16_t *src, float4 *lds, int lane) {
+  lds[lane] = ldr4<bf16_t>(src);
 }
 
 // Program-order fence for LDS traffic between lanes of one wave.

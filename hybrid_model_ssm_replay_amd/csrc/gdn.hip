@@ -108,14 +108,6 @@ __device__ __forceinline__ void store_rows_g(const float4 (&s)[RBW][NCH], float 
   }
 }
 
-// A vector (key or query) in the lane's column order.
-template <int NCH, int CM>
-__device__ __forceinline__ void load_vec(float4 (&v)[NCH], const float *p, int lane) {
-  const int q = lane >> 4;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) v[c] = ld4(p + colq<NCH, CM>(c, q));
-}
-
 // ---- state storage formats ------------------------------------------------------
 // Where one head's state lives: element offset `head` of the head tile, the
 // data array and, for e2m1, the scale array (one byte per 16 elements).
@@ -612,8 +604,8 @@ __device__ __forceinline__ void gdn_window(const float4 (&s)[RBW][NCH], const fl
 // resident) and the B operand ub[k][st] = weight x u of record 4 st + q at row
 // 16 (rb0 + k) + (lane % 16), supplied by the caller.  The tile accumulates in
 // place, four records at a time, so that only one group of keys is live.
-template <int NCH, int RBW, int CM>
-__device__ __forceinline__ void fold_rank(float4 (&s)[RBW][NCH], int cnt, int s0, const float *rk, size_t ks, int L,
+template <int NCH, int RBW, int CM, typename R>
+__device__ __forceinline__ void fold_rank(float4 (&s)[RBW][NCH], int cnt, int s0, const R *rk, size_t ks, int L,
                                           float escale, const float (&ub)[RBW][4], int lane) {
   const int q = lane >> 4, r16 = lane & 15;
   const int nsteps = (cnt + 3) >> 2;
@@ -626,11 +618,11 @@ __device__ __forceinline__ void fold_rank(float4 (&s)[RBW][NCH], int cnt, int s0
   for (int st = 0; st < 4; ++st) {
     if (st < nsteps) {
       const int r = 4 * st + q;
-      const float *kr = rk + (size_t)wrap(s0, r < cnt ? r : cnt - 1, L) * ks;
+      const R *kr = rk + (size_t)wrap(s0, r < cnt ? r : cnt - 1, L) * ks;
       float aK[NCH];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const float v = kr[colq<NCH, CM>(c, r16 >> 2) + (r16 & 3)];  // M = r16 in chunk c
+        const float v = ldr<R>(kr + colq<NCH, CM>(c, r16 >> 2) + (r16 & 3));  // M = r16 in chunk c
         aK[c] = r < cnt ? v : 0.f;
       }
 #pragma unroll
@@ -644,19 +636,26 @@ __device__ __forceinline__ void fold_rank(float4 (&s)[RBW][NCH], int cnt, int s0
   }
 }
 
+// Head bases of the ring fields: k, u, v slot-major (v: re-solving folds only;
+// k and v hold record elements of type R), alpha and beta rows.
+template <typename R>
 struct GdnRingPtrs {
-  float *rk, *ru, *rv, *ral, *rbe;  // head bases: k, u, v slot-major (v: re-solving folds only); alpha, beta rows
-  size_t ks, vs;                    // slot strides of the k ring and of the u and v rings
+  R *rk;
+  float *ru;
+  R *rv;
+  float *ral, *rbe;
+  size_t ks, vs;  // slot strides of the k ring and of the u and v rings
 };
 
-__device__ __forceinline__ GdnRingPtrs gdn_ring_ptrs(const GdnRing &r, const Shape &sh, int b, int h) {
-  GdnRingPtrs p;
+template <typename R>
+__device__ __forceinline__ GdnRingPtrs<R> gdn_ring_ptrs(const GdnRing &r, const Shape &sh, int b, int h) {
+  GdnRingPtrs<R> p;
   const size_t bh = (size_t)b * sh.H + h;
   p.ks = (size_t)sh.B * sh.H * sh.N;
   p.vs = (size_t)sh.B * sh.H * sh.P;
-  p.rk = r.k + bh * sh.N;
+  p.rk = static_cast<R *>(r.k) + bh * sh.N;
   p.ru = r.u + bh * sh.P;
-  p.rv = r.v ? r.v + bh * sh.P : nullptr;
+  p.rv = r.v ? static_cast<R *>(r.v) + bh * sh.P : nullptr;
   p.ral = r.alpha + bh * sh.L;
   p.rbe = r.beta + bh * sh.L;
   return p;
@@ -664,25 +663,27 @@ __device__ __forceinline__ GdnRingPtrs gdn_ring_ptrs(const GdnRing &r, const Sha
 
 // Keys of window records 0..cnt-1 at ring positions starting at slot s0, in
 // operand layout (zeros beyond cnt).
-template <int NCH, int CM>
-__device__ __forceinline__ void load_keys(float4 (&X)[NCH], int cnt, const GdnRingPtrs &rp, int s0, int L, int lane) {
+template <int NCH, int CM, typename R>
+__device__ __forceinline__ void load_keys(float4 (&X)[NCH], int cnt, const GdnRingPtrs<R> &rp, int s0, int L,
+                                          int lane) {
   const int q = lane >> 4, r16 = lane & 15;
   const int j = r16 < cnt ? r16 : cnt - 1;
-  const float *kj = rp.rk + (size_t)wrap(s0, j, L) * rp.ks;
+  const R *kj = rp.rk + (size_t)wrap(s0, j, L) * rp.ks;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const float4 v = ld4(kj + colq<NCH, CM>(c, q));
+    const float4 v = ldr4<R>(kj + colq<NCH, CM>(c, q));
     X[c] = r16 < cnt ? v : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
 // Row `row` of ring field f (u or v) for window records 0..cnt-1 from slot s0.
-__device__ __forceinline__ void load_ring_rows(float (&vr)[16], int cnt, const float *f, size_t vs, int s0, int L,
+template <typename E>
+__device__ __forceinline__ void load_ring_rows(float (&vr)[16], int cnt, const E *f, size_t vs, int s0, int L,
                                                int row) {
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     const int tc = t < cnt ? t : (cnt > 0 ? cnt - 1 : 0);
-    const float v = f[(size_t)wrap(s0, tc, L) * vs + row];
+    const float v = ldr<E>(f + (size_t)wrap(s0, tc, L) * vs + row);
     vr[t] = t < cnt ? v : 0.f;
   }
 }
@@ -695,8 +696,8 @@ __device__ __forceinline__ void load_ring_rows(float (&vr)[16], int cnt, const f
 // computed from the read copy, so the fold re-solves them from the checkpoint
 // and the values v (a full-window solve through sm), and the read copy's
 // rounding never enters the recurrence.
-template <int CF, int RF, int NCH, int RBW>
-__device__ __forceinline__ void gdn_fold(float4 (&s)[RBW][NCH], int cnt, int s0, const GdnRingPtrs &rp, int L,
+template <int CF, int RF, int NCH, int RBW, typename R>
+__device__ __forceinline__ void gdn_fold(float4 (&s)[RBW][NCH], int cnt, int s0, const GdnRingPtrs<R> &rp, int L,
                                          int rb0, int lane, GdnLds<RBW> *sm) {
   constexpr int CM = col_map(CF, RF);
   const int q = lane >> 4, r16 = lane & 15;
@@ -707,7 +708,7 @@ __device__ __forceinline__ void gdn_fold(float4 (&s)[RBW][NCH], int cnt, int s0,
   if constexpr (CF != RF) {
     float4 X[NCH];
     float vr[16];
-    load_keys<NCH, CM>(X, cnt, rp, s0, L, lane);
+    load_keys<NCH, CM, R>(X, cnt, rp, s0, L, lane);
     load_ring_rows(vr, cnt, rp.rv, rp.vs, s0, L, rb0 * 16 + (lane < 16 * RBW ? lane : 0));
     const float be = rp.rbe[wrap(s0, j, L)];
     gdn_window<NCH, RBW>(s, X, cnt, 0, al, be, vr, *sm, lane);
@@ -731,7 +732,7 @@ __device__ __forceinline__ void gdn_fold(float4 (&s)[RBW][NCH], int cnt, int s0,
       for (int k = 0; k < RBW; ++k) ub[k][st] = w * ur[(rb0 + k) * 16 + r16];
     }
   }
-  fold_rank<NCH, RBW, CM>(s, cnt, s0, rp.rk, rp.ks, L, escale, ub, lane);
+  fold_rank<NCH, RBW, CM, R>(s, cnt, s0, rp.rk, rp.ks, L, escale, ub, lane);
 }
 
 // ---- replay step ------------------------------------------------------------
@@ -748,12 +749,12 @@ __device__ __forceinline__ void gdn_fold(float4 (&s)[RBW][NCH], int cnt, int s0,
 // and k_m, q_m reach every wave through LDS, so no lane holds them whole.
 // A step that finds the window full folds it first, stores both copies and
 // starts the next window from what the read copy now holds.
-template <int NCH>
-__device__ __forceinline__ void load_cols(float (&v)[NCH], const float *p) {
+template <int NCH, typename R>
+__device__ __forceinline__ void load_cols(float (&v)[NCH], const R *p) {
   if constexpr (NCH % 4 == 0) {
 #pragma unroll
     for (int i = 0; i < NCH / 4; ++i) {
-      const float4 t = ld4(p + 4 * i);
+      const float4 t = ldr4<R>(p + 4 * i);
       v[4 * i] = t.x;
       v[4 * i + 1] = t.y;
       v[4 * i + 2] = t.z;
@@ -761,14 +762,13 @@ __device__ __forceinline__ void load_cols(float (&v)[NCH], const float *p) {
     }
   } else {
     static_assert(NCH == 2, "NCH is 2, 4 or 8");
-    const float2 t = *reinterpret_cast<const float2 *>(p);
-    v[0] = t.x;
-    v[1] = t.y;
+    v[0] = ldr<R>(p);
+    v[1] = ldr<R>(p + 1);
   }
 }
 
 // Float32 copies: held to 128 VGPRs (four waves per SIMD), which fits without spills.
-template <int CF, int RF, int NCH, int RBW>
+template <int CF, int RF, int NCH, int RBW, typename R>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32 ? 4 : 1))) void gdn_replay_step(GdnStepArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
@@ -785,19 +785,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   const int DV = sh.P, L = sh.L, rb0 = wave * RBW;
   const size_t bh = (size_t)b * sh.H + h;
   const size_t head = bh * DV * DK;
-  const GdnRingPtrs rp = gdn_ring_ptrs(a.ring, sh, b, h);
-  const float *qin = a.q + bh * DK, *kin = a.k + bh * DK, *vin = a.v + bh * DV;
+  const GdnRingPtrs<R> rp = gdn_ring_ptrs<R>(a.ring, sh, b, h);
+  const R *qin = static_cast<const R *>(a.q) + bh * DK, *kin = static_cast<const R *>(a.k) + bh * DK;
+  const R *vin = static_cast<const R *>(a.v) + bh * DV;
   const int orow = (rb0 + (q < RBW ? q : 0)) * 16 + r16;  // this lane's output row (q < RBW)
 
   // 1. The read copy first (a non-fold step reads only it), then what needs no pointer.
   typename SIO<RF, NCH, RBW, CM>::Raw raw;
   SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
   float km[NCH], qm[NCH];  // columns NCH r16 .. of k_m and q_m
-  load_cols<NCH>(km, kin + NCH * r16);
-  load_cols<NCH>(qm, qin + NCH * r16);
+  load_cols<NCH, R>(km, kin + NCH * r16);
+  load_cols<NCH, R>(qm, qin + NCH * r16);
   const float al_row = rp.ral[r16 < L ? r16 : 0];
   const float al_in = a.alpha[bh], be_in = a.beta[bh];
-  const float v_in = vin[orow];
+  const float v_in = ldr<R>(vin + orow);
 
   // 2. Pointers.
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
@@ -820,13 +821,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   if (fold) {
     if constexpr (RF == CF) {
       SIO<RF, NCH, RBW, CM>::decode(s, raw);
-      gdn_fold<CF, RF, NCH, RBW>(s, L, s0, rp, L, rb0, lane, nullptr);
+      gdn_fold<CF, RF, NCH, RBW, R>(s, L, s0, rp, L, rb0, lane, nullptr);
     } else {
       __shared__ GdnLds<RBW> lds_all[4];
       typename SIO<CF, NCH, RBW, CM>::Raw rc;
       SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
       SIO<CF, NCH, RBW, CM>::decode(s, rc);
-      gdn_fold<CF, RF, NCH, RBW>(s, L, s0, rp, L, rb0, lane, &lds_all[wave]);
+      gdn_fold<CF, RF, NCH, RBW, R>(s, L, s0, rp, L, rb0, lane, &lds_all[wave]);
     }
     store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
@@ -838,7 +839,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   } else {
     // The count older records, then the read copy (after the ring loads in program order).
     const int j = grp < count ? grp : 0;
-    load_cols<NCH>(kj, rp.rk + (size_t)wrap(s0, j, L) * rp.ks + NCH * r16);
+    load_cols<NCH, R>(kj, rp.rk + (size_t)wrap(s0, j, L) * rp.ks + NCH * r16);
 #pragma unroll
     for (int t = 0; t < kMaxOld; ++t) {
       const int tc = t < count ? t : 0;
@@ -925,7 +926,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   if (q < RBW) {
     a.y[bh * DV + orow] = o;
     rp.ru[(size_t)slot * rp.vs + orow] = um;
-    if constexpr (RF != CF) rp.rv[(size_t)slot * rp.vs + orow] = v_in;
+    if constexpr (RF != CF) str<R>(rp.rv + (size_t)slot * rp.vs + orow, v_in);
   }
   for (int i = threadIdx.x; i < DK; i += 64 * nwaves) rp.rk[(size_t)slot * rp.ks + i] = kin[i];
   if (threadIdx.x == 0) {
@@ -939,7 +940,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 }
 
 // ---- explicit flush -------------------------------------------------------------
-template <int CF, int RF, int NCH, int RBW>
+template <int CF, int RF, int NCH, int RBW, typename R>
 __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
   constexpr int CM = col_map(CF, RF);
@@ -961,14 +962,14 @@ __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a, GdnStateBufs sb
     a.ptr.ckpt_out[b] = fold ? pos : ck;
   }
   if (!fold) return;
-  const GdnRingPtrs rp = gdn_ring_ptrs(a.ring, sh, b, h);
+  const GdnRingPtrs<R> rp = gdn_ring_ptrs<R>(a.ring, sh, b, h);
   float4 s[RBW][NCH];
   {
     typename SIO<CF, NCH, RBW, CM>::Raw rc;
     SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
     SIO<CF, NCH, RBW, CM>::decode(s, rc);
   }
-  gdn_fold<CF, RF, NCH, RBW>(s, count, fmod_(ck, sh.fL), rp, L, rb0, lane, &lds_all[RF != CF ? wave : 0]);
+  gdn_fold<CF, RF, NCH, RBW, R>(s, count, fmod_(ck, sh.fL), rp, L, rb0, lane, &lds_all[RF != CF ? wave : 0]);
   store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
 }
 
@@ -1008,7 +1009,7 @@ union GdnWaveLds {
   GdnVerifyLds<RBW> verify;  // the drafts (after the fold)
 };
 
-template <int CF, int RF, int NCH, int RBW>
+template <int CF, int RF, int NCH, int RBW, typename R>
 __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
   constexpr int CM = col_map(CF, RF);
@@ -1026,11 +1027,12 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
   const int DV = sh.P, L = sh.L, rb0 = wave * RBW, H = sh.H;
   const size_t bh = (size_t)b * H + h;
   const size_t head = bh * DV * DK;
-  const GdnRingPtrs rp = gdn_ring_ptrs(a.ring, sh, b, h);
+  const GdnRingPtrs<R> rp = gdn_ring_ptrs<R>(a.ring, sh, b, h);
   const int row = rb0 * 16 + (lane < 16 * RBW ? lane : 0);  // this lane's row in the solve
-  auto dq_ = [&](int i) { return a.q + (((size_t)b * T + i) * H + h) * DK; };
-  auto dk_ = [&](int i) { return a.k + (((size_t)b * T + i) * H + h) * DK; };
-  auto dv_ = [&](int i) { return a.v + (((size_t)b * T + i) * H + h) * DV; };
+  const R *gq_ = static_cast<const R *>(a.q), *gk_ = static_cast<const R *>(a.k), *gv_ = static_cast<const R *>(a.v);
+  auto dq_ = [&](int i) { return gq_ + (((size_t)b * T + i) * H + h) * DK; };
+  auto dk_ = [&](int i) { return gk_ + (((size_t)b * T + i) * H + h) * DK; };
+  auto dv_ = [&](int i) { return gv_ + (((size_t)b * T + i) * H + h) * DV; };
   auto dsc = [&](const float *f, int i) { return f[((size_t)b * T + i) * H + h]; };
   const int npass = (T + 3) >> 2;
 
@@ -1048,13 +1050,13 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
       const int q2 = slot & 3, m2 = (slot >> 2) & 3, pwc = slot >> 4;  // pwc = (p 2 + w) NCH + cc
       const int cc = pwc % NCH, pw = pwc / NCH;
       const int n = 4 * (pw >> 1) + m2;
-      const float *src = (pw & 1) ? dq_(n < T ? n : T - 1) : dk_(n < T ? n : T - 1);
-      dma16(src + colq<NCH, CM>(cc, q2), &ldsD[64 * j]);
+      const R *src = (pw & 1) ? dq_(n < T ? n : T - 1) : dk_(n < T ? n : T - 1);
+      stage4<R>(src + colq<NCH, CM>(cc, q2), &ldsD[64 * j], lane);
     }
   }
   float vrow[kMaxL];
 #pragma unroll
-  for (int d = 0; d < kMaxL; ++d) vrow[d] = dv_(d < T ? d : T - 1)[row];
+  for (int d = 0; d < kMaxL; ++d) vrow[d] = ldr<R>(dv_(d < T ? d : T - 1) + row);
 
   // 2. Pointers; fold-first when the window cannot take T more records.
   const int count = pos - ck;
@@ -1079,7 +1081,7 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
       SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
       SIO<CF, NCH, RBW, CM>::decode(s, rc);
     }
-    gdn_fold<CF, RF, NCH, RBW>(s, count, s0, rp, L, rb0, lane, &lds_all[wave].fold);
+    gdn_fold<CF, RF, NCH, RBW, R>(s, count, s0, rp, L, rb0, lane, &lds_all[wave].fold);
     store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
     sb0 = wrap(s0, count, L);
@@ -1091,8 +1093,8 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
   //    committed pseudo-values, and alpha, beta of record r16.
   {
     const int j = r16 < nrec ? r16 : nrec - 1;
-    const float *kj = j < c ? rp.rk + (size_t)wrap(sb0, j, L) * rp.ks : dk_(j - c);
-    for (int cc = wave; cc < NCH; cc += nwaves) dma16(kj + colq<NCH, CM>(cc, q), &ldsK[cc][0]);
+    const R *kj = j < c ? rp.rk + (size_t)wrap(sb0, j, L) * rp.ks : dk_(j - c);
+    for (int cc = wave; cc < NCH; cc += nwaves) stage4<R>(kj + colq<NCH, CM>(cc, q), &ldsK[cc][0], lane);
   }
   float uc[kMaxL - 1];
 #pragma unroll
@@ -1209,7 +1211,7 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
         for (int j = 0; j <= t; ++j) o += sv.Bq[d][j] * u[j];
         a.y[(((size_t)b * T + d) * H + h) * DV + row] = o;
         rp.ru[(size_t)wrap(sb0, t, L) * rp.vs + row] = v;  // stage the pseudo-value
-        if constexpr (RF != CF) rp.rv[(size_t)wrap(sb0, t, L) * rp.vs + row] = vrow[d];
+        if constexpr (RF != CF) str<R>(rp.rv + (size_t)wrap(sb0, t, L) * rp.vs + row, vrow[d]);
       }
     }
   }
@@ -1261,17 +1263,17 @@ __global__ __launch_bounds__(256) void gdn_encode_state(GdnEncodeArgs a, GdnStat
 // ---- baselines: conventional step and snapshot-per-draft verify ----------------
 // One token of the stepwise recurrence on the register tile:
 //   Sk = S k;  S <- alpha S + (beta v - alpha beta Sk) k^T;  o = S q.
-template <int NCH, int RBW>
-__device__ __forceinline__ void gdn_update_rows(float4 (&s)[RBW][NCH], const float *qin, const float *kin,
-                                                const float *vin, float alpha, float beta, int rb0, int lane,
+template <int NCH, int RBW, typename R>
+__device__ __forceinline__ void gdn_update_rows(float4 (&s)[RBW][NCH], const R *qin, const R *kin, const R *vin,
+                                                float alpha, float beta, int rb0, int lane,
                                                 float *o_rows /* nullptr: no store */) {
   constexpr int CM = kColIlv;
   const int q = lane >> 4, r16 = lane & 15;
   float4 kv[NCH], qv[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    kv[c] = ld4(kin + colq<NCH, CM>(c, q));
-    qv[c] = ld4(qin + colq<NCH, CM>(c, q));
+    kv[c] = ldr4<R>(kin + colq<NCH, CM>(c, q));
+    qv[c] = ldr4<R>(qin + colq<NCH, CM>(c, q));
   }
   float acc[RBW];
 #pragma unroll
@@ -1281,7 +1283,7 @@ __device__ __forceinline__ void gdn_update_rows(float4 (&s)[RBW][NCH], const flo
 #pragma unroll
     for (int c = 0; c < NCH; ++c) sk += dot4(s[k][c], kv[c]);
     sk = sum_quarters(sk);
-    const float coef = beta * vin[row] - alpha * beta * sk;
+    const float coef = beta * ldr<R>(vin + row) - alpha * beta * sk;
     float so = 0.f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -1302,7 +1304,7 @@ __device__ __forceinline__ void gdn_update_rows(float4 (&s)[RBW][NCH], const flo
   }
 }
 
-template <int NCH, int RBW>
+template <int NCH, int RBW, typename R>
 __global__ __launch_bounds__(256) void gdn_conv_step(GdnConvArgs a) {
   constexpr int DK = 16 * NCH;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1314,12 +1316,13 @@ __global__ __launch_bounds__(256) void gdn_conv_step(GdnConvArgs a) {
   float *S = a.state + bh * DV * DK;
   float4 s[RBW][NCH];
   load_rows_g<NCH, RBW, kColIlv>(s, S, rb0, lane);
-  gdn_update_rows<NCH, RBW>(s, a.q + bh * DK, a.k + bh * DK, a.v + bh * DV, a.alpha[bh], a.beta[bh], rb0, lane,
-                            a.y + bh * DV);
+  gdn_update_rows<NCH, RBW, R>(s, static_cast<const R *>(a.q) + bh * DK, static_cast<const R *>(a.k) + bh * DK,
+                               static_cast<const R *>(a.v) + bh * DV, a.alpha[bh], a.beta[bh], rb0, lane,
+                               a.y + bh * DV);
   store_rows_g<NCH, RBW, kColIlv>(s, S, rb0, lane);
 }
 
-template <int NCH, int RBW>
+template <int NCH, int RBW, typename R>
 __global__ __launch_bounds__(256) void gdn_snapshot_verify(GdnSnapArgs a) {
   constexpr int DK = 16 * NCH;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1334,8 +1337,8 @@ __global__ __launch_bounds__(256) void gdn_snapshot_verify(GdnSnapArgs a) {
   load_rows_g<NCH, RBW, kColIlv>(s, slot_ptr(cur), rb0, lane);
   for (int i = 0; i < T; ++i) {
     const size_t d = ((size_t)b * T + i) * H + h;
-    gdn_update_rows<NCH, RBW>(s, a.q + d * DK, a.k + d * DK, a.v + d * DV, a.alpha[d], a.beta[d], rb0, lane,
-                              a.y + d * DV);
+    gdn_update_rows<NCH, RBW, R>(s, static_cast<const R *>(a.q) + d * DK, static_cast<const R *>(a.k) + d * DK,
+                                 static_cast<const R *>(a.v) + d * DV, a.alpha[d], a.beta[d], rb0, lane, a.y + d * DV);
     store_rows_g<NCH, RBW, kColIlv>(s, slot_ptr((cur + 1 + i) % a.nslots), rb0, lane);
   }
 }
@@ -1392,20 +1395,30 @@ int gdn_dispatch_f32(const Args &a, hipStream_t st) {
   return (int)hipErrorInvalidValue;
 }
 
-#define RSSM_WRAP4(name, kern)                           \
-  template <int CF, int RF, int NCH, int RBW>            \
-  struct name {                                          \
-    static constexpr auto fn = kern<CF, RF, NCH, RBW>;   \
+// Kernel wrappers over the record element type (float32, or bf16 records).
+#define RSSM_WRAP4(name, kern)                              \
+  template <typename R>                                     \
+  struct name {                                             \
+    template <int CF, int RF, int NCH, int RBW>             \
+    struct K {                                              \
+      static constexpr auto fn = kern<CF, RF, NCH, RBW, R>; \
+    };                                                      \
   };
 RSSM_WRAP4(GStepK, gdn_replay_step)
 RSSM_WRAP4(GFlushK, gdn_flush)
 RSSM_WRAP4(GVerifyK, gdn_replay_verify)
-RSSM_WRAP4(GEncodeK, gdn_encode_state)
 #undef RSSM_WRAP4
-#define RSSM_WRAP(name, kern)                  \
-  template <int NCH, int RBW>                  \
-  struct name {                                \
-    static constexpr auto fn = kern<NCH, RBW>; \
+template <int CF, int RF, int NCH, int RBW>
+struct GEncodeK {
+  static constexpr auto fn = gdn_encode_state<CF, RF, NCH, RBW>;
+};
+#define RSSM_WRAP(name, kern)                       \
+  template <typename R>                             \
+  struct name {                                     \
+    template <int NCH, int RBW>                     \
+    struct K {                                      \
+      static constexpr auto fn = kern<NCH, RBW, R>; \
+    };                                              \
   };
 RSSM_WRAP(GConvK, gdn_conv_step)
 RSSM_WRAP(GSnapK, gdn_snapshot_verify)
@@ -1423,18 +1436,25 @@ GdnStateBufs state_bufs(const GdnFormatBufs &f) {
 }  // namespace
 
 int launch_gdn_step(const GdnStepArgs &a, const GdnFormatBufs &f, hipStream_t st) {
-  return gdn_dispatch<GStepK>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
+  return a.bf16 ? gdn_dispatch<GStepK<bf16_t>::template K>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st)
+                : gdn_dispatch<GStepK<float>::template K>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
 }
 int launch_gdn_flush(const GdnFlushArgs &a, const GdnFormatBufs &f, hipStream_t st) {
-  return gdn_dispatch<GFlushK>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
+  return a.bf16 ? gdn_dispatch<GFlushK<bf16_t>::template K>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st)
+                : gdn_dispatch<GFlushK<float>::template K>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
 }
 int launch_gdn_verify(const GdnVerifyArgs &a, const GdnFormatBufs &f, hipStream_t st) {
-  return gdn_dispatch<GVerifyK>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
+  return a.bf16 ? gdn_dispatch<GVerifyK<bf16_t>::template K>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st)
+                : gdn_dispatch<GVerifyK<float>::template K>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
 }
 int launch_gdn_encode(const GdnEncodeArgs &a, const GdnFormatBufs &f, hipStream_t st) {
   return gdn_dispatch<GEncodeK>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
 }
-int launch_gdn_conv(const GdnConvArgs &a, hipStream_t st) { return gdn_dispatch_f32<GConvK>(a, st); }
-int launch_gdn_snapshot(const GdnSnapArgs &a, hipStream_t st) { return gdn_dispatch_f32<GSnapK>(a, st); }
+int launch_gdn_conv(const GdnConvArgs &a, hipStream_t st) {
+  return a.bf16 ? gdn_dispatch_f32<GConvK<bf16_t>::template K>(a, st) : gdn_dispatch_f32<GConvK<float>::template K>(a, st);
+}
+int launch_gdn_snapshot(const GdnSnapArgs &a, hipStream_t st) {
+  return a.bf16 ? gdn_dispatch_f32<GSnapK<bf16_t>::template K>(a, st) : gdn_dispatch_f32<GSnapK<float>::template K>(a, st);
+}
 
 }  // namespace rssm

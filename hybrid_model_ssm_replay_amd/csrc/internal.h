@@ -12,7 +12,9 @@ constexpr uint32_t kCtxMagic = 0x52535331u;  // "RSS1"
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Ring layout.  Every field is float32 and indexed by ring slot; the record at
+// Ring layout.  Fields are float32, except the record vector fields (Mamba-2
+// x and B, GDN k and v), which are bf16 with REPLAY_FLAG_BF16_RECORDS; each is
+// indexed by ring slot; the record at
 // token position t lives in slot t % L, except the Mamba-2 B field, which is
 // shared by the heads of a group and lives in slot t % (2 L): a tile that
 // appends a record may then never overwrite a B record that another tile of
@@ -34,25 +36,28 @@ struct RingLayout {
 // copy and must not enter the recurrence), or folds the cached pseudo-values.
 inline bool gdn_refold(const replay_config &c) { return c.ckpt_fmt != c.read_fmt; }
 
+inline bool bf16_records(const replay_config &c) { return (c.flags & REPLAY_FLAG_BF16_RECORDS) != 0; }
+
 inline RingLayout ring_layout(const replay_config &c) {
   RingLayout r{};
+  const size_t re = bf16_records(c) ? 2 : 4;  // bytes per record vector element
   const size_t B = c.batch, H = c.heads, G = c.groups, L = c.window, P = c.head_dim, N = c.state_dim;
-  size_t sz[5] = {0, 0, 0, 0, 0};
+  size_t sz[5] = {0, 0, 0, 0, 0};  // bytes
   if (c.kind == REPLAY_KIND_MAMBA2) {
-    sz[0] = B * H * L * P;
-    sz[1] = B * G * 2 * L * N;
-    sz[2] = B * H * L;
+    sz[0] = B * H * L * P * re;
+    sz[1] = B * G * 2 * L * N * re;
+    sz[2] = B * H * L * 4;
   } else {
-    sz[0] = B * H * L * N;
-    sz[1] = B * H * L * P;
-    sz[2] = B * H * L;
-    sz[3] = B * H * L;
-    sz[4] = gdn_refold(c) ? B * H * L * P : 0;
+    sz[0] = B * H * L * N * re;
+    sz[1] = B * H * L * P * 4;
+    sz[2] = B * H * L * 4;
+    sz[3] = B * H * L * 4;
+    sz[4] = gdn_refold(c) ? B * H * L * P * re : 0;
   }
   size_t o = 0;
   for (int i = 0; i < 5; ++i) {
     r.off[i] = o;
-    o += align256(sz[i] * sizeof(float));
+    o += align256(sz[i]);
   }
   r.bytes = o;
   return r;
@@ -71,9 +76,12 @@ inline Shape make_shape(int B, int H, int G, int P, int N, int L) {
 }
 
 // Mamba-2 ---------------------------------------------------------------
+// Record vector fields (x, B, C here; q, k, v for GDN) and their ring copies
+// are float32, or bf16 when `bf16` is set (REPLAY_FLAG_BF16_RECORDS); the
+// kernels take the element type as a template parameter.
 struct M2Ring {
-  float *x;   // [L][B][H][P]
-  float *Bm;  // [B][G][2L][N]
+  void *x;    // [L][B][H][P]
+  void *Bm;   // [B][G][2L][N]
   float *dt;  // [B][H][L]
 };
 
@@ -85,8 +93,10 @@ struct M2StepArgs {
   PtrHalves ptr;
   int32_t *status;
   const float *A, *D;
-  const float *x, *Bm, *Cm, *dt;  // this token: [B][H][P], [B][G][N], [B][G][N], [B][H]
-  float *y;                        // [B][H][P]
+  const void *x, *Bm, *Cm;  // this token: [B][H][P], [B][G][N], [B][G][N]
+  const float *dt;           // [B][H]
+  int bf16;
+  float *y;                  // [B][H][P]
 };
 
 struct M2VerifyArgs {
@@ -98,8 +108,10 @@ struct M2VerifyArgs {
   PtrHalves ptr;
   int32_t *status;
   const float *A, *D;
-  const float *x, *Bm, *Cm, *dt;  // drafts: [B][T][H][P], [B][T][G][N], [B][T][G][N], [B][T][H]
-  float *y;                        // [B][T][H][P]
+  const void *x, *Bm, *Cm;  // drafts: [B][T][H][P], [B][T][G][N], [B][T][G][N]
+  const float *dt;           // [B][T][H]
+  int bf16;
+  float *y;                  // [B][T][H][P]
 };
 
 struct M2FlushArgs {
@@ -111,13 +123,16 @@ struct M2FlushArgs {
   int32_t *status;
   const float *A;
   const uint8_t *mask;  // [B] or NULL
+  int bf16;
 };
 
 struct M2ConvArgs {
   Shape s;
   float *state;  // [B][H][P][N]
   const float *A, *D;
-  const float *x, *Bm, *Cm, *dt;
+  const void *x, *Bm, *Cm;
+  const float *dt;
+  int bf16;
   float *y;
 };
 
@@ -127,17 +142,19 @@ struct M2SnapArgs {
   float *slots;  // [B][nslots][H][P][N]
   const int32_t *cur;
   const float *A, *D;
-  const float *x, *Bm, *Cm, *dt;  // drafts, as M2VerifyArgs
+  const void *x, *Bm, *Cm;  // drafts, as M2VerifyArgs
+  const float *dt;
+  int bf16;
   float *y;
 };
 
 // Gated DeltaNet ---------------------------------------------------------
 struct GdnRing {
-  float *k;      // [L][B][H][dk] (slot-major)
+  void *k;       // [L][B][H][dk] (slot-major)
   float *u;      // [L][B][H][dv] (slot-major): pseudo-values
   float *alpha;  // [B][H][L]
   float *beta;   // [B][H][L]
-  float *v;      // [L][B][H][dv] (slot-major), separate read copy only; else NULL
+  void *v;       // [L][B][H][dv] (slot-major), separate read copy only; else NULL
 };
 
 struct GdnStepArgs {
@@ -145,8 +162,10 @@ struct GdnStepArgs {
   GdnRing ring;
   PtrHalves ptr;
   int32_t *status;
-  const float *q, *k, *v, *alpha, *beta;  // this token: [B][H][dk], [B][H][dk], [B][H][dv], [B][H], [B][H]
-  float *y;                               // [B][H][dv]
+  const void *q, *k, *v;        // this token: [B][H][dk], [B][H][dk], [B][H][dv]
+  const float *alpha, *beta;    // [B][H]
+  int bf16;
+  float *y;                     // [B][H][dv]
 };
 
 struct GdnVerifyArgs {
@@ -155,8 +174,10 @@ struct GdnVerifyArgs {
   GdnRing ring;
   PtrHalves ptr;
   int32_t *status;
-  const float *q, *k, *v, *alpha, *beta;  // drafts: [B][T][H][...]
-  float *y;                               // [B][T][H][dv]
+  const void *q, *k, *v;  // drafts: [B][T][H][...]
+  const float *alpha, *beta;
+  int bf16;
+  float *y;               // [B][T][H][dv]
 };
 
 struct GdnFlushArgs {
@@ -165,12 +186,15 @@ struct GdnFlushArgs {
   PtrHalves ptr;
   int32_t *status;
   const uint8_t *mask;
+  int bf16;
 };
 
 struct GdnConvArgs {
   Shape s;
   float *state;  // [B][H][dv][dk]
-  const float *q, *k, *v, *alpha, *beta;
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  int bf16;
   float *y;
 };
 
@@ -179,7 +203,9 @@ struct GdnSnapArgs {
   int T, nslots;
   float *slots;  // [B][nslots][H][dv][dk]
   const int32_t *cur;
-  const float *q, *k, *v, *alpha, *beta;  // drafts
+  const void *q, *k, *v;  // drafts
+  const float *alpha, *beta;
+  int bf16;
   float *y;
 };
 

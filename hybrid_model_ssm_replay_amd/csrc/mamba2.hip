@@ -102,9 +102,9 @@ __device__ __forceinline__ float suffix_sum16(float v, int lane, float *total) {
 // Fold the cnt (1..L) committed records at positions base .. base+cnt-1 into
 // the register tile: s <- exp(A s_{1..cnt}) s + sum_r exp(A s_{r+1..cnt}) dt_r x_r B_r^T.
 // Ends with a barrier; sm.Bs is free again afterwards.
-template <int NCH, int RBW, bool SKIP>
+template <int NCH, int RBW, bool SKIP, typename R>
 __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm, int cnt, int base,
-                                          float Ah, const float *rx, const float *rdt, const float *rB,
+                                          float Ah, const R *rx, const float *rdt, const R *rB,
                                           int L, size_t xs, const TileCtx &t) {
   constexpr int N = 16 * NCH;
   // Stage B_r (cnt x N) in LDS; zero the rows up to the next multiple of 4.
@@ -112,7 +112,7 @@ __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm
   for (int e = 4 * t.tid; e < rows4 * N; e += 4 * t.nthreads) {
     const int r = e / N, n = e - r * N;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r < cnt) v = ld4(rB + (size_t)((base + r) % (2 * L)) * N + n);
+    if (r < cnt) v = ldr4<R>(rB + (size_t)((base + r) % (2 * L)) * N + n);
     *reinterpret_cast<float4 *>(&sm.Bs[r][n]) = v;
   }
   // Decay weights, per wave, record r in lane r.
@@ -131,7 +131,7 @@ __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm
     for (int st = 0; st < 4; ++st) {
       const int r = 4 * st + t.q;
       const float fr = __shfl(f, r, kWave);
-      xb[st] = (r < cnt) ? fr * rx[(size_t)((base + r) % L) * xs + row] : 0.f;
+      xb[st] = (r < cnt) ? fr * ldr<R>(rx + (size_t)((base + r) % L) * xs + row) : 0.f;
     }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -171,9 +171,9 @@ struct FoldIn {
   int nsteps;          // ceil(cnt / 4)
 };
 
-template <int NCH, int RBW>
-__device__ __forceinline__ void fold_load(FoldIn<NCH, RBW> &fi, int cnt, int s0, int s0b, const float *rx,
-                                          const float *rdt, const float *rB, int L, size_t xs, int rb0, int lane) {
+template <int NCH, int RBW, typename R>
+__device__ __forceinline__ void fold_load(FoldIn<NCH, RBW> &fi, int cnt, int s0, int s0b, const R *rx,
+                                          const float *rdt, const R *rB, int L, size_t xs, int rb0, int lane) {
   // s0 = (position of record 0) mod L, s0b = the same mod 2 L; xs = x-ring slot stride.
   const int q = lane >> 4, r16 = lane & 15;
   const float dtl = rdt[wrap(s0, r16 < cnt ? r16 : cnt - 1, L)];
@@ -183,16 +183,16 @@ __device__ __forceinline__ void fold_load(FoldIn<NCH, RBW> &fi, int cnt, int s0,
   for (int st = 0; st < 4; ++st) {
     const int r = 4 * st + q;
     const int rc = r < cnt ? r : cnt - 1;
-    const float *Br = rB + wrap(s0b, rc, 2 * L) * (16 * NCH);
+    const R *Br = rB + wrap(s0b, rc, 2 * L) * (16 * NCH);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const float v = Br[16 * c + r16];
+      const float v = ldr<R>(Br + 16 * c + r16);
       fi.aB[c][st] = r < cnt ? v : 0.f;
     }
-    const float *xr = rx + wrap(s0, rc, L) * xs;
+    const R *xr = rx + wrap(s0, rc, L) * xs;
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
-      const float v = xr[(rb0 + k) * 16 + r16];
+      const float v = ldr<R>(xr + (rb0 + k) * 16 + r16);
       fi.xraw[st][k] = r < cnt ? v : 0.f;
     }
   }
@@ -283,7 +283,7 @@ __device__ __forceinline__ float replay_output(const float4 (&s)[RBW][NCH], cons
   return pick<RBW>(acc, q);
 }
 
-template <int NCH, int RBW, bool SKIP>
+template <int NCH, int RBW, bool SKIP, typename R>
 __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   constexpr int N = 16 * NCH;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
@@ -296,12 +296,12 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   const int rb0 = wave * RBW;
   float *S = a.ckpt + ((size_t)b * sh.H + h) * P * N;
   const size_t xs = (size_t)sh.B * sh.H * P;  // x-ring slot stride (slot-major ring)
-  float *rx = a.ring.x + ((size_t)b * sh.H + h) * P;
+  R *rx = static_cast<R *>(a.ring.x) + ((size_t)b * sh.H + h) * P;
   float *rdt = a.ring.dt + ((size_t)b * sh.H + h) * L;
-  float *rB = a.ring.Bm + ((size_t)b * sh.G + g) * 2 * L * N;
-  const float *xin = a.x + ((size_t)b * sh.H + h) * P;
-  const float *Bin = a.Bm + ((size_t)b * sh.G + g) * N;
-  const float *Cin = a.Cm + ((size_t)b * sh.G + g) * N;
+  R *rB = static_cast<R *>(a.ring.Bm) + ((size_t)b * sh.G + g) * 2 * L * N;
+  const R *xin = static_cast<const R *>(a.x) + ((size_t)b * sh.H + h) * P;
+  const R *Bin = static_cast<const R *>(a.Bm) + ((size_t)b * sh.G + g) * N;
+  const R *Cin = static_cast<const R *>(a.Cm) + ((size_t)b * sh.G + g) * N;
 
   // 1. Everything whose address needs no pointer, checkpoint first: its loads
   //    are then in flight while the pointers arrive.  (Loads complete in issue
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   if constexpr (!SKIP) load_rows<NCH, RBW>(s, S, rb0, lane);
   float4 cv[NCH];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) cv[c] = ld4(Cin + 16 * c + 4 * q);
+  for (int c = 0; c < NCH; ++c) cv[c] = ldr4<R>(Cin + 16 * c + 4 * q);
   const float dtrow = rdt[r16 < L ? r16 : 0];  // the head's whole dt ring, slot = r16
   const float dt_in = a.dt[(size_t)b * sh.H + h];
   const float Ah = a.A[h], Dh = a.D[h];
@@ -359,18 +359,18 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
     float4 bj[NCH];
     {
       const int j = r16 < m ? r16 : m - 1;
-      const float *Bj = (j == m - 1) ? Bin : rB + wrap(s0b, j, 2 * L) * N;
+      const R *Bj = (j == m - 1) ? Bin : rB + wrap(s0b, j, 2 * L) * N;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) bj[c] = ld4(Bj + 16 * c + 4 * q);
+      for (int c = 0; c < NCH; ++c) bj[c] = ldr4<R>(Bj + 16 * c + 4 * q);
     }
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int j = 4 * st + q;
       const int jc = j < m ? j : m - 1;
-      const float *xj = (jc == m - 1) ? xin : rx + wrap(s0, jc, L) * xs;
+      const R *xj = (jc == m - 1) ? xin : rx + wrap(s0, jc, L) * xs;
 #pragma unroll
       for (int k = 0; k < RBW; ++k) {
-        const float v = xj[(rb0 + k) * 16 + r16];
+        const float v = ldr<R>(xj + (rb0 + k) * 16 + r16);
         xr[st][k] = j < m ? v : 0.f;
       }
     }
@@ -387,10 +387,10 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
     // Fold the full window into the checkpoint, store it, and start the next
     // window with this token as its only record.
     FoldIn<NCH, RBW> fi;
-    fold_load<NCH, RBW>(fi, L, s0, s0b, rx, rdt, rB, L, xs, rb0, lane);
+    fold_load<NCH, RBW, R>(fi, L, s0, s0b, rx, rdt, rB, L, xs, rb0, lane);
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
-      const float v = xin[(rb0 + k) * 16 + r16];
+      const float v = ldr<R>(xin + (rb0 + k) * 16 + r16);
 #pragma unroll
       for (int st = 0; st < 4; ++st) xr[st][k] = (st == 0 && q == 0) ? v : 0.f;
     }
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
     // This token's B . C after the fold: computing it earlier keeps more
     // registers live across the fold and costs occupancy on every step.
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) bdot += dot4(ld4(Bin + 16 * c + 4 * q), cv[c]);
+    for (int c = 0; c < NCH; ++c) bdot += dot4(ldr4<R>(Bin + 16 * c + 4 * q), cv[c]);
     bdot = r16 == 0 ? bdot : 0.f;
   }
   const int m = pos - base + 1;
@@ -412,9 +412,9 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   if (fold && nwaves > 1) __syncthreads();
   if (q < RBW) {
     const int row = (rb0 + q) * 16 + r16;
-    const float xv = xin[row];
+    const float xv = ldr<R>(xin + row);
     a.y[((size_t)b * sh.H + h) * P + row] = out + Dh * xv;
-    rx[slot * xs + row] = xv;
+    str<R>(rx + slot * xs + row, xv);
   }
   if (threadIdx.x == 0) rdt[slot] = dt_in;
   if (h - g * (sh.H / sh.G) == 0 && wave == 0)
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
 }
 
 // ---- explicit flush ---------------------------------------------------------
-template <int NCH, int RBW, bool SKIP>
+template <int NCH, int RBW, bool SKIP, typename R>
 __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
   constexpr int N = 16 * NCH;
   __shared__ M2Smem<NCH> sm;
@@ -448,9 +448,9 @@ __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
   if (!fold) return;
   float *S = a.ckpt + ((size_t)b * sh.H + h) * P * N;
   const size_t xs = (size_t)sh.B * sh.H * P;
-  const float *rx = a.ring.x + ((size_t)b * sh.H + h) * P;
+  const R *rx = static_cast<const R *>(a.ring.x) + ((size_t)b * sh.H + h) * P;
   const float *rdt = a.ring.dt + ((size_t)b * sh.H + h) * L;
-  const float *rB = a.ring.Bm + ((size_t)b * sh.G + g) * 2 * L * N;
+  const R *rB = static_cast<const R *>(a.ring.Bm) + ((size_t)b * sh.G + g) * 2 * L * N;
   float4 s[RBW][NCH];
   bool keep = true;  // the checkpoint term survives the decay skip
   if constexpr (SKIP) {
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) s[k][c] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  fold_tile<NCH, RBW, SKIP>(s, sm, count, ck, a.A[h], rx, rdt, rB, L, xs, t);
+  fold_tile<NCH, RBW, SKIP, R>(s, sm, count, ck, a.A[h], rx, rdt, rB, L, xs, t);
   store_tile<NCH, RBW>(s, S, t);
 }
 
@@ -495,7 +495,7 @@ __device__ __forceinline__ floatx4 mfma_4x4x1(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
 
-template <int NCH, int RBW, bool SKIP>
+template <int NCH, int RBW, bool SKIP, typename R>
 __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   constexpr int N = 16 * NCH;
   constexpr int kPass = kMaxL / 4;
@@ -513,12 +513,13 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   const int rb0 = wave * RBW;
   float *S = a.ckpt + ((size_t)b * H + h) * P * N;
   const size_t xs = (size_t)sh.B * H * P;
-  float *rx = a.ring.x + ((size_t)b * H + h) * P;
+  R *rx = static_cast<R *>(a.ring.x) + ((size_t)b * H + h) * P;
   float *rdt = a.ring.dt + ((size_t)b * H + h) * L;
-  float *rB = a.ring.Bm + ((size_t)b * G + g) * 2 * L * N;
-  auto draft_x = [&](int i) { return a.x + (((size_t)b * T + i) * H + h) * P; };
-  auto draft_B = [&](int i) { return a.Bm + (((size_t)b * T + i) * G + g) * N; };
-  auto draft_C = [&](int i) { return a.Cm + (((size_t)b * T + i) * G + g) * N; };
+  R *rB = static_cast<R *>(a.ring.Bm) + ((size_t)b * G + g) * 2 * L * N;
+  const R *dx = static_cast<const R *>(a.x), *dB = static_cast<const R *>(a.Bm), *dC = static_cast<const R *>(a.Cm);
+  auto draft_x = [&](int i) { return dx + (((size_t)b * T + i) * H + h) * P; };
+  auto draft_B = [&](int i) { return dB + (((size_t)b * T + i) * G + g) * N; };
+  auto draft_C = [&](int i) { return dC + (((size_t)b * T + i) * G + g) * N; };
   const int npass = (T + 3) >> 2;
 
   // 1. The checkpoint stream, the pointers, then the drafts' C into LDS (load
@@ -536,7 +537,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
       const int q2 = slot & 3, m2 = (slot >> 2) & 3, pc = slot >> 4;  // pc = p NCH + cc
       const int p2 = pc / NCH, cc = pc - p2 * NCH;
       const int n = 4 * p2 + m2;
-      dma16(draft_C(n < T ? n : T - 1) + 16 * cc + 4 * q2, &ldsC[64 * j]);
+      stage4<R>(draft_C(n < T ? n : T - 1) + 16 * cc + 4 * q2, &ldsC[64 * j], lane);
     }
   }
 
@@ -555,7 +556,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   int base = ck;
   if (fold) {
     FoldIn<NCH, RBW> fi;
-    fold_load<NCH, RBW>(fi, count, fmod_(ck, sh.fL), fmod_(ck, sh.f2L), rx, rdt, rB, L, xs, rb0, lane);
+    fold_load<NCH, RBW, R>(fi, count, fmod_(ck, sh.fL), fmod_(ck, sh.f2L), rx, rdt, rB, L, xs, rb0, lane);
     fold_apply<NCH, RBW, SKIP>(s, fi, Ah, lane);
     store_rows<NCH, RBW>(s, S, rb0, lane);
     base = pos;
@@ -569,18 +570,18 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   //    (record-sum A operand); dt of record r16.
   {
     const int rc = r16 < nrec ? r16 : nrec - 1;
-    const float *Br = rc < c ? rB + (size_t)wrap(sbb, rc, 2 * L) * N : draft_B(rc - c);
-    for (int cc = wave; cc < NCH; cc += nwaves) dma16(Br + 16 * cc + 4 * q, &ldsB[cc][0]);
+    const R *Br = rc < c ? rB + (size_t)wrap(sbb, rc, 2 * L) * N : draft_B(rc - c);
+    for (int cc = wave; cc < NCH; cc += nwaves) stage4<R>(Br + 16 * cc + 4 * q, &ldsB[cc][0], lane);
   }
   float xa[RBW][4];
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     const int r = 4 * st + q;
     const int rc = r < nrec ? r : nrec - 1;
-    const float *xr = rc < c ? rx + (size_t)wrap(sb, rc, L) * xs : draft_x(rc - c);
+    const R *xr = rc < c ? rx + (size_t)wrap(sb, rc, L) * xs : draft_x(rc - c);
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
-      const float v = xr[(rb0 + k) * 16 + r16];
+      const float v = ldr<R>(xr + (rb0 + k) * 16 + r16);
       xa[k][st] = r < nrec ? v : 0.f;
     }
   }
@@ -600,7 +601,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
     const int nc = n < T ? n : T - 1;
     float4 xl[RBW];  // x_n at rows 16 rb + 4 g + 0..3 (the D x term)
 #pragma unroll
-    for (int k = 0; k < RBW; ++k) xl[k] = ld4(draft_x(nc) + (rb0 + k) * 16 + 4 * gq);
+    for (int k = 0; k < RBW; ++k) xl[k] = ldr4<R>(draft_x(nc) + (rb0 + k) * 16 + 4 * gq);
     const float4 *cdp = &ldsC[(p * NCH * 4 + m4) * 4 + q];  // C_n at tile chunk cc: cdp[16 cc]
 
     // dots[4 g + v][n] (register v, summed over q), transposed through LDS.
@@ -677,14 +678,14 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
     const int r = 4 * st + q;
     if (r >= c && r < nrec) {
 #pragma unroll
-      for (int k = 0; k < RBW; ++k) rx[(size_t)wrap(sb, r, L) * xs + (rb0 + k) * 16 + r16] = xa[k][st];
+      for (int k = 0; k < RBW; ++k) str<R>(rx + (size_t)wrap(sb, r, L) * xs + (rb0 + k) * 16 + r16, xa[k][st]);
     }
   }
   if (wave == 0) {
     if (lane >= c && lane < nrec) rdt[wrap(sb, lane, L)] = dtl;
     if (h - g * (H / G) == 0 && r16 >= c && r16 < nrec) {
 #pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) st4(rB + (size_t)wrap(sbb, r16, 2 * L) * N + 16 * cc + 4 * q, ldsB[cc][lane]);
+      for (int cc = 0; cc < NCH; ++cc) str4<R>(rB + (size_t)wrap(sbb, r16, 2 * L) * N + 16 * cc + 4 * q, ldsB[cc][lane]);
     }
   }
   if (h == 0 && threadIdx.x == 0) {
@@ -696,7 +697,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
 // ---- baseline: conventional load-update-store step -------------------------
 // Same geometry and load order as the replay step: one wave per head, every
 // load issued before any arithmetic.
-template <int NCH, int RBW>
+template <int NCH, int RBW, typename R>
 __global__ __launch_bounds__(256) void m2_conv_step(M2ConvArgs a) {
   constexpr int N = 16 * NCH;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -709,18 +710,18 @@ __global__ __launch_bounds__(256) void m2_conv_step(M2ConvArgs a) {
   float *S = a.state + ((size_t)b * sh.H + h) * P * N;
   float4 s[RBW][NCH];
   load_rows<NCH, RBW>(s, S, rb0, lane);
-  const float *Bin = a.Bm + ((size_t)b * sh.G + g) * N;
-  const float *Cin = a.Cm + ((size_t)b * sh.G + g) * N;
+  const R *Bin = static_cast<const R *>(a.Bm) + ((size_t)b * sh.G + g) * N;
+  const R *Cin = static_cast<const R *>(a.Cm) + ((size_t)b * sh.G + g) * N;
   float4 bv[NCH], cv[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    bv[c] = ld4(Bin + 16 * c + 4 * q);
-    cv[c] = ld4(Cin + 16 * c + 4 * q);
+    bv[c] = ldr4<R>(Bin + 16 * c + 4 * q);
+    cv[c] = ldr4<R>(Cin + 16 * c + 4 * q);
   }
-  const float *xin = a.x + ((size_t)b * sh.H + h) * P;
+  const R *xin = static_cast<const R *>(a.x) + ((size_t)b * sh.H + h) * P;
   float xr[RBW];
 #pragma unroll
-  for (int k = 0; k < RBW; ++k) xr[k] = xin[(rb0 + k) * 16 + r16];
+  for (int k = 0; k < RBW; ++k) xr[k] = ldr<R>(xin + (rb0 + k) * 16 + r16);
   const float dt = a.dt[(size_t)b * sh.H + h];
   const float decay = __expf(dt * a.A[h]);
   const float Dh = a.D[h];
@@ -743,12 +744,12 @@ __global__ __launch_bounds__(256) void m2_conv_step(M2ConvArgs a) {
   store_rows<NCH, RBW>(s, S, rb0, lane);
   if (q < RBW) {
     const int row = (rb0 + q) * 16 + r16;
-    a.y[((size_t)b * sh.H + h) * P + row] = pick<RBW>(acc, q) + Dh * xin[row];
+    a.y[((size_t)b * sh.H + h) * P + row] = pick<RBW>(acc, q) + Dh * ldr<R>(xin + row);
   }
 }
 
 // ---- baseline: snapshot-per-draft verify -----------------------------------
-template <int NCH, int RBW>
+template <int NCH, int RBW, typename R>
 __global__ __launch_bounds__(256) void m2_snapshot_verify(M2SnapArgs a) {
   constexpr int N = 16 * NCH;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -768,19 +769,19 @@ __global__ __launch_bounds__(256) void m2_snapshot_verify(M2SnapArgs a) {
   for (int i = 0; i < T; ++i) {
     const float dt = a.dt[((size_t)b * T + i) * H + h];
     const float decay = __expf(dt * Ah);
-    const float *xin = a.x + (((size_t)b * T + i) * H + h) * P;
-    const float *Bin = a.Bm + (((size_t)b * T + i) * G + g) * N;
-    const float *Cin = a.Cm + (((size_t)b * T + i) * G + g) * N;
+    const R *xin = static_cast<const R *>(a.x) + (((size_t)b * T + i) * H + h) * P;
+    const R *Bin = static_cast<const R *>(a.Bm) + (((size_t)b * T + i) * G + g) * N;
+    const R *Cin = static_cast<const R *>(a.Cm) + (((size_t)b * T + i) * G + g) * N;
     float4 bv[NCH], cv[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      bv[c] = ld4(Bin + 16 * c + 4 * q);
-      cv[c] = ld4(Cin + 16 * c + 4 * q);
+      bv[c] = ldr4<R>(Bin + 16 * c + 4 * q);
+      cv[c] = ldr4<R>(Cin + 16 * c + 4 * q);
     }
     float acc[RBW];
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
-      const float dx = dt * xin[(rb0 + k) * 16 + r16];
+      const float dx = dt * ldr<R>(xin + (rb0 + k) * 16 + r16);
       float v = 0.f;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
@@ -795,7 +796,7 @@ __global__ __launch_bounds__(256) void m2_snapshot_verify(M2SnapArgs a) {
     }
     if (q < RBW) {
       const int row = (rb0 + q) * 16 + r16;
-      a.y[(((size_t)b * T + i) * H + h) * P + row] = pick<RBW>(acc, q) + Dh * xin[row];
+      a.y[(((size_t)b * T + i) * H + h) * P + row] = pick<RBW>(acc, q) + Dh * ldr<R>(xin + row);
     }
     store_rows<NCH, RBW>(s, slot_ptr((cur + 1 + i) % a.nslots), rb0, lane);
   }
@@ -822,15 +823,22 @@ int dispatch(const Args &a, int N, int P, int B, int H, bool wave_per_head, hipS
   return (int)hipErrorInvalidValue;
 }
 
-#define RSSM_WRAP(name, kern)                  \
-  template <int NCH, int RBW>                  \
-  struct name {                                \
-    static constexpr auto fn = kern<NCH, RBW>; \
+// Kernel wrappers over the record element type (float32, or bf16 records).
+#define RSSM_WRAP(name, kern)                     \
+  template <typename R>                           \
+  struct name {                                   \
+    template <int NCH, int RBW>                   \
+    struct K {                                    \
+      static constexpr auto fn = kern<NCH, RBW, R>; \
+    };                                            \
   };
-#define RSSM_WRAP_SKIP(name, kern, SKIP_)             \
-  template <int NCH, int RBW>                         \
-  struct name {                                       \
-    static constexpr auto fn = kern<NCH, RBW, SKIP_>; \
+#define RSSM_WRAP_SKIP(name, kern, SKIP_)                \
+  template <typename R>                                  \
+  struct name {                                          \
+    template <int NCH, int RBW>                          \
+    struct K {                                           \
+      static constexpr auto fn = kern<NCH, RBW, SKIP_, R>; \
+    };                                                   \
   };
 RSSM_WRAP_SKIP(StepK, m2_replay_step, false)
 RSSM_WRAP_SKIP(StepSkipK, m2_replay_step, true)
@@ -843,25 +851,25 @@ RSSM_WRAP(SnapK, m2_snapshot_verify)
 #undef RSSM_WRAP_SKIP
 #undef RSSM_WRAP
 
+// Launch W<float>::K or W<bf16_t>::K by the record element type.
+template <template <typename> class W, typename Args>
+int dispatch_rec(const Args &a, bool wave_per_head, hipStream_t st) {
+  return a.bf16 ? dispatch<W<bf16_t>::template K>(a, a.s.N, a.s.P, a.s.B, a.s.H, wave_per_head, st)
+                : dispatch<W<float>::template K>(a, a.s.N, a.s.P, a.s.B, a.s.H, wave_per_head, st);
+}
+
 }  // namespace
 
 int launch_m2_step(const M2StepArgs &a, hipStream_t st) {
-  return a.decay_skip ? dispatch<StepSkipK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st)
-                      : dispatch<StepK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
+  return a.decay_skip ? dispatch_rec<StepSkipK>(a, true, st) : dispatch_rec<StepK>(a, true, st);
 }
 int launch_m2_flush(const M2FlushArgs &a, hipStream_t st) {
-  return a.decay_skip ? dispatch<FlushSkipK>(a, a.s.N, a.s.P, a.s.B, a.s.H, false, st)
-                      : dispatch<FlushK>(a, a.s.N, a.s.P, a.s.B, a.s.H, false, st);
+  return a.decay_skip ? dispatch_rec<FlushSkipK>(a, false, st) : dispatch_rec<FlushK>(a, false, st);
 }
 int launch_m2_verify(const M2VerifyArgs &a, hipStream_t st) {
-  return a.decay_skip ? dispatch<VerifySkipK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st)
-                      : dispatch<VerifyK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
+  return a.decay_skip ? dispatch_rec<VerifySkipK>(a, true, st) : dispatch_rec<VerifyK>(a, true, st);
 }
-int launch_m2_conv(const M2ConvArgs &a, hipStream_t st) {
-  return dispatch<ConvK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
-}
-int launch_m2_snapshot(const M2SnapArgs &a, hipStream_t st) {
-  return dispatch<SnapK>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
-}
+int launch_m2_conv(const M2ConvArgs &a, hipStream_t st) { return dispatch_rec<ConvK>(a, true, st); }
+int launch_m2_snapshot(const M2SnapArgs &a, hipStream_t st) { return dispatch_rec<SnapK>(a, true, st); }
 
 }  // namespace rssm

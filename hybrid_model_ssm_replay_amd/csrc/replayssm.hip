@@ -31,7 +31,7 @@ int check_cfg(const replay_config *c) {
     if (c->head_dim != 64 && c->head_dim != 128) return REPLAY_EINVAL;
     if (c->state_dim < 32) return REPLAY_EINVAL;
   }
-  if ((c->flags & ~REPLAY_FLAG_DECAY_SKIP) || c->reserved) return REPLAY_EINVAL;
+  if ((c->flags & ~(REPLAY_FLAG_DECAY_SKIP | REPLAY_FLAG_BF16_RECORDS)) || c->reserved) return REPLAY_EINVAL;
   if ((c->flags & REPLAY_FLAG_DECAY_SKIP) && c->kind != REPLAY_KIND_MAMBA2) return REPLAY_ENOTSUP;
   if (c->ckpt_fmt < REPLAY_FMT_F32 || c->ckpt_fmt > REPLAY_FMT_F4E2M1_CS) return REPLAY_EINVAL;
   if (c->read_fmt < REPLAY_FMT_F32 || c->read_fmt > REPLAY_FMT_F4E2M1_CS) return REPLAY_EINVAL;
@@ -225,6 +225,7 @@ int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *strea
     a.Bm = rec->f1;
     a.Cm = rec->f2;
     a.dt = rec->f3;
+    a.bf16 = bf16_records(c);
     a.y = y;
     e = launch_m2_step(a, (hipStream_t)stream);
   } else {
@@ -238,6 +239,7 @@ int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *strea
     a.v = rec->f2;
     a.alpha = rec->f3;
     a.beta = rec->f4;
+    a.bf16 = bf16_records(c);
     a.y = y;
     e = launch_gdn_step(a, gdn_formats(*ctx), (hipStream_t)stream);
   }
@@ -261,6 +263,7 @@ int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream) {
     a.status = ctx->buf.status;
     a.A = ctx->buf.A;
     a.mask = seq_mask;
+    a.bf16 = bf16_records(c);
     e = launch_m2_flush(a, (hipStream_t)stream);
   } else {
     GdnFlushArgs a{};
@@ -269,6 +272,7 @@ int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream) {
     a.ptr = halves(*ctx);
     a.status = ctx->buf.status;
     a.mask = seq_mask;
+    a.bf16 = bf16_records(c);
     e = launch_gdn_flush(a, gdn_formats(*ctx), (hipStream_t)stream);
   }
   if (e) return REPLAY_EHIP;
@@ -297,6 +301,7 @@ int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float
     a.Bm = drafts->f1;
     a.Cm = drafts->f2;
     a.dt = drafts->f3;
+    a.bf16 = bf16_records(c);
     a.y = y;
     e = launch_m2_verify(a, (hipStream_t)stream);
   } else {
@@ -311,6 +316,7 @@ int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float
     a.v = drafts->f2;
     a.alpha = drafts->f3;
     a.beta = drafts->f4;
+    a.bf16 = bf16_records(c);
     a.y = y;
     e = launch_gdn_verify(a, gdn_formats(*ctx), (hipStream_t)stream);
   }
@@ -346,6 +352,7 @@ int replay_conv_step(const replay_config *cfg, float *state, const float *A, con
     a.Bm = rec->f1;
     a.Cm = rec->f2;
     a.dt = rec->f3;
+    a.bf16 = bf16_records(*cfg);
     a.y = y;
     return hip_status(launch_m2_conv(a, (hipStream_t)stream));
   }
@@ -357,6 +364,7 @@ int replay_conv_step(const replay_config *cfg, float *state, const float *A, con
   a.v = rec->f2;
   a.alpha = rec->f3;
   a.beta = rec->f4;
+  a.bf16 = bf16_records(*cfg);
   a.y = y;
   return hip_status(launch_gdn_conv(a, (hipStream_t)stream));
 }
@@ -382,6 +390,7 @@ int replay_snapshot_verify(const replay_config *cfg, float *slots, const int32_t
     a.Bm = drafts->f1;
     a.Cm = drafts->f2;
     a.dt = drafts->f3;
+    a.bf16 = bf16_records(*cfg);
     a.y = y;
     return hip_status(launch_m2_snapshot(a, (hipStream_t)stream));
   }
@@ -396,6 +405,7 @@ int replay_snapshot_verify(const replay_config *cfg, float *slots, const int32_t
   a.v = drafts->f2;
   a.alpha = drafts->f3;
   a.beta = drafts->f4;
+  a.bf16 = bf16_records(*cfg);
   a.y = y;
   return hip_status(launch_gdn_snapshot(a, (hipStream_t)stream));
 }

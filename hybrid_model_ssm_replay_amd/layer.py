@@ -13,6 +13,7 @@ import torch
 from . import binding as B
 
 _FIELDS = {B.KIND_MAMBA2: ("x", "B", "C", "dt"), B.KIND_GDN: ("q", "k", "v", "alpha", "beta")}
+_VECTOR_FIELDS = ("x", "B", "C", "q", "k", "v")  # bf16 with FLAG_BF16_RECORDS; the scalars stay float32
 
 
 def _kind(kind) -> int:
@@ -27,18 +28,19 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def _dev_f32(t: torch.Tensor, shape, name) -> torch.Tensor:
-    if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous()):
-        raise ValueError(f"{name} must be a contiguous float32 device tensor")
+def _dev_f32(t: torch.Tensor, shape, name, dtype=torch.float32) -> torch.Tensor:
+    if not (t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     return t
 
 
 class _Shapes:
-    def __init__(self, kind, batch, heads, groups, head_dim, state_dim):
+    def __init__(self, kind, batch, heads, groups, head_dim, state_dim, flags=0):
         self.kind, self.batch, self.heads, self.groups = kind, batch, heads, groups
         self.head_dim, self.state_dim = head_dim, state_dim
+        self.vec_dtype = torch.bfloat16 if flags & B.FLAG_BF16_RECORDS else torch.float32
 
     def field_shapes(self, lead):
         H, G, P, N = self.heads, self.groups, self.head_dim, self.state_dim
@@ -49,7 +51,8 @@ class _Shapes:
 
     def record(self, fields: dict, lead) -> tuple[B.replay_record, list]:
         shapes = self.field_shapes(lead)
-        keep = [_dev_f32(fields[n], shapes[n], n) for n in _FIELDS[self.kind]]
+        keep = [_dev_f32(fields[n], shapes[n], n, self.vec_dtype if n in _VECTOR_FIELDS else torch.float32)
+                for n in _FIELDS[self.kind]]
         return B.make_record(*[t.data_ptr() for t in keep]), keep
 
 
@@ -62,7 +65,7 @@ class ReplayLayer:
         B.load_library()
         k = _kind(kind)
         groups = heads if groups is None else groups
-        self.shapes = _Shapes(k, batch, heads, groups, head_dim, state_dim)
+        self.shapes = _Shapes(k, batch, heads, groups, head_dim, state_dim, flags)
         self.cfg = B.make_config(k, batch, heads, groups, head_dim, state_dim, window, max_draft, ckpt_fmt,
                                  read_fmt, seed, flags)
         rc = B.replay_validate_config(self.cfg)
@@ -166,12 +169,12 @@ class ConvLayer:
     """Baseline: conventional load-update-store decode step on an F32 state."""
 
     def __init__(self, kind, batch, heads, head_dim, state_dim, groups=None, A=None, D=None, state0=None,
-                 device="cuda"):
+                 device="cuda", flags=0):
         B.load_library()
         k = _kind(kind)
         groups = heads if groups is None else groups
-        self.shapes = _Shapes(k, batch, heads, groups, head_dim, state_dim)
-        self.cfg = B.make_config(k, batch, heads, groups, head_dim, state_dim, 1, 0)
+        self.shapes = _Shapes(k, batch, heads, groups, head_dim, state_dim, flags)
+        self.cfg = B.make_config(k, batch, heads, groups, head_dim, state_dim, 1, 0, flags=flags)
         dev = torch.device(device)
         self.state = torch.zeros((batch, heads, head_dim, state_dim), dtype=torch.float32, device=dev)
         if state0 is not None:
@@ -193,12 +196,13 @@ class SnapshotLayer:
     """Baseline: verification that stores one state snapshot per draft token."""
 
     def __init__(self, kind, batch, heads, head_dim, state_dim, max_draft, groups=None, A=None, D=None,
-                 state0=None, device="cuda"):
+                 state0=None, device="cuda", flags=0):
         B.load_library()
         k = _kind(kind)
         groups = heads if groups is None else groups
-        self.shapes = _Shapes(k, batch, heads, groups, head_dim, state_dim)
-        self.cfg = B.make_config(k, batch, heads, groups, head_dim, state_dim, max(max_draft, 1), max_draft)
+        self.shapes = _Shapes(k, batch, heads, groups, head_dim, state_dim, flags)
+        self.cfg = B.make_config(k, batch, heads, groups, head_dim, state_dim, max(max_draft, 1), max_draft,
+                                 flags=flags)
         dev = torch.device(device)
         self.nslots = max_draft + 1
         self.slots = torch.zeros((batch, self.nslots, heads, head_dim, state_dim), dtype=torch.float32, device=dev)

@@ -57,7 +57,8 @@ extern "C" {
 #define REPLAY_FMT_F4E2M1_CS 4  /* F4E2M1_B16 plus a power-of-two scale per state column (read copy only) */
 
 /* Option flags (replay_config.flags). */
-#define REPLAY_FLAG_DECAY_SKIP 0x1u /* Mamba-2: drop the checkpoint term of heads whose decay is below 2^-24 */
+#define REPLAY_FLAG_DECAY_SKIP 0x1u   /* Mamba-2: drop the checkpoint term of heads whose decay is below 2^-24 */
+#define REPLAY_FLAG_BF16_RECORDS 0x2u /* record vector fields (Mamba-2 x, B, C; GDN q, k, v) are bf16 */
 
 /* Return codes. */
 #define REPLAY_OK 0
@@ -93,7 +94,8 @@ extern "C" {
  *               fold that sets ckpt_pos of sequence b draws element e of head h
  *               from word e % 4 of Philox(counter (e / 4, h, b, ckpt_pos),
  *               key (seed low 32 bits, seed high 32 bits)), top 24 bits).
- *   flags       0 or REPLAY_FLAG_DECAY_SKIP (Mamba-2 only, else REPLAY_ENOTSUP):
+ *   flags       an OR of REPLAY_FLAG_DECAY_SKIP and REPLAY_FLAG_BF16_RECORDS.
+ *               REPLAY_FLAG_DECAY_SKIP (Mamba-2 only, else REPLAY_ENOTSUP):
  *               a head whose window decay exp(A s) (s = the dt summed over the
  *               window records a computation uses) is below 2^-24 drops the
  *               checkpoint term: a step then does not read that head's
@@ -101,6 +103,12 @@ extern "C" {
  *               [P3, Perspective, paragraph 1].  An approximation: each output
  *               moves by at most 2^-24 |S0 C|.  Verify applies the same rule to
  *               its outputs and fold-first but always reads the checkpoint.
+ *               REPLAY_FLAG_BF16_RECORDS: the record vector fields (Mamba-2
+ *               x, B, C; GDN q, k, v) of every call, and their copies in the
+ *               ring, are bf16, which halves the record traffic the pages
+ *               count next to the state [P1, Synopsis]; values are widened
+ *               exactly, so the arithmetic (float32) and the state, pseudo-
+ *               values and outputs (float32) are unchanged.
  *   reserved    must be 0.
  * Supported format pairs (ckpt_fmt, read_fmt): (F32, F32) for both families;
  * for Gated DeltaNet with state_dim = 128 also (F32 | F16_SR | F8E4M3, F4E2M1_B16)
@@ -172,7 +180,10 @@ typedef struct replay_buffers {
 } replay_buffers;
 
 /*
- * One record per sequence (step) or T records per sequence (verify), float32:
+ * One record per sequence (step) or T records per sequence (verify).  The
+ * vector fields f0, f1, f2 are float32, or bf16 (IEEE binary32 with the low 16
+ * bits dropped) when the configuration sets REPLAY_FLAG_BF16_RECORDS; the
+ * per-head scalars f3, f4 are always float32:
  *   Mamba-2: f0 = x [batch][heads][P], f1 = B [batch][groups][N],
  *            f2 = C [batch][groups][N], f3 = dt [batch][heads] (already
  *            positive, i.e. after any softplus), f4 unused.
@@ -182,9 +193,9 @@ typedef struct replay_buffers {
  * For verify every field has a draft axis after batch: x [batch][T][heads][P] etc.
  */
 typedef struct replay_record {
-  const float *f0;
-  const float *f1;
-  const float *f2;
+  const void *f0;
+  const void *f1;
+  const void *f2;
   const float *f3;
   const float *f4;
 } replay_record;

@@ -37,6 +37,17 @@ def _sigmoid(z: np.ndarray) -> np.ndarray:
     return 1.0 / (1.0 + np.exp(-z))
 
 
+VECTOR_FIELDS = ("x", "B", "C", "q", "k", "v")
+
+
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """float32 values rounded to the nearest bf16 (ties to even), kept as float32
+    (finite inputs): records that a bf16 tensor holds exactly."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).reshape(np.shape(a))
+
+
 @dataclass(frozen=True)
 class LayerShape:
     """Shape of one decode layer.
@@ -87,8 +98,11 @@ class InputStream:
     ``[batch, T, ...]``.
     """
 
-    def __init__(self, shape: LayerShape, seed: int):
+    def __init__(self, shape: LayerShape, seed: int, bf16_vectors: bool = False):
+        """bf16_vectors: the vector fields (x, B, C / q, k, v) are rounded to bf16
+        values after drawing (the same draws, so the stream stays aligned)."""
         self.shape = shape
+        self.bf16_vectors = bf16_vectors
         self.rng = np.random.Generator(np.random.PCG64(seed))
         self.params = self._draw_params()
 
@@ -119,7 +133,10 @@ class InputStream:
             alpha = np.exp(-0.1 * _softplus(r.standard_normal(lead + (s.heads,))))
             beta = _sigmoid(r.standard_normal(lead + (s.heads,)))
             out = {"q": q, "k": k, "v": v, "alpha": alpha, "beta": beta}
-        return {n: np.ascontiguousarray(a.astype(np.float32)) for n, a in out.items()}
+        out = {n: np.ascontiguousarray(a.astype(np.float32)) for n, a in out.items()}
+        if self.bf16_vectors:
+            out = {n: round_to_bf16(a) if n in VECTOR_FIELDS else a for n, a in out.items()}
+        return out
 
     def record(self) -> dict[str, np.ndarray]:
         """One decode token for every sequence: fields shaped [batch, ...]."""
@@ -160,7 +177,8 @@ class DeviceInputStream:
     the same stream as InputStream's.  Only Gated DeltaNet layers.
     """
 
-    def __init__(self, shape: LayerShape, seed: int, device="cuda", key_spread: float = 0.0):
+    def __init__(self, shape: LayerShape, seed: int, device="cuda", key_spread: float = 0.0,
+                 bf16_vectors: bool = False):
         """key_spread > 0 gives every (head, key dimension) of q and of k a fixed
         magnitude weight exp(key_spread N(0, 1)) (drawn once, before the first
         record) applied before the L2 normalisation: key dimensions of uneven
@@ -173,6 +191,7 @@ class DeviceInputStream:
         self.gen = torch.Generator(device=device)
         self.gen.manual_seed(seed)
         self.device = device
+        self.bf16_vectors = bf16_vectors  # q, k, v returned as bfloat16 tensors
         self.wq = self.wk = None
         if key_spread > 0:
             w = lambda: torch.exp(key_spread * torch.randn(shape.heads, shape.state_dim, generator=self.gen,  # noqa: E731
@@ -192,5 +211,7 @@ class DeviceInputStream:
         v = n(*lead, s.head_dim)
         alpha = t.exp(-0.1 * t.nn.functional.softplus(n(*lead)))
         beta = t.sigmoid(n(*lead))
+        if self.bf16_vectors:
+            q, k, v = (x.to(t.bfloat16) for x in (q, k, v))
         return {"q": q.contiguous(), "k": k.contiguous(), "v": v.contiguous(), "alpha": alpha.contiguous(),
                 "beta": beta.contiguous()}

@@ -10,9 +10,15 @@ def announce(*parts):
     sys.stdout.flush()
 
 
-def to_dev(rec):
+def to_dev(rec, bf16=False):
+    """Device copies of a record; with bf16 the vector fields become bfloat16
+    tensors (the values must already be bf16-representable: exact)."""
     import torch
-    return {n: torch.from_numpy(np.ascontiguousarray(a)).cuda() for n, a in rec.items()}
+    from synth import VECTOR_FIELDS
+    out = {n: torch.from_numpy(np.ascontiguousarray(a)).cuda() for n, a in rec.items()}
+    if bf16:
+        out = {n: t.to(torch.bfloat16) if n in VECTOR_FIELDS else t for n, t in out.items()}
+    return out
 
 
 def host(t):

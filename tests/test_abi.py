@@ -66,6 +66,22 @@ def test_sizes(B):
     assert B.replay_ring_bytes(cfg) == ring
 
 
+def test_sizes_bf16_records(B):
+    """bf16 records halve the ring's record vector fields (Mamba-2 x, B; GDN k and,
+    with a separate read copy, v); scalars, pseudo-values and the state do not change."""
+    cfg = B.make_config(0, 256, 128, 8, 64, 128, 16, 8, flags=B.FLAG_BF16_RECORDS)
+    assert B.replay_validate_config(cfg) == B.OK
+    assert B.replay_ckpt_bytes(cfg) == 256 * 128 * 64 * 128 * 4
+    assert B.replay_ring_bytes(cfg) == 256 * 128 * 16 * 64 * 2 + 256 * 8 * 32 * 128 * 2 + 256 * 128 * 16 * 4
+    g = B.make_config(1, 64, 32, 32, 128, 128, 16, 4, B.FMT_F32, B.FMT_F4E2M1_B16, flags=B.FLAG_BF16_RECORDS)
+    k, u, sc, v = 64 * 32 * 16 * 128 * 2, 64 * 32 * 16 * 128 * 4, 64 * 32 * 16 * 4, 64 * 32 * 16 * 128 * 2
+    assert B.replay_ring_bytes(g) == k + u + 2 * sc + v
+
+
+def test_unknown_flag_rejected(B):
+    assert B.replay_validate_config(B.make_config(0, 2, 4, 1, 16, 16, 4, flags=0x4)) == B.EINVAL
+
+
 def test_calls_reject_uninitialised_context(B):
     ctx = B.replay_ctx()
     rec = B.make_record(16, 16, 16, 16)
