@@ -76,15 +76,23 @@ class Timer:
         return e0.elapsed_time(e1) * 1e3 / n  # microseconds per call
 
 
-def dev_records(torch, ins, n):
-    return [{k: torch.from_numpy(v).cuda() for k, v in ins.record().items()} for _ in range(n)]
+def dev_records(torch, ins, n, bf16=False):
+    """n device records; with bf16 the vector fields are bfloat16 tensors."""
+    from synth import VECTOR_FIELDS
+    cast = (lambda k, t: t.to(torch.bfloat16) if bf16 and k in VECTOR_FIELDS else t)  # noqa: E731
+    return [{k: cast(k, torch.from_numpy(v).cuda()) for k, v in ins.record().items()} for _ in range(n)]
+
+
+def _bf16(flags):
+    from hybrid_model_ssm_replay_amd.binding import FLAG_BF16_RECORDS
+    return bool(flags & FLAG_BF16_RECORDS)
 
 
 def bench_replay(torch, shape, seed, steps, warmup, pool=32, flags=0):
     from hybrid_model_ssm_replay_amd.layer import ReplayLayer
     from synth import InputStream
-    ins = InputStream(shape, seed)
-    recs = dev_records(torch, ins, pool)
+    ins = InputStream(shape, seed, bf16_vectors=_bf16(flags))
+    recs = dev_records(torch, ins, pool, _bf16(flags))
     kw = dict(A=ins.params["A"], D=ins.params["D"]) if shape.kind == "mamba2" else {}
     lay = ReplayLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
                       groups=shape.groups, flags=flags, **kw)
@@ -97,13 +105,14 @@ def bench_replay(torch, shape, seed, steps, warmup, pool=32, flags=0):
     return us
 
 
-def bench_conv(torch, shape, seed, steps, warmup, pool=32):
+def bench_conv(torch, shape, seed, steps, warmup, pool=32, flags=0):
     from hybrid_model_ssm_replay_amd.layer import ConvLayer
     from synth import InputStream
-    ins = InputStream(shape, seed)
-    recs = dev_records(torch, ins, pool)
+    ins = InputStream(shape, seed, bf16_vectors=_bf16(flags))
+    recs = dev_records(torch, ins, pool, _bf16(flags))
     kw = dict(A=ins.params["A"], D=ins.params["D"]) if shape.kind == "mamba2" else {}
-    conv = ConvLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, groups=shape.groups, **kw)
+    conv = ConvLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, groups=shape.groups,
+                     flags=flags, **kw)
     y = torch.empty((shape.batch, shape.heads, shape.head_dim), device="cuda")
     tm = Timer(torch)
     tm.run(lambda i: conv.step(recs[i % pool], y), warmup)
@@ -190,7 +199,7 @@ SPLIT_PAIRS = ((0, 0), (0, 3), (1, 3), (2, 3), (3, 3), (0, 4), (1, 4))
 FMT_NAMES = {0: "f32", 1: "f16sr", 2: "e4m3", 3: "e2m1", 4: "e2m1cs"}
 
 
-def bench_split(torch, seed=5, layers=8, steps=64, warmup=32):
+def bench_split(torch, seed=5, layers=8, steps=64, warmup=32, flags=0, pairs=None):
     """Split-precision Gated DeltaNet layer (32 heads, d = 128, L = 16, batch 64).
 
     `layers` independent layer instances are stepped in rotation, so that the
@@ -204,14 +213,15 @@ def bench_split(torch, seed=5, layers=8, steps=64, warmup=32):
     from synth import WORKLOADS, InputStream
     name = "gdn_b64_h32_d128_l16"
     shape = WORKLOADS[name]
-    lm = Layer("gdn", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.groups, shape.window)
-    recs = dev_records(torch, InputStream(shape, seed), 16)
+    lm = Layer("gdn", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.groups, shape.window,
+               2 if _bf16(flags) else 4)
+    recs = dev_records(torch, InputStream(shape, seed, bf16_vectors=_bf16(flags)), 16, _bf16(flags))
     y = torch.empty((shape.batch, shape.heads, shape.head_dim), device="cuda")
     out = {"workload": name, "layers_rotated": layers, "pairs": {}}
     tm = Timer(torch)
-    for cf, rf in SPLIT_PAIRS:
+    for cf, rf in pairs or SPLIT_PAIRS:
         lays = [ReplayLayer("gdn", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
-                            ckpt_fmt=cf, read_fmt=rf, seed=seed) for _ in range(layers)]
+                            ckpt_fmt=cf, read_fmt=rf, seed=seed, flags=flags) for _ in range(layers)]
         tm.run(lambda i: lays[i % layers].step(recs[(i // layers) % 16], y), warmup * layers)
         us = tm.run(lambda i: lays[i % layers].step(recs[(i // layers) % 16], y), steps * layers)
         rd, wr = split_window_mean(lm, cf, rf)
@@ -220,6 +230,30 @@ def bench_split(torch, seed=5, layers=8, steps=64, warmup=32):
                                                           "frac_of_peak": (rd + wr) / us / 1e3 / HBM_PEAK_GBS}
         del lays
         torch.cuda.empty_cache()
+    return out
+
+
+def bench_bf16_records(torch, steps, warmup):
+    """bf16 records (REPLAY_FLAG_BF16_RECORDS) against float32 records, same run:
+    the replay and conventional steps of the Mamba-2 and GDN batch-256 layers,
+    and the split-precision GDN layer at batch 64."""
+    from hybrid_model_ssm_replay_amd.binding import FLAG_BF16_RECORDS as F
+    from hybrid_model_ssm_replay_amd.traffic import Layer, conventional_step_bytes, replay_window_mean
+    from synth import WORKLOADS
+    out = {}
+    for name, seed in (("mamba2_b256_h128_p64_n128_g8_l16", 1), ("gdn_b256_h32_d128_l16", 2)):
+        shape = WORKLOADS[name]
+        r32 = bench_replay(torch, shape, seed, steps, warmup)
+        r16 = bench_replay(torch, shape, seed, steps, warmup, flags=F)
+        c16 = bench_conv(torch, shape, seed, steps, warmup, flags=F)
+        lm = Layer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.groups, shape.window, 2)
+        rb = sum(replay_window_mean(lm))
+        out[name] = {"replay_f32_records_us": r32, "replay_bf16_records_us": r16, "speedup_vs_f32_records": r32 / r16,
+                     "replay_bf16_model_bytes": rb, "replay_bf16_gbs": rb / r16 / 1e3,
+                     "conventional_bf16_records_us": c16, "speedup_vs_conventional": c16 / r16,
+                     "conventional_bf16_gbs": sum(conventional_step_bytes(lm)) / c16 / 1e3}
+        torch.cuda.empty_cache()
+    out["gdn_split_b64"] = bench_split(torch, flags=F, pairs=((0, 3), (2, 3), (3, 3)))["pairs"]
     return out
 
 
@@ -370,6 +404,8 @@ def main(argv=None):
         extra["gdn_split_b64"] = bench_split(torch)
         log("read copy error")
         extra["gdn_split_b64"]["read_copy_error"] = bench_read_copy_error(torch)
+        log("bf16 records")
+        extra["bf16_records"] = bench_bf16_records(torch, args.steps, args.warmup)
         log("batch and window sweeps")
         extra["mamba2_sweeps"] = bench_sweeps(torch)
 

@@ -18,6 +18,9 @@ pseudo-value u (d_v), alpha, beta):
   per record): written by every step, read back by the fold, which re-solves
   the pseudo-values from the checkpoint.
 Conventional step: read state + record_in, write state + y.
+With bf16 records (vec_bytes = 2) the record vector fields (Mamba-2 x, B, C;
+GDN q, k, v) count 2 bytes in the inputs and in the ring; scalars, GDN
+pseudo-values, outputs and the state stay 4.
 Replay verify of T drafts after c committed records: read state + c ring_rec +
 T record_in, write T ring_rec + T y (+ fold-first: L' ring_rec read, state written).
 Snapshot verify: read state + T record_in, write T states + T y.
@@ -52,6 +55,7 @@ class Layer:
     state_dim: int
     groups: int
     window: int
+    vec_bytes: int = 4  # bytes per record vector element (4 float32, 2 bf16)
 
     @property
     def state(self) -> int:
@@ -59,17 +63,17 @@ class Layer:
 
     @property
     def record_in(self) -> int:
-        H, P, N, G = self.heads, self.head_dim, self.state_dim, self.groups
+        H, P, N, G, V = self.heads, self.head_dim, self.state_dim, self.groups, self.vec_bytes
         if self.kind == "mamba2":
-            return (H * P + 2 * G * N + H) * E
-        return H * (2 * N + P + 2) * E
+            return (H * P + 2 * G * N) * V + H * E
+        return H * (2 * N + P) * V + 2 * H * E
 
     @property
     def ring_rec(self) -> int:
-        H, P, N, G = self.heads, self.head_dim, self.state_dim, self.groups
+        H, P, N, G, V = self.heads, self.head_dim, self.state_dim, self.groups, self.vec_bytes
         if self.kind == "mamba2":
-            return (H * P + G * N + H) * E
-        return H * (N + P + 2) * E
+            return (H * P + G * N) * V + H * E
+        return H * N * V + H * P * E + 2 * H * E  # k, the pseudo-value u (float32), alpha, beta
 
     @property
     def y(self) -> int:
@@ -106,7 +110,7 @@ def split_window_mean(l: Layer, ckpt_fmt: int, read_fmt: int) -> tuple[float, fl
     read copy; a fold reads the checkpoint and writes both copies (Gated DeltaNet;
     a separate read copy adds the buffered values v)."""
     ck, rd = stored_state_bytes(l, ckpt_fmt), stored_state_bytes(l, read_fmt)
-    vrec = l.heads * l.head_dim * E if read_fmt != ckpt_fmt else 0
+    vrec = l.heads * l.head_dim * l.vec_bytes if read_fmt != ckpt_fmt else 0
     rd_sum = wr_sum = 0.0
     for m in range(1, l.window + 1):
         fold = m == 1
