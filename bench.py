@@ -314,6 +314,10 @@ def cpu_baseline(shape, seed, budget_s=12.0):
                       f"({el:.1f} s), scaled linearly to the full batch"}
 
 
+# Extras after the headline measurement, in run order.
+SECTIONS = ("conv", "skip", "verify", "gdn", "gdn_verify", "split", "read_error", "bf16", "sweeps")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,7 +325,14 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--no-extra", action="store_true", help="skip baselines and other layers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--sections", default="all",
+                    help="comma list of extras to run (default all): " + ",".join(SECTIONS))
     args = ap.parse_args(argv)
+    wanted = set(SECTIONS) if args.sections == "all" else set(args.sections.split(","))
+    if wanted - set(SECTIONS):
+        print(f"unknown sections {sorted(wanted - set(SECTIONS))}", file=sys.stderr)
+        return 2
+    want = (lambda sec: not args.no_extra and sec in wanted)  # noqa: E731
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the replay decode path has no cross-GPU step "
               "(sequences and heads shard with no exchange); --gpus above 1 is not measured.", file=sys.stderr)
@@ -350,18 +361,21 @@ def main(argv=None):
     log("hbm probe")
     rgbs, cgbs = bench_probe(torch)
     extra.update({"hbm_probe_read_gbs": rgbs, "hbm_probe_copy_gbs": cgbs})
-    if not args.no_extra:
+    if want("conv"):
         log("conventional step", name)
         us_c = bench_conv(torch, shape, 1, args.steps, args.warmup)
         crd, cwr = conventional_step_bytes(lay)
         extra.update({"conventional_step_us": us_c, "conventional_gbs": (crd + cwr) / us_c / 1e3,
                       "speedup_vs_conventional": us_c / us})
+    if want("skip"):
         from hybrid_model_ssm_replay_amd.binding import FLAG_DECAY_SKIP
         log("replay step with the decay skip", name)
         us_s = bench_replay(torch, shape, 1, args.steps, args.warmup, flags=FLAG_DECAY_SKIP)
         extra["decay_skip"] = {"replay_step_us": us_s, "speedup_vs_exact_replay": us / us_s,
-                               "speedup_vs_conventional": us_c / us_s,
                                "rule": "checkpoint term dropped where exp(A s) < 2^-24 (an approximation)"}
+        if "conventional_step_us" in extra:
+            extra["decay_skip"]["speedup_vs_conventional"] = extra["conventional_step_us"] / us_s
+    if want("verify"):
         vshape = WORKLOADS["mamba2_b512_h128_p64_n128_g8_l16"]
         for T in (4, 8):
             log("verify T", T)
@@ -374,7 +388,7 @@ def main(argv=None):
             v["replay_over_standard_step"] = v["replay_verify_commit_us"] / us_std
             v["snapshot_over_standard_step"] = v["snapshot_verify_commit_us"] / us_std
 
-    if not args.no_extra:
+    if want("gdn"):
         gname = "gdn_b256_h32_d128_l16"
         gshape = WORKLOADS[gname]
         log("gdn replay step", gname)
@@ -392,26 +406,29 @@ def main(argv=None):
                              "tokens_per_s": gshape.batch / us_g * 1e6,
                              "traffic_bytes_per_launch": stored_traffic("gdn_replay_step_b256_traffic.txt", "gdn")}
 
-        for T in (4, 8):
+        for T in (4, 8) if want("gdn_verify") else ():
             log("gdn verify T", T)
             us_rv, us_sv = bench_verify(torch, gshape, T, 2)
             extra["gdn_b256"][f"verify_T{T}"] = {"replay_verify_commit_us": us_rv, "snapshot_verify_commit_us": us_sv,
                                                  "replay_over_conventional_step": us_rv / us_gc,
                                                  "snapshot_over_conventional_step": us_sv / us_gc}
 
-    if not args.no_extra:
+    if want("split"):
         log("split precision")
         extra["gdn_split_b64"] = bench_split(torch)
+    if want("read_error"):
         log("read copy error")
-        extra["gdn_split_b64"]["read_copy_error"] = bench_read_copy_error(torch)
+        extra["read_copy_error_b64"] = bench_read_copy_error(torch)
+    if want("bf16"):
         log("bf16 records")
         extra["bf16_records"] = bench_bf16_records(torch, args.steps, args.warmup)
+    if want("sweeps"):
         log("batch and window sweeps")
         extra["mamba2_sweeps"] = bench_sweeps(torch)
 
     traffic = stored_traffic("m2_replay_step_b256_traffic.txt", "m2")
     roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-            "traffic": traffic, "kernel": "m2_replay_step<8, 2, false>",
+            "traffic": traffic, "kernel": "m2_replay_step<8, 2, false, float>",
             "bytes_per_launch": rd + wr}
     cpu = None if args.no_cpu else cpu_baseline(shape, 1)
     out = {
