@@ -14,7 +14,8 @@ import pytest
 from _gpu import announce, ckpt_rel_err, host, pointers_host, to_dev
 from _metrics import max_rel_err
 from oracle.pointers import PointerMachine
-from oracle.session import FMT_F32, FMT_F4E2M1_B16, FMT_F8E4M3, SplitReplaySession, StepwiseSession
+from oracle.session import (FMT_F32, FMT_F4E2M1_B16, FMT_F4E2M1_CS, FMT_F8E4M3, SplitReplaySession,
+                            StepwiseSession)
 from synth import WORKLOADS, InputStream, LayerShape, take_batch
 
 pytestmark = pytest.mark.gpu
@@ -121,7 +122,8 @@ def test_baselines(kind):
         assert ckpt_rel_err(host(snap.state()), ref2.state) <= TOL
 
 
-@pytest.mark.parametrize("cf,rf", [(FMT_F32, FMT_F4E2M1_B16), (FMT_F8E4M3, FMT_F4E2M1_B16)])
+@pytest.mark.parametrize("cf,rf", [(FMT_F32, FMT_F4E2M1_B16), (FMT_F8E4M3, FMT_F4E2M1_B16), (FMT_F32, FMT_F4E2M1_CS),
+                                   (FMT_F4E2M1_B16, FMT_F4E2M1_B16)])
 def test_gdn_split_precision(cf, rf):
     """Split-precision GDN with bf16 records (the buffered v is bf16 too):
     outputs within 1e-4 before the first fold and within one e2m1 step
