@@ -14,6 +14,7 @@ FMT_F32, FMT_F16_SR, FMT_F8E4M3, FMT_F4E2M1_B16, FMT_F4E2M1_CS = 0, 1, 2, 3, 4
 STATUS_ACCEPT_CLAMPED, STATUS_BAD_POINTERS = 0x1, 0x2
 FLAG_DECAY_SKIP = 0x1
 FLAG_BF16_RECORDS = 0x2
+FLAG_RECORDS_IN_RING = 0x4
 OK, EINVAL, EHIP, ENOTSUP = 0, -1, -2, -3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +49,10 @@ class replay_record(ctypes.Structure):
                 ("f3", ctypes.c_void_p), ("f4", ctypes.c_void_p)]
 
 
+class replay_ring_view(ctypes.Structure):
+    _fields_ = [("f", ctypes.c_void_p * 5), ("slots", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class replay_ctx(ctypes.Structure):
     _fields_ = [("cfg", replay_config), ("buf", replay_buffers), ("parity", ctypes.c_int32),
                 ("t_pending", ctypes.c_int32), ("magic", ctypes.c_uint32), ("reserved", ctypes.c_int32)]
@@ -74,6 +79,8 @@ _SIG = {
     "replay_commit": (ctypes.c_int, [ctypes.POINTER(replay_ctx), _P, _P]),
     "replay_current_pointers": (ctypes.c_int, [ctypes.POINTER(replay_ctx), ctypes.POINTER(ctypes.c_void_p),
                                                ctypes.POINTER(ctypes.c_void_p)]),
+    "replay_ring_fields": (ctypes.c_int, [ctypes.POINTER(replay_ctx), ctypes.POINTER(replay_ring_view)]),
+    "replay_record_slots": (ctypes.c_int, [ctypes.POINTER(replay_ctx), _P, _P]),
     "replay_conv_step": (ctypes.c_int, [ctypes.POINTER(replay_config), _P, _P, _P, ctypes.POINTER(replay_record),
                                         _P, _P]),
     "replay_snapshot_verify": (ctypes.c_int, [ctypes.POINTER(replay_config), _P, _P, ctypes.c_int32, _P, _P,
@@ -186,6 +193,16 @@ def replay_current_pointers(ctx) -> tuple[int, int]:
     _check("replay_current_pointers",
            load_library().replay_current_pointers(ctypes.byref(ctx), ctypes.byref(pos), ctypes.byref(ck)))
     return pos.value, ck.value
+
+
+def replay_ring_fields(ctx) -> replay_ring_view:
+    view = replay_ring_view()
+    _check("replay_ring_fields", load_library().replay_ring_fields(ctypes.byref(ctx), ctypes.byref(view)))
+    return view
+
+
+def replay_record_slots(ctx, slots: int, stream: int) -> None:
+    _check("replay_record_slots", load_library().replay_record_slots(ctypes.byref(ctx), slots, stream))
 
 
 def replay_conv_step(cfg, state: int, A: int, D: int, rec: replay_record, y: int, stream: int) -> None:

@@ -656,8 +656,8 @@ __device__ __forceinline__ GdnRingPtrs<R> gdn_ring_ptrs(const GdnRing &r, const 
   p.rk = static_cast<R *>(r.k) + bh * sh.N;
   p.ru = r.u + bh * sh.P;
   p.rv = r.v ? static_cast<R *>(r.v) + bh * sh.P : nullptr;
-  p.ral = r.alpha + bh * sh.L;
-  p.rbe = r.beta + bh * sh.L;
+  p.ral = r.alpha + bh * sh.Ls;
+  p.rbe = r.beta + bh * sh.Ls;
   return p;
 }
 
@@ -697,20 +697,20 @@ __device__ __forceinline__ void load_ring_rows(float (&vr)[16], int cnt, const E
 // and the values v (a full-window solve through sm), and the read copy's
 // rounding never enters the recurrence.
 template <int CF, int RF, int NCH, int RBW, typename R>
-__device__ __forceinline__ void gdn_fold(float4 (&s)[RBW][NCH], int cnt, int s0, const GdnRingPtrs<R> &rp, int L,
+__device__ __forceinline__ void gdn_fold(float4 (&s)[RBW][NCH], int cnt, int s0, const GdnRingPtrs<R> &rp, int Ls,
                                          int rb0, int lane, GdnLds<RBW> *sm) {
   constexpr int CM = col_map(CF, RF);
   const int q = lane >> 4, r16 = lane & 15;
   const int j = r16 < cnt ? r16 : cnt - 1;
-  const float al = rp.ral[wrap(s0, j, L)];
+  const float al = rp.ral[wrap(s0, j, Ls)];
   float ub[RBW][4];
   float escale;
   if constexpr (CF != RF) {
     float4 X[NCH];
     float vr[16];
-    load_keys<NCH, CM, R>(X, cnt, rp, s0, L, lane);
-    load_ring_rows(vr, cnt, rp.rv, rp.vs, s0, L, rb0 * 16 + (lane < 16 * RBW ? lane : 0));
-    const float be = rp.rbe[wrap(s0, j, L)];
+    load_keys<NCH, CM, R>(X, cnt, rp, s0, Ls, lane);
+    load_ring_rows(vr, cnt, rp.rv, rp.vs, s0, Ls, rb0 * 16 + (lane < 16 * RBW ? lane : 0));
+    const float be = rp.rbe[wrap(s0, j, Ls)];
     gdn_window<NCH, RBW>(s, X, cnt, 0, al, be, vr, *sm, lane);
     escale = __expf(sm->g[cnt - 1]);
 #pragma unroll
@@ -727,12 +727,12 @@ __device__ __forceinline__ void gdn_fold(float4 (&s)[RBW][NCH], int cnt, int s0,
     for (int st = 0; st < 4; ++st) {
       const int r = 4 * st + q;
       const float w = __shfl(us, r, kWave);
-      const float *ur = rp.ru + (size_t)wrap(s0, r < cnt ? r : cnt - 1, L) * rp.vs;
+      const float *ur = rp.ru + (size_t)wrap(s0, r < cnt ? r : cnt - 1, Ls) * rp.vs;
 #pragma unroll
       for (int k = 0; k < RBW; ++k) ub[k][st] = w * ur[(rb0 + k) * 16 + r16];
     }
   }
-  fold_rank<NCH, RBW, CM, R>(s, cnt, s0, rp.rk, rp.ks, L, escale, ub, lane);
+  fold_rank<NCH, RBW, CM, R>(s, cnt, s0, rp.rk, rp.ks, Ls, escale, ub, lane);
 }
 
 // ---- replay step ------------------------------------------------------------
@@ -782,11 +782,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   const Shape &sh = a.s;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int b = fdiv(tile, sh.fH), h = tile - b * sh.H;
-  const int DV = sh.P, L = sh.L, rb0 = wave * RBW;
+  const int DV = sh.P, L = sh.L, Ls = sh.Ls, rb0 = wave * RBW;
+  const bool zc = a.in_ring;  // this token's k, alpha, beta are already in their ring slots
   const size_t bh = (size_t)b * sh.H + h;
   const size_t head = bh * DV * DK;
   const GdnRingPtrs<R> rp = gdn_ring_ptrs<R>(a.ring, sh, b, h);
-  const R *qin = static_cast<const R *>(a.q) + bh * DK, *kin = static_cast<const R *>(a.k) + bh * DK;
+  const R *qin = static_cast<const R *>(a.q) + bh * DK;
+  const R *kin = zc ? nullptr : static_cast<const R *>(a.k) + bh * DK;
   const R *vin = static_cast<const R *>(a.v) + bh * DV;
   const int orow = (rb0 + (q < RBW ? q : 0)) * 16 + r16;  // this lane's output row (q < RBW)
 
@@ -794,10 +796,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   typename SIO<RF, NCH, RBW, CM>::Raw raw;
   SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
   float km[NCH], qm[NCH];  // columns NCH r16 .. of k_m and q_m
-  load_cols<NCH, R>(km, kin + NCH * r16);
+  if (!zc) load_cols<NCH, R>(km, kin + NCH * r16);
   load_cols<NCH, R>(qm, qin + NCH * r16);
-  const float al_row = rp.ral[r16 < L ? r16 : 0];
-  const float al_in = a.alpha[bh], be_in = a.beta[bh];
+  const float al_row = rp.ral[lane < Ls ? lane : 0];  // the head's alpha ring, slot = lane
+  float al_in = zc ? 0.f : a.alpha[bh], be_in = zc ? 0.f : a.beta[bh];
   const float v_in = ldr<R>(vin + orow);
 
   // 2. Pointers.
@@ -812,8 +814,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     return;
   }
   const bool fold = count == L;
-  const int s0 = fmod_(ck, sh.fL);
-  const int slot = wrap(s0, count, L);  // this token's slot
+  const int s0 = fmod_(ck, sh.fLs);
+  const int slot = wrap(s0, count, Ls);  // this token's slot
+  if (zc) {
+    kin = rp.rk + (size_t)slot * rp.ks;
+    load_cols<NCH, R>(km, kin + NCH * r16);
+    al_in = __shfl(al_row, slot, kWave);
+    be_in = rp.rbe[slot];
+  }
   int base = ck, sb0 = s0;
   float4 s[RBW][NCH];
   float kj[NCH];         // this thread's slice of key grp (an older record)
@@ -821,13 +829,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   if (fold) {
     if constexpr (RF == CF) {
       SIO<RF, NCH, RBW, CM>::decode(s, raw);
-      gdn_fold<CF, RF, NCH, RBW, R>(s, L, s0, rp, L, rb0, lane, nullptr);
+      gdn_fold<CF, RF, NCH, RBW, R>(s, L, s0, rp, Ls, rb0, lane, nullptr);
     } else {
       __shared__ GdnLds<RBW> lds_all[4];
       typename SIO<CF, NCH, RBW, CM>::Raw rc;
       SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
       SIO<CF, NCH, RBW, CM>::decode(s, rc);
-      gdn_fold<CF, RF, NCH, RBW, R>(s, L, s0, rp, L, rb0, lane, &lds_all[wave]);
+      gdn_fold<CF, RF, NCH, RBW, R>(s, L, s0, rp, Ls, rb0, lane, &lds_all[wave]);
     }
     store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
@@ -839,11 +847,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   } else {
     // The count older records, then the read copy (after the ring loads in program order).
     const int j = grp < count ? grp : 0;
-    load_cols<NCH, R>(kj, rp.rk + (size_t)wrap(s0, j, L) * rp.ks + NCH * r16);
+    load_cols<NCH, R>(kj, rp.rk + (size_t)wrap(s0, j, Ls) * rp.ks + NCH * r16);
 #pragma unroll
     for (int t = 0; t < kMaxOld; ++t) {
       const int tc = t < count ? t : 0;
-      const float v = rp.ru[(size_t)wrap(s0, tc, L) * rp.vs + orow];
+      const float v = rp.ru[(size_t)wrap(s0, tc, Ls) * rp.vs + orow];
       uo[t] = t < count ? v : 0.f;
     }
     SIO<RF, NCH, RBW, CM>::decode(s, raw);
@@ -885,7 +893,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   float al;
   {
     const int j = r16 < nold ? r16 : 0;
-    const float a1 = __shfl(al_row, wrap(sb0, j, L), kWave);
+    const float a1 = __shfl(al_row, wrap(sb0, j, Ls), kWave);
     al = r16 < nold ? a1 : (r16 == nold ? al_in : 1.f);
   }
   const float g = prefix_sum16(lane < 16 ? __logf(al) : 0.f, lane);
@@ -928,10 +936,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     rp.ru[(size_t)slot * rp.vs + orow] = um;
     if constexpr (RF != CF) str<R>(rp.rv + (size_t)slot * rp.vs + orow, v_in);
   }
-  for (int i = threadIdx.x; i < DK; i += 64 * nwaves) rp.rk[(size_t)slot * rp.ks + i] = kin[i];
+  if (!zc)
+    for (int i = threadIdx.x; i < DK; i += 64 * nwaves) rp.rk[(size_t)slot * rp.ks + i] = kin[i];
   if (threadIdx.x == 0) {
-    rp.ral[slot] = al_in;
-    rp.rbe[slot] = be_in;
+    if (!zc) {
+      rp.ral[slot] = al_in;
+      rp.rbe[slot] = be_in;
+    }
     if (h == 0) {
       a.ptr.pos_out[b] = pos + 1;
       a.ptr.ckpt_out[b] = base;
@@ -969,7 +980,7 @@ __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a, GdnStateBufs sb
     SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
     SIO<CF, NCH, RBW, CM>::decode(s, rc);
   }
-  gdn_fold<CF, RF, NCH, RBW, R>(s, count, fmod_(ck, sh.fL), rp, L, rb0, lane, &lds_all[RF != CF ? wave : 0]);
+  gdn_fold<CF, RF, NCH, RBW, R>(s, count, fmod_(ck, sh.fLs), rp, sh.Ls, rb0, lane, &lds_all[RF != CF ? wave : 0]);
   store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
 }
 
@@ -1024,14 +1035,16 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
   const int T = a.T;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int b = fdiv(tile, sh.fH), h = tile - b * sh.H;
-  const int DV = sh.P, L = sh.L, rb0 = wave * RBW, H = sh.H;
+  const int DV = sh.P, L = sh.L, Ls = sh.Ls, rb0 = wave * RBW, H = sh.H;
+  const bool zc = a.in_ring;  // the drafts' k, alpha, beta are already in their ring slots
   const size_t bh = (size_t)b * H + h;
   const size_t head = bh * DV * DK;
   const GdnRingPtrs<R> rp = gdn_ring_ptrs<R>(a.ring, sh, b, h);
   const int row = rb0 * 16 + (lane < 16 * RBW ? lane : 0);  // this lane's row in the solve
   const R *gq_ = static_cast<const R *>(a.q), *gk_ = static_cast<const R *>(a.k), *gv_ = static_cast<const R *>(a.v);
+  int sp = 0;  // slot of position pos: draft i lives in slot (pos + i) mod Ls
   auto dq_ = [&](int i) { return gq_ + (((size_t)b * T + i) * H + h) * DK; };
-  auto dk_ = [&](int i) { return gk_ + (((size_t)b * T + i) * H + h) * DK; };
+  auto dk_ = [&](int i) { return zc ? rp.rk + (size_t)wrap(sp, i, Ls) * rp.ks : gk_ + (((size_t)b * T + i) * H + h) * DK; };
   auto dv_ = [&](int i) { return gv_ + (((size_t)b * T + i) * H + h) * DV; };
   auto dsc = [&](const float *f, int i) { return f[((size_t)b * T + i) * H + h]; };
   const int npass = (T + 3) >> 2;
@@ -1043,6 +1056,7 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
   typename SIO<RF, NCH, RBW, CM>::Raw raw;
   SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
+  sp = fmod_(pos, sh.fLs);
   {
     const int nload = (npass * 2 * NCH * 16) >> 6;
     for (int j = wave; j < nload; j += nwaves) {
@@ -1070,7 +1084,7 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
     return;
   }
   const bool fold = count + T > L;  // implies count >= 1 because T <= L
-  const int s0 = fmod_(ck, sh.fL);
+  const int s0 = fmod_(ck, sh.fLs);
   int base = ck, sb0 = s0;
   float4 s[RBW][NCH];
   if (fold) {
@@ -1081,10 +1095,10 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
       SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
       SIO<CF, NCH, RBW, CM>::decode(s, rc);
     }
-    gdn_fold<CF, RF, NCH, RBW, R>(s, count, s0, rp, L, rb0, lane, &lds_all[wave].fold);
+    gdn_fold<CF, RF, NCH, RBW, R>(s, count, s0, rp, Ls, rb0, lane, &lds_all[wave].fold);
     store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
-    sb0 = wrap(s0, count, L);
+    sb0 = wrap(s0, count, Ls);
   }
   const int c = pos - base, nrec = c + T;
 
@@ -1093,21 +1107,21 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
   //    committed pseudo-values, and alpha, beta of record r16.
   {
     const int j = r16 < nrec ? r16 : nrec - 1;
-    const R *kj = j < c ? rp.rk + (size_t)wrap(sb0, j, L) * rp.ks : dk_(j - c);
+    const R *kj = j < c ? rp.rk + (size_t)wrap(sb0, j, Ls) * rp.ks : dk_(j - c);
     for (int cc = wave; cc < NCH; cc += nwaves) stage4<R>(kj + colq<NCH, CM>(cc, q), &ldsK[cc][0], lane);
   }
   float uc[kMaxL - 1];
 #pragma unroll
   for (int j = 0; j < kMaxL - 1; ++j) {
     const int jc = j < c ? j : 0;
-    const float v = rp.ru[(size_t)wrap(sb0, jc, L) * rp.vs + row];
+    const float v = rp.ru[(size_t)wrap(sb0, jc, Ls) * rp.vs + row];
     uc[j] = j < c ? v : 0.f;
   }
   float al, be;
   {
     const int j = r16 < nrec ? r16 : nrec - 1;
-    const float a1 = j < c ? rp.ral[wrap(sb0, j, L)] : dsc(a.alpha, j - c);
-    const float b1 = j < c ? rp.rbe[wrap(sb0, j, L)] : dsc(a.beta, j - c);
+    const float a1 = (j < c || zc) ? rp.ral[wrap(sb0, j, Ls)] : dsc(a.alpha, j - c);
+    const float b1 = (j < c || zc) ? rp.rbe[wrap(sb0, j, Ls)] : dsc(a.beta, j - c);
     al = r16 < nrec ? a1 : 1.f;
     be = r16 < nrec ? b1 : 0.f;
   }
@@ -1210,19 +1224,20 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
 #pragma unroll
         for (int j = 0; j <= t; ++j) o += sv.Bq[d][j] * u[j];
         a.y[(((size_t)b * T + d) * H + h) * DV + row] = o;
-        rp.ru[(size_t)wrap(sb0, t, L) * rp.vs + row] = v;  // stage the pseudo-value
-        if constexpr (RF != CF) str<R>(rp.rv + (size_t)wrap(sb0, t, L) * rp.vs + row, vrow[d]);
+        rp.ru[(size_t)wrap(sb0, t, Ls) * rp.vs + row] = v;  // stage the pseudo-value
+        if constexpr (RF != CF) str<R>(rp.rv + (size_t)wrap(sb0, t, Ls) * rp.vs + row, vrow[d]);
       }
     }
   }
-  // 6. Stage the drafts' keys and scalars.  The workgroup barrier above already
-  //    ordered every wave's reads of the folded slots before these writes.
-  for (int i = 0; i < T; ++i) {
-    const int sl = wrap(sb0, c + i, L);
+  // 6. Stage the drafts' keys and scalars (unless the producer put them in the
+  //    ring).  The workgroup barrier above already ordered every wave's reads
+  //    of the folded slots before these writes.
+  for (int i = 0; i < (zc ? 0 : T); ++i) {
+    const int sl = wrap(sb0, c + i, Ls);
     for (int e = threadIdx.x; e < DK; e += 64 * nwaves) rp.rk[(size_t)sl * rp.ks + e] = dk_(i)[e];
   }
-  if (threadIdx.x < T) {
-    const int sl = wrap(sb0, c + threadIdx.x, L);
+  if (!zc && threadIdx.x < T) {
+    const int sl = wrap(sb0, c + threadIdx.x, Ls);
     rp.ral[sl] = dsc(a.alpha, threadIdx.x);
     rp.rbe[sl] = dsc(a.beta, threadIdx.x);
   }

@@ -12,7 +12,8 @@ constexpr uint32_t kCtxMagic = 0x52535331u;  // "RSS1"
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Ring layout.  Fields are float32, except the record vector fields (Mamba-2
+// Ring layout (Ls = L, or 2L with REPLAY_FLAG_RECORDS_IN_RING, for every field
+// below written [L] or [B][H][L]).  Fields are float32, except the record vector fields (Mamba-2
 // x and B, GDN k and v), which are bf16 with REPLAY_FLAG_BF16_RECORDS; each is
 // indexed by ring slot; the record at
 // token position t lives in slot t % L, except the Mamba-2 B field, which is
@@ -37,22 +38,26 @@ struct RingLayout {
 inline bool gdn_refold(const replay_config &c) { return c.ckpt_fmt != c.read_fmt; }
 
 inline bool bf16_records(const replay_config &c) { return (c.flags & REPLAY_FLAG_BF16_RECORDS) != 0; }
+inline bool records_in_ring(const replay_config &c) { return (c.flags & REPLAY_FLAG_RECORDS_IN_RING) != 0; }
+// Slots of the ring fields indexed by position mod Ls (all but the Mamba-2 B field).
+inline int ring_slots(const replay_config &c) { return records_in_ring(c) ? 2 * c.window : c.window; }
 
 inline RingLayout ring_layout(const replay_config &c) {
   RingLayout r{};
   const size_t re = bf16_records(c) ? 2 : 4;  // bytes per record vector element
+  const size_t Ls = ring_slots(c);
   const size_t B = c.batch, H = c.heads, G = c.groups, L = c.window, P = c.head_dim, N = c.state_dim;
   size_t sz[5] = {0, 0, 0, 0, 0};  // bytes
   if (c.kind == REPLAY_KIND_MAMBA2) {
-    sz[0] = B * H * L * P * re;
+    sz[0] = B * H * Ls * P * re;
     sz[1] = B * G * 2 * L * N * re;
-    sz[2] = B * H * L * 4;
+    sz[2] = B * H * Ls * 4;
   } else {
-    sz[0] = B * H * L * N * re;
-    sz[1] = B * H * L * P * 4;
-    sz[2] = B * H * L * 4;
-    sz[3] = B * H * L * 4;
-    sz[4] = gdn_refold(c) ? B * H * L * P * re : 0;
+    sz[0] = B * H * Ls * N * re;
+    sz[1] = B * H * Ls * P * 4;
+    sz[2] = B * H * Ls * 4;
+    sz[3] = B * H * Ls * 4;
+    sz[4] = gdn_refold(c) ? B * H * Ls * P * re : 0;
   }
   size_t o = 0;
   for (int i = 0; i < 5; ++i) {
@@ -65,14 +70,17 @@ inline RingLayout ring_layout(const replay_config &c) {
 
 // Shape of one launch, as the kernels see it, with the launch-invariant
 // divisors the kernels need (heads, heads per group, L, 2 L).
+// Ls is the slot count of the slot-indexed ring fields other than the Mamba-2
+// B field (which always has 2L): L, or 2L when the caller writes the records
+// into the ring (REPLAY_FLAG_RECORDS_IN_RING).
 struct Shape {
-  int B, H, G, P, N, L;
-  FastDiv fH, fHpg, fL, f2L;
+  int B, H, G, P, N, L, Ls;
+  FastDiv fH, fHpg, fL, f2L, fLs;
 };
 
-inline Shape make_shape(int B, int H, int G, int P, int N, int L) {
-  return Shape{B, H, G, P, N, L, make_fastdiv((uint32_t)H), make_fastdiv((uint32_t)(H / G)),
-               make_fastdiv((uint32_t)L), make_fastdiv((uint32_t)(2 * L))};
+inline Shape make_shape(int B, int H, int G, int P, int N, int L, int Ls) {
+  return Shape{B, H, G, P, N, L, Ls, make_fastdiv((uint32_t)H), make_fastdiv((uint32_t)(H / G)),
+               make_fastdiv((uint32_t)L), make_fastdiv((uint32_t)(2 * L)), make_fastdiv((uint32_t)Ls)};
 }
 
 // Mamba-2 ---------------------------------------------------------------
@@ -96,6 +104,7 @@ struct M2StepArgs {
   const void *x, *Bm, *Cm;  // this token: [B][H][P], [B][G][N], [B][G][N]
   const float *dt;           // [B][H]
   int bf16;
+  int in_ring;               // x, B, dt are already in their ring slots (x, Bm, dt unused)
   float *y;                  // [B][H][P]
 };
 
@@ -111,6 +120,7 @@ struct M2VerifyArgs {
   const void *x, *Bm, *Cm;  // drafts: [B][T][H][P], [B][T][G][N], [B][T][G][N]
   const float *dt;           // [B][T][H]
   int bf16;
+  int in_ring;               // the drafts' x, B, dt are already in their ring slots
   float *y;                  // [B][T][H][P]
 };
 
@@ -165,6 +175,7 @@ struct GdnStepArgs {
   const void *q, *k, *v;        // this token: [B][H][dk], [B][H][dk], [B][H][dv]
   const float *alpha, *beta;    // [B][H]
   int bf16;
+  int in_ring;                  // k, alpha, beta are already in their ring slots
   float *y;                     // [B][H][dv]
 };
 
@@ -177,6 +188,7 @@ struct GdnVerifyArgs {
   const void *q, *k, *v;  // drafts: [B][T][H][...]
   const float *alpha, *beta;
   int bf16;
+  int in_ring;            // the drafts' k, alpha, beta are already in their ring slots
   float *y;               // [B][T][H][dv]
 };
 
@@ -251,6 +263,7 @@ int launch_gdn_flush(const GdnFlushArgs &a, const GdnFormatBufs &f, hipStream_t 
 int launch_gdn_encode(const GdnEncodeArgs &a, const GdnFormatBufs &f, hipStream_t st);
 int launch_gdn_conv(const GdnConvArgs &a, hipStream_t st);
 int launch_gdn_snapshot(const GdnSnapArgs &a, hipStream_t st);
+int launch_record_slots(const int32_t *pos, int batch, int slots, int32_t *out, hipStream_t st);
 int launch_m2_step(const M2StepArgs &a, hipStream_t st);
 int launch_m2_verify(const M2VerifyArgs &a, hipStream_t st);
 int launch_m2_flush(const M2FlushArgs &a, hipStream_t st);

@@ -105,7 +105,7 @@ __device__ __forceinline__ float suffix_sum16(float v, int lane, float *total) {
 template <int NCH, int RBW, bool SKIP, typename R>
 __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm, int cnt, int base,
                                           float Ah, const R *rx, const float *rdt, const R *rB,
-                                          int L, size_t xs, const TileCtx &t) {
+                                          int L, int Ls, size_t xs, const TileCtx &t) {
   constexpr int N = 16 * NCH;
   // Stage B_r (cnt x N) in LDS; zero the rows up to the next multiple of 4.
   const int rows4 = (cnt + 3) & ~3;
@@ -116,7 +116,7 @@ __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm
     *reinterpret_cast<float4 *>(&sm.Bs[r][n]) = v;
   }
   // Decay weights, per wave, record r in lane r.
-  const float dtv = t.lane < cnt ? rdt[(base + t.lane) % L] : 0.f;
+  const float dtv = t.lane < cnt ? rdt[(base + t.lane) % Ls] : 0.f;
   float total;
   const float seg = suffix_sum16(dtv, t.lane, &total);
   const float f = __expf(Ah * seg) * dtv;
@@ -131,7 +131,7 @@ __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm
     for (int st = 0; st < 4; ++st) {
       const int r = 4 * st + t.q;
       const float fr = __shfl(f, r, kWave);
-      xb[st] = (r < cnt) ? fr * ldr<R>(rx + (size_t)((base + r) % L) * xs + row) : 0.f;
+      xb[st] = (r < cnt) ? fr * ldr<R>(rx + (size_t)((base + r) % Ls) * xs + row) : 0.f;
     }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -173,10 +173,12 @@ struct FoldIn {
 
 template <int NCH, int RBW, typename R>
 __device__ __forceinline__ void fold_load(FoldIn<NCH, RBW> &fi, int cnt, int s0, int s0b, const R *rx,
-                                          const float *rdt, const R *rB, int L, size_t xs, int rb0, int lane) {
-  // s0 = (position of record 0) mod L, s0b = the same mod 2 L; xs = x-ring slot stride.
+                                          const float *rdt, const R *rB, int L, int Ls, size_t xs, int rb0,
+                                          int lane) {
+  // s0 = (position of record 0) mod Ls (x and dt slots), s0b = the same mod 2 L (B slots);
+  // xs = x-ring slot stride.
   const int q = lane >> 4, r16 = lane & 15;
-  const float dtl = rdt[wrap(s0, r16 < cnt ? r16 : cnt - 1, L)];
+  const float dtl = rdt[wrap(s0, r16 < cnt ? r16 : cnt - 1, Ls)];
   fi.f = lane < cnt ? dtl : 0.f;  // dt for now; fold_apply turns it into the weight
   fi.nsteps = (cnt + 3) >> 2;
 #pragma unroll
@@ -189,7 +191,7 @@ __device__ __forceinline__ void fold_load(FoldIn<NCH, RBW> &fi, int cnt, int s0,
       const float v = ldr<R>(Br + 16 * c + r16);
       fi.aB[c][st] = r < cnt ? v : 0.f;
     }
-    const R *xr = rx + wrap(s0, rc, L) * xs;
+    const R *xr = rx + wrap(s0, rc, Ls) * xs;
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
       const float v = ldr<R>(xr + (rb0 + k) * 16 + r16);
@@ -292,15 +294,16 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int b = fdiv(tile, sh.fH), h = tile - b * sh.H;
   const int g = fdiv(h, sh.fHpg);
-  const int P = sh.P, L = sh.L;
+  const int P = sh.P, L = sh.L, Ls = sh.Ls;
   const int rb0 = wave * RBW;
+  const bool zc = a.in_ring;  // this token's x, B, dt are already in their ring slots
   float *S = a.ckpt + ((size_t)b * sh.H + h) * P * N;
   const size_t xs = (size_t)sh.B * sh.H * P;  // x-ring slot stride (slot-major ring)
   R *rx = static_cast<R *>(a.ring.x) + ((size_t)b * sh.H + h) * P;
-  float *rdt = a.ring.dt + ((size_t)b * sh.H + h) * L;
+  float *rdt = a.ring.dt + ((size_t)b * sh.H + h) * Ls;
   R *rB = static_cast<R *>(a.ring.Bm) + ((size_t)b * sh.G + g) * 2 * L * N;
-  const R *xin = static_cast<const R *>(a.x) + ((size_t)b * sh.H + h) * P;
-  const R *Bin = static_cast<const R *>(a.Bm) + ((size_t)b * sh.G + g) * N;
+  const R *xin = zc ? nullptr : static_cast<const R *>(a.x) + ((size_t)b * sh.H + h) * P;
+  const R *Bin = zc ? nullptr : static_cast<const R *>(a.Bm) + ((size_t)b * sh.G + g) * N;
   const R *Cin = static_cast<const R *>(a.Cm) + ((size_t)b * sh.G + g) * N;
 
   // 1. Everything whose address needs no pointer, checkpoint first: its loads
@@ -313,8 +316,8 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   float4 cv[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) cv[c] = ldr4<R>(Cin + 16 * c + 4 * q);
-  const float dtrow = rdt[r16 < L ? r16 : 0];  // the head's whole dt ring, slot = r16
-  const float dt_in = a.dt[(size_t)b * sh.H + h];
+  const float dtrow = rdt[lane < Ls ? lane : 0];  // the head's whole dt ring, slot = lane
+  float dt_in = zc ? 0.f : a.dt[(size_t)b * sh.H + h];
   const float Ah = a.A[h], Dh = a.D[h];
 
   // 2. Pointers.
@@ -329,14 +332,19 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
     return;
   }
   const bool fold = count == L;
-  const int s0 = fmod_(ck, sh.fL), s0b = fmod_(ck, sh.f2L);  // slots of window record 0
-  const int slot = wrap(s0, count, L), slotb = wrap(s0b, count, 2 * L);  // slots of this token
+  const int s0 = fmod_(ck, sh.fLs), s0b = fmod_(ck, sh.f2L);  // slots of window record 0
+  const int slot = wrap(s0, count, Ls), slotb = wrap(s0b, count, 2 * L);  // slots of this token
+  if (zc) {
+    xin = rx + (size_t)slot * xs;
+    Bin = rB + (size_t)slotb * N;
+    dt_in = __shfl(dtrow, slot, kWave);
+  }
   if constexpr (SKIP) {
     // The checkpoint term this call uses: the fold's (L records) or this
     // token's output (count + 1 records).  Read the checkpoint only if it stays.
     const int n = fold ? L : count + 1;
     const int j = r16 < n ? r16 : 0;
-    const float d = __shfl(dtrow, wrap(s0, j < count ? j : 0, L), kWave);
+    const float d = __shfl(dtrow, wrap(s0, j < count ? j : 0, Ls), kWave);
     const float tot = sum16(r16 < n ? ((!fold && r16 == count) ? dt_in : d) : 0.f);
     if (Ah * tot < kDecaySkipLog) {
 #pragma unroll
@@ -367,7 +375,7 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
     for (int st = 0; st < 4; ++st) {
       const int j = 4 * st + q;
       const int jc = j < m ? j : m - 1;
-      const R *xj = (jc == m - 1) ? xin : rx + wrap(s0, jc, L) * xs;
+      const R *xj = (jc == m - 1) ? xin : rx + wrap(s0, jc, Ls) * xs;
 #pragma unroll
       for (int k = 0; k < RBW; ++k) {
         const float v = ldr<R>(xj + (rb0 + k) * 16 + r16);
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
     {
       // dt of record `lane`, permuted out of the ring row loaded up front (after
       // the loads above in program order, so it does not hold them back).
-      const float d = __shfl(dtrow, wrap(s0, r16 < m - 1 ? r16 : 0, L), kWave);
+      const float d = __shfl(dtrow, wrap(s0, r16 < m - 1 ? r16 : 0, Ls), kWave);
       dtv = lane < m - 1 ? d : (lane == m - 1 ? dt_in : 0.f);
     }
 #pragma unroll
@@ -387,7 +395,7 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
     // Fold the full window into the checkpoint, store it, and start the next
     // window with this token as its only record.
     FoldIn<NCH, RBW> fi;
-    fold_load<NCH, RBW, R>(fi, L, s0, s0b, rx, rdt, rB, L, xs, rb0, lane);
+    fold_load<NCH, RBW, R>(fi, L, s0, s0b, rx, rdt, rB, L, Ls, xs, rb0, lane);
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
       const float v = ldr<R>(xin + (rb0 + k) * 16 + r16);
@@ -407,18 +415,21 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   const int m = pos - base + 1;
   const float out = replay_output<NCH, RBW, SKIP>(s, cv, bdot, dtv, xr, m, Ah, lane);
 
-  // 4. Append this token's record.  After a fold the dt slot being written
-  //    held a record that the other waves of a multi-wave head also read.
-  if (fold && nwaves > 1) __syncthreads();
+  // 4. Append this token's record (unless the producer wrote it into the ring).
+  //    After a fold the dt slot being written held a record that the other
+  //    waves of a multi-wave head also read.
+  if (fold && nwaves > 1 && !zc) __syncthreads();
   if (q < RBW) {
     const int row = (rb0 + q) * 16 + r16;
     const float xv = ldr<R>(xin + row);
     a.y[((size_t)b * sh.H + h) * P + row] = out + Dh * xv;
-    str<R>(rx + slot * xs + row, xv);
+    if (!zc) str<R>(rx + slot * xs + row, xv);
   }
-  if (threadIdx.x == 0) rdt[slot] = dt_in;
-  if (h - g * (sh.H / sh.G) == 0 && wave == 0)
-    for (int i = lane; i < N; i += kWave) rB[slotb * N + i] = Bin[i];
+  if (!zc) {
+    if (threadIdx.x == 0) rdt[slot] = dt_in;
+    if (h - g * (sh.H / sh.G) == 0 && wave == 0)
+      for (int i = lane; i < N; i += kWave) rB[slotb * N + i] = Bin[i];
+  }
   if (h == 0 && threadIdx.x == 0) {
     a.ptr.pos_out[b] = pos + 1;
     a.ptr.ckpt_out[b] = base;
@@ -449,12 +460,12 @@ __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
   float *S = a.ckpt + ((size_t)b * sh.H + h) * P * N;
   const size_t xs = (size_t)sh.B * sh.H * P;
   const R *rx = static_cast<const R *>(a.ring.x) + ((size_t)b * sh.H + h) * P;
-  const float *rdt = a.ring.dt + ((size_t)b * sh.H + h) * L;
+  const float *rdt = a.ring.dt + ((size_t)b * sh.H + h) * sh.Ls;
   const R *rB = static_cast<const R *>(a.ring.Bm) + ((size_t)b * sh.G + g) * 2 * L * N;
   float4 s[RBW][NCH];
   bool keep = true;  // the checkpoint term survives the decay skip
   if constexpr (SKIP) {
-    const float d = rdt[(ck + (t.r16 < count ? t.r16 : 0)) % L];
+    const float d = rdt[(ck + (t.r16 < count ? t.r16 : 0)) % sh.Ls];
     keep = !(a.A[h] * sum16(t.r16 < count ? d : 0.f) < kDecaySkipLog);
   }
   if (keep) {
@@ -465,7 +476,7 @@ __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) s[k][c] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  fold_tile<NCH, RBW, SKIP, R>(s, sm, count, ck, a.A[h], rx, rdt, rB, L, xs, t);
+  fold_tile<NCH, RBW, SKIP, R>(s, sm, count, ck, a.A[h], rx, rdt, rB, L, sh.Ls, xs, t);
   store_tile<NCH, RBW>(s, S, t);
 }
 
@@ -509,16 +520,19 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int b = fdiv(tile, sh.fH), h = tile - b * sh.H;
   const int g = fdiv(h, sh.fHpg);
-  const int P = sh.P, L = sh.L, H = sh.H, G = sh.G;
+  const int P = sh.P, L = sh.L, H = sh.H, G = sh.G, Ls = sh.Ls;
   const int rb0 = wave * RBW;
+  const bool zc = a.in_ring;  // the drafts' x, B, dt are already in their ring slots
   float *S = a.ckpt + ((size_t)b * H + h) * P * N;
   const size_t xs = (size_t)sh.B * H * P;
   R *rx = static_cast<R *>(a.ring.x) + ((size_t)b * H + h) * P;
-  float *rdt = a.ring.dt + ((size_t)b * H + h) * L;
+  float *rdt = a.ring.dt + ((size_t)b * H + h) * Ls;
   R *rB = static_cast<R *>(a.ring.Bm) + ((size_t)b * G + g) * 2 * L * N;
   const R *dx = static_cast<const R *>(a.x), *dB = static_cast<const R *>(a.Bm), *dC = static_cast<const R *>(a.Cm);
-  auto draft_x = [&](int i) { return dx + (((size_t)b * T + i) * H + h) * P; };
-  auto draft_B = [&](int i) { return dB + (((size_t)b * T + i) * G + g) * N; };
+  int sb = 0, sbb = 0, c = 0;  // window slots of record 0 (mod Ls, mod 2 L), committed records
+  // Draft i is window record c + i; with zc its x and B are in the ring.
+  auto draft_x = [&](int i) { return zc ? rx + (size_t)wrap(sb, c + i, Ls) * xs : dx + (((size_t)b * T + i) * H + h) * P; };
+  auto draft_B = [&](int i) { return zc ? rB + (size_t)wrap(sbb, c + i, 2 * L) * N : dB + (((size_t)b * T + i) * G + g) * N; };
   auto draft_C = [&](int i) { return dC + (((size_t)b * T + i) * G + g) * N; };
   const int npass = (T + 3) >> 2;
 
@@ -556,14 +570,15 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   int base = ck;
   if (fold) {
     FoldIn<NCH, RBW> fi;
-    fold_load<NCH, RBW, R>(fi, count, fmod_(ck, sh.fL), fmod_(ck, sh.f2L), rx, rdt, rB, L, xs, rb0, lane);
+    fold_load<NCH, RBW, R>(fi, count, fmod_(ck, sh.fLs), fmod_(ck, sh.f2L), rx, rdt, rB, L, Ls, xs, rb0, lane);
     fold_apply<NCH, RBW, SKIP>(s, fi, Ah, lane);
     store_rows<NCH, RBW>(s, S, rb0, lane);
     base = pos;
   }
-  const int c = pos - base;  // committed records in the window
-  const int nrec = c + T;    // <= L
-  const int sb = fmod_(base, sh.fL), sbb = fmod_(base, sh.f2L);
+  c = pos - base;          // committed records in the window
+  const int nrec = c + T;  // <= L
+  sb = fmod_(base, sh.fLs);
+  sbb = fmod_(base, sh.f2L);
 
   // 3. Window records.  B of record r16 at the tile columns into LDS (chunk cc
   //    by wave cc % nwaves); x of record 4 st + q at this lane's rows
@@ -578,7 +593,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   for (int st = 0; st < 4; ++st) {
     const int r = 4 * st + q;
     const int rc = r < nrec ? r : nrec - 1;
-    const R *xr = rc < c ? rx + (size_t)wrap(sb, rc, L) * xs : draft_x(rc - c);
+    const R *xr = rc < c ? rx + (size_t)wrap(sb, rc, Ls) * xs : draft_x(rc - c);
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
       const float v = ldr<R>(xr + (rb0 + k) * 16 + r16);
@@ -588,7 +603,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   float dtl;
   {
     const int rc = r16 < nrec ? r16 : nrec - 1;
-    const float v = rc < c ? rdt[wrap(sb, rc, L)] : a.dt[((size_t)b * T + (rc - c)) * H + h];
+    const float v = (rc < c || zc) ? rdt[wrap(sb, rc, Ls)] : a.dt[((size_t)b * T + (rc - c)) * H + h];
     dtl = r16 < nrec ? v : 0.f;
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's global-to-LDS loads have landed
@@ -671,18 +686,19 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
     }
   }
 
-  // 5. Stage the drafts (records c .. nrec-1) in the ring.  The workgroup
-  //    barrier above already ordered every wave's fold reads before this.
+  // 5. Stage the drafts (records c .. nrec-1) in the ring, unless the producer
+  //    put them there.  The workgroup barrier above already ordered every
+  //    wave's fold reads before this.
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     const int r = 4 * st + q;
-    if (r >= c && r < nrec) {
+    if (!zc && r >= c && r < nrec) {
 #pragma unroll
-      for (int k = 0; k < RBW; ++k) str<R>(rx + (size_t)wrap(sb, r, L) * xs + (rb0 + k) * 16 + r16, xa[k][st]);
+      for (int k = 0; k < RBW; ++k) str<R>(rx + (size_t)wrap(sb, r, Ls) * xs + (rb0 + k) * 16 + r16, xa[k][st]);
     }
   }
-  if (wave == 0) {
-    if (lane >= c && lane < nrec) rdt[wrap(sb, lane, L)] = dtl;
+  if (wave == 0 && !zc) {
+    if (lane >= c && lane < nrec) rdt[wrap(sb, lane, Ls)] = dtl;
     if (h - g * (H / G) == 0 && r16 >= c && r16 < nrec) {
 #pragma unroll
       for (int cc = 0; cc < NCH; ++cc) str4<R>(rB + (size_t)wrap(sbb, r16, 2 * L) * N + 16 * cc + 4 * q, ldsB[cc][lane]);

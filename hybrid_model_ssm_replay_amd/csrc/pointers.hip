@@ -22,6 +22,15 @@ __global__ void commit_k(PtrHalves p, int B, const int32_t *accepted, int T, int
   p.ckpt_out[b] = p.ckpt_in[b];
 }
 
+// Ring slot of each sequence's next record: pos mod the slot count.  A
+// negative pos (never produced by the library) maps to slot 0.
+__global__ void record_slots_k(const int32_t *pos, int B, int slots, int32_t *out) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int p = pos[b];
+  out[b] = p < 0 ? 0 : p % slots;
+}
+
 __global__ void snapshot_commit_k(int32_t *cur, const int32_t *accepted, int B, int T, int nslots) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
@@ -52,6 +61,11 @@ int launch_init_pointers(int32_t *words, int nwords, int32_t *status, hipStream_
 
 int launch_commit(PtrHalves p, int B, const int32_t *accepted, int T, int32_t *status, hipStream_t st) {
   hipLaunchKernelGGL(commit_k, dim3((B + 255) / 256), dim3(256), 0, st, p, B, accepted, T, status);
+  return (int)hipGetLastError();
+}
+
+int launch_record_slots(const int32_t *pos, int batch, int slots, int32_t *out, hipStream_t st) {
+  hipLaunchKernelGGL(record_slots_k, dim3((batch + 255) / 256), dim3(256), 0, st, pos, batch, slots, out);
   return (int)hipGetLastError();
 }
 

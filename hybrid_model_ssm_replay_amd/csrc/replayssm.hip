@@ -31,7 +31,8 @@ int check_cfg(const replay_config *c) {
     if (c->head_dim != 64 && c->head_dim != 128) return REPLAY_EINVAL;
     if (c->state_dim < 32) return REPLAY_EINVAL;
   }
-  if ((c->flags & ~(REPLAY_FLAG_DECAY_SKIP | REPLAY_FLAG_BF16_RECORDS)) || c->reserved) return REPLAY_EINVAL;
+  if ((c->flags & ~(REPLAY_FLAG_DECAY_SKIP | REPLAY_FLAG_BF16_RECORDS | REPLAY_FLAG_RECORDS_IN_RING)) || c->reserved)
+    return REPLAY_EINVAL;
   if ((c->flags & REPLAY_FLAG_DECAY_SKIP) && c->kind != REPLAY_KIND_MAMBA2) return REPLAY_ENOTSUP;
   if (c->ckpt_fmt < REPLAY_FMT_F32 || c->ckpt_fmt > REPLAY_FMT_F4E2M1_CS) return REPLAY_EINVAL;
   if (c->read_fmt < REPLAY_FMT_F32 || c->read_fmt > REPLAY_FMT_F4E2M1_CS) return REPLAY_EINVAL;
@@ -53,7 +54,7 @@ int check_ctx(const replay_ctx *ctx) {
 }
 
 Shape shape_of(const replay_config &c) {
-  return make_shape(c.batch, c.heads, c.groups, c.head_dim, c.state_dim, c.window);
+  return make_shape(c.batch, c.heads, c.groups, c.head_dim, c.state_dim, c.window, ring_slots(c));
 }
 
 PtrHalves halves(const replay_ctx &ctx) {
@@ -99,8 +100,15 @@ GdnFormatBufs gdn_formats(const replay_ctx &ctx) {
 
 int hip_status(int e) { return e == 0 ? REPLAY_OK : REPLAY_EHIP; }
 
-bool rec_ok(const replay_record *r, int kind) {
-  if (!r || !r->f0 || !r->f1 || !r->f2 || !r->f3) return false;
+// The fields a call reads from its record argument are present and aligned;
+// with the records in the ring only Mamba-2 C and GDN q, v are read.
+bool rec_ok(const replay_record *r, int kind, bool in_ring = false) {
+  if (!r) return false;
+  if (in_ring) {
+    if (kind == REPLAY_KIND_MAMBA2) return r->f2 && aligned16(r->f2);
+    return r->f0 && r->f2 && aligned16(r->f0) && aligned16(r->f2);
+  }
+  if (!r->f0 || !r->f1 || !r->f2 || !r->f3) return false;
   if (kind == REPLAY_KIND_GDN && !r->f4) return false;
   return aligned16(r->f0) && aligned16(r->f1) && aligned16(r->f2);
 }
@@ -147,6 +155,7 @@ size_t replay_abi_sizeof(int which) {
     case 1: return sizeof(replay_buffers);
     case 2: return sizeof(replay_record);
     case 3: return sizeof(replay_ctx);
+    case 4: return sizeof(replay_ring_view);
     default: return 0;
   }
 }
@@ -198,6 +207,30 @@ int replay_set_state(replay_ctx *ctx, const float *state, void *stream) {
   return hip_status(launch_gdn_encode(a, gdn_formats(*ctx), (hipStream_t)stream));
 }
 
+int replay_ring_fields(const replay_ctx *ctx, replay_ring_view *view) {
+  if (check_ctx(ctx) != REPLAY_OK || !view || !records_in_ring(ctx->cfg)) return REPLAY_EINVAL;
+  const RingLayout lay = ring_layout(ctx->cfg);
+  char *base = (char *)ctx->buf.ring;
+  *view = replay_ring_view{};
+  view->slots = ring_slots(ctx->cfg);
+  if (ctx->cfg.kind == REPLAY_KIND_MAMBA2) {
+    view->f[0] = base + lay.off[0];
+    view->f[1] = base + lay.off[1];
+    view->f[3] = base + lay.off[2];
+  } else {
+    view->f[1] = base + lay.off[0];
+    view->f[3] = base + lay.off[2];
+    view->f[4] = base + lay.off[3];
+  }
+  return REPLAY_OK;
+}
+
+int replay_record_slots(const replay_ctx *ctx, int32_t *slots, void *stream) {
+  if (check_ctx(ctx) != REPLAY_OK || !slots || !records_in_ring(ctx->cfg)) return REPLAY_EINVAL;
+  return hip_status(launch_record_slots(halves(*ctx).pos_in, ctx->cfg.batch, ring_slots(ctx->cfg), slots,
+                                        (hipStream_t)stream));
+}
+
 int replay_current_pointers(const replay_ctx *ctx, const int32_t **pos, const int32_t **ckpt_pos) {
   if (check_ctx(ctx) != REPLAY_OK || !pos || !ckpt_pos) return REPLAY_EINVAL;
   const PtrHalves p = halves(*ctx);
@@ -209,7 +242,7 @@ int replay_current_pointers(const replay_ctx *ctx, const int32_t **pos, const in
 int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *stream) {
   if (check_ctx(ctx) != REPLAY_OK) return REPLAY_EINVAL;
   const replay_config &c = ctx->cfg;
-  if (!rec_ok(rec, c.kind) || !y || !aligned16(y)) return REPLAY_EINVAL;
+  if (!rec_ok(rec, c.kind, records_in_ring(c)) || !y || !aligned16(y)) return REPLAY_EINVAL;
   int e;
   if (c.kind == REPLAY_KIND_MAMBA2) {
     M2StepArgs a{};
@@ -226,6 +259,7 @@ int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *strea
     a.Cm = rec->f2;
     a.dt = rec->f3;
     a.bf16 = bf16_records(c);
+    a.in_ring = records_in_ring(c) ? 1 : 0;
     a.y = y;
     e = launch_m2_step(a, (hipStream_t)stream);
   } else {
@@ -240,6 +274,7 @@ int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *strea
     a.alpha = rec->f3;
     a.beta = rec->f4;
     a.bf16 = bf16_records(c);
+    a.in_ring = records_in_ring(c) ? 1 : 0;
     a.y = y;
     e = launch_gdn_step(a, gdn_formats(*ctx), (hipStream_t)stream);
   }
@@ -284,7 +319,7 @@ int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float
   if (check_ctx(ctx) != REPLAY_OK) return REPLAY_EINVAL;
   const replay_config &c = ctx->cfg;
   if (T < 1 || T > c.max_draft || T > c.window) return REPLAY_EINVAL;
-  if (!rec_ok(drafts, c.kind) || !y || !aligned16(y)) return REPLAY_EINVAL;
+  if (!rec_ok(drafts, c.kind, records_in_ring(c)) || !y || !aligned16(y)) return REPLAY_EINVAL;
   int e;
   if (c.kind == REPLAY_KIND_MAMBA2) {
     M2VerifyArgs a{};
@@ -302,6 +337,7 @@ int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float
     a.Cm = drafts->f2;
     a.dt = drafts->f3;
     a.bf16 = bf16_records(c);
+    a.in_ring = records_in_ring(c) ? 1 : 0;
     a.y = y;
     e = launch_m2_verify(a, (hipStream_t)stream);
   } else {
@@ -317,6 +353,7 @@ int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float
     a.alpha = drafts->f3;
     a.beta = drafts->f4;
     a.bf16 = bf16_records(c);
+    a.in_ring = records_in_ring(c) ? 1 : 0;
     a.y = y;
     e = launch_gdn_verify(a, gdn_formats(*ctx), (hipStream_t)stream);
   }

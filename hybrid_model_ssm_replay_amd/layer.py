@@ -14,6 +14,8 @@ from . import binding as B
 
 _FIELDS = {B.KIND_MAMBA2: ("x", "B", "C", "dt"), B.KIND_GDN: ("q", "k", "v", "alpha", "beta")}
 _VECTOR_FIELDS = ("x", "B", "C", "q", "k", "v")  # bf16 with FLAG_BF16_RECORDS; the scalars stay float32
+# Fields the ring keeps, written by the producer with FLAG_RECORDS_IN_RING (record field index).
+RING_FIELDS = {B.KIND_MAMBA2: {"x": 0, "B": 1, "dt": 3}, B.KIND_GDN: {"k": 1, "alpha": 3, "beta": 4}}
 
 
 def _kind(kind) -> int:
@@ -41,6 +43,7 @@ class _Shapes:
         self.kind, self.batch, self.heads, self.groups = kind, batch, heads, groups
         self.head_dim, self.state_dim = head_dim, state_dim
         self.vec_dtype = torch.bfloat16 if flags & B.FLAG_BF16_RECORDS else torch.float32
+        self.in_ring = bool(flags & B.FLAG_RECORDS_IN_RING)
 
     def field_shapes(self, lead):
         H, G, P, N = self.heads, self.groups, self.head_dim, self.state_dim
@@ -49,11 +52,15 @@ class _Shapes:
         return {"q": lead + (H, N), "k": lead + (H, N), "v": lead + (H, P), "alpha": lead + (H,),
                 "beta": lead + (H,)}
 
-    def record(self, fields: dict, lead) -> tuple[B.replay_record, list]:
+    def record(self, fields: dict, lead, use_ring=False) -> tuple[B.replay_record, list]:
+        """The record struct of `fields`; with use_ring the fields the ring keeps
+        are not passed (the producer wrote them into their ring slots)."""
         shapes = self.field_shapes(lead)
-        keep = [_dev_f32(fields[n], shapes[n], n, self.vec_dtype if n in _VECTOR_FIELDS else torch.float32)
+        skip = RING_FIELDS[self.kind] if use_ring else {}
+        keep = [None if n in skip else
+                _dev_f32(fields[n], shapes[n], n, self.vec_dtype if n in _VECTOR_FIELDS else torch.float32)
                 for n in _FIELDS[self.kind]]
-        return B.make_record(*[t.data_ptr() for t in keep]), keep
+        return B.make_record(*[0 if t is None else t.data_ptr() for t in keep]), keep
 
 
 class ReplayLayer:
@@ -137,9 +144,39 @@ class ReplayLayer:
         s = self.shapes
         return torch.empty(lead + (s.heads, s.head_dim), dtype=torch.float32, device=self.ckpt.device)
 
+    def ring_fields(self) -> dict:
+        """Device views of the ring fields a producer writes (FLAG_RECORDS_IN_RING):
+        Mamba-2 x [slots][B][H][P], B [B][G][slots][N], dt [B][H][slots];
+        GDN k [slots][B][H][dk], alpha and beta [B][H][slots]."""
+        view = B.replay_ring_fields(self.ctx)
+        s, n = self.shapes, view.slots
+        base = self.ring.data_ptr()
+        vec_size = 2 if s.vec_dtype == torch.bfloat16 else 4
+
+        def at(addr, dtype, shape, esize):
+            off = addr - base
+            numel = 1
+            for d in shape:
+                numel *= d
+            return self.ring[off:off + numel * esize].view(dtype).view(shape)
+
+        if s.kind == B.KIND_MAMBA2:
+            return {"x": at(view.f[0], s.vec_dtype, (n, s.batch, s.heads, s.head_dim), vec_size),
+                    "B": at(view.f[1], s.vec_dtype, (s.batch, s.groups, n, s.state_dim), vec_size),
+                    "dt": at(view.f[3], torch.float32, (s.batch, s.heads, n), 4)}
+        return {"k": at(view.f[1], s.vec_dtype, (n, s.batch, s.heads, s.state_dim), vec_size),
+                "alpha": at(view.f[3], torch.float32, (s.batch, s.heads, n), 4),
+                "beta": at(view.f[4], torch.float32, (s.batch, s.heads, n), 4)}
+
+    def record_slots(self) -> torch.Tensor:
+        """Ring slot of each sequence's next record (int32 [batch], FLAG_RECORDS_IN_RING)."""
+        out = torch.empty(self.shapes.batch, dtype=torch.int32, device=self.ckpt.device)
+        B.replay_record_slots(self.ctx, out.data_ptr(), _stream())
+        return out
+
     def step(self, rec: dict, y: torch.Tensor | None = None) -> torch.Tensor:
         lead = (self.shapes.batch,)
-        r, keep = self.shapes.record(rec, lead)
+        r, keep = self.shapes.record(rec, lead, self.shapes.in_ring)
         y = self._out(lead) if y is None else _dev_f32(y, lead + (self.shapes.heads, self.shapes.head_dim), "y")
         B.replay_step(self.ctx, r, y.data_ptr(), _stream())
         return y
@@ -147,7 +184,7 @@ class ReplayLayer:
     def verify(self, drafts: dict, y: torch.Tensor | None = None) -> torch.Tensor:
         T = int(next(iter(drafts.values())).shape[1])
         lead = (self.shapes.batch, T)
-        r, keep = self.shapes.record(drafts, lead)
+        r, keep = self.shapes.record(drafts, lead, self.shapes.in_ring)
         y = self._out(lead) if y is None else _dev_f32(y, lead + (self.shapes.heads, self.shapes.head_dim), "y")
         B.replay_verify(self.ctx, T, r, y.data_ptr(), _stream())
         return y

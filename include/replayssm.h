@@ -59,6 +59,7 @@ extern "C" {
 /* Option flags (replay_config.flags). */
 #define REPLAY_FLAG_DECAY_SKIP 0x1u   /* Mamba-2: drop the checkpoint term of heads whose decay is below 2^-24 */
 #define REPLAY_FLAG_BF16_RECORDS 0x2u /* record vector fields (Mamba-2 x, B, C; GDN q, k, v) are bf16 */
+#define REPLAY_FLAG_RECORDS_IN_RING 0x4u /* the caller writes the stored record fields into the ring */
 
 /* Return codes. */
 #define REPLAY_OK 0
@@ -94,7 +95,8 @@ extern "C" {
  *               fold that sets ckpt_pos of sequence b draws element e of head h
  *               from word e % 4 of Philox(counter (e / 4, h, b, ckpt_pos),
  *               key (seed low 32 bits, seed high 32 bits)), top 24 bits).
- *   flags       an OR of REPLAY_FLAG_DECAY_SKIP and REPLAY_FLAG_BF16_RECORDS.
+ *   flags       an OR of REPLAY_FLAG_DECAY_SKIP, REPLAY_FLAG_BF16_RECORDS and
+ *               REPLAY_FLAG_RECORDS_IN_RING.
  *               REPLAY_FLAG_DECAY_SKIP (Mamba-2 only, else REPLAY_ENOTSUP):
  *               a head whose window decay exp(A s) (s = the dt summed over the
  *               window records a computation uses) is below 2^-24 drops the
@@ -109,6 +111,15 @@ extern "C" {
  *               count next to the state [P1, Synopsis]; values are widened
  *               exactly, so the arithmetic (float32) and the state, pseudo-
  *               values and outputs (float32) are unchanged.
+ *               REPLAY_FLAG_RECORDS_IN_RING (zero-copy append): the producer of
+ *               the records writes the fields the ring keeps (Mamba-2 x, B,
+ *               dt; GDN k, alpha, beta) straight into their ring slots before
+ *               each step or verify (replay_record_slots, replay_ring_view),
+ *               and those calls take only the other fields from their record
+ *               argument (Mamba-2 C; GDN q, v), so no call copies a record into
+ *               the ring.  The ring then has 2L slots per field: the slot of a
+ *               step's new record, or of T <= L drafts, is never one the
+ *               window still holds.
  *   reserved    must be 0.
  * Supported format pairs (ckpt_fmt, read_fmt): (F32, F32) for both families;
  * for Gated DeltaNet with state_dim = 128 also (F32 | F16_SR | F8E4M3, F4E2M1_B16)
@@ -192,6 +203,8 @@ typedef struct replay_buffers {
  *            f4 = beta [batch][heads].
  * For verify every field has a draft axis after batch: x [batch][T][heads][P] etc.
  */
+/* With REPLAY_FLAG_RECORDS_IN_RING the fields kept in the ring (Mamba-2 f0, f1,
+ * f3; GDN f1, f3, f4) are not read and may be NULL. */
 typedef struct replay_record {
   const void *f0;
   const void *f1;
@@ -223,7 +236,7 @@ size_t replay_pointer_words(const replay_config *cfg);
 /* Static text for a return code. */
 const char *replay_strerror(int code);
 /* sizeof of the ABI structs, for bindings: 0 replay_config, 1 replay_buffers,
- * 2 replay_record, 3 replay_ctx. */
+ * 2 replay_record, 3 replay_ctx, 4 replay_ring_view. */
 size_t replay_abi_sizeof(int which);
 
 /* ---- the decode calls -------------------------------------------------- */
@@ -270,6 +283,31 @@ int replay_commit(replay_ctx *ctx, const int32_t *accepted, void *stream);
 /* Device addresses of the current pos[batch] and ckpt_pos[batch] arrays (valid
  * until the next call that enqueues work on ctx). */
 int replay_current_pointers(const replay_ctx *ctx, const int32_t **pos, const int32_t **ckpt_pos);
+
+/* ---- zero-copy append (REPLAY_FLAG_RECORDS_IN_RING) ------------------------ */
+
+/* Where a producer writes the stored record fields (device addresses inside the
+ * ring buffer; f[i] matches record field fi, NULL for fields not kept):
+ *   Mamba-2: f[0] = x  [slots][batch][heads][P]   (slot-major),
+ *            f[1] = B  [batch][groups][slots][N],
+ *            f[3] = dt [batch][heads][slots]      (float32);
+ *   GDN:     f[1] = k  [slots][batch][heads][d_k] (slot-major),
+ *            f[3] = alpha, f[4] = beta [batch][heads][slots] (float32).
+ * slots = 2 window; vector fields are bf16 with REPLAY_FLAG_BF16_RECORDS.
+ * REPLAY_EINVAL unless the context was configured with RECORDS_IN_RING. */
+typedef struct replay_ring_view {
+  void *f[5];
+  int32_t slots;
+  int32_t reserved;
+} replay_ring_view;
+int replay_ring_fields(const replay_ctx *ctx, replay_ring_view *view);
+
+/* Enqueue slot[b] = pos[b] mod slots (device int32 [batch]): the ring slot of
+ * sequence b's next record; draft i of a verify goes to (slot[b] + i) mod slots.
+ * The slots stay valid until the next step, verify, commit or flush of ctx, so
+ * the producer writes between this call and the step or verify it feeds, on
+ * the same stream (or ordered after it).  REPLAY_EINVAL unless RECORDS_IN_RING. */
+int replay_record_slots(const replay_ctx *ctx, int32_t *slots, void *stream);
 
 /* ---- in-run baselines (for measurement, not part of the replay method) ---- */
 

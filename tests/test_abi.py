@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported_and_bound(B):
 def test_struct_sizes_match(B):
     import ctypes
     lib = B.load_library()
-    for i, st in enumerate((B.replay_config, B.replay_buffers, B.replay_record, B.replay_ctx)):
+    for i, st in enumerate((B.replay_config, B.replay_buffers, B.replay_record, B.replay_ctx, B.replay_ring_view)):
         assert lib.replay_abi_sizeof(i) == ctypes.sizeof(st)
 
 
@@ -78,8 +78,18 @@ def test_sizes_bf16_records(B):
     assert B.replay_ring_bytes(g) == k + u + 2 * sc + v
 
 
+def test_sizes_records_in_ring(B):
+    """The zero-copy ring has 2L slots per field (the Mamba-2 B field has 2L anyway)."""
+    cfg = B.make_config(0, 256, 128, 8, 64, 128, 16, 8, flags=B.FLAG_RECORDS_IN_RING)
+    assert B.replay_ring_bytes(cfg) == 256 * 128 * 32 * 64 * 4 + 256 * 8 * 32 * 128 * 4 + 256 * 128 * 32 * 4
+    g = B.make_config(1, 4, 2, 2, 64, 32, 8, 8, flags=B.FLAG_RECORDS_IN_RING)
+    k, u, sc = 4 * 2 * 16 * 32 * 4, 4 * 2 * 16 * 64 * 4, 4 * 2 * 16 * 4
+    a256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    assert B.replay_ring_bytes(g) == a256(k) + a256(u) + 2 * a256(sc)
+
+
 def test_unknown_flag_rejected(B):
-    assert B.replay_validate_config(B.make_config(0, 2, 4, 1, 16, 16, 4, flags=0x4)) == B.EINVAL
+    assert B.replay_validate_config(B.make_config(0, 2, 4, 1, 16, 16, 4, flags=0x8)) == B.EINVAL
 
 
 def test_calls_reject_uninitialised_context(B):
