@@ -257,6 +257,64 @@ def bench_bf16_records(torch, steps, warmup):
     return out
 
 
+def bench_zero_copy(torch, steps, warmup, rounds=3):
+    """Zero-copy append (REPLAY_FLAG_RECORDS_IN_RING) on the Mamba-2 and GDN
+    batch-256 layers, float32 and bf16 records: every ring slot is filled with
+    records before timing, and each timed step reads the record in its slot and
+    takes only the other fields as arguments (Mamba-2 C; GDN q, v).  The
+    producer's write of a record is its own output and is not in the timed
+    step.  The copying step is the comparison; the three layers are timed in
+    alternation, `rounds` times, and each reports its median."""
+    import statistics
+
+    from hybrid_model_ssm_replay_amd.binding import FLAG_BF16_RECORDS, FLAG_RECORDS_IN_RING
+    from hybrid_model_ssm_replay_amd.layer import ReplayLayer
+    from hybrid_model_ssm_replay_amd.traffic import Layer, replay_window_mean
+    from synth import WORKLOADS, InputStream
+    out = {}
+    for name, seed in (("mamba2_b256_h128_p64_n128_g8_l16", 1), ("gdn_b256_h32_d128_l16", 2)):
+        shape = WORKLOADS[name]
+        cases = {}
+        for label, flags, bf16 in (("copying", 0, False), ("f32_records", FLAG_RECORDS_IN_RING, False),
+                                   ("bf16_records", FLAG_RECORDS_IN_RING | FLAG_BF16_RECORDS, True)):
+            ins = InputStream(shape, seed, bf16_vectors=bf16)
+            recs = dev_records(torch, ins, 32, bf16)
+            kw = dict(A=ins.params["A"], D=ins.params["D"]) if shape.kind == "mamba2" else {}
+            lay = ReplayLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
+                              groups=shape.groups, flags=flags, **kw)
+            if flags:
+                f = lay.ring_fields()
+                first = "x" if "x" in f else "k"
+                for sl in range(f[first].shape[0]):  # every slot holds a record
+                    r = recs[sl % 32]
+                    f[first][sl] = r[first]
+                    for n in (("B", "dt") if first == "x" else ("alpha", "beta")):
+                        f[n][:, :, sl] = r[n]
+            cases[label] = (lay, recs, bf16, [])
+        y = torch.empty((shape.batch, shape.heads, shape.head_dim), device="cuda")
+        tm = Timer(torch)
+        for _ in range(rounds):
+            for label, (lay, recs, _, times) in cases.items():
+                tm.run(lambda i: lay.step(recs[i % 32], y), warmup)
+                times.append(tm.run(lambda i: lay.step(recs[(warmup + i) % 32], y), steps))
+        entry = {}
+        for label, (lay, _, bf16, times) in cases.items():
+            if lay.status != 0:
+                raise RuntimeError(f"device status {lay.status:#x}")
+            us = statistics.median(times)
+            lm = Layer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.groups,
+                       shape.window, 2 if bf16 else 4)
+            mb = sum(replay_window_mean(lm, in_ring=label != "copying"))
+            entry[label] = {"step_us": us, "model_bytes_per_step": mb, "gbs": mb / us / 1e3,
+                            "frac_of_peak": mb / us / 1e3 / HBM_PEAK_GBS}
+        for label in ("f32_records", "bf16_records"):
+            entry[label]["speedup_vs_copying_step"] = entry["copying"]["step_us"] / entry[label]["step_us"]
+        out[name] = entry
+        del cases
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_read_copy_error(torch, seed=6, steps=512, skip=64):
     """Output error of the e2m1 read copies (block scales only, and two-axis)
     against the float32 path of the same library, on the split-precision layer
@@ -315,7 +373,7 @@ def cpu_baseline(shape, seed, budget_s=12.0):
 
 
 # Extras after the headline measurement, in run order.
-SECTIONS = ("conv", "skip", "verify", "gdn", "gdn_verify", "split", "read_error", "bf16", "sweeps")
+SECTIONS = ("conv", "skip", "verify", "gdn", "gdn_verify", "split", "read_error", "bf16", "zero_copy", "sweeps")
 
 
 def main(argv=None):
@@ -422,6 +480,9 @@ def main(argv=None):
     if want("bf16"):
         log("bf16 records")
         extra["bf16_records"] = bench_bf16_records(torch, args.steps, args.warmup)
+    if want("zero_copy"):
+        log("zero-copy append")
+        extra["zero_copy"] = bench_zero_copy(torch, args.steps, args.warmup)
     if want("sweeps"):
         log("batch and window sweeps")
         extra["mamba2_sweeps"] = bench_sweeps(torch)

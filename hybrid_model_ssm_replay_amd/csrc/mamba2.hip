@@ -285,7 +285,9 @@ __device__ __forceinline__ float replay_output(const float4 (&s)[RBW][NCH], cons
   return pick<RBW>(acc, q);
 }
 
-template <int NCH, int RBW, bool SKIP, typename R>
+// ZC: the token's x, B, dt are already in their ring slots (zero-copy append); a
+// compile-time choice, because a run-time one costs the standard path 58 VGPRs.
+template <int NCH, int RBW, bool SKIP, typename R, bool ZC>
 __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   constexpr int N = 16 * NCH;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   const int g = fdiv(h, sh.fHpg);
   const int P = sh.P, L = sh.L, Ls = sh.Ls;
   const int rb0 = wave * RBW;
-  const bool zc = a.in_ring;  // this token's x, B, dt are already in their ring slots
+  constexpr bool zc = ZC;
   float *S = a.ckpt + ((size_t)b * sh.H + h) * P * N;
   const size_t xs = (size_t)sh.B * sh.H * P;  // x-ring slot stride (slot-major ring)
   R *rx = static_cast<R *>(a.ring.x) + ((size_t)b * sh.H + h) * P;
@@ -856,8 +858,6 @@ int dispatch(const Args &a, int N, int P, int B, int H, bool wave_per_head, hipS
       static constexpr auto fn = kern<NCH, RBW, SKIP_, R>; \
     };                                                   \
   };
-RSSM_WRAP_SKIP(StepK, m2_replay_step, false)
-RSSM_WRAP_SKIP(StepSkipK, m2_replay_step, true)
 RSSM_WRAP_SKIP(FlushK, m2_flush, false)
 RSSM_WRAP_SKIP(FlushSkipK, m2_flush, true)
 RSSM_WRAP_SKIP(VerifyK, m2_replay_verify, false)
@@ -866,6 +866,20 @@ RSSM_WRAP(ConvK, m2_conv_step)
 RSSM_WRAP(SnapK, m2_snapshot_verify)
 #undef RSSM_WRAP_SKIP
 #undef RSSM_WRAP
+
+template <bool SKIP, typename R, bool ZC>
+struct StepW {
+  template <int NCH, int RBW>
+  struct K {
+    static constexpr auto fn = m2_replay_step<NCH, RBW, SKIP, R, ZC>;
+  };
+};
+
+template <bool SKIP, bool ZC>
+int launch_step(const M2StepArgs &a, hipStream_t st) {
+  return a.bf16 ? dispatch<StepW<SKIP, bf16_t, ZC>::template K>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st)
+                : dispatch<StepW<SKIP, float, ZC>::template K>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
+}
 
 // Launch W<float>::K or W<bf16_t>::K by the record element type.
 template <template <typename> class W, typename Args>
@@ -877,7 +891,8 @@ int dispatch_rec(const Args &a, bool wave_per_head, hipStream_t st) {
 }  // namespace
 
 int launch_m2_step(const M2StepArgs &a, hipStream_t st) {
-  return a.decay_skip ? dispatch_rec<StepSkipK>(a, true, st) : dispatch_rec<StepK>(a, true, st);
+  if (a.decay_skip) return a.in_ring ? launch_step<true, true>(a, st) : launch_step<true, false>(a, st);
+  return a.in_ring ? launch_step<false, true>(a, st) : launch_step<false, false>(a, st);
 }
 int launch_m2_flush(const M2FlushArgs &a, hipStream_t st) {
   return a.decay_skip ? dispatch_rec<FlushSkipK>(a, false, st) : dispatch_rec<FlushK>(a, false, st);

@@ -18,6 +18,9 @@ pseudo-value u (d_v), alpha, beta):
   per record): written by every step, read back by the fold, which re-solves
   the pseudo-values from the checkpoint.
 Conventional step: read state + record_in, write state + y.
+With the records in the ring (zero-copy append) a step reads the same bytes but
+appends only what it computes itself (GDN: the pseudo-value u; Mamba-2: nothing);
+the producer's write of the record is the producer's output, not counted here.
 With bf16 records (vec_bytes = 2) the record vector fields (Mamba-2 x, B, C;
 GDN q, k, v) count 2 bytes in the inputs and in the ring; scalars, GDN
 pseudo-values, outputs and the state stay 4.
@@ -79,18 +82,24 @@ class Layer:
     def y(self) -> int:
         return self.heads * self.head_dim * E
 
+    def appended(self, in_ring: bool = False) -> int:
+        """Bytes a step writes into the ring."""
+        if not in_ring:
+            return self.ring_rec
+        return 0 if self.kind == "mamba2" else self.heads * self.head_dim * E
 
-def replay_step_bytes(l: Layer, m: int, fold: bool) -> tuple[int, int]:
+
+def replay_step_bytes(l: Layer, m: int, fold: bool, in_ring: bool = False) -> tuple[int, int]:
     """(read, write) bytes of one step for the whole batch; m = window records after the append."""
     rd = l.state + (m - 1) * l.ring_rec + l.record_in
-    wr = l.ring_rec + l.y
+    wr = l.appended(in_ring) + l.y
     if fold:
         rd += l.window * l.ring_rec
         wr += l.state
     return rd * l.batch, wr * l.batch
 
 
-def replay_window_mean(l: Layer) -> tuple[float, float]:
+def replay_window_mean(l: Layer, in_ring: bool = False) -> tuple[float, float]:
     """Mean (read, write) bytes per step over a steady-state window of L steps.
 
     In steady state the step that finds the window full folds it and then
@@ -98,7 +107,7 @@ def replay_window_mean(l: Layer) -> tuple[float, float]:
     """
     rd = wr = 0
     for m in range(1, l.window + 1):
-        r, w = replay_step_bytes(l, m, fold=(m == 1))
+        r, w = replay_step_bytes(l, m, fold=(m == 1), in_ring=in_ring)
         rd += r
         wr += w
     return rd / l.window, wr / l.window
