@@ -237,3 +237,39 @@ def test_error_curves_over_32768_steps():
     assert split[-1] <= 1.5 * split[0]                  # the read copy's error does not grow with length
     assert f16[-1] <= 1.2 * split[-1]                   # FP16-SR recurrence tracks the FP32 one
     assert shared[-1] >= split[-1]
+
+
+@pytest.mark.parametrize("cf,rf", [(FMT_F32, FMT_F4E2M1_B16), (FMT_F8E4M3, FMT_F4E2M1_B16),
+                                   (FMT_F4E2M1_B16, FMT_F4E2M1_B16), (FMT_F32, FMT_F4E2M1_CS)])
+def test_full_size_sampled(cf, rf):
+    """The benchmarked split-precision layer (Gated DeltaNet, 32 heads, d = 128,
+    L = 16, batch 64) in the bench's launch configuration: 24 steps from a zero
+    state (one fold) and a T = 4 verify, checked on 4 sampled sequences against
+    SplitReplaySession on those sequences (these pairs draw no random bits, so the
+    sample's encodings equal the full batch's).  Bars as above: 1e-4 before the
+    first fold (the read copy is the exact zero state), the format step after it."""
+    import torch
+    from synth import WORKLOADS, take_batch
+    shape = WORKLOADS["gdn_b64_h32_d128_l16"]
+    announce("split full size", shape, cf, rf)
+    ins = InputStream(shape, 61)
+    lay = _layer(shape, cf, rf, None, max_draft=4)
+    sample = np.array([0, 21, 42, 63])
+    idx = torch.from_numpy(sample).cuda()
+    sess = SplitReplaySession("gdn", np.zeros((len(sample), shape.heads, shape.head_dim, shape.state_dim)),
+                              shape.window, None, cf, rf, seed=SEED)
+    worst_pre = worst_post = 0.0
+    for t in range(24):
+        r = ins.record()
+        y = lay.step(to_dev(r))
+        e = max_rel_err(host(y[idx]), sess.step(take_batch(r, sample)))
+        if t < shape.window:
+            worst_pre = max(worst_pre, e)
+        else:
+            worst_post = max(worst_post, e)
+    d = ins.drafts(4)
+    y = lay.verify(to_dev(d))
+    worst_post = max(worst_post, max_rel_err(host(y[idx]), sess.verify(take_batch(d, sample))))
+    print(f"[split full] cf={cf} rf={rf} pre-fold {worst_pre:.2e} post-fold {worst_post:.2e}")
+    assert worst_pre <= 1e-4, worst_pre
+    assert worst_post <= POST_FOLD_TOL[rf], worst_post
