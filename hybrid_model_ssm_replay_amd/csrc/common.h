@@ -30,24 +30,6 @@ __device__ __forceinline__ floatx4 mfma_16x16x4(float a, float b, floatx4 c) {
 __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 __device__ __forceinline__ void st4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
 
-// Streaming loads of data touched exactly once per launch (the checkpoint):
-// non-temporal, so they do not evict the ring records and parameters that the
-// other tiles of the same sequence re-read.
-__device__ __forceinline__ float4 ld4_stream(const float *p) {
-  float4 v;
-  v.x = __builtin_nontemporal_load(p + 0);
-  v.y = __builtin_nontemporal_load(p + 1);
-  v.z = __builtin_nontemporal_load(p + 2);
-  v.w = __builtin_nontemporal_load(p + 3);
-  return v;
-}
-__device__ __forceinline__ void st4_stream(float *p, float4 v) {
-  __builtin_nontemporal_store(v.x, p + 0);
-  __builtin_nontemporal_store(v.y, p + 1);
-  __builtin_nontemporal_store(v.z, p + 2);
-  __builtin_nontemporal_store(v.w, p + 3);
-}
-
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
