@@ -36,6 +36,11 @@
 //   * W goes through per-wave LDS so that each lane owns one row and runs the
 //     m x m forward substitution for it with no cross-lane traffic,
 //   * the fold's MFMA output layout equals the register layout of S0.
+// Kernels are templated on the stored formats (CF, RF), the tile shape and R,
+// the element type of the record vector fields and their ring copies (float,
+// or bf16_t with bf16 records).  With zero-copy append (a.in_ring) the caller
+// writes k, alpha, beta into their ring slots (2L slots per field) and the
+// kernels read them there instead of copying them.
 #include "codecs.h"
 #include "internal.h"
 
@@ -1000,7 +1005,8 @@ __device__ __forceinline__ floatx4 mfma_4x4x1(float a, float b, floatx4 c) {
 // S0 q_d) or records 4 g + 0..3 (k_j . k_d, k_j . q_d) over the columns of
 // quarter q, and a sum over the quarters completes them, so absent drafts
 // cost no MFMA work.  The drafts' keys and queries and the window's keys
-// reach LDS by direct global-to-LDS loads in the lane-linear operand layout.
+// reach LDS by direct global-to-LDS loads in the lane-linear operand layout
+// (bf16 records: a load, exact widening and LDS store in the same layout).
 // The draft rows of the triangular system are then solved per state row (one
 // lane per row) with the committed rows known.  The drafts' keys, pseudo-
 // values and scalars are staged in the ring, so that a commit is only a

@@ -11,6 +11,12 @@
 //     S^T = e^{...} S0^T + B^T X~^T (M = state column, N = row, K = record),
 // so the fold result never leaves registers before it is stored.
 //
+// Kernel template parameters besides the tile shape: R, the element type of the
+// record vector fields and their ring copies (float, or bf16_t with bf16
+// records), SKIP (the decay skip below) and, for the step, ZC (zero-copy
+// append: the caller wrote this token's x, B, dt into their ring slots, and the
+// ring fields have 2L slots).
+//
 // Replay identities (derived from the Mamba-2 decode recurrence
 // S <- exp(dt A) S + dt x B^T, y = S C + D x by unrolling the window; the
 // method keeps a checkpoint plus the recent inputs [P1, Synopsis; P2,
@@ -146,12 +152,13 @@ __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm
   __syncthreads();
 }
 
-// ---- replay step (one wave per head) -----------------------------------------
-// The whole head's checkpoint lives in one wave's registers (RBW row blocks of
-// 16 rows; a second wave takes the other half when P = 128).  Every load that
-// does not depend on the pointers is issued first, so the checkpoint stream is
-// in flight while the pointers, then the ring records, arrive.  No LDS and no
-// workgroup barrier on the non-fold path.
+// ---- replay step ---------------------------------------------------------------
+// The head's checkpoint lives in registers: each wave holds RBW row blocks of
+// 16 rows, and a head takes P / (16 RBW) waves (two at P = 64).  Every load
+// that does not depend on the pointers is issued first, so the checkpoint
+// stream is in flight while the pointers, then the ring records, arrive.  No
+// LDS and no workgroup barrier on the non-fold path (a barrier there costs
+// more than any LDS sharing it would allow).
 //
 // Lane (r16, q) roles:  checkpoint rows 16 rb + r16, columns 16 c + 4 q + 0..3;
 // for the B_j . C dots lane r16 stands for window record j = r16 and sums over
@@ -500,7 +507,8 @@ __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
 // The drafts' C and the records' B reach LDS by direct global-to-LDS loads
 // (global_load_lds_dwordx4: lane l of a load writes 16 bytes at base + 16 l),
 // laid out so that every read is linear in the lane (no bank conflicts) and
-// no VGPR holds them while the checkpoint stream is in flight.  Loads that
+// no VGPR holds them while the checkpoint stream is in flight (bf16 records:
+// a load, exact widening and LDS store in the same layout).  Loads that
 // need no pointer (checkpoint, drafts' C and x) are issued first; the drafts
 // are staged in the ring from registers and LDS; no state is written except
 // by a fold-first when c + T > L.
