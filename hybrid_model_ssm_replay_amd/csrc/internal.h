@@ -12,15 +12,15 @@ constexpr uint32_t kCtxMagic = 0x52535331u;  // "RSS1"
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Ring layout (Ls = L, or 2L with REPLAY_FLAG_RECORDS_IN_RING, for every field
-// below written [L] or [B][H][L]).  Fields are float32, except the record vector fields (Mamba-2
-// x and B, GDN k and v), which are bf16 with REPLAY_FLAG_BF16_RECORDS; each is
-// indexed by ring slot; the record at
-// token position t lives in slot t % L, except the Mamba-2 B field, which is
-// shared by the heads of a group and lives in slot t % (2 L): a tile that
-// appends a record may then never overwrite a B record that another tile of
-// the same group is still folding or reading in the same launch (the window
-// plus the drafts of one call span at most 2 L positions).
+// Ring layout.  Every field is indexed by ring slot: the record at token
+// position t lives in slot t % Ls, with Ls = L, or 2L when the caller writes
+// the records into the ring (REPLAY_FLAG_RECORDS_IN_RING); the L below stands
+// for Ls.  The exception is the Mamba-2 B field, shared by the heads of a
+// group, which always has 2L slots: a tile that appends a record may then never
+// overwrite a B record that another tile of the same group is still folding or
+// reading in the same launch (the window plus the drafts of one call span at
+// most 2L positions).  Fields are float32, except the record vector fields
+// (Mamba-2 x and B, GDN k and v), which are bf16 with REPLAY_FLAG_BF16_RECORDS.
 struct RingLayout {
   // Mamba-2: f0 = x [L][B][H][P] (slot-major: one step's appends form one
   //          contiguous block), f1 = B [B][G][2L][N], f2 = dt [B][H][L].
