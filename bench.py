@@ -105,6 +105,40 @@ def bench_replay(torch, shape, seed, steps, warmup, pool=32, flags=0):
     return us
 
 
+def step_distribution(torch, shape, seed, windows=8, pool=32):
+    """Per-step times of the replay step (an event pair around every step) over
+    `windows` whole windows after one warm-up window: p50 and p99 over all
+    steps, and the mean of the fold steps (window position 0) and of the others."""
+    import statistics
+
+    from hybrid_model_ssm_replay_amd.layer import ReplayLayer
+    from synth import InputStream
+    L = shape.window
+    ins = InputStream(shape, seed)
+    recs = dev_records(torch, ins, pool)
+    kw = dict(A=ins.params["A"], D=ins.params["D"]) if shape.kind == "mamba2" else {}
+    lay = ReplayLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, L,
+                      groups=shape.groups, **kw)
+    y = torch.empty((shape.batch, shape.heads, shape.head_dim), device="cuda")
+    for i in range(L):
+        lay.step(recs[i % pool], y)
+    n = windows * L
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n):
+        lay.step(recs[(L + i) % pool], y)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    d = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)]
+    sorted_d = sorted(d)
+    fold = [x for i, x in enumerate(d) if i % L == 0]   # the first step of each window folds the previous one
+    rest = [x for i, x in enumerate(d) if i % L != 0]
+    return {"p50_us": statistics.median(d), "p99_us": sorted_d[min(n - 1, int(0.99 * n))],
+            "fold_step_mean_us": statistics.mean(fold), "non_fold_step_mean_us": statistics.mean(rest),
+            "steps": n}
+
+
 def bench_conv(torch, shape, seed, steps, warmup, pool=32, flags=0):
     from hybrid_model_ssm_replay_amd.layer import ConvLayer
     from synth import InputStream
@@ -416,6 +450,8 @@ def main(argv=None):
     gbs = (rd + wr) / us / 1e3
     extra = {"replay_step_us": us, "replay_model_bytes_per_step": rd + wr, "replay_gbs": gbs,
              "tokens_per_s": shape.batch / us * 1e6}
+    log("per-step distribution", name)
+    extra["replay_step_distribution"] = step_distribution(torch, shape, 1)
     log("hbm probe")
     rgbs, cgbs = bench_probe(torch)
     extra.update({"hbm_probe_read_gbs": rgbs, "hbm_probe_copy_gbs": cgbs})
@@ -440,11 +476,14 @@ def main(argv=None):
             us_rv, us_sv = bench_verify(torch, vshape, T, 3)
             extra[f"verify_b512_T{T}"] = {"replay_verify_commit_us": us_rv, "snapshot_verify_commit_us": us_sv}
         us_std = bench_conv(torch, vshape, 3, 32, 8)
+        us_rep = bench_replay(torch, vshape, 3, 32, 16)
         extra["conventional_step_b512_us"] = us_std
+        extra["replay_step_b512_us"] = us_rep
         for T in (4, 8):
             v = extra[f"verify_b512_T{T}"]
             v["replay_over_standard_step"] = v["replay_verify_commit_us"] / us_std
             v["snapshot_over_standard_step"] = v["snapshot_verify_commit_us"] / us_std
+            v["replay_over_replay_step"] = v["replay_verify_commit_us"] / us_rep
 
     if want("gdn"):
         gname = "gdn_b256_h32_d128_l16"
