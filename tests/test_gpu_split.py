@@ -273,3 +273,39 @@ def test_full_size_sampled(cf, rf):
     print(f"[split full] cf={cf} rf={rf} pre-fold {worst_pre:.2e} post-fold {worst_post:.2e}")
     assert worst_pre <= 1e-4, worst_pre
     assert worst_post <= POST_FOLD_TOL[rf], worst_post
+
+
+@pytest.mark.parametrize("cf,rf", PAIRS)
+def test_explicit_flush_matches_oracle(cf, rf):
+    """replay_flush with a sequence mask for every format pair: the masked
+    sequences fold their committed records (re-solving from the checkpoint with
+    a separate read copy) and re-encode both copies; outputs and stored bytes
+    against SplitReplaySession with the same flushes, bars as above (the first
+    flush is the first fold)."""
+    import torch
+    shape = LayerShape("gdn", 3, 3, 128, 128, 3, 6)
+    announce("split flush", shape, cf, rf)
+    ins = InputStream(shape, 12)
+    S0 = ins.initial_state(zeros=False, scale=0.3)
+    lay = _layer(shape, cf, rf, S0, max_draft=2)
+    sess = SplitReplaySession("gdn", S0, shape.window, None, cf, rf, seed=SEED)
+    worst_pre, worst_post, folded = 0.0, 0.0, False
+    masks = {3: [1, 0, 1], 7: [0, 1, 1], 8: [1, 1, 1], 12: [0, 0, 1]}
+    for t in range(15):
+        if t in masks:
+            m = np.array(masks[t], np.uint8)
+            lay.flush(torch.from_numpy(m).cuda())
+            sess.flush(m.astype(bool))
+            folded = True
+            continue
+        r = ins.record()
+        e = max_rel_err(host(lay.step(to_dev(r))), sess.step(r))
+        if folded:
+            worst_post = max(worst_post, e)
+        else:
+            worst_pre = max(worst_pre, e)
+    flips = _check_copies(lay, sess, shape, cf, rf, exact=False)
+    print(f"[split flush] cf={cf} rf={rf} pre {worst_pre:.2e} post {worst_post:.2e} flipped bytes {flips:.2e}")
+    assert worst_pre <= 1e-4, worst_pre
+    assert flips <= 1e-3, flips
+    assert worst_post <= POST_FOLD_TOL[rf], worst_post
