@@ -179,3 +179,39 @@ def test_mamba2_full_size_sampled():
     y = lay.verify(to_dev(d, bf16=True))
     worst = max(worst, max_rel_err(host(y[idx]), ref.verify(take_batch(d, sample))))
     assert worst <= TOL, worst
+
+
+def test_mamba2_with_decay_skip():
+    """bf16 records with REPLAY_FLAG_DECAY_SKIP, against the oracle session with
+    the same rule on the same bf16-valued inputs."""
+    import torch
+    from hybrid_model_ssm_replay_amd import binding as B
+    from hybrid_model_ssm_replay_amd.layer import ReplayLayer
+    from oracle.session import ReplaySession
+    shape = LayerShape("mamba2", 3, 8, 64, 128, 2, 16)
+    announce("bf16 decay skip", shape)
+    ins = InputStream(shape, 36, bf16_vectors=True)
+    params = {"A": ins.params["A"].copy(), "D": ins.params["D"]}
+    params["A"][:3] = np.array([-80.0, -40.0, -25.0], np.float32)  # heads that skip within a window
+    S0 = ins.initial_state(zeros=False, scale=0.5)
+    lay = ReplayLayer("mamba2", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
+                      groups=shape.groups, max_draft=6, A=params["A"], D=params["D"], ckpt0=S0,
+                      flags=B.FLAG_DECAY_SKIP | B.FLAG_BF16_RECORDS)
+    skip = ReplaySession("mamba2", S0, shape.window, params, decay_skip=True)
+    rng = np.random.default_rng(36)
+    worst = 0.0
+    for it in range(45):
+        if it % 7 == 6:
+            T = int(rng.integers(1, 7))
+            d = ins.drafts(T)
+            worst = max(worst, max_rel_err(host(lay.verify(to_dev(d, bf16=True))), skip.verify(d)))
+            acc = ins.accepted(T)
+            lay.commit(torch.from_numpy(acc).cuda())
+            skip.commit(acc)
+        else:
+            r = ins.record()
+            worst = max(worst, max_rel_err(host(lay.step(to_dev(r, bf16=True))), skip.step(r)))
+    lay.flush()
+    skip.flush()
+    assert worst <= TOL, worst
+    assert ckpt_rel_err(host(lay.checkpoint), skip.ckpt) <= TOL
