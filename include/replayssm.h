@@ -26,7 +26,8 @@
  *   - Return value: REPLAY_OK, or a negative code.  REPLAY_EINVAL (bad shape,
  *     NULL pointer, misaligned pointer, unsupported pair of formats) is returned
  *     before anything is enqueued; REPLAY_EHIP reports a failed kernel launch.
- *   - Floating-point arrays are float32, C-contiguous, 16-byte aligned.
+ *   - Floating-point arrays are float32 (the record vector fields are bf16 with
+ *     REPLAY_FLAG_BF16_RECORDS), C-contiguous, 16-byte aligned.
  *   - Calls on one context must be issued on one stream (or be ordered by the
  *     caller): they read pointer words written by the previous call.
  *   - Anomalies found on the device (a clamped accept count, a corrupted
