@@ -349,6 +349,38 @@ def bench_zero_copy(torch, steps, warmup, rounds=3):
     return out
 
 
+def bench_split_error_growth(torch, seed=7, steps=4096):
+    """Output error of each split-precision pair against the float32 path of the
+    same library (which matches the float64 oracle to float32 rounding) on the
+    batch-64 GDN layer from a zero state, as the mean normwise error over step
+    ranges: whether it grows with generation length.  (The 32768-step curves
+    against the float64 oracle itself are a GPU test.)"""
+    from hybrid_model_ssm_replay_amd.layer import ReplayLayer
+    from synth import WORKLOADS, DeviceInputStream
+    shape = WORKLOADS["gdn_b64_h32_d128_l16"]
+    pairs = ((0, 3), (1, 3), (2, 3), (3, 3), (1, 1), (2, 2), (0, 4))
+    bins = ((16, 256), (256, 1024), (1024, steps))
+    lays = {p: ReplayLayer("gdn", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
+                           ckpt_fmt=p[0], read_fmt=p[1], seed=seed) for p in ((0, 0),) + pairs}
+    ys = {p: torch.empty((shape.batch, shape.heads, shape.head_dim), device="cuda") for p in lays}
+    err = {p: torch.zeros(steps, device="cuda", dtype=torch.float64) for p in pairs}
+    ins = DeviceInputStream(shape, seed)
+    for t in range(steps):
+        r = ins.record()
+        for p, lay in lays.items():
+            lay.step(r, ys[p])
+        nref = torch.linalg.vector_norm(ys[(0, 0)])
+        for p in pairs:
+            err[p][t] = (torch.linalg.vector_norm(ys[p] - ys[(0, 0)]) / nref).double()
+    out = {"steps": steps, "bins": [list(b) for b in bins], "pairs": {}}
+    for p in pairs:
+        e = err[p].cpu()
+        out["pairs"][f"{FMT_NAMES[p[0]]}/{FMT_NAMES[p[1]]}"] = [float(e[a:b].mean()) for a, b in bins]
+    del lays
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_read_copy_error(torch, seed=6, steps=512, skip=64):
     """Output error of the e2m1 read copies (block scales only, and two-axis)
     against the float32 path of the same library, on the split-precision layer
@@ -407,7 +439,8 @@ def cpu_baseline(shape, seed, budget_s=12.0):
 
 
 # Extras after the headline measurement, in run order.
-SECTIONS = ("conv", "skip", "verify", "gdn", "gdn_verify", "split", "read_error", "bf16", "zero_copy", "sweeps")
+SECTIONS = ("conv", "skip", "verify", "gdn", "gdn_verify", "split", "split_error", "read_error", "bf16", "zero_copy",
+            "sweeps")
 
 
 def main(argv=None):
@@ -513,6 +546,9 @@ def main(argv=None):
     if want("split"):
         log("split precision")
         extra["gdn_split_b64"] = bench_split(torch)
+    if want("split_error"):
+        log("split-precision error growth")
+        extra["split_error_growth_b64"] = bench_split_error_growth(torch)
     if want("read_error"):
         log("read copy error")
         extra["read_copy_error_b64"] = bench_read_copy_error(torch)
