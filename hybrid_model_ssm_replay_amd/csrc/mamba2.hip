@@ -265,13 +265,13 @@ __device__ __forceinline__ float pick(const float (&acc)[RBW], int sel) {
 }
 
 // Output of the newest of m window records from the checkpoint rows in s.
-// Inputs are the already-loaded pieces: cv (this token's C at the lane's
-// columns), bdot (the lane's partial B_{r16} . C), dtv (dt of record `lane`,
+// Inputs are the already-loaded pieces: Cs (this token's C, in the wave's LDS
+// region), bdot (the lane's partial B_{r16} . C), dtv (dt of record `lane`,
 // lanes 0..15), xr[st][k] (x of record 4 st + q at row block k).  Returns the
 // finished output of row 16 (rb0 + q) + r16 (lanes with q < RBW).
-template <int NCH, int RBW, bool SKIP>
-__device__ __forceinline__ float replay_output(const float4 (&s)[RBW][NCH], const float4 (&cv)[NCH], float bdot,
-                                               float dtv, const float (&xr)[4][RBW], int m, float Ah, int lane) {
+template <int NCH, int RBW, bool SKIP, typename R>
+__device__ __forceinline__ float replay_output(const float4 (&s)[RBW][NCH], const R *Cs, float bdot, float dtv,
+                                               const float (&xr)[4][RBW], int m, float Ah, int lane) {
   const int q = lane >> 4;
   const float dot = sum_quarters(bdot);
   float total;
@@ -283,7 +283,7 @@ __device__ __forceinline__ float replay_output(const float4 (&s)[RBW][NCH], cons
   for (int k = 0; k < RBW; ++k) {
     float v = 0.f;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) v += dot4(s[k][c], cv[c]);
+    for (int c = 0; c < NCH; ++c) v += dot4(s[k][c], ldr4<R>(Cs + 16 * c + 4 * q));
     v *= scale;
 #pragma unroll
     for (int st = 0; st < 4; ++st) v += __shfl(w, 4 * st + q, kWave) * xr[st][k];
@@ -292,11 +292,109 @@ __device__ __forceinline__ float replay_output(const float4 (&s)[RBW][NCH], cons
   return pick<RBW>(acc, q);
 }
 
+// One record vector (N elements of type R) into LDS at dst, which is the same
+// for the whole wave, by direct global-to-LDS loads: lane l < N sizeof(R) / 16
+// moves bytes 16 l .. 16 l + 15.  The data is there once vmcnt reaches zero.
+template <int N, typename R>
+__device__ __forceinline__ void dma_row(const R *src, R *dst, int lane) {
+  constexpr int kLanes = N * (int)sizeof(R) / 16;
+  static_assert(kLanes >= 1 && kLanes <= kWave, "record vector must be 16 .. 1024 bytes");
+  if (lane < kLanes)
+    dma16(reinterpret_cast<const float *>(reinterpret_cast<const char *>(src) + 16 * lane),
+          reinterpret_cast<float4 *>(dst));
+}
+
+// Bytes of one LDS row of the step kernel (a record vector plus 16 bytes, so
+// that the rows of consecutive records start on different banks), and of one
+// wave's region: this token's C, then the B of up to kMaxL window records.
+template <int NCH, typename R>
+constexpr int step_lds_row() { return 16 * NCH * (int)sizeof(R) + 16; }
+template <int NCH, typename R>
+constexpr int step_lds_wave() { return step_lds_row<NCH, R>() * (kMaxL + 1); }
+
+// The fold's record operands that stay in registers: x of record 4 st + q at
+// the lane's rows, and dt of record `lane` (from the head's dt ring row, held
+// by lane = slot).  The B operands are read from LDS by fold_apply_lds.
+template <int RBW, typename R>
+__device__ __forceinline__ float fold_load_x(float (&xraw)[4][RBW], int cnt, int s0, const R *rx, float dtrow,
+                                             int Ls, size_t xs, int rb0, int lane) {
+  const int q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int r = 4 * st + q;
+    const int rc = r < cnt ? r : cnt - 1;
+    const R *xr = rx + wrap(s0, rc, Ls) * xs;
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      const float v = ldr<R>(xr + (rb0 + k) * 16 + r16);
+      xraw[st][k] = r < cnt ? v : 0.f;
+    }
+  }
+  const float d = __shfl(dtrow, wrap(s0, r16 < cnt ? r16 : cnt - 1, Ls), kWave);
+  return lane < cnt ? d : 0.f;
+}
+
+// s <- exp(A s_{1..cnt}) s + sum_r exp(A s_{r+1..cnt}) dt_r x_r B_r^T by
+// v_mfma_f32_16x16x4f32 (K = record), with B_r read from LDS row r of bs.
+// Column chunk outermost: its four B operands are read once (rows past cnt
+// are read and zeroed; every row lies inside the wave's region) and serve
+// every row block, and all four MFMA steps run (zero operands past cnt).
+template <int NCH, int RBW, bool SKIP, typename R>
+__device__ __forceinline__ void fold_apply_lds(float4 (&s)[RBW][NCH], const unsigned char *bs, float dtv,
+                                               const float (&xraw)[4][RBW], int cnt, float Ah, int lane) {
+  constexpr int kRow = step_lds_row<NCH, R>();
+  const int q = lane >> 4, r16 = lane & 15;
+  float total;
+  const float seg = suffix_sum16(dtv, lane, &total);
+  const float f = __expf(Ah * seg) * dtv;
+  const float scale = s0_weight<SKIP>(Ah * total);
+  float xb[RBW][4];  // MFMA B operand: f_r x_r[row], r = 4 st + q  (K = record, N = row)
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const float fr = __shfl(f, 4 * st + q, kWave);
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) xb[k][st] = fr * xraw[st][k];
+  }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    float bv[4];  // MFMA A operand: B_r[16 c + r16], r = 4 st + q
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int r = 4 * st + q;
+      const float v = ldr<R>(reinterpret_cast<const R *>(bs + r * kRow) + 16 * c + r16);
+      bv[st] = r < cnt ? v : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      floatx4 acc = {s[k][c].x * scale, s[k][c].y * scale, s[k][c].z * scale, s[k][c].w * scale};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) acc = mfma_16x16x4(bv[st], xb[k][st], acc);
+      s[k][c] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+  }
+}
+
 // ZC: the token's x, B, dt are already in their ring slots (zero-copy append); a
 // compile-time choice, because a run-time one costs the standard path 58 VGPRs.
+//
+// LDS: each wave has a private region (step_lds_wave bytes, dynamic shared
+// memory) holding this token's C and the B of the window records it reads.
+// Both arrive by direct global-to-LDS loads issued behind the checkpoint
+// stream, so no VGPR holds them while the stream is in flight and the wave
+// waits only for its own loads: there is no workgroup barrier on the
+// non-fold path.
+// Occupancy target: four waves per SIMD (at most 128 VGPRs) for the copying
+// step.  The zero-copy variants get no target: their ring-slot addressing
+// would then spill to scratch.
+template <bool SKIP, bool ZC>
+constexpr int step_waves_per_eu() { return ZC ? 1 : 4; }
+
 template <int NCH, int RBW, bool SKIP, typename R, bool ZC>
-__global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(step_waves_per_eu<SKIP, ZC>())))
+void m2_replay_step(M2StepArgs a) {
   constexpr int N = 16 * NCH;
+  constexpr int kRow = step_lds_row<NCH, R>();
+  extern __shared__ __align__(16) unsigned char m2_step_lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r16 = lane & 15;
   const Shape &sh = a.s;
@@ -306,6 +404,10 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   const int P = sh.P, L = sh.L, Ls = sh.Ls;
   const int rb0 = wave * RBW;
   constexpr bool zc = ZC;
+  unsigned char *wl = m2_step_lds + wave * step_lds_wave<NCH, R>();
+  R *Cs = reinterpret_cast<R *>(wl);                             // this token's C
+  unsigned char *Bs = wl + kRow;                                 // row j: B of window record j
+  auto Brow = [&](int j) { return reinterpret_cast<R *>(Bs + j * kRow); };
   float *S = a.ckpt + ((size_t)b * sh.H + h) * P * N;
   const size_t xs = (size_t)sh.B * sh.H * P;  // x-ring slot stride (slot-major ring)
   R *rx = static_cast<R *>(a.ring.x) + ((size_t)b * sh.H + h) * P;
@@ -317,29 +419,27 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
 
   // 1. Everything whose address needs no pointer, checkpoint first: its loads
   //    are then in flight while the pointers arrive.  (Loads complete in issue
-  //    order, so nothing issued later can delay it.)
+  //    order, so nothing issued later can delay it.)  The pointer words and the
+  //    per-head scalars are read before the first global-to-LDS load, after
+  //    which the compiler would no longer use scalar loads.
   //    With the decay skip the checkpoint stream waits for the decision, which
   //    needs the pointers and the head's dt ring row.
   float4 s[RBW][NCH];
   if constexpr (!SKIP) load_rows<NCH, RBW>(s, S, rb0, lane);
-  float4 cv[NCH];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) cv[c] = ldr4<R>(Cin + 16 * c + 4 * q);
-  const float dtrow = rdt[lane < Ls ? lane : 0];  // the head's whole dt ring, slot = lane
+  const int pos_raw = a.ptr.pos_in[b], ck_raw = a.ptr.ckpt_in[b];
   float dt_in = zc ? 0.f : a.dt[(size_t)b * sh.H + h];
   const float Ah = a.A[h], Dh = a.D[h];
+  const float dtrow = rdt[lane < Ls ? lane : 0];  // the head's whole dt ring, slot = lane
+  dma_row<N, R>(Cin, Cs, lane);
 
-  // 2. Pointers.
-  const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
+  // 2. Pointers.  A corrupted pair (count outside [0, L]) is flagged and the
+  //    sequence skipped: it computes on pointers (0, 0), so every ring index
+  //    stays in range, and stores nothing.  No early return here: the compiler
+  //    would sink the checkpoint loads below the branch, and every tile would
+  //    then wait for the pointers before starting its stream.
+  const bool bad = pos_raw - ck_raw < 0 || pos_raw - ck_raw > L;
+  const int pos = bad ? 0 : pos_raw, ck = bad ? 0 : ck_raw;
   const int count = pos - ck;
-  if (count < 0 || count > L) {
-    if (h == 0 && threadIdx.x == 0) {
-      atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
-      a.ptr.pos_out[b] = pos;
-      a.ptr.ckpt_out[b] = ck;
-    }
-    return;
-  }
   const bool fold = count == L;
   const int s0 = fmod_(ck, sh.fLs), s0b = fmod_(ck, sh.f2L);  // slots of window record 0
   const int slot = wrap(s0, count, Ls), slotb = wrap(s0b, count, 2 * L);  // slots of this token
@@ -369,17 +469,12 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
   float xr[4][RBW];
   int base;
   if (!fold) {
-    // 3. Window records (ring slots known now).  Every load is unconditional on
-    //    a clamped record index, masked afterwards: no per-load branches.
+    // 3. Window records (ring slots known now): B of records 0 .. m-1 into the
+    //    wave's LDS rows, x of record 4 st + q at the lane's rows.  The x loads
+    //    are unconditional on a clamped record index, masked afterwards.
     base = ck;
     const int m = count + 1;
-    float4 bj[NCH];
-    {
-      const int j = r16 < m ? r16 : m - 1;
-      const R *Bj = (j == m - 1) ? Bin : rB + wrap(s0b, j, 2 * L) * N;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) bj[c] = ldr4<R>(Bj + 16 * c + 4 * q);
-    }
+    for (int j = 0; j < m; ++j) dma_row<N, R>((j == m - 1) ? Bin : rB + wrap(s0b, j, 2 * L) * N, Brow(j), lane);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int j = 4 * st + q;
@@ -392,13 +487,17 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
       }
     }
     {
-      // dt of record `lane`, permuted out of the ring row loaded up front (after
-      // the loads above in program order, so it does not hold them back).
+      // dt of record `lane`, permuted out of the ring row loaded up front.
       const float d = __shfl(dtrow, wrap(s0, r16 < m - 1 ? r16 : 0, Ls), kWave);
       dtv = lane < m - 1 ? d : (lane == m - 1 ? dt_in : 0.f);
     }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's global-to-LDS loads have landed
+    wave_lds_sync();
+    {
+      const R *Bj = Brow(r16 < m ? r16 : m - 1);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) bdot += dot4(bj[c], cv[c]);
+      for (int c = 0; c < NCH; ++c) bdot += dot4(ldr4<R>(Bj + 16 * c + 4 * q), ldr4<R>(Cs + 16 * c + 4 * q));
+    }
     bdot = r16 < m ? bdot : 0.f;
   } else {
     // Fold the full window into the checkpoint, store it, and start the next
@@ -412,22 +511,32 @@ __global__ __launch_bounds__(256) void m2_replay_step(M2StepArgs a) {
       for (int st = 0; st < 4; ++st) xr[st][k] = (st == 0 && q == 0) ? v : 0.f;
     }
     dtv = lane == 0 ? dt_in : 0.f;
+    __builtin_amdgcn_s_waitcnt(0);  // this token's C (global-to-LDS) has landed
+    wave_lds_sync();
     fold_apply<NCH, RBW, SKIP>(s, fi, Ah, lane);
     store_rows<NCH, RBW>(s, S, rb0, lane);
     base = pos;
     // This token's B . C after the fold: computing it earlier keeps more
-    // registers live across the fold and costs occupancy on every step.
+    // registers live across the fold.
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) bdot += dot4(ldr4<R>(Bin + 16 * c + 4 * q), cv[c]);
+    for (int c = 0; c < NCH; ++c) bdot += dot4(ldr4<R>(Bin + 16 * c + 4 * q), ldr4<R>(Cs + 16 * c + 4 * q));
     bdot = r16 == 0 ? bdot : 0.f;
   }
   const int m = pos - base + 1;
-  const float out = replay_output<NCH, RBW, SKIP>(s, cv, bdot, dtv, xr, m, Ah, lane);
+  const float out = replay_output<NCH, RBW, SKIP, R>(s, Cs, bdot, dtv, xr, m, Ah, lane);
 
   // 4. Append this token's record (unless the producer wrote it into the ring).
   //    After a fold the dt slot being written held a record that the other
   //    waves of a multi-wave head also read.
   if (fold && nwaves > 1 && !zc) __syncthreads();
+  if (bad) {
+    if (h == 0 && threadIdx.x == 0) {
+      atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
+      a.ptr.pos_out[b] = pos_raw;
+      a.ptr.ckpt_out[b] = ck_raw;
+    }
+    return;
+  }
   if (q < RBW) {
     const int row = (rb0 + q) * 16 + r16;
     const float xv = ldr<R>(xin + row);
@@ -875,18 +984,28 @@ RSSM_WRAP(SnapK, m2_snapshot_verify)
 #undef RSSM_WRAP_SKIP
 #undef RSSM_WRAP
 
+// The step kernel takes step_lds_wave bytes of dynamic LDS per wave.
 template <bool SKIP, typename R, bool ZC>
-struct StepW {
-  template <int NCH, int RBW>
-  struct K {
-    static constexpr auto fn = m2_replay_step<NCH, RBW, SKIP, R, ZC>;
-  };
-};
+int launch_step_r(const M2StepArgs &a, hipStream_t st) {
+  int waves, rbw;
+  if (!tile_geometry(a.s.P, true, &waves, &rbw)) return (int)hipErrorInvalidValue;
+  const dim3 grid((unsigned)((size_t)a.s.B * a.s.H)), block(64 * waves);
+#define RSSM_CASE(NCH_, RBW_)                                                                    \
+  if (a.s.N == 16 * NCH_ && rbw == RBW_) {                                                       \
+    const size_t lds = (size_t)waves * step_lds_wave<NCH_, R>();                                \
+    hipLaunchKernelGGL((m2_replay_step<NCH_, RBW_, SKIP, R, ZC>), grid, block, lds, st, a);      \
+    return (int)hipGetLastError();                                                               \
+  }
+#define RSSM_NCH(RBW_) RSSM_CASE(1, RBW_) RSSM_CASE(2, RBW_) RSSM_CASE(4, RBW_) RSSM_CASE(8, RBW_)
+  RSSM_NCH(1) RSSM_NCH(2)
+#undef RSSM_NCH
+#undef RSSM_CASE
+  return (int)hipErrorInvalidValue;
+}
 
 template <bool SKIP, bool ZC>
 int launch_step(const M2StepArgs &a, hipStream_t st) {
-  return a.bf16 ? dispatch<StepW<SKIP, bf16_t, ZC>::template K>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st)
-                : dispatch<StepW<SKIP, float, ZC>::template K>(a, a.s.N, a.s.P, a.s.B, a.s.H, true, st);
+  return a.bf16 ? launch_step_r<SKIP, bf16_t, ZC>(a, st) : launch_step_r<SKIP, float, ZC>(a, st);
 }
 
 // Launch W<float>::K or W<bf16_t>::K by the record element type.
