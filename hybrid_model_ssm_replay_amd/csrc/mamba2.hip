@@ -157,13 +157,14 @@ __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm
 // 16 rows, and a head takes P / (16 RBW) waves (two at P = 64).  Every load
 // that does not depend on the pointers is issued first, so the checkpoint
 // stream is in flight while the pointers, then the ring records, arrive.  No
-// LDS and no workgroup barrier on the non-fold path (a barrier there costs
-// more than any LDS sharing it would allow).
+// workgroup barrier on the non-fold path (a barrier there costs more than any
+// LDS sharing it would allow): each wave stages what it reads of C and B in
+// its own LDS region.
 //
 // Lane (r16, q) roles:  checkpoint rows 16 rb + r16, columns 16 c + 4 q + 0..3;
 // for the B_j . C dots lane r16 stands for window record j = r16 and sums over
-// the same columns as its checkpoint slice, so the C values it already holds
-// serve both products.
+// the same columns as its checkpoint slice, reading the same C chunks from LDS
+// for both products.
 
 // Fold the cnt committed records at positions base.. into the register tile,
 // wave-locally: s <- exp(A s_{1..cnt}) s + sum_r exp(A s_{r+1..cnt}) dt_r x_r B_r^T.
