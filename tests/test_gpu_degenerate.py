@@ -8,6 +8,9 @@
   beta = 0.  The outputs are then those of the checkpoint alone.
 * All-zero records from a zero state: outputs are exactly zero.
 * A long run (1024 steps, 64 folds): float32 rounding does not accumulate.
+* Corrupted pointer pairs (a negative count, a count above L) on a full window:
+  the step stores nothing at all (ring, checkpoint and output byte-identical),
+  leaves the pointers as they were and sets the status bit.
 """
 import numpy as np
 import pytest
@@ -158,3 +161,31 @@ def test_long_run_stays_at_float32_rounding(kind):
     assert worst <= TOL, worst
     lay.flush()
     assert ckpt_rel_err(host(lay.checkpoint), ref.state) <= TOL
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_corrupted_pointers_store_nothing(kind):
+    import torch
+
+    from _gpu import pointers_host
+    shape = LayerShape(kind, 2, 4, 32, 32, 2, 4) if kind == "mamba2" else LayerShape(kind, 2, 4, 64, 32, 4, 4)
+    announce("corrupted pointers", shape)
+    ins = InputStream(shape, 8)
+    S0 = ins.initial_state(zeros=False, scale=0.3)
+    lay = _m2_layer(shape, ins.params["A"], ins.params["D"], S0) if kind == "mamba2" else _gdn_layer(shape, S0)
+    for _ in range(shape.window):  # full windows: a good next step would fold
+        lay.step(to_dev(ins.record()))
+    pos, ck = lay.pointers()
+    pos[0] = ck[0] - 1                      # count -1
+    pos[1] = ck[1] + shape.window + 1       # count L + 1
+    torch.cuda.synchronize()
+    want_pos, want_ck = pointers_host(lay)
+    ring0, ckpt0 = lay.ring.clone(), lay.ckpt.clone()
+    y = torch.full((shape.batch, shape.heads, shape.head_dim), 7.0, device="cuda")
+    lay.step(to_dev(ins.record()), y=y)
+    torch.cuda.synchronize()
+    got_pos, got_ck = pointers_host(lay)
+    assert lay.status & 0x2
+    assert np.array_equal(got_pos, want_pos) and np.array_equal(got_ck, want_ck)
+    assert torch.equal(lay.ring, ring0) and torch.equal(lay.ckpt, ckpt0)
+    assert torch.all(y == 7.0)
