@@ -129,6 +129,18 @@ __device__ __forceinline__ void dma16(const float *src, float4 *lds) {
   __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src), (lds_void *)(lds), 16, 0, 0);
 }
 
+// One record vector (N elements of type R) into LDS at dst, which is the same
+// for the whole wave, by direct global-to-LDS loads: lane l < N sizeof(R) / 16
+// moves bytes 16 l .. 16 l + 15.  The data is there once vmcnt reaches zero.
+template <int N, typename R>
+__device__ __forceinline__ void dma_vec(const R *src, void *dst, int lane) {
+  constexpr int kLanes = N * (int)sizeof(R) / 16;
+  static_assert(kLanes >= 1 && kLanes <= kWave, "record vector must be 16 .. 1024 bytes");
+  if (lane < kLanes)
+    dma16(reinterpret_cast<const float *>(reinterpret_cast<const char *>(src) + 16 * lane),
+          reinterpret_cast<float4 *>(dst));
+}
+
 // Four elements per lane into LDS as float32, lane l's at lds[l] (lds the same
 // for the whole wave): a direct global-to-LDS load for float32 fields, a load,
 // exact widening and LDS store for bf16 fields.  Either way the data is in

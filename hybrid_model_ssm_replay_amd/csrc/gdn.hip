@@ -1287,7 +1287,7 @@ __global__ __launch_bounds__(256) void gdn_encode_state(GdnEncodeArgs a, GdnStat
 template <int NCH, int RBW, typename R>
 __device__ __forceinline__ void gdn_update_rows(float4 (&s)[RBW][NCH], const R *qin, const R *kin, const R *vin,
                                                 float alpha, float beta, int rb0, int lane,
-                                                float *o_rows /* nullptr: no store */) {
+                                                float *o_rows /* nullptr: no store */, int vrow0 = 0) {
   constexpr int CM = kColIlv;
   const int q = lane >> 4, r16 = lane & 15;
   float4 kv[NCH], qv[NCH];
@@ -1304,7 +1304,7 @@ __device__ __forceinline__ void gdn_update_rows(float4 (&s)[RBW][NCH], const R *
 #pragma unroll
     for (int c = 0; c < NCH; ++c) sk += dot4(s[k][c], kv[c]);
     sk = sum_quarters(sk);
-    const float coef = beta * ldr<R>(vin + row) - alpha * beta * sk;
+    const float coef = beta * ldr<R>(vin + (row - vrow0)) - alpha * beta * sk;  // vin holds rows vrow0 ..
     float so = 0.f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -1343,9 +1343,20 @@ __global__ __launch_bounds__(256) void gdn_conv_step(GdnConvArgs a) {
   store_rows_g<NCH, RBW, kColIlv>(s, S, rb0, lane);
 }
 
+// Bytes one draft takes in a wave's LDS region of the snapshot baseline: its q
+// and k, and v at the wave's rows.
+template <int NCH, int RBW, typename R>
+constexpr int gsnap_lds_draft() { return 2 * 16 * NCH * (int)sizeof(R) + 16 * RBW * (int)sizeof(R); }
+
+// Every draft's q, k and v (at the wave's rows) are staged into the wave's LDS
+// region by direct global-to-LDS loads before the first snapshot store, so the
+// draft loop issues no global load: a load issued after stores waits for them
+// to complete, which would serialise the T snapshot writes.
 template <int NCH, int RBW, typename R>
 __global__ __launch_bounds__(256) void gdn_snapshot_verify(GdnSnapArgs a) {
   constexpr int DK = 16 * NCH;
+  constexpr int kVec = DK * (int)sizeof(R), kDraft = gsnap_lds_draft<NCH, RBW, R>();
+  extern __shared__ __align__(16) unsigned char gdn_snap_lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const Shape &sh = a.s;
   const int T = a.T, H = sh.H, DV = sh.P, rb0 = wave * RBW;
@@ -1354,12 +1365,23 @@ __global__ __launch_bounds__(256) void gdn_snapshot_verify(GdnSnapArgs a) {
   const int cur = a.cur[b];
   if (cur < 0 || cur >= a.nslots) return;  // never index outside the slot array
   auto slot_ptr = [&](int sl) { return a.slots + (((size_t)b * a.nslots + sl) * H + h) * (size_t)DV * DK; };
+  unsigned char *wl = gdn_snap_lds + (size_t)wave * T * kDraft;
   float4 s[RBW][NCH];
   load_rows_g<NCH, RBW, kColIlv>(s, slot_ptr(cur), rb0, lane);
   for (int i = 0; i < T; ++i) {
     const size_t d = ((size_t)b * T + i) * H + h;
-    gdn_update_rows<NCH, RBW, R>(s, static_cast<const R *>(a.q) + d * DK, static_cast<const R *>(a.k) + d * DK,
-                                 static_cast<const R *>(a.v) + d * DV, a.alpha[d], a.beta[d], rb0, lane, a.y + d * DV);
+    dma_vec<DK, R>(static_cast<const R *>(a.q) + d * DK, wl + i * kDraft, lane);
+    dma_vec<DK, R>(static_cast<const R *>(a.k) + d * DK, wl + i * kDraft + kVec, lane);
+    dma_vec<16 * RBW, R>(static_cast<const R *>(a.v) + d * DV + rb0 * 16, wl + i * kDraft + 2 * kVec, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's global-to-LDS loads have landed
+  wave_lds_sync();
+  for (int i = 0; i < T; ++i) {
+    const size_t d = ((size_t)b * T + i) * H + h;
+    gdn_update_rows<NCH, RBW, R>(s, reinterpret_cast<const R *>(wl + i * kDraft),
+                                 reinterpret_cast<const R *>(wl + i * kDraft + kVec),
+                                 reinterpret_cast<const R *>(wl + i * kDraft + 2 * kVec), a.alpha[d], a.beta[d], rb0,
+                                 lane, a.y + d * DV, rb0 * 16);
     store_rows_g<NCH, RBW, kColIlv>(s, slot_ptr((cur + 1 + i) % a.nslots), rb0, lane);
   }
 }
@@ -1442,7 +1464,6 @@ struct GEncodeK {
     };                                              \
   };
 RSSM_WRAP(GConvK, gdn_conv_step)
-RSSM_WRAP(GSnapK, gdn_snapshot_verify)
 #undef RSSM_WRAP
 
 GdnStateBufs state_bufs(const GdnFormatBufs &f) {
@@ -1474,8 +1495,31 @@ int launch_gdn_encode(const GdnEncodeArgs &a, const GdnFormatBufs &f, hipStream_
 int launch_gdn_conv(const GdnConvArgs &a, hipStream_t st) {
   return a.bf16 ? gdn_dispatch_f32<GConvK<bf16_t>::template K>(a, st) : gdn_dispatch_f32<GConvK<float>::template K>(a, st);
 }
+// The snapshot baseline takes T gsnap_lds_draft bytes of dynamic LDS per wave.
+template <typename R>
+int launch_gsnap_r(const GdnSnapArgs &a, hipStream_t st) {
+  const int DK = a.s.N, DV = a.s.P;
+  if (DV != 64 && DV != 128) return (int)hipErrorInvalidValue;
+  const int rbw = DV / 64;
+  const dim3 grid((unsigned)((size_t)a.s.B * a.s.H)), block(256);
+#define RSSM_CASE(NCH_, RBW_)                                                                  \
+  if (DK == 16 * NCH_ && rbw == RBW_) {                                                        \
+    const size_t lds = (size_t)4 * a.T * gsnap_lds_draft<NCH_, RBW_, R>();                    \
+    if (lds > 65536) {                                                                         \
+      const hipError_t e = hipFuncSetAttribute((const void *)gdn_snapshot_verify<NCH_, RBW_, R>, \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,     \
+                                               (int)lds);                                      \
+      if (e != hipSuccess) return (int)e;                                                      \
+    }                                                                                          \
+    hipLaunchKernelGGL((gdn_snapshot_verify<NCH_, RBW_, R>), grid, block, lds, st, a);         \
+    return (int)hipGetLastError();                                                             \
+  }
+  RSSM_CASE(2, 1) RSSM_CASE(4, 1) RSSM_CASE(8, 1) RSSM_CASE(2, 2) RSSM_CASE(4, 2) RSSM_CASE(8, 2)
+#undef RSSM_CASE
+  return (int)hipErrorInvalidValue;
+}
 int launch_gdn_snapshot(const GdnSnapArgs &a, hipStream_t st) {
-  return a.bf16 ? gdn_dispatch_f32<GSnapK<bf16_t>::template K>(a, st) : gdn_dispatch_f32<GSnapK<float>::template K>(a, st);
+  return a.bf16 ? launch_gsnap_r<bf16_t>(a, st) : launch_gsnap_r<float>(a, st);
 }
 
 }  // namespace rssm

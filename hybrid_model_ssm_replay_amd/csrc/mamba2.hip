@@ -293,18 +293,6 @@ __device__ __forceinline__ float replay_output(const float4 (&s)[RBW][NCH], cons
   return pick<RBW>(acc, q);
 }
 
-// One record vector (N elements of type R) into LDS at dst, which is the same
-// for the whole wave, by direct global-to-LDS loads: lane l < N sizeof(R) / 16
-// moves bytes 16 l .. 16 l + 15.  The data is there once vmcnt reaches zero.
-template <int N, typename R>
-__device__ __forceinline__ void dma_row(const R *src, R *dst, int lane) {
-  constexpr int kLanes = N * (int)sizeof(R) / 16;
-  static_assert(kLanes >= 1 && kLanes <= kWave, "record vector must be 16 .. 1024 bytes");
-  if (lane < kLanes)
-    dma16(reinterpret_cast<const float *>(reinterpret_cast<const char *>(src) + 16 * lane),
-          reinterpret_cast<float4 *>(dst));
-}
-
 // Bytes of one LDS row of the step kernel (a record vector plus 16 bytes, so
 // that the rows of consecutive records start on different banks), and of one
 // wave's region: this token's C, then the B of up to kMaxL window records.
@@ -431,7 +419,7 @@ void m2_replay_step(M2StepArgs a) {
   float dt_in = zc ? 0.f : a.dt[(size_t)b * sh.H + h];
   const float Ah = a.A[h], Dh = a.D[h];
   const float dtrow = rdt[lane < Ls ? lane : 0];  // the head's whole dt ring, slot = lane
-  dma_row<N, R>(Cin, Cs, lane);
+  dma_vec<N, R>(Cin, Cs, lane);
 
   // 2. Pointers.  A corrupted pair (count outside [0, L]) is flagged and the
   //    sequence skipped: it computes on pointers (0, 0), so every ring index
@@ -475,7 +463,7 @@ void m2_replay_step(M2StepArgs a) {
     //    are unconditional on a clamped record index, masked afterwards.
     base = ck;
     const int m = count + 1;
-    for (int j = 0; j < m; ++j) dma_row<N, R>((j == m - 1) ? Bin : rB + wrap(s0b, j, 2 * L) * N, Brow(j), lane);
+    for (int j = 0; j < m; ++j) dma_vec<N, R>((j == m - 1) ? Bin : rB + wrap(s0b, j, 2 * L) * N, Brow(j), lane);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int j = 4 * st + q;
@@ -885,9 +873,20 @@ __global__ __launch_bounds__(256) void m2_conv_step(M2ConvArgs a) {
 }
 
 // ---- baseline: snapshot-per-draft verify -----------------------------------
+// Bytes one draft takes in a wave's LDS region of the snapshot baseline: its B
+// and C, and x at the wave's rows.
+template <int NCH, int RBW, typename R>
+constexpr int snap_lds_draft() { return 2 * 16 * NCH * (int)sizeof(R) + 16 * RBW * (int)sizeof(R); }
+
+// Every draft's B, C and x (at the wave's rows) are staged into the wave's LDS
+// region by direct global-to-LDS loads before the first snapshot store, so the
+// draft loop issues no global load: a load issued after stores waits for them
+// to complete, which would serialise the T snapshot writes.
 template <int NCH, int RBW, typename R>
 __global__ __launch_bounds__(256) void m2_snapshot_verify(M2SnapArgs a) {
   constexpr int N = 16 * NCH;
+  constexpr int kVec = N * (int)sizeof(R), kDraft = snap_lds_draft<NCH, RBW, R>();
+  extern __shared__ __align__(16) unsigned char m2_snap_lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4, r16 = lane & 15;
   const Shape &sh = a.s;
@@ -899,40 +898,53 @@ __global__ __launch_bounds__(256) void m2_snapshot_verify(M2SnapArgs a) {
   if (cur < 0 || cur >= a.nslots) return;  // never index outside the slot array
   const size_t head_elems = (size_t)P * N;
   auto slot_ptr = [&](int sl) { return a.slots + (((size_t)b * a.nslots + sl) * H + h) * head_elems; };
+  unsigned char *wl = m2_snap_lds + (size_t)wave * T * kDraft;
   float4 s[RBW][NCH];
   load_rows<NCH, RBW>(s, slot_ptr(cur), rb0, lane);
   const float Ah = a.A[h], Dh = a.D[h];
   for (int i = 0; i < T; ++i) {
+    const R *xin = static_cast<const R *>(a.x) + (((size_t)b * T + i) * H + h) * P;
+    dma_vec<N, R>(static_cast<const R *>(a.Bm) + (((size_t)b * T + i) * G + g) * N,
+                  reinterpret_cast<R *>(wl + i * kDraft), lane);
+    dma_vec<N, R>(static_cast<const R *>(a.Cm) + (((size_t)b * T + i) * G + g) * N,
+                  reinterpret_cast<R *>(wl + i * kDraft + kVec), lane);
+    dma_vec<16 * RBW, R>(xin + rb0 * 16, reinterpret_cast<R *>(wl + i * kDraft + 2 * kVec), lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's global-to-LDS loads have landed
+  wave_lds_sync();
+  for (int i = 0; i < T; ++i) {
     const float dt = a.dt[((size_t)b * T + i) * H + h];
     const float decay = __expf(dt * Ah);
-    const R *xin = static_cast<const R *>(a.x) + (((size_t)b * T + i) * H + h) * P;
-    const R *Bin = static_cast<const R *>(a.Bm) + (((size_t)b * T + i) * G + g) * N;
-    const R *Cin = static_cast<const R *>(a.Cm) + (((size_t)b * T + i) * G + g) * N;
-    float4 bv[NCH], cv[NCH];
+    const R *Bl = reinterpret_cast<const R *>(wl + i * kDraft);
+    const R *Cl = reinterpret_cast<const R *>(wl + i * kDraft + kVec);
+    const R *xl = reinterpret_cast<const R *>(wl + i * kDraft + 2 * kVec);  // x at rows rb0 16 ..
+    float dx[RBW], v[RBW];
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+      dx[k] = dt * ldr<R>(xl + k * 16 + r16);
+      v[k] = 0.f;
+    }
+    // Column chunk outermost (each chunk of B and C read from LDS once); every
+    // row's sum still runs over the chunks in order.
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      bv[c] = ldr4<R>(Bin + 16 * c + 4 * q);
-      cv[c] = ldr4<R>(Cin + 16 * c + 4 * q);
+      const float4 bv = ldr4<R>(Bl + 16 * c + 4 * q), cv = ldr4<R>(Cl + 16 * c + 4 * q);
+#pragma unroll
+      for (int k = 0; k < RBW; ++k) {
+        float4 &e = s[k][c];
+        e.x = decay * e.x + dx[k] * bv.x;
+        e.y = decay * e.y + dx[k] * bv.y;
+        e.z = decay * e.z + dx[k] * bv.z;
+        e.w = decay * e.w + dx[k] * bv.w;
+        v[k] += dot4(e, cv);
+      }
     }
     float acc[RBW];
 #pragma unroll
-    for (int k = 0; k < RBW; ++k) {
-      const float dx = dt * ldr<R>(xin + (rb0 + k) * 16 + r16);
-      float v = 0.f;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        float4 &e = s[k][c];
-        e.x = decay * e.x + dx * bv[c].x;
-        e.y = decay * e.y + dx * bv[c].y;
-        e.z = decay * e.z + dx * bv[c].z;
-        e.w = decay * e.w + dx * bv[c].w;
-        v += dot4(e, cv[c]);
-      }
-      acc[k] = sum_quarters(v);
-    }
+    for (int k = 0; k < RBW; ++k) acc[k] = sum_quarters(v[k]);
     if (q < RBW) {
       const int row = (rb0 + q) * 16 + r16;
-      a.y[(((size_t)b * T + i) * H + h) * P + row] = pick<RBW>(acc, q) + Dh * ldr<R>(xin + row);
+      a.y[(((size_t)b * T + i) * H + h) * P + row] = pick<RBW>(acc, q) + Dh * ldr<R>(xl + q * 16 + r16);
     }
     store_rows<NCH, RBW>(s, slot_ptr((cur + 1 + i) % a.nslots), rb0, lane);
   }
@@ -981,7 +993,6 @@ RSSM_WRAP_SKIP(FlushSkipK, m2_flush, true)
 RSSM_WRAP_SKIP(VerifyK, m2_replay_verify, false)
 RSSM_WRAP_SKIP(VerifySkipK, m2_replay_verify, true)
 RSSM_WRAP(ConvK, m2_conv_step)
-RSSM_WRAP(SnapK, m2_snapshot_verify)
 #undef RSSM_WRAP_SKIP
 #undef RSSM_WRAP
 
@@ -1029,6 +1040,32 @@ int launch_m2_verify(const M2VerifyArgs &a, hipStream_t st) {
   return a.decay_skip ? dispatch_rec<VerifySkipK>(a, true, st) : dispatch_rec<VerifyK>(a, true, st);
 }
 int launch_m2_conv(const M2ConvArgs &a, hipStream_t st) { return dispatch_rec<ConvK>(a, true, st); }
-int launch_m2_snapshot(const M2SnapArgs &a, hipStream_t st) { return dispatch_rec<SnapK>(a, true, st); }
+// The snapshot baseline takes T snap_lds_draft bytes of dynamic LDS per wave.
+template <typename R>
+int launch_snapshot_r(const M2SnapArgs &a, hipStream_t st) {
+  int waves, rbw;
+  if (!tile_geometry(a.s.P, true, &waves, &rbw)) return (int)hipErrorInvalidValue;
+  const dim3 grid((unsigned)((size_t)a.s.B * a.s.H)), block(64 * waves);
+#define RSSM_CASE(NCH_, RBW_)                                                               \
+  if (a.s.N == 16 * NCH_ && rbw == RBW_) {                                                  \
+    const size_t lds = (size_t)waves * a.T * snap_lds_draft<NCH_, RBW_, R>();              \
+    if (lds > 65536) {                                                                      \
+      const hipError_t e = hipFuncSetAttribute((const void *)m2_snapshot_verify<NCH_, RBW_, R>, \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,  \
+                                               (int)lds);                                   \
+      if (e != hipSuccess) return (int)e;                                                   \
+    }                                                                                       \
+    hipLaunchKernelGGL((m2_snapshot_verify<NCH_, RBW_, R>), grid, block, lds, st, a);       \
+    return (int)hipGetLastError();                                                          \
+  }
+#define RSSM_NCH(RBW_) RSSM_CASE(1, RBW_) RSSM_CASE(2, RBW_) RSSM_CASE(4, RBW_) RSSM_CASE(8, RBW_)
+  RSSM_NCH(1) RSSM_NCH(2)
+#undef RSSM_NCH
+#undef RSSM_CASE
+  return (int)hipErrorInvalidValue;
+}
+int launch_m2_snapshot(const M2SnapArgs &a, hipStream_t st) {
+  return a.bf16 ? launch_snapshot_r<bf16_t>(a, st) : launch_snapshot_r<float>(a, st);
+}
 
 }  // namespace rssm
