@@ -868,7 +868,7 @@ __global__ __launch_bounds__(256) void m2_conv_step(M2ConvArgs a) {
   store_rows<NCH, RBW>(s, S, rb0, lane);
   if (q < RBW) {
     const int row = (rb0 + q) * 16 + r16;
-    a.y[((size_t)b * sh.H + h) * P + row] = pick<RBW>(acc, q) + Dh * pick<RBW>(xr, q);  // x at row: no load after the stores
+    a.y[((size_t)b * sh.H + h) * P + row] = pick<RBW>(acc, q) + Dh * ldr<R>(xin + row);
   }
 }
 
