@@ -301,68 +301,6 @@ constexpr int step_lds_row() { return 16 * NCH * (int)sizeof(R) + 16; }
 template <int NCH, typename R>
 constexpr int step_lds_wave() { return step_lds_row<NCH, R>() * (kMaxL + 1); }
 
-// The fold's record operands that stay in registers: x of record 4 st + q at
-// the lane's rows, and dt of record `lane` (from the head's dt ring row, held
-// by lane = slot).  The B operands are read from LDS by fold_apply_lds.
-template <int RBW, typename R>
-__device__ __forceinline__ float fold_load_x(float (&xraw)[4][RBW], int cnt, int s0, const R *rx, float dtrow,
-                                             int Ls, size_t xs, int rb0, int lane) {
-  const int q = lane >> 4, r16 = lane & 15;
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    const int r = 4 * st + q;
-    const int rc = r < cnt ? r : cnt - 1;
-    const R *xr = rx + wrap(s0, rc, Ls) * xs;
-#pragma unroll
-    for (int k = 0; k < RBW; ++k) {
-      const float v = ldr<R>(xr + (rb0 + k) * 16 + r16);
-      xraw[st][k] = r < cnt ? v : 0.f;
-    }
-  }
-  const float d = __shfl(dtrow, wrap(s0, r16 < cnt ? r16 : cnt - 1, Ls), kWave);
-  return lane < cnt ? d : 0.f;
-}
-
-// s <- exp(A s_{1..cnt}) s + sum_r exp(A s_{r+1..cnt}) dt_r x_r B_r^T by
-// v_mfma_f32_16x16x4f32 (K = record), with B_r read from LDS row r of bs.
-// Column chunk outermost: its four B operands are read once (rows past cnt
-// are read and zeroed; every row lies inside the wave's region) and serve
-// every row block, and all four MFMA steps run (zero operands past cnt).
-template <int NCH, int RBW, bool SKIP, typename R>
-__device__ __forceinline__ void fold_apply_lds(float4 (&s)[RBW][NCH], const unsigned char *bs, float dtv,
-                                               const float (&xraw)[4][RBW], int cnt, float Ah, int lane) {
-  constexpr int kRow = step_lds_row<NCH, R>();
-  const int q = lane >> 4, r16 = lane & 15;
-  float total;
-  const float seg = suffix_sum16(dtv, lane, &total);
-  const float f = __expf(Ah * seg) * dtv;
-  const float scale = s0_weight<SKIP>(Ah * total);
-  float xb[RBW][4];  // MFMA B operand: f_r x_r[row], r = 4 st + q  (K = record, N = row)
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    const float fr = __shfl(f, 4 * st + q, kWave);
-#pragma unroll
-    for (int k = 0; k < RBW; ++k) xb[k][st] = fr * xraw[st][k];
-  }
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    float bv[4];  // MFMA A operand: B_r[16 c + r16], r = 4 st + q
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int r = 4 * st + q;
-      const float v = ldr<R>(reinterpret_cast<const R *>(bs + r * kRow) + 16 * c + r16);
-      bv[st] = r < cnt ? v : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < RBW; ++k) {
-      floatx4 acc = {s[k][c].x * scale, s[k][c].y * scale, s[k][c].z * scale, s[k][c].w * scale};
-#pragma unroll
-      for (int st = 0; st < 4; ++st) acc = mfma_16x16x4(bv[st], xb[k][st], acc);
-      s[k][c] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    }
-  }
-}
-
 // ZC: the token's x, B, dt are already in their ring slots (zero-copy append); a
 // compile-time choice, because a run-time one costs the standard path 58 VGPRs.
 //
@@ -375,11 +313,11 @@ __device__ __forceinline__ void fold_apply_lds(float4 (&s)[RBW][NCH], const unsi
 // Occupancy target: four waves per SIMD (at most 128 VGPRs) for the copying
 // step.  The zero-copy variants get no target: their ring-slot addressing
 // would then spill to scratch.
-template <bool SKIP, bool ZC>
+template <bool ZC>
 constexpr int step_waves_per_eu() { return ZC ? 1 : 4; }
 
 template <int NCH, int RBW, bool SKIP, typename R, bool ZC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(step_waves_per_eu<SKIP, ZC>())))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(step_waves_per_eu<ZC>())))
 void m2_replay_step(M2StepArgs a) {
   constexpr int N = 16 * NCH;
   constexpr int kRow = step_lds_row<NCH, R>();
