@@ -1,14 +1,20 @@
 """Summaries of rocprofv3 output for the replay kernels.
 
     python -m hybrid_model_ssm_replay_amd.rocprof_summary trace <kernel_trace.csv>
+    python -m hybrid_model_ssm_replay_amd.rocprof_summary verify <fetch_counter_collection.csv> \
+        <write_counter_collection.csv> <kernel_trace.csv>
     python -m hybrid_model_ssm_replay_amd.rocprof_summary traffic <fetch_counter_collection.csv> \
-        <write_counter_collection.csv> <kernel-substring> <probe-copy-bytes> [grid-size [first-n]]
+        <write_counter_collection.csv> <kernel-substring> <probe-copy-bytes> [grid-size [first-n [skip-n]]]
 
+``verify`` prints, for the verify measurements of bench.py (Mamba-2 at batch
+512 and Gated DeltaNet at batch 256, T = 4 then T = 8, replay and snapshot
+kernels), the calibrated traffic and mean duration per launch next to the byte
+model, the replay model replaying the bench's seeded accepted counts.
 ``trace`` prints the mean, min and max duration per kernel and launch size
 (grid size in work-items).  ``traffic`` prints FETCH_SIZE and WRITE_SIZE (KiB
 per dispatch) of the named kernel (only its launches of the given grid size,
-when one is given, and only the first n of those in dispatch order, when n is
-given), calibrated
+when one is given, and only the first n of those in dispatch order after
+skipping the first skip-n, when n is given), calibrated
 against the library's HBM probe copy kernel, whose bytes are known: it reads and
 writes exactly the same number of bytes, so factor_read = WRITE_SIZE / FETCH_SIZE
 of the probe and factor_write = 1 when the probe's WRITE_SIZE equals the bytes
@@ -38,13 +44,18 @@ def _order(r) -> int:
 
 
 def _by_kernel(path: str, value_field: str, grid: int | None = None, with_grid: bool = False,
-               first: int | None = None):
+               first: int | None = None, skip: int = 0):
     d = collections.defaultdict(list)
+    seen = collections.Counter()
     for r in sorted(csv.DictReader(open(path)), key=_order):
         g = _grid(r)
         if grid is not None and g != grid and PROBE_COPY not in r["Kernel_Name"]:
             continue
         key = (r["Kernel_Name"], g) if with_grid else r["Kernel_Name"]
+        if PROBE_COPY not in r["Kernel_Name"]:
+            seen[key] += 1
+            if seen[key] <= skip:
+                continue
         if first is not None and PROBE_COPY not in r["Kernel_Name"] and len(d[key]) >= first:
             continue
         if value_field == "duration":
@@ -70,9 +81,9 @@ def trace(path: str) -> str:
 
 
 def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int | None = None,
-            grid: int | None = None, first: int | None = None) -> dict:
-    fe = _by_kernel(fetch_csv, "Counter_Value", grid, first=first)
-    wr = _by_kernel(write_csv, "Counter_Value", grid, first=first)
+            grid: int | None = None, first: int | None = None, skip: int = 0) -> dict:
+    fe = _by_kernel(fetch_csv, "Counter_Value", grid, first=first, skip=skip)
+    wr = _by_kernel(write_csv, "Counter_Value", grid, first=first, skip=skip)
     pk_f, pk_w = _find(fe, PROBE_COPY), _find(wr, PROBE_COPY)
     probe_fetch = sum(fe[pk_f]) / len(fe[pk_f])
     probe_write = sum(wr[pk_w]) / len(wr[pk_w])
@@ -86,12 +97,52 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int | None 
             "factor_write": f_w, "traffic_bytes_per_launch": kf * 1024 * f_r + kw * 1024 * f_w}
 
 
+# The verify runs of bench.py: workload, seed, T values, launches per T of the
+# replay kernel (8 warm-up + 16 timed) and of the snapshot kernel (4 + 16).
+VERIFY_RUNS = (("mamba2_b512_h128_p64_n128_g8_l16", 3, "m2_replay_verify<8, 2, false, float>",
+                "m2_snapshot_verify<8, 2, float>"),
+               ("gdn_b256_h32_d128_l16", 2, "gdn_replay_verify<0, 0, 8, 2, float>",
+                "gdn_snapshot_verify<8, 2, float>"))
+VERIFY_TS, REPLAY_CALLS, SNAP_CALLS, DRAFT_SETS = (4, 8), 24, 20, 4
+
+
+def verify(fetch_csv: str, write_csv: str, trace_csv: str, copy_bytes: int = 1 << 30) -> str:
+    import os
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from synth import WORKLOADS, InputStream
+    from hybrid_model_ssm_replay_amd.traffic import Layer, snapshot_verify_bytes, verify_session_bytes
+    dur = _by_kernel(trace_csv, "duration")
+    lines = ["| workload | T | kernel | launches | mean us | traffic GB | model GB | traffic / model | GB/s (model) |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for name, seed, rk, sk in VERIFY_RUNS:
+        shape = WORKLOADS[name]
+        lay = Layer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.groups, shape.window)
+        for ti, T in enumerate(VERIFY_TS):
+            ins = InputStream(shape, seed)  # the bench's draws: draft sets first, then accepted counts
+            for _ in range(DRAFT_SETS):
+                ins.drafts(T)
+            accs = [ins.accepted(T) for _ in range(DRAFT_SETS)]
+            rd, wr = verify_session_bytes(lay, T, accs, REPLAY_CALLS)
+            srd, swr = snapshot_verify_bytes(lay, T)
+            for kern, calls, model in ((rk, REPLAY_CALLS, rd + wr), (sk, SNAP_CALLS, srd + swr)):
+                r = traffic(fetch_csv, write_csv, kern, copy_bytes, None, calls, ti * calls)
+                ds = dur[_find(dur, kern)][ti * calls:(ti + 1) * calls]
+                us = sum(ds) / len(ds)
+                t = r["traffic_bytes_per_launch"]
+                lines.append(f"| {name} | {T} | `{kern}` | {r['dispatches']} | {us:.1f} | {t / 1e9:.3f} | "
+                             f"{model / 1e9:.3f} | {t / model:.3f} | {model / us / 1e3:.0f} |")
+    return "\n".join(lines)
+
+
 def main(argv):
     if argv[0] == "trace":
         print(trace(argv[1]))
+    elif argv[0] == "verify":
+        print(verify(argv[1], argv[2], argv[3]))
     elif argv[0] == "traffic":
         r = traffic(argv[1], argv[2], argv[3], int(argv[4]) if len(argv) > 4 else None,
-                    int(argv[5]) if len(argv) > 5 else None, int(argv[6]) if len(argv) > 6 else None)
+                    int(argv[5]) if len(argv) > 5 else None, int(argv[6]) if len(argv) > 6 else None,
+                    int(argv[7]) if len(argv) > 7 else 0)
         for k, v in r.items():
             print(f"{k}: {v}")
     else:

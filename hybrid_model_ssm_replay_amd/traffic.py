@@ -147,3 +147,22 @@ def replay_verify_bytes(l: Layer, T: int, committed: int, fold_first: bool) -> t
 
 def snapshot_verify_bytes(l: Layer, T: int) -> tuple[int, int]:
     return (l.state + T * l.record_in) * l.batch, (T * l.state + T * l.y) * l.batch
+
+
+def verify_session_bytes(l: Layer, T: int, accepted: list, calls: int) -> tuple[float, float]:
+    """Mean (read, write) model bytes per replay-verify launch over `calls`
+    verify + commit rounds from empty windows, the accepted counts cycling
+    through `accepted` (int arrays [batch]).  Per sequence, a verify folds first
+    when its window cannot take T more records (count + T > L), and either way
+    reads the count committed records once; the commit then appends
+    min(a, T) records to what is left in the window."""
+    import numpy as np
+    count = np.zeros(l.batch, dtype=np.int64)
+    rd = wr = 0.0
+    for i in range(calls):
+        fold = count + T > l.window
+        rd += float(l.state * l.batch + count.sum() * l.ring_rec + T * l.record_in * l.batch)
+        wr += float(T * (l.ring_rec + l.y) * l.batch + fold.sum() * l.state)
+        a = np.minimum(np.asarray(accepted[i % len(accepted)], dtype=np.int64), T)
+        count = np.where(fold, 0, count) + a
+    return rd / calls, wr / calls
