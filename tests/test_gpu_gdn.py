@@ -173,3 +173,23 @@ def test_conventional_and_snapshot_baselines():
         snap.commit(torch.from_numpy(acc).cuda())
         ref2.commit(acc)
         assert ckpt_rel_err(host(snap.state()), ref2.state) <= TOL
+
+
+def test_snapshot_baseline_large_lds():
+    """T = 16 drafts at d_v = d_k = 128: the staged inputs take 72 KiB of LDS per
+    workgroup, above the default dynamic limit, which the launch raises."""
+    import torch
+    from hybrid_model_ssm_replay_amd.layer import SnapshotLayer
+    shape = LayerShape("gdn", 2, 3, 128, 128, 3, 16)
+    announce("gdn snapshot T=16", shape)
+    ins = InputStream(shape, 11)
+    S0 = ins.initial_state(zeros=False, scale=0.3)
+    snap = SnapshotLayer("gdn", shape.batch, shape.heads, shape.head_dim, shape.state_dim, 16, state0=S0)
+    ref = StepwiseSession("gdn", S0)
+    for T in (16, 9):
+        d = ins.drafts(T)
+        assert max_rel_err(host(snap.verify(to_dev(d))), ref.verify(d)) <= TOL
+        acc = ins.accepted(T)
+        snap.commit(torch.from_numpy(acc).cuda())
+        ref.commit(acc)
+        assert ckpt_rel_err(host(snap.state()), ref.state) <= TOL

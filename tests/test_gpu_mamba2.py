@@ -244,6 +244,27 @@ def test_snapshot_baseline():
         assert ckpt_rel_err(host(snap.state()), ref.state) <= TOL
 
 
+def test_snapshot_baseline_large_lds():
+    """T = 16 drafts at P = 128 (four waves): the staged inputs take 72 KiB of LDS
+    per workgroup, above the default dynamic limit, which the launch raises."""
+    import torch
+    from hybrid_model_ssm_replay_amd.layer import SnapshotLayer
+    shape = LayerShape("mamba2", 2, 4, 128, 128, 2, 16)
+    announce("mamba2 snapshot T=16", shape)
+    ins = InputStream(shape, 10)
+    S0 = ins.initial_state(zeros=False, scale=0.5)
+    snap = SnapshotLayer("mamba2", shape.batch, shape.heads, shape.head_dim, shape.state_dim, 16, groups=shape.groups,
+                         A=ins.params["A"], D=ins.params["D"], state0=S0)
+    ref = StepwiseSession("mamba2", S0, ins.params)
+    for T in (16, 7):
+        d = ins.drafts(T)
+        assert max_rel_err(host(snap.verify(to_dev(d))), ref.verify(d)) <= TOL
+        acc = ins.accepted(T)
+        snap.commit(torch.from_numpy(acc).cuda())
+        ref.commit(acc)
+        assert ckpt_rel_err(host(snap.state()), ref.state) <= TOL
+
+
 def test_decay_skip_matches_oracle():
     """REPLAY_FLAG_DECAY_SKIP: steps, verifies, commits and a flush against the
     oracle session with the same rule (heads whose window decay is below 2^-24
