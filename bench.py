@@ -535,6 +535,7 @@ def main(argv=None):
                              "conventional_gbs": (gcrd + gcwr) / us_gc / 1e3, "speedup_vs_conventional": us_gc / us_g,
                              "tokens_per_s": gshape.batch / us_g * 1e6,
                              "traffic_bytes_per_launch": stored_traffic("gdn_replay_step_b256_traffic.txt", "gdn")}
+        extra["gdn_b256"]["replay_step_distribution"] = step_distribution(torch, gshape, 2)
 
         for T in (4, 8) if want("gdn_verify") else ():
             log("gdn verify T", T)
