@@ -1026,8 +1026,14 @@ union GdnWaveLds {
   GdnVerifyLds<RBW> verify;  // the drafts (after the fold)
 };
 
+// Occupancy target for the float32 copies: three waves per SIMD (at most 168
+// VGPRs; the LDS of three workgroups fits a CU).
+template <int CF, int RF>
+constexpr int verify_waves_per_eu() { return (CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32) ? 3 : 1; }
+
 template <int CF, int RF, int NCH, int RBW, typename R>
-__global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<CF, RF>())))
+void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
   constexpr int CM = col_map(CF, RF);
   constexpr int kPass = kMaxL / 4;
@@ -1074,10 +1080,6 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
       stage4<R>(src + colq<NCH, CM>(cc, q2), &ldsD[64 * j], lane);
     }
   }
-  float vrow[kMaxL];
-#pragma unroll
-  for (int d = 0; d < kMaxL; ++d) vrow[d] = ldr<R>(dv_(d < T ? d : T - 1) + row);
-
   // 2. Pointers; fold-first when the window cannot take T more records.
   const int count = pos - ck;
   if (count < 0 || count > L) {
@@ -1109,19 +1111,11 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
   const int c = pos - base, nrec = c + T;
 
   // 3. Window records: every key into LDS (committed from the ring, drafts from
-  //    the input; chunk cc by wave cc % nwaves), this lane's row of the
-  //    committed pseudo-values, and alpha, beta of record r16.
+  //    the input; chunk cc by wave cc % nwaves), and alpha, beta of record r16.
   {
     const int j = r16 < nrec ? r16 : nrec - 1;
     const R *kj = j < c ? rp.rk + (size_t)wrap(sb0, j, Ls) * rp.ks : dk_(j - c);
     for (int cc = wave; cc < NCH; cc += nwaves) stage4<R>(kj + colq<NCH, CM>(cc, q), &ldsK[cc][0], lane);
-  }
-  float uc[kMaxL - 1];
-#pragma unroll
-  for (int j = 0; j < kMaxL - 1; ++j) {
-    const int jc = j < c ? j : 0;
-    const float v = rp.ru[(size_t)wrap(sb0, jc, Ls) * rp.vs + row];
-    uc[j] = j < c ? v : 0.f;
   }
   float al, be;
   {
@@ -1213,10 +1207,19 @@ __global__ __launch_bounds__(256) void gdn_replay_verify(GdnVerifyArgs a, GdnSta
   wave_lds_sync();
 
   // 5. The drafts' rows of the system and their outputs, one lane per state row.
+  //    This row of the committed pseudo-values and of the drafts' values is
+  //    loaded only now: held through the passes above it would cost a wave per
+  //    SIMD.
   if (lane < 16 * RBW) {
-    float u[kMaxL];
+    float u[kMaxL], vrow[kMaxL];
 #pragma unroll
-    for (int j = 0; j < kMaxL; ++j) u[j] = j < kMaxL - 1 ? uc[j] : 0.f;
+    for (int j = 0; j < kMaxL; ++j) {
+      const int jc = j < c ? j : 0;
+      const float v = rp.ru[(size_t)wrap(sb0, jc, Ls) * rp.vs + row];
+      u[j] = j < c ? v : 0.f;
+    }
+#pragma unroll
+    for (int d = 0; d < kMaxL; ++d) vrow[d] = ldr<R>(dv_(d < T ? d : T - 1) + row);
 #pragma unroll
     for (int t = 0; t < kMaxL; ++t) {
       if (t >= c && t < nrec) {
