@@ -559,6 +559,10 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   __shared__ float4 ldsB[NCH][64];          // [chunk cc][r + 16 q]: B_r[16 cc + 4 q .. + 3]
   __shared__ float4 ldsC[kPass * NCH * 16];  // [(p NCH + cc) 16 + 4 m + q]: C_{4 p + m}[16 cc + 4 q .. + 3]
   __shared__ float dots_all[4][kMaxL][4];    // per wave: [record][draft of the pass] B_r . C_n
+  // Per wave: x of draft i at the wave's rows (16 RBW elements of type R), for
+  // the D x term; from LDS, the passes issue no global load, which would wait
+  // for the previous pass's output stores.
+  __shared__ __align__(16) unsigned char ldsX[4][kMaxL][16 * RBW * sizeof(R)];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r16 = lane & 15, gq = r16 >> 2, m4 = r16 & 3;
   const Shape &sh = a.s;
@@ -652,6 +656,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
     const float v = (rc < c || zc) ? rdt[wrap(sb, rc, Ls)] : a.dt[((size_t)b * T + (rc - c)) * H + h];
     dtl = r16 < nrec ? v : 0.f;
   }
+  for (int i = 0; i < T; ++i) dma_vec<16 * RBW, R>(draft_x(i) + rb0 * 16, ldsX[wave][i], lane);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's global-to-LDS loads have landed
   __syncthreads();                // and every other wave's
 
@@ -662,7 +667,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
     const int nc = n < T ? n : T - 1;
     float4 xl[RBW];  // x_n at rows 16 rb + 4 g + 0..3 (the D x term)
 #pragma unroll
-    for (int k = 0; k < RBW; ++k) xl[k] = ldr4<R>(draft_x(nc) + (rb0 + k) * 16 + 4 * gq);
+    for (int k = 0; k < RBW; ++k) xl[k] = ldr4<R>(reinterpret_cast<const R *>(ldsX[wave][nc]) + k * 16 + 4 * gq);
     const float4 *cdp = &ldsC[(p * NCH * 4 + m4) * 4 + q];  // C_n at tile chunk cc: cdp[16 cc]
 
     // dots[4 g + v][n] (register v, summed over q), transposed through LDS.
