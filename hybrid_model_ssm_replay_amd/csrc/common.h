@@ -207,6 +207,14 @@ __device__ __forceinline__ int fdiv(int n, const FastDiv &f) {
 }
 __device__ __forceinline__ int fmod_(int n, const FastDiv &f) { return n - fdiv(n, f) * (int)f.d; }
 
+// A pointer pair the kernels act on: 0 <= ckpt_pos <= pos <= ckpt_pos + L.
+// Any other pair (corrupted, or negative) flags its sequence, which is then
+// skipped: ring slots are only ever computed from non-negative positions, the
+// domain of fdiv / fmod_ above.
+__device__ __forceinline__ bool pointers_ok(int pos, int ck, int L) {
+  return ck >= 0 && pos >= ck && pos - ck <= L;
+}
+
 // (s0 + j) mod d for 0 <= s0 < d and 0 <= j < d: one compare, no division.
 __device__ __forceinline__ int wrap(int s0, int j, int d) {
   const int v = s0 + j;

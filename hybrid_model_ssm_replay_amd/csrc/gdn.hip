@@ -810,7 +810,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   // 2. Pointers.
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
   const int count = pos - ck;
-  if (count < 0 || count > L) {
+  if (!pointers_ok(pos, ck, L)) {
     if (h == 0 && threadIdx.x == 0) {
       atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
       a.ptr.pos_out[b] = pos;
@@ -970,7 +970,7 @@ __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a, GdnStateBufs sb
   const size_t head = bh * DV * DK;
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
   const int count = pos - ck;
-  const bool bad = count < 0 || count > L;
+  const bool bad = !pointers_ok(pos, ck, L);
   const bool fold = !bad && count > 0 && (a.mask == nullptr || a.mask[b] != 0);
   if (h == 0 && threadIdx.x == 0) {
     if (bad) atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
@@ -1068,7 +1068,8 @@ void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
   typename SIO<RF, NCH, RBW, CM>::Raw raw;
   SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
-  sp = fmod_(pos, sh.fLs);
+  const bool ok = pointers_ok(pos, ck, L);
+  sp = fmod_(ok ? pos : 0, sh.fLs);  // a flagged sequence stages from slot 0 and stores nothing
   {
     const int nload = (npass * 2 * NCH * 16) >> 6;
     for (int j = wave; j < nload; j += nwaves) {
@@ -1082,7 +1083,7 @@ void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
   }
   // 2. Pointers; fold-first when the window cannot take T more records.
   const int count = pos - ck;
-  if (count < 0 || count > L) {
+  if (!ok) {
     if (h == 0 && threadIdx.x == 0) {
       atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
       a.ptr.pos_out[b] = pos;

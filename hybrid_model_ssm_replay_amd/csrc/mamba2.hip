@@ -359,12 +359,12 @@ void m2_replay_step(M2StepArgs a) {
   const float dtrow = rdt[lane < Ls ? lane : 0];  // the head's whole dt ring, slot = lane
   dma_vec<N, R>(Cin, Cs, lane);
 
-  // 2. Pointers.  A corrupted pair (count outside [0, L]) is flagged and the
+  // 2. Pointers.  A corrupted pair (count outside [0, L], or ckpt_pos < 0) is flagged and the
   //    sequence skipped: it computes on pointers (0, 0), so every ring index
   //    stays in range, and stores nothing.  No early return here: the compiler
   //    would sink the checkpoint loads below the branch, and every tile would
   //    then wait for the pointers before starting its stream.
-  const bool bad = pos_raw - ck_raw < 0 || pos_raw - ck_raw > L;
+  const bool bad = !pointers_ok(pos_raw, ck_raw, L);
   const int pos = bad ? 0 : pos_raw, ck = bad ? 0 : ck_raw;
   const int count = pos - ck;
   const bool fold = count == L;
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
   const int P = sh.P, L = sh.L;
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
   const int count = pos - ck;
-  const bool bad = count < 0 || count > L;
+  const bool bad = !pointers_ok(pos, ck, L);
   const bool fold = !bad && count > 0 && (a.mask == nullptr || a.mask[b] != 0);
   if (h == 0 && t.tid == 0) {
     if (bad) atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
 
   // 2. Pointers; fold-first when the window cannot take T more records.
   const int count = pos - ck;
-  if (count < 0 || count > L) {
+  if (!pointers_ok(pos, ck, L)) {
     if (h == 0 && threadIdx.x == 0) {
       atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
       a.ptr.pos_out[b] = pos;

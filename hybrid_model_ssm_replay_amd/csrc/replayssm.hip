@@ -312,6 +312,7 @@ int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream) {
   }
   if (e) return REPLAY_EHIP;
   ctx->parity ^= 1;
+  ctx->t_pending = 0;  // a flush discards pending drafts, like a step or a verify
   return REPLAY_OK;
 }
 

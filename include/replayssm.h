@@ -70,7 +70,7 @@ extern "C" {
 
 /* Sticky bits of the device status word. */
 #define REPLAY_STATUS_ACCEPT_CLAMPED 0x1 /* commit got accepted < 0 or > drafts pending */
-#define REPLAY_STATUS_BAD_POINTERS 0x2   /* pos - ckpt_pos outside 0..L: sequence skipped */
+#define REPLAY_STATUS_BAD_POINTERS 0x2   /* ckpt_pos < 0 or pos - ckpt_pos outside 0..L: sequence skipped */
 
 /*
  * Layer shape and options.
@@ -265,8 +265,12 @@ int replay_set_state(replay_ctx *ctx, const float *state, void *stream);
 int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *stream);
 
 /* Fold every committed record of the sequences with seq_mask[b] != 0 (device
- * uint8 [batch]; NULL = all) into the checkpoint.  Sequences with an empty
- * window are left unchanged.  Pending drafts stay pending. */
+ * uint8 [batch]; NULL = all) into the checkpoint, which is rewritten only when
+ * a window is folded [P2, paragraph 3; P3, Interpretation 2]: the call for a
+ * caller that needs the state in the checkpoint alone before the window has
+ * filled (e.g. to save it).  Sequences with an empty window are left unchanged.
+ * Drafts still pending from a verify are discarded, as by a step (the same as
+ * commit of 0): a later commit finds none and clamps its counts to 0. */
 int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream);
 
 /* Speculative verification of T drafts per sequence, 1 <= T <= max_draft

@@ -29,10 +29,11 @@ Decay factors are always formed from segment sums s_m - s_j, never as a ratio
 of two cumulative decays, which would underflow to 0/0 for strongly decaying
 heads.
 
-Decay skip (optional).  The pages name as a next direction letting heads whose
-decay has become negligible skip the checkpoint read on non-fold steps and
-turning their fold into a pure write [P3, Perspective, paragraph 1], without a
-threshold.  Reading taken: the checkpoint term of a head is dropped when
+Decay skip (optional).  A future direction on the pages [P3, Perspective,
+paragraph 1]: once a head has decayed so far that the checkpoint no longer
+matters, its steps need not load the checkpoint, and its fold only stores
+the folded records.  No threshold is given.  Reading taken: the checkpoint
+term of a head is dropped when
 A s_m < ln 2^-24 (the decay exp(A s_m) is below float32's unit roundoff), in
 outputs and in folds alike: replay_output and fold take skip_below = that
 logarithm.

@@ -20,8 +20,8 @@ Rules (the pages state the behaviour; the exact flush timing is a reading):
 * commit(a): pos += min(max(a, 0), T_pending); rollback of rejected drafts is
   just not advancing the pointer [P1, Interpretation 3; P3, Interpretation 3].
   An out-of-range a is clamped and flagged.
-* A step or verify issued while drafts are pending discards them (the same as
-  commit(0)).
+* A step, verify or flush issued while drafts are pending discards them (the
+  same as commit(0)); only commit consumes them.
 * flush(mask): fold every committed record of the masked sequences
   (ckpt_pos = pos); sequences with an empty window are left alone.
 """
@@ -78,4 +78,5 @@ class PointerMachine:
         m = np.ones_like(self.pos, bool) if mask is None else np.asarray(mask, bool)
         folded = m & (self.count > 0)
         self.ckpt_pos = np.where(folded, self.pos, self.ckpt_pos)
+        self.t_pending = 0
         return folded

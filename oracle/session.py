@@ -84,7 +84,7 @@ class StepwiseSession:
         self.pending = None
 
     def flush(self, mask=None):
-        pass                                            # the state is always exact
+        self.pending = None                             # the state is always exact; drafts are dropped
 
 
 class ReplaySession:
@@ -192,16 +192,22 @@ def decode_state(stored, fmt):
 
 class SplitReplaySession(ReplaySession):
     """Replay with the checkpoint stored in ckpt_fmt (it carries the recurrence)
-    and a read copy in read_fmt (non-fold outputs read it); read_fmt == ckpt_fmt
-    is one shared copy.  The pages separate the two precisions so that the read
-    copy's rounding never re-enters the recurrence [P1, Interpretation 4; P3,
-    Interpretation 3].  Readings: a fold starts from the decoded recurrence copy,
-    folds in full precision, rounds to float32 and encodes both copies from that
-    float32 state; every output, including that of a step or verify that folded
-    first, comes from the decoded read copy as it stands after the call's fold
-    plus the buffered records (which are exact).  The pages fix only that
-    non-fold outputs read the approximate copy; reading it for the fold step's
-    output too makes all outputs of a window one recurrence from one S0."""
+    and a read copy in read_fmt; read_fmt == ckpt_fmt is one shared copy.  The
+    pages separate the two precisions so that the read copy's rounding never
+    re-enters the recurrence [P1, Interpretation 4; P3, Interpretation 3], and
+    say that the outputs of steps that do not fold still depend on the
+    approximate copy [P3, Perspective, paragraph 2]; the call that folds holds
+    the exact fold result.  Readings:
+
+    * a fold starts from the decoded recurrence copy, folds in full precision,
+      rounds to float32 and encodes both copies from that float32 state;
+    * the outputs of a step or verify that folds first come from the fold
+      result itself (full precision), with the call's records;
+    * every other output comes from the decoded read copy plus the buffered
+      records (which are exact), so within a window the pseudo-values of the
+      Gated DeltaNet form are those of the read copy, also for the record the
+      fold step appended.
+    """
 
     def __init__(self, kind, state0, window, params=None, ckpt_fmt=FMT_F32, read_fmt=FMT_F32, seed=0):
         super().__init__(kind, state0, window, params)
@@ -210,6 +216,7 @@ class SplitReplaySession(ReplaySession):
         B = S32.shape[0]
         self.R = [encode_state(S32[b], ckpt_fmt, seed, b, 0) for b in range(B)]
         self.Q = self.R if read_fmt == ckpt_fmt else [encode_state(S32[b], read_fmt, seed, b, 0) for b in range(B)]
+        self.last_fold = {}                             # b -> float64 fold result of the latest fold
 
     def read_state(self, b):
         return decode_state(self.Q[b], self.rf)
@@ -224,26 +231,27 @@ class SplitReplaySession(ReplaySession):
         self.R[b] = encode_state(S32, self.cf, self.seed, b, pos)
         if self.Q is not self.R:
             self.Q[b] = encode_state(S32, self.rf, self.seed, b, pos)
+        self.last_fold[b] = S
         for p in [p for p in self.recs[b] if p < pos]:
             del self.recs[b][p]
+        return S
 
     def step(self, rec):
         will_fold = self.ptr.count == self.ptr.L
-        for b in np.nonzero(will_fold)[0]:
-            self._fold(b)
+        fresh = {int(b): self._fold(b) for b in np.nonzero(will_fold)[0]}
         pos_before = self.ptr.pos.copy()
         self.ptr.step()
         ys = []
         for b in range(self.batch):
             self.recs[b][int(pos_before[b])] = _rec_b(rec, b)
-            ys.append(self.k.output(self.read_state(b), self._window(b, int(self.ptr.pos[b]))))
+            S0 = fresh[b] if b in fresh else self.read_state(b)
+            ys.append(self.k.output(S0, self._window(b, int(self.ptr.pos[b]))))
         return np.stack(ys)
 
     def verify(self, drafts):
         T = next(iter(drafts.values())).shape[1]
         will_fold = self.ptr.count + T > self.ptr.L
-        for b in np.nonzero(will_fold)[0]:
-            self._fold(b)
+        fresh = {int(b): self._fold(b) for b in np.nonzero(will_fold)[0]}
         self.ptr.verify(T)
         out = []
         for b in range(self.batch):
@@ -251,7 +259,7 @@ class SplitReplaySession(ReplaySession):
             for i in range(T):
                 self.recs[b][p0 + i] = _draft_b(drafts, b, i)
             committed = self._window(b, p0)
-            S0 = self.read_state(b)
+            S0 = fresh[b] if b in fresh else self.read_state(b)
             out.append(np.stack([self.k.output(S0, committed + [self.recs[b][p0 + j] for j in range(i + 1)])
                                  for i in range(T)]))
         return np.stack(out)

@@ -24,7 +24,7 @@ def _load_trace():
 def test_hand_worked_trace():
     pm = PointerMachine(1, 4)
     rows = _load_trace()
-    assert len(rows) == 20
+    assert len(rows) == 26
     for op, arg, (pos, ckpt, folded, status) in rows:
         if op == "step":
             f = pm.step()[0]
@@ -92,3 +92,15 @@ def test_rejects_bad_draft_count():
         pm.verify(5)
     with pytest.raises(ValueError):
         pm.verify(0)
+
+
+def test_flush_discards_pending_drafts():
+    # Only a commit consumes pending drafts; a flush between a verify and its
+    # commit drops them (as a step or a verify would), so the commit clamps.
+    pm = PointerMachine(2, 8)
+    pm.step(); pm.step()
+    pm.verify(3)
+    folded = pm.flush(np.array([True, False]))
+    assert list(folded) == [True, False] and list(pm.ckpt_pos) == [2, 0]
+    pm.commit([2, 0])
+    assert list(pm.pos) == [2, 2] and pm.status == STATUS_ACCEPT_CLAMPED

@@ -80,3 +80,52 @@ def test_encode_decode_error_bounds(fmt):
         amax = np.abs(blk).max(-1, keepdims=True)
         err = np.abs(D - S).reshape(2, 32, 2, 16)
         assert np.all(err <= amax / 6 * 1.07 * 2 + 1e-12)
+
+
+def _kind_inputs(kind, seed):
+    shape = LayerShape(kind, 2, 2, 16, 32, 1 if kind == "mamba2" else 2, 4)
+    ins = InputStream(shape, seed)
+    return shape, ins, ins.initial_state(zeros=False, scale=0.3)
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("cf,rf", [(FMT_F32, FMT_F4E2M1_B16), (FMT_F16_SR, FMT_F4E2M1_B16),
+                                   (FMT_F4E2M1_B16, FMT_F4E2M1_B16)])
+def test_fold_step_outputs_come_from_the_exact_fold(kind, cf, rf):
+    """The step that folds outputs from the fold result, not from the read copy
+    [P3, Perspective, paragraph 2]: at the first fold both sessions fold the same
+    decoded checkpoint with the same records, so in float64 that output equals
+    the exact replay form's to rounding, while the outputs of the steps around it
+    read the approximate copy and do not."""
+    shape, ins, S0 = _kind_inputs(kind, 3)
+    sp = SplitReplaySession(kind, S0, shape.window, ins.params, cf, rf, seed=5)
+    start = np.stack([sp.recurrence_state(b) for b in range(shape.batch)])
+    rp = ReplaySession(kind, start, shape.window, ins.params)
+    errs = []
+    for _ in range(shape.window + 3):
+        r = ins.record()
+        y, ye = sp.step(r), rp.step(r)
+        errs.append(np.max(np.abs(y - ye)) / np.max(np.abs(ye)))
+    fold_step = shape.window                              # the (L+1)-th step folds first
+    assert errs[fold_step] <= 1e-12, errs
+    # the steps after it read the encoded fold result (and, with a separate read
+    # copy, so do the steps before it: a shared copy starts as the checkpoint)
+    approx = errs[fold_step + 1:] + (errs[:fold_step] if rf != cf else [])
+    assert min(approx) > 1e-4, errs
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_verify_fold_first_outputs_come_from_the_exact_fold(kind):
+    shape, ins, S0 = _kind_inputs(kind, 8)
+    sp = SplitReplaySession(kind, S0, shape.window, ins.params, FMT_F32, FMT_F4E2M1_B16, seed=5)
+    rp = ReplaySession(kind, S0, shape.window, ins.params)
+    for _ in range(3):
+        r = ins.record()
+        sp.step(r), rp.step(r)
+    d = ins.drafts(3)                                     # 3 + 3 > 4: folds first
+    y, ye = sp.verify(d), rp.verify(d)
+    assert np.max(np.abs(y - ye)) / np.max(np.abs(ye)) <= 1e-12
+    sp.commit(np.array([1, 3])), rp.commit(np.array([1, 3]))
+    r = ins.record()                                      # a non-fold step reads the e2m1 copy again
+    y, ye = sp.step(r), rp.step(r)
+    assert np.max(np.abs(y - ye)) / np.max(np.abs(ye)) > 1e-4
