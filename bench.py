@@ -3,7 +3,8 @@
 Headline: one decode step (``replay_step``) of a Mamba-2 layer whose float32
 state is 4 MiB per sequence (128 heads, P = 64, N = 128, 8 B/C groups), batch
 256, window L = 16, with its inputs already resident in HBM.  K steps are timed
-(K a multiple of L covers whole windows, so folds are included in proportion).
+(rounded up to whole windows of L steps, so folds are timed in proportion; the
+count actually timed is reported as steps_timed).
 
 Printed: one JSON line with the headline (microseconds per step), the roofline
 of the step kernel (algorithmic bytes per launch over its measured average
@@ -413,18 +414,20 @@ def bench_read_copy_error(torch, seed=6, steps=512, skip=64):
     return out
 
 
-def cpu_baseline(shape, seed, budget_s=12.0):
-    """The float64 stepwise oracle on a bounded sample of sequences, scaled to the full batch."""
+def _oracle_worker(args):
+    """One process of the CPU baseline: the float64 stepwise oracle on `nseq`
+    sequences of the workload for about budget_s seconds, single-threaded."""
+    kind, shape_fields, seed, first, nseq, budget_s = args
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle.session import StepwiseSession
-    from synth import InputStream, take_batch
-    nseq = 4
+    from synth import InputStream, LayerShape, take_batch
+    shape = LayerShape(*shape_fields)
     ins = InputStream(shape, seed)
-    recs = [take_batch(ins.record(), np.arange(nseq)) for _ in range(8)]
-    ref = StepwiseSession(shape.kind, np.zeros((nseq, shape.heads, shape.head_dim, shape.state_dim)),
-                          ins.params)
+    idx = np.arange(first, first + nseq)
+    recs = [take_batch(ins.record(), idx) for _ in range(8)]
+    ref = StepwiseSession(kind, np.zeros((nseq, shape.heads, shape.head_dim, shape.state_dim)), ins.params)
     steps = 0
     with threadpool_limits(1):
         t0 = time.perf_counter()
@@ -432,10 +435,36 @@ def cpu_baseline(shape, seed, budget_s=12.0):
             ref.step(recs[steps % len(recs)])
             steps += 1
         el = time.perf_counter() - t0
-    us_per_step_full = el / steps * (shape.batch / nseq) * 1e6
-    return {"value": us_per_step_full, "unit": "us/step", "cores": 1, "kind": "oracle",
-            "sample": f"float64 stepwise oracle, {nseq} of {shape.batch} sequences, {steps} steps "
-                      f"({el:.1f} s), scaled linearly to the full batch"}
+    return steps * nseq, el
+
+
+def host_cores() -> int:
+    """Cores this process may use: its CPU affinity, capped by OMP_NUM_THREADS when
+    that is set (the share of the host a GPU job is given)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS")
+    return max(1, min(n, int(cap))) if cap and cap.isdigit() else max(1, n)
+
+
+def cpu_baseline(shape, seed, budget_s=12.0):
+    """The float64 stepwise oracle on the host's cores: one single-threaded
+    process per core, each stepping one sequence of the workload for about
+    budget_s seconds; the summed sequence-steps per second give the time of a
+    full-batch step.  Processes are spawned fresh (they never touch the GPU)."""
+    import multiprocessing as mp
+    from dataclasses import astuple
+    cores = host_cores()
+    nseq = 1
+    jobs = [(shape.kind, astuple(shape), seed, (nseq * i) % shape.batch, nseq, budget_s) for i in range(cores)]
+    with mp.get_context("spawn").Pool(cores) as pool:
+        res = pool.map(_oracle_worker, jobs)
+    rate = sum(n / el for n, el in res)                   # sequence-steps per second, all processes
+    us_per_step_full = shape.batch / rate * 1e6
+    nsteps = sum(n for n, _ in res)
+    return {"value": us_per_step_full, "unit": "us/step", "cores": cores, "kind": "oracle",
+            "sample": f"float64 stepwise oracle, {cores} processes (one per core, one thread each), {nseq} sequences "
+                      f"each, {nsteps} sequence-steps in about {budget_s:.0f} s; the summed rate is scaled to "
+                      f"{shape.batch} sequences per step"}
 
 
 # Extras after the headline measurement, in run order.
@@ -474,10 +503,13 @@ def main(argv=None):
     name = "mamba2_b256_h128_p64_n128_g8_l16"
     shape = WORKLOADS[name]
     L = shape.window
-    if args.steps % L or args.warmup % L:
-        log(f"note: steps/warmup not multiples of L={L}; the window mean is approximate")
+    # Whole windows only: a window's fold is timed in proportion (one fold per L steps).
+    steps_timed = -(-max(args.steps, 1) // L) * L
+    warmup_timed = -(-args.warmup // L) * L
+    if (steps_timed, warmup_timed) != (args.steps, args.warmup):
+        log(f"timing {steps_timed} steps after {warmup_timed} warm-up steps (whole windows of L = {L})")
     log("replay step", name)
-    us = bench_replay(torch, shape, 1, args.steps, args.warmup)
+    us = bench_replay(torch, shape, 1, steps_timed, warmup_timed)
     lay = Layer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.groups, L)
     rd, wr = replay_window_mean(lay)
     gbs = (rd + wr) / us / 1e3
@@ -490,14 +522,14 @@ def main(argv=None):
     extra.update({"hbm_probe_read_gbs": rgbs, "hbm_probe_copy_gbs": cgbs})
     if want("conv"):
         log("conventional step", name)
-        us_c = bench_conv(torch, shape, 1, args.steps, args.warmup)
+        us_c = bench_conv(torch, shape, 1, steps_timed, warmup_timed)
         crd, cwr = conventional_step_bytes(lay)
         extra.update({"conventional_step_us": us_c, "conventional_gbs": (crd + cwr) / us_c / 1e3,
                       "speedup_vs_conventional": us_c / us})
     if want("skip"):
         from hybrid_model_ssm_replay_amd.binding import FLAG_DECAY_SKIP
         log("replay step with the decay skip", name)
-        us_s = bench_replay(torch, shape, 1, args.steps, args.warmup, flags=FLAG_DECAY_SKIP)
+        us_s = bench_replay(torch, shape, 1, steps_timed, warmup_timed, flags=FLAG_DECAY_SKIP)
         extra["decay_skip"] = {"replay_step_us": us_s, "speedup_vs_exact_replay": us / us_s,
                                "rule": "checkpoint term dropped where exp(A s) < 2^-24 (an approximation)"}
         if "conventional_step_us" in extra:
@@ -522,12 +554,12 @@ def main(argv=None):
         gname = "gdn_b256_h32_d128_l16"
         gshape = WORKLOADS[gname]
         log("gdn replay step", gname)
-        us_g = bench_replay(torch, gshape, 2, args.steps, args.warmup)
+        us_g = bench_replay(torch, gshape, 2, steps_timed, warmup_timed)
         glay = Layer("gdn", gshape.batch, gshape.heads, gshape.head_dim, gshape.state_dim, gshape.groups,
                      gshape.window)
         grd, gwr = replay_window_mean(glay)
         log("gdn conventional step", gname)
-        us_gc = bench_conv(torch, gshape, 2, args.steps, args.warmup)
+        us_gc = bench_conv(torch, gshape, 2, steps_timed, warmup_timed)
         gcrd, gcwr = conventional_step_bytes(glay)
         extra["gdn_b256"] = {"replay_step_us": us_g, "replay_gbs": (grd + gwr) / us_g / 1e3,
                              "replay_frac_of_peak": (grd + gwr) / us_g / 1e3 / HBM_PEAK_GBS,
@@ -555,10 +587,10 @@ def main(argv=None):
         extra["read_copy_error_b64"] = bench_read_copy_error(torch)
     if want("bf16"):
         log("bf16 records")
-        extra["bf16_records"] = bench_bf16_records(torch, args.steps, args.warmup)
+        extra["bf16_records"] = bench_bf16_records(torch, steps_timed, warmup_timed)
     if want("zero_copy"):
         log("zero-copy append")
-        extra["zero_copy"] = bench_zero_copy(torch, args.steps, args.warmup)
+        extra["zero_copy"] = bench_zero_copy(torch, steps_timed, warmup_timed)
     if want("sweeps"):
         log("batch and window sweeps")
         extra["mamba2_sweeps"] = bench_sweeps(torch)
@@ -571,6 +603,7 @@ def main(argv=None):
     out = {
         "metric": "SSM decode us/step + achieved HBM GB/s, B=256 L=16 (Mamba-2 & GDN)",
         "value": us, "unit": "us/step", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "steps_timed": steps_timed, "warmup_timed": warmup_timed,
         "ms_per_step": us / 1e3, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": name, "layer": "Mamba-2", "batch": shape.batch, "heads": shape.heads,

@@ -212,7 +212,7 @@ __device__ __forceinline__ int fmod_(int n, const FastDiv &f) { return n - fdiv(
 // skipped: ring slots are only ever computed from non-negative positions, the
 // domain of fdiv / fmod_ above.
 __device__ __forceinline__ bool pointers_ok(int pos, int ck, int L) {
-  return ck >= 0 && pos >= ck && pos - ck <= L;
+  return (uint32_t)(pos - ck) <= (uint32_t)L && ck >= 0;  // one unsigned compare for 0 <= count <= L
 }
 
 // (s0 + j) mod d for 0 <= s0 < d and 0 <= j < d: one compare, no division.

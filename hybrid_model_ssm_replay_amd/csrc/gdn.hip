@@ -752,8 +752,11 @@ __device__ __forceinline__ void gdn_fold(float4 (&s)[RBW][NCH], int cnt, int s0,
 // The key dot products are spread over the tile: thread group j (16 threads)
 // takes k_j . k_m and k_j . q_m over NCH columns each (group 15: k_m . q_m),
 // and k_m, q_m reach every wave through LDS, so no lane holds them whole.
-// A step that finds the window full folds it first, stores both copies and
-// starts the next window from what the read copy now holds.
+// A step that finds the window full folds it first and stores both copies.
+// Its own output comes from the float32 fold result it holds in registers
+// (the outputs of steps that do not fold are the ones that read the
+// approximate copy [P3, Perspective, paragraph 2]); the pseudo-value it caches
+// for the next steps of the window is that of the read copy, which they read.
 template <int NCH, typename R>
 __device__ __forceinline__ void load_cols(float (&v)[NCH], const R *p) {
   if constexpr (NCH % 4 == 0) {
@@ -778,6 +781,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32 ? 4 : 1))) void gdn_replay_step(GdnStepArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
   constexpr int CM = col_map(CF, RF);
+  constexpr bool kLossy = RF != REPLAY_FMT_F32;  // the read copy is not the float32 fold result
   constexpr int kMaxOld = 15;            // older records of a window (L <= 16)
   __shared__ float4 kq_s[2][DK / 4];     // k_m, q_m in natural column order
   __shared__ float dot_s[2][16];         // [0][j] = k_j . k_m, [1][j] = k_j . q_m; [1][15] = k_m . q_m
@@ -810,7 +814,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   // 2. Pointers.
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
   const int count = pos - ck;
-  if (!pointers_ok(pos, ck, L)) {
+  if (count < 0 || count > L || ck < 0) {  // a flagged pair: no ring slot is computed from it
     if (h == 0 && threadIdx.x == 0) {
       atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
       a.ptr.pos_out[b] = pos;
@@ -842,7 +846,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       SIO<CF, NCH, RBW, CM>::decode(s, rc);
       gdn_fold<CF, RF, NCH, RBW, R>(s, L, s0, rp, Ls, rb0, lane, &lds_all[wave]);
     }
-    store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
+    // Float32 copies: s already is what the copy holds.  Otherwise the copies
+    // are stored after this token's products with the fold result (below).
+    if constexpr (!kLossy) store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
     sb0 = slot;
 #pragma unroll
@@ -926,19 +932,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       sqr = aq;
     }
   }
+  // After a fold of a low-precision read copy, skr and sqr came from the fold
+  // result; store both copies now and take S0 k_m for the cached pseudo-value
+  // from what the read copy holds, which the window's later steps read.
+  float skc = skr;
+  if constexpr (kLossy) {
+    if (fold) {
+      store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
+#pragma unroll
+      for (int k = 0; k < RBW; ++k) {
+        float ak = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) ak += dot4(s[k][c], kq_s[0][colq<NCH, CM>(c, q) >> 2]);
+        ak = sum_quarters(ak);
+        if (q == k) skc = ak;
+      }
+    }
+  }
   float acc_k = 0.f, acc_q = 0.f;
 #pragma unroll
   for (int t = 0; t < kMaxOld; ++t) {
     acc_k += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), t)) * uo[t];
     acc_q += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), t)) * uo[t];
   }
-  const float um = be_in * (v_in - egm * skr - acc_k);
+  const float um = be_in * (v_in - egm * skr - acc_k);  // this token's pseudo-value for its output
+  const float uc = kLossy ? be_in * (v_in - egm * skc - acc_k) : um;  // ... as the window's S0 (the read copy) gives it
   const float o = egm * sqr + acc_q + kmq * um;
 
   // 3. Output and append.
   if (q < RBW) {
     a.y[bh * DV + orow] = o;
-    rp.ru[(size_t)slot * rp.vs + orow] = um;
+    rp.ru[(size_t)slot * rp.vs + orow] = uc;
     if constexpr (RF != CF) str<R>(rp.rv + (size_t)slot * rp.vs + orow, v_in);
   }
   if (!zc)
@@ -1011,19 +1035,20 @@ __device__ __forceinline__ floatx4 mfma_4x4x1(float a, float b, floatx4 c) {
 // lane per row) with the committed rows known.  The drafts' keys, pseudo-
 // values and scalars are staged in the ring, so that a commit is only a
 // pointer move.
-template <int RBW>
+template <int RBW, bool DUAL>
 struct GdnVerifyLds {
   float W[16 * RBW][17];   // [row][draft]: S0 k_d
   float SQ[16 * RBW][17];  // [row][draft]: S0 q_d
   float A[16][17];         // [draft][record]: beta_t e^{g_t - g_j} (k_j . k_t) for j < t, else 0
   float Bq[16][17];        // [draft][record]: e^{g_t - g_j} (k_j . q_d) for j <= t, else 0
   float g[16], beta[16];   // record j: decay prefix, beta
+  float WQ[DUAL ? 16 * RBW : 1][17];  // after a fold-first: Q k_d for the read copy Q (cached pseudo-values)
 };
 
-template <int RBW>
+template <int RBW, bool DUAL>
 union GdnWaveLds {
-  GdnLds<RBW> fold;          // a re-solving fold-first
-  GdnVerifyLds<RBW> verify;  // the drafts (after the fold)
+  GdnLds<RBW> fold;                // a re-solving fold-first
+  GdnVerifyLds<RBW, DUAL> verify;  // the drafts (after the fold)
 };
 
 // Occupancy target for the float32 copies: three waves per SIMD (at most 168
@@ -1037,12 +1062,13 @@ void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
   constexpr int DK = 16 * NCH;
   constexpr int CM = col_map(CF, RF);
   constexpr int kPass = kMaxL / 4;
+  constexpr bool kLossy = RF != REPLAY_FMT_F32;  // the read copy is not the float32 fold result
   __shared__ float4 ldsK[NCH][64];                 // [chunk cc][record j + 16 q]: k_j at colq(cc, q)
   __shared__ float4 ldsD[kPass * 2 * NCH * 16];    // [((p 2 + w) NCH + cc) 16 + 4 m + q]: w = 0: k, 1: q of draft 4 p + m
-  __shared__ GdnWaveLds<RBW> lds_all[4];
+  __shared__ GdnWaveLds<RBW, kLossy> lds_all[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r16 = lane & 15, gq = r16 >> 2, m4 = r16 & 3;
-  GdnVerifyLds<RBW> &sv = lds_all[wave].verify;
+  GdnVerifyLds<RBW, kLossy> &sv = lds_all[wave].verify;
   const Shape &sh = a.s;
   const int T = a.T;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -1068,8 +1094,7 @@ void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
   typename SIO<RF, NCH, RBW, CM>::Raw raw;
   SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
-  const bool ok = pointers_ok(pos, ck, L);
-  sp = fmod_(ok ? pos : 0, sh.fLs);  // a flagged sequence stages from slot 0 and stores nothing
+  sp = fmod_(pos > 0 ? pos : 0, sh.fLs);  // never from a negative position (a flagged pair stores nothing)
   {
     const int nload = (npass * 2 * NCH * 16) >> 6;
     for (int j = wave; j < nload; j += nwaves) {
@@ -1083,7 +1108,7 @@ void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
   }
   // 2. Pointers; fold-first when the window cannot take T more records.
   const int count = pos - ck;
-  if (!ok) {
+  if (count < 0 || count > L || ck < 0) {
     if (h == 0 && threadIdx.x == 0) {
       atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
       a.ptr.pos_out[b] = pos;
@@ -1105,7 +1130,10 @@ void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
       SIO<CF, NCH, RBW, CM>::decode(s, rc);
     }
     gdn_fold<CF, RF, NCH, RBW, R>(s, count, s0, rp, Ls, rb0, lane, &lds_all[wave].fold);
-    store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
+    // Float32 copies: s already is what the copy holds.  Otherwise the drafts'
+    // outputs come from the fold result s, and the copies are stored after
+    // the passes (below).
+    if constexpr (!kLossy) store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
     sb0 = wrap(s0, count, Ls);
   }
@@ -1207,6 +1235,39 @@ void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
   }
   wave_lds_sync();
 
+  // 4b. After a fold-first of a low-precision read copy: store both copies,
+  //     then Q k_d from the read copy Q they now hold, for the pseudo-values
+  //     the ring caches (the window's next steps read Q).
+  if constexpr (kLossy) {
+    if (fold) {
+      store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
+      for (int p = 0; p < npass; ++p) {
+        const int d = 4 * p + m4;
+        const float4 *kd = &ldsD[(p * 2 * NCH) * 16 + 4 * m4 + q];
+#pragma unroll
+        for (int k = 0; k < RBW; ++k) {
+          floatx4 w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int cc = 0; cc < NCH; ++cc) {
+            const float4 kv = kd[16 * cc];
+            w = mfma_4x4x1(s[k][cc].x, kv.x, w);
+            w = mfma_4x4x1(s[k][cc].y, kv.y, w);
+            w = mfma_4x4x1(s[k][cc].z, kv.z, w);
+            w = mfma_4x4x1(s[k][cc].w, kv.w, w);
+          }
+          float wv[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) wv[v] = sum_quarters(w[v]);
+          if (q == 0) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sv.WQ[16 * k + 4 * gq + v][d] = wv[v];
+          }
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+
   // 5. The drafts' rows of the system and their outputs, one lane per state row.
   //    This row of the committed pseudo-values and of the drafts' values is
   //    loaded only now: held through the passes above it would cost a wave per
@@ -1221,6 +1282,7 @@ void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
     }
 #pragma unroll
     for (int d = 0; d < kMaxL; ++d) vrow[d] = ldr<R>(dv_(d < T ? d : T - 1) + row);
+    const bool dual = kLossy && fold;  // outputs from the fold result, cached values from the read copy
 #pragma unroll
     for (int t = 0; t < kMaxL; ++t) {
       if (t >= c && t < nrec) {
@@ -1234,8 +1296,23 @@ void gdn_replay_verify(GdnVerifyArgs a, GdnStateBufs sb) {
 #pragma unroll
         for (int j = 0; j <= t; ++j) o += sv.Bq[d][j] * u[j];
         a.y[(((size_t)b * T + d) * H + h) * DV + row] = o;
-        rp.ru[(size_t)wrap(sb0, t, Ls) * rp.vs + row] = v;  // stage the pseudo-value
+        if (!dual) rp.ru[(size_t)wrap(sb0, t, Ls) * rp.vs + row] = v;  // stage the pseudo-value
         if constexpr (RF != CF) str<R>(rp.rv + (size_t)wrap(sb0, t, Ls) * rp.vs + row, vrow[d]);
+      }
+    }
+    if constexpr (kLossy) {
+      if (dual) {  // c = 0 after a fold-first: the drafts are the whole window
+#pragma unroll
+        for (int t = 0; t < kMaxL; ++t) {
+          if (t < nrec) {
+            const float bt = sv.beta[t], et = __expf(sv.g[t]);
+            float v = bt * vrow[t] - bt * et * sv.WQ[lane][t];
+#pragma unroll
+            for (int j = 0; j < t; ++j) v -= sv.A[t][j] * u[j];
+            u[t] = v;
+            rp.ru[(size_t)wrap(sb0, t, Ls) * rp.vs + row] = v;
+          }
+        }
       }
     }
   }

@@ -73,6 +73,12 @@ extern "C" {
 #define REPLAY_STATUS_BAD_POINTERS 0x2   /* ckpt_pos < 0 or pos - ckpt_pos outside 0..L: sequence skipped */
 
 /*
+ * Every output is read from the state that includes its own token [P3,
+ * Interpretation 1].  Outputs of a step or verify that folds first come from
+ * the fold result (float32); all other outputs read the read copy plus the
+ * buffered records, so only they carry the read copy's rounding [P3,
+ * Perspective, paragraph 2].
+ *
  * Layer shape and options.
  *   kind        REPLAY_KIND_MAMBA2 or REPLAY_KIND_GDN.
  *   batch       sequences, >= 1.
@@ -87,9 +93,8 @@ extern "C" {
  *   ckpt_fmt    format of the checkpoint that carries the recurrence.
  *   read_fmt    format of the copy the outputs read; equal to ckpt_fmt
  *               means a single copy [P1, Interpretation 4; P3, Interpretation 3].
- *               Every output (also that of a step or verify that folds first)
- *               reads the read copy as it stands after the call's fold, plus
- *               the buffered records in float32; a fold starts from the
+ *               Outputs of calls that do not fold read the read copy plus the
+ *               buffered records in float32; a fold starts from the
  *               checkpoint, so the read copy's rounding never enters the
  *               recurrence.
  *   seed        key of the stochastic-rounding generator (Philox-4x32-10; the
@@ -242,11 +247,17 @@ size_t replay_abi_sizeof(int which);
 
 /* ---- the decode calls -------------------------------------------------- */
 
-/* Fill *ctx from cfg and buf, and enqueue: pos = ckpt_pos = 0 for every
- * sequence, status = 0.  The checkpoint buffer already holds the initial state
- * in ckpt_fmt; with an F32 checkpoint and a separate read copy, the read copy
- * is written from it here.  (For other formats load the state with
- * replay_set_state, or start from all-zero buffers.) */
+/* Set up one layer's state as the method holds it: a checkpoint plus a buffer
+ * of the inputs since it [P1, Synopsis; P2, paragraph 3], here with an empty
+ * buffer.  Fills *ctx from cfg and buf (both copied; buf's device buffers stay
+ * owned by the caller) and enqueues pos = ckpt_pos = 0 for every sequence and
+ * status = 0.  The checkpoint buffer already holds the initial state in
+ * ckpt_fmt; with an F32 checkpoint and a separate read copy (the split
+ * precision of [P1, Interpretation 4; P3, Interpretation 3]) the read copy is
+ * written from it here.  (For other formats load the state with
+ * replay_set_state, or start from all-zero buffers.)  REPLAY_EINVAL for a NULL
+ * or misaligned buffer, REPLAY_EINVAL / REPLAY_ENOTSUP for the configuration;
+ * *ctx is then left unusable. */
 int replay_init(replay_ctx *ctx, const replay_config *cfg, const replay_buffers *buf, void *stream);
 
 /* Replace the state of every sequence with the float32 `state`
@@ -265,10 +276,11 @@ int replay_set_state(replay_ctx *ctx, const float *state, void *stream);
 int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *stream);
 
 /* Fold every committed record of the sequences with seq_mask[b] != 0 (device
- * uint8 [batch]; NULL = all) into the checkpoint, which is rewritten only when
- * a window is folded [P2, paragraph 3; P3, Interpretation 2]: the call for a
- * caller that needs the state in the checkpoint alone before the window has
- * filled (e.g. to save it).  Sequences with an empty window are left unchanged.
+ * uint8 [batch]; NULL = all) into the checkpoint -- the fold a full buffer
+ * triggers [P2, paragraph 3; P3, Interpretation 2], here on demand: the call
+ * for a caller that needs the state in the checkpoint alone before the window
+ * has filled (e.g. to save it; copying the stored copies and the current
+ * pointers then saves the whole state).  Sequences with an empty window are left unchanged.
  * Drafts still pending from a verify are discarded, as by a step (the same as
  * commit of 0): a later commit finds none and clamps its counts to 0. */
 int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream);
@@ -280,9 +292,13 @@ int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream);
  * without writing any intermediate state. */
 int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float *y, void *stream);
 
-/* Accept the first accepted[b] drafts of each sequence (device int32 [batch]):
- * a pointer move only.  Values outside 0..T_pending are clamped and set
- * REPLAY_STATUS_ACCEPT_CLAMPED.  Rejected drafts are simply left behind. */
+/* Accept the first accepted[b] drafts of each sequence (device int32 [batch],
+ * read on the device: no host round trip): a pointer move only, since rolling
+ * back to the accepted prefix needs no state restore [P1, Interpretation 3;
+ * P3, Interpretation 3].  pos[b] += accepted[b]; values outside 0..T_pending
+ * (T_pending = the T of the last verify, 0 after any other call) are clamped
+ * and set REPLAY_STATUS_ACCEPT_CLAMPED.  Rejected drafts are simply left behind
+ * in the ring, to be overwritten. */
 int replay_commit(replay_ctx *ctx, const int32_t *accepted, void *stream);
 
 /* Device addresses of the current pos[batch] and ckpt_pos[batch] arrays (valid

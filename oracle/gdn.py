@@ -102,3 +102,13 @@ def fold(S0, recs):
         kj = np.asarray(r["k"], np.float64)
         S = S + np.exp(g[-1] - g[j])[:, None, None] * U[j][:, :, None] * kj[:, None, :]
     return S
+
+
+def output_scale(S, q):
+    """Size of the terms an output sums, per head: max_v (|S| |q|)_v.
+
+    One sequence after a token: S [H, dv, dk] the state the output reads,
+    q [H, dk].  See mamba2.output_scale.
+    """
+    return np.einsum("hvk,hk->hv", np.abs(np.asarray(S, np.float64)),
+                     np.abs(np.asarray(q, np.float64))).max(axis=-1)

@@ -124,3 +124,17 @@ def fold(S0, recs, A, skip_below=None):
         Bj = np.asarray(r["B"], np.float64)[g]
         S = S + coef[:, None, None] * xj[:, :, None] * Bj[:, None, :]
     return S
+
+
+def output_scale(S, C, D, x):
+    """Size of the terms an output sums, per head: max_p (|S| |C|)_p + |D| max_p |x_p|.
+
+    One sequence after a token: S [H, P, N] the state the output reads, C [G, N],
+    x [H, P].  A relative error of a head's output vector is measured against
+    the larger of this and the output itself (a head's output can cancel).
+    """
+    S = np.abs(np.asarray(S, np.float64))
+    H, G = S.shape[0], np.shape(C)[0]
+    Ch = np.abs(np.asarray(C, np.float64))[head_group(H, G)]
+    return (np.einsum("hpn,hn->hp", S, Ch).max(axis=-1)
+            + np.abs(np.asarray(D, np.float64)) * np.abs(np.asarray(x, np.float64)).max(axis=-1))

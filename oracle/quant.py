@@ -108,15 +108,23 @@ def e2m1_block_encode(x):
     blk = x.reshape(x.shape[:-1] + (n // 16, 16))
     amax = np.max(np.abs(blk), axis=-1)
     scode = e4m3_encode((amax / np.float32(6.0)).astype(np.float32))
-    s = e4m3_decode(scode).astype(np.float64)[..., None]
-    a = np.abs(blk).astype(np.float64)
+    codes = e2m1_codes_for_scale(blk, e4m3_decode(scode)).reshape(x.shape)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed, scode
+
+
+def e2m1_codes_for_scale(blk, s) -> np.ndarray:
+    """4-bit codes of the elements blk [..., 16] under the block scales s [...]
+    (decoded e4m3 values): |x| against the midpoints t s of the grid, ties to
+    the even code, clamped at 6 s; all zero where s == 0."""
+    s = np.asarray(s, np.float64)[..., None]
+    blk = np.asarray(blk, np.float64)
+    a = np.abs(blk)
     mag = np.select([a <= 0.25 * s, a < 0.75 * s, a <= 1.25 * s, a < 1.75 * s, a <= 2.5 * s, a < 3.5 * s,
                      a <= 5.0 * s], [0, 1, 2, 3, 4, 5, 6], default=7).astype(np.uint8)
     mag = np.where(s > 0, mag, 0).astype(np.uint8)
     sign = np.where((blk < 0) & (mag != 0), 8, 0).astype(np.uint8)
-    codes = (mag | sign).reshape(x.shape)
-    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
-    return packed, scode
+    return (mag | sign).astype(np.uint8)
 
 
 def e2m1_block_decode(packed, scales) -> np.ndarray:

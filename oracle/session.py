@@ -12,6 +12,10 @@ Both expose init-time state and the calls step / verify / commit / flush with
 the same argument shapes: a record is a dict of per-field arrays with a
 leading batch axis; drafts have axes [batch, T, ...]; outputs are
 [batch, H, head_dim] for a step and [batch, T, H, head_dim] for a verify.
+After a step or verify, ``scale`` ([batch, H] or [batch, T, H]) is the size
+of the terms each output vector sums (``mamba2.output_scale``,
+``gdn.output_scale``) for the state that output reads, the denominator floor
+of the parity tests' relative error.
 The pages state that replay outputs equal conventional decoding up to
 floating-point rounding [P2, paragraph 3; P3, Interpretation 2]; the tests
 check exactly that between the two classes.
@@ -54,25 +58,56 @@ class _Kind:
             return mamba2.fold(S0, recs, self.params["A"], skip_below)
         return gdn.fold(S0, recs)
 
+    def scale(self, S, r):
+        """Output term size for the state S after record r (one sequence)."""
+        if self.kind == "mamba2":
+            return mamba2.output_scale(S, r["C"], self.params["D"], r["x"])
+        return gdn.output_scale(S, r["q"])
+
+
+class _Scales:
+    """Lazily computed output scales: a list of (S0, window records) per output,
+    the state being the fold of the window into S0."""
+
+    def __init__(self, k, shape):
+        self.k, self.shape, self.items = k, shape, []
+
+    def add(self, S0, recs, skip_below=None):
+        self.items.append((S0, list(recs), skip_below))
+
+    def value(self):
+        out = [self.k.scale(self.k.fold(S0, recs, sk), recs[-1]) for S0, recs, sk in self.items]
+        return np.stack(out).reshape(self.shape + (-1,))
+
 
 class StepwiseSession:
     def __init__(self, kind: str, state0, params: dict | None = None):
         self.k = _Kind(kind, params or {})
         self.state = np.array(state0, np.float64)       # [batch, H, P, N]
         self.pending = None
+        self._outs = []                                 # (state, record) of each output of the last call
+
+    @property
+    def scale(self):
+        """Output term sizes of the last call ([batch, H] or [batch, T, H]), computed on demand."""
+        sc = [np.stack([self.k.scale(S[b], _rec_b(r, b)) for b in range(len(S))]) for S, r in self._outs]
+        return sc[0] if self._lead_T is None else np.stack(sc, axis=1)
 
     def step(self, rec):
         self.pending = None
         self.state, y = self.k.step(self.state, rec)
+        self._outs, self._lead_T = [(self.state, rec)], None
         return y
 
     def verify(self, drafts):
         T = next(iter(drafts.values())).shape[1]
         S = self.state.copy()
-        ys = []
+        ys, self._outs, self._lead_T = [], [], T
         for i in range(T):
-            S, y = self.k.step(S, {n: a[:, i] for n, a in drafts.items()})
+            r = {n: a[:, i] for n, a in drafts.items()}
+            S, y = self.k.step(S, r)
             ys.append(y)
+            self._outs.append((S, r))
         self.pending = drafts
         return np.stack(ys, axis=1)
 
@@ -98,6 +133,11 @@ class ReplaySession:
         self.ckpt = np.array(state0, np.float64)        # [batch, H, P, N]
         self.ptr = PointerMachine(self.ckpt.shape[0], window)
         self.recs = [dict() for _ in range(self.ckpt.shape[0])]   # position -> record
+        self._scales = None
+
+    @property
+    def scale(self):
+        return self._scales.value()
 
     @property
     def batch(self):
@@ -119,9 +159,12 @@ class ReplaySession:
         pos_before = self.ptr.pos.copy()
         self.ptr.step()
         ys = []
+        self._scales = _Scales(self.k, (self.batch,))
         for b in range(self.batch):
             self.recs[b][int(pos_before[b])] = _rec_b(rec, b)
-            ys.append(self.k.output(self.ckpt[b], self._window(b, int(self.ptr.pos[b])), self.skip))
+            win = self._window(b, int(self.ptr.pos[b]))
+            ys.append(self.k.output(self.ckpt[b], win, self.skip))
+            self._scales.add(self.ckpt[b], win, self.skip)
         return np.stack(ys)
 
     def verify(self, drafts):
@@ -131,14 +174,16 @@ class ReplaySession:
             self._fold(b)
         self.ptr.verify(T)
         out = []
+        self._scales = _Scales(self.k, (self.batch, T))
         for b in range(self.batch):
             p0 = int(self.ptr.pos[b])
             for i in range(T):
                 self.recs[b][p0 + i] = _draft_b(drafts, b, i)
             committed = self._window(b, p0)
-            out.append(np.stack([self.k.output(self.ckpt[b], committed + [self.recs[b][p0 + j] for j in range(i + 1)],
-                                               self.skip)
-                                 for i in range(T)]))
+            wins = [committed + [self.recs[b][p0 + j] for j in range(i + 1)] for i in range(T)]
+            out.append(np.stack([self.k.output(self.ckpt[b], w, self.skip) for w in wins]))
+            for w in wins:
+                self._scales.add(self.ckpt[b], w, self.skip)
         return np.stack(out)
 
     def commit(self, accepted):
@@ -242,10 +287,13 @@ class SplitReplaySession(ReplaySession):
         pos_before = self.ptr.pos.copy()
         self.ptr.step()
         ys = []
+        self._scales = _Scales(self.k, (self.batch,))
         for b in range(self.batch):
             self.recs[b][int(pos_before[b])] = _rec_b(rec, b)
             S0 = fresh[b] if b in fresh else self.read_state(b)
-            ys.append(self.k.output(S0, self._window(b, int(self.ptr.pos[b]))))
+            win = self._window(b, int(self.ptr.pos[b]))
+            ys.append(self.k.output(S0, win))
+            self._scales.add(S0, win)
         return np.stack(ys)
 
     def verify(self, drafts):
@@ -254,14 +302,17 @@ class SplitReplaySession(ReplaySession):
         fresh = {int(b): self._fold(b) for b in np.nonzero(will_fold)[0]}
         self.ptr.verify(T)
         out = []
+        self._scales = _Scales(self.k, (self.batch, T))
         for b in range(self.batch):
             p0 = int(self.ptr.pos[b])
             for i in range(T):
                 self.recs[b][p0 + i] = _draft_b(drafts, b, i)
             committed = self._window(b, p0)
             S0 = fresh[b] if b in fresh else self.read_state(b)
-            out.append(np.stack([self.k.output(S0, committed + [self.recs[b][p0 + j] for j in range(i + 1)])
-                                 for i in range(T)]))
+            wins = [committed + [self.recs[b][p0 + j] for j in range(i + 1)] for i in range(T)]
+            out.append(np.stack([self.k.output(S0, w) for w in wins]))
+            for w in wins:
+                self._scales.add(S0, w)
         return np.stack(out)
 
     def flush(self, mask=None):

@@ -49,12 +49,12 @@ def _spec_run(shape, seed, ops, T_max):
         op = rng.integers(4)
         if op == 0:
             r = ins.record()
-            worst = max(worst, max_rel_err(host(lay.step(to_dev(r, bf16=True))), ref.step(r)))
+            worst = max(worst, max_rel_err(host(lay.step(to_dev(r, bf16=True))), ref.step(r), ref.scale))
             pm.step()
         elif op in (1, 2):
             T = int(rng.integers(1, T_max + 1))
             d = ins.drafts(T)
-            worst = max(worst, max_rel_err(host(lay.verify(to_dev(d, bf16=True))), ref.verify(d)))
+            worst = max(worst, max_rel_err(host(lay.verify(to_dev(d, bf16=True))), ref.verify(d), ref.scale))
             pm.verify(T)
             acc = rng.integers(0, T + 1, size=shape.batch).astype(np.int32)
             if op == 2 and it % 3 == 0:
@@ -111,11 +111,11 @@ def test_baselines(kind):
     ref, ref2 = StepwiseSession(kind, S0, ins.params), StepwiseSession(kind, S0, ins.params)
     for _ in range(5):
         r = ins.record()
-        assert max_rel_err(host(conv.step(to_dev(r, bf16=True))), ref.step(r)) <= TOL
+        assert max_rel_err(host(conv.step(to_dev(r, bf16=True))), ref.step(r), ref.scale) <= TOL
     assert ckpt_rel_err(host(conv.state), ref.state) <= TOL
     for T in (8, 3, 5):
         d = ins.drafts(T)
-        assert max_rel_err(host(snap.verify(to_dev(d, bf16=True))), ref2.verify(d)) <= TOL
+        assert max_rel_err(host(snap.verify(to_dev(d, bf16=True))), ref2.verify(d), ref2.scale) <= TOL
         acc = ins.accepted(T)
         snap.commit(torch.from_numpy(acc).cuda())
         ref2.commit(acc)
@@ -141,13 +141,13 @@ def test_gdn_split_precision(cf, rf):
         if t in (6, 11):
             T = int(rng.integers(1, 4))
             d = ins.drafts(T)
-            e = max_rel_err(host(lay.verify(to_dev(d, bf16=True))), sess.verify(d))
+            e = max_rel_err(host(lay.verify(to_dev(d, bf16=True))), sess.verify(d), sess.scale)
             acc = ins.accepted(T)
             lay.commit(torch.from_numpy(acc).cuda())
             sess.commit(acc)
         else:
             r = ins.record()
-            e = max_rel_err(host(lay.step(to_dev(r, bf16=True))), sess.step(r))
+            e = max_rel_err(host(lay.step(to_dev(r, bf16=True))), sess.step(r), sess.scale)
         if t < shape.window:
             worst_pre = max(worst_pre, e)
         else:
@@ -174,10 +174,10 @@ def test_mamba2_full_size_sampled():
     for _ in range(20):
         r = ins.record()
         y = lay.step(to_dev(r, bf16=True))
-        worst = max(worst, max_rel_err(host(y[idx]), ref.step(take_batch(r, sample))))
+        worst = max(worst, max_rel_err(host(y[idx]), ref.step(take_batch(r, sample)), ref.scale))
     d = ins.drafts(8)
     y = lay.verify(to_dev(d, bf16=True))
-    worst = max(worst, max_rel_err(host(y[idx]), ref.verify(take_batch(d, sample))))
+    worst = max(worst, max_rel_err(host(y[idx]), ref.verify(take_batch(d, sample)), ref.scale))
     assert worst <= TOL, worst
 
 
@@ -204,13 +204,13 @@ def test_mamba2_with_decay_skip():
         if it % 7 == 6:
             T = int(rng.integers(1, 7))
             d = ins.drafts(T)
-            worst = max(worst, max_rel_err(host(lay.verify(to_dev(d, bf16=True))), skip.verify(d)))
+            worst = max(worst, max_rel_err(host(lay.verify(to_dev(d, bf16=True))), skip.verify(d), skip.scale))
             acc = ins.accepted(T)
             lay.commit(torch.from_numpy(acc).cuda())
             skip.commit(acc)
         else:
             r = ins.record()
-            worst = max(worst, max_rel_err(host(lay.step(to_dev(r, bf16=True))), skip.step(r)))
+            worst = max(worst, max_rel_err(host(lay.step(to_dev(r, bf16=True))), skip.step(r), skip.scale))
     lay.flush()
     skip.flush()
     assert worst <= TOL, worst

@@ -8,9 +8,10 @@
   beta = 0.  The outputs are then those of the checkpoint alone.
 * All-zero records from a zero state: outputs are exactly zero.
 * A long run (1024 steps, 64 folds): float32 rounding does not accumulate.
-* Corrupted pointer pairs (a negative count, a count above L) on a full window:
-  the step stores nothing at all (ring, checkpoint and output byte-identical),
-  leaves the pointers as they were and sets the status bit.
+* Corrupted pointer pairs (a negative count, a count above L, a negative pair)
+  on a full window: a step, verify or flush stores nothing at all (ring,
+  checkpoint and output byte-identical), leaves the pointers as they were and
+  sets the status bit.
 """
 import numpy as np
 import pytest
@@ -45,14 +46,14 @@ def _run(lay, ref, records, drafts_at=()):
             d = {n: np.stack([a, a], axis=1) for n, a in r.items()}   # two drafts: the record twice
             y = host(lay.verify(to_dev(d)))
             assert np.all(np.isfinite(y))
-            worst = max(worst, max_rel_err(y, ref.verify(d)))
+            worst = max(worst, max_rel_err(y, ref.verify(d), ref.scale))
             acc = np.full(lay.shapes.batch, 2, np.int32)
             lay.commit(torch.from_numpy(acc).cuda())
             ref.commit(acc)
         else:
             y = host(lay.step(to_dev(r)))
             assert np.all(np.isfinite(y))
-            worst = max(worst, max_rel_err(y, ref.step(r)))
+            worst = max(worst, max_rel_err(y, ref.step(r), ref.scale))
     assert worst <= TOL, worst
     lay.flush()
     assert ckpt_rel_err(host(lay.checkpoint), ref.state) <= TOL
@@ -151,41 +152,60 @@ def test_long_run_stays_at_float32_rounding(kind):
     for t in range(1024):
         if t % 50 == 49:
             d = ins.drafts(4)
-            worst = max(worst, max_rel_err(host(lay.verify(to_dev(d))), ref.verify(d)))
+            worst = max(worst, max_rel_err(host(lay.verify(to_dev(d))), ref.verify(d), ref.scale))
             acc = ins.accepted(4)
             lay.commit(torch.from_numpy(acc).cuda())
             ref.commit(acc)
         else:
             r = ins.record()
-            worst = max(worst, max_rel_err(host(lay.step(to_dev(r))), ref.step(r)))
+            worst = max(worst, max_rel_err(host(lay.step(to_dev(r))), ref.step(r), ref.scale))
     assert worst <= TOL, worst
     lay.flush()
     assert ckpt_rel_err(host(lay.checkpoint), ref.state) <= TOL
 
 
+@pytest.mark.parametrize("in_ring", [False, True])
+@pytest.mark.parametrize("call", ["step", "verify", "flush"])
 @pytest.mark.parametrize("kind", ["mamba2", "gdn"])
-def test_corrupted_pointers_store_nothing(kind):
+def test_corrupted_pointers_store_nothing(kind, call, in_ring):
+    """Three corrupted pointer pairs on a full window -- a negative count, a count
+    above L, and a negative pair whose count (2) is in range -- for a step, a
+    verify and a flush, with the records copied or in the ring: every sequence
+    is flagged and skipped, so nothing is stored (ring, checkpoint and output
+    byte-identical) and the pointers stay as they were."""
     import torch
 
     from _gpu import pointers_host
-    shape = LayerShape(kind, 2, 4, 32, 32, 2, 4) if kind == "mamba2" else LayerShape(kind, 2, 4, 64, 32, 4, 4)
-    announce("corrupted pointers", shape)
+    from hybrid_model_ssm_replay_amd import binding as B
+    from hybrid_model_ssm_replay_amd.layer import ReplayLayer
+    shape = LayerShape(kind, 3, 4, 32, 32, 2, 4) if kind == "mamba2" else LayerShape(kind, 3, 4, 64, 32, 4, 4)
+    announce("corrupted pointers", shape, call, "in_ring", in_ring)
     ins = InputStream(shape, 8)
     S0 = ins.initial_state(zeros=False, scale=0.3)
-    lay = _m2_layer(shape, ins.params["A"], ins.params["D"], S0) if kind == "mamba2" else _gdn_layer(shape, S0)
+    kw = dict(groups=shape.groups, A=ins.params["A"], D=ins.params["D"]) if kind == "mamba2" else {}
+    lay = ReplayLayer(kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
+                      max_draft=2, ckpt0=S0, flags=B.FLAG_RECORDS_IN_RING if in_ring else 0, **kw)
     for _ in range(shape.window):  # full windows: a good next step would fold
         lay.step(to_dev(ins.record()))
     pos, ck = lay.pointers()
-    pos[0] = ck[0] - 1                      # count -1
+    pos[0] = ck[0] - 1                      # count -1 (a negative pos here: ck is 0)
     pos[1] = ck[1] + shape.window + 1       # count L + 1
+    pos[2], ck[2] = -3, -5                  # count 2, both negative
     torch.cuda.synchronize()
     want_pos, want_ck = pointers_host(lay)
     ring0, ckpt0 = lay.ring.clone(), lay.ckpt.clone()
-    y = torch.full((shape.batch, shape.heads, shape.head_dim), 7.0, device="cuda")
-    lay.step(to_dev(ins.record()), y=y)
+    if call == "step":
+        y = torch.full((shape.batch, shape.heads, shape.head_dim), 7.0, device="cuda")
+        lay.step(to_dev(ins.record()), y=y)
+    elif call == "verify":
+        y = torch.full((shape.batch, 2, shape.heads, shape.head_dim), 7.0, device="cuda")
+        lay.verify(to_dev(ins.drafts(2)), y=y)
+    else:
+        y = None
+        lay.flush()
     torch.cuda.synchronize()
     got_pos, got_ck = pointers_host(lay)
     assert lay.status & 0x2
     assert np.array_equal(got_pos, want_pos) and np.array_equal(got_ck, want_ck)
     assert torch.equal(lay.ring, ring0) and torch.equal(lay.ckpt, ckpt0)
-    assert torch.all(y == 7.0)
+    assert y is None or torch.all(y == 7.0)

@@ -34,7 +34,7 @@ def _run_steps(shape, seed, steps, zero_state=True):
     for t in range(steps):
         r = ins.record()
         y = host(lay.step(to_dev(r)))
-        worst = max(worst, max_rel_err(y, ref.step(r)))
+        worst = max(worst, max_rel_err(y, ref.step(r), ref.scale))
         rep.step(r)
         pos, ck = pointers_host(lay)
         assert np.array_equal(pos, rep.ptr.pos) and np.array_equal(ck, rep.ptr.ckpt_pos), t
@@ -67,19 +67,34 @@ def _spec_run(shape, seed, ops, T_max):
     pm = PointerMachine(shape.batch, shape.window)
     rng = np.random.default_rng(seed)
     for it in range(ops):
-        op = rng.integers(4)
+        op = rng.integers(5)
         if op == 0:
             r = ins.record()
-            assert max_rel_err(host(lay.step(to_dev(r))), ref.step(r)) <= TOL, it
+            assert max_rel_err(host(lay.step(to_dev(r))), ref.step(r), ref.scale) <= TOL, it
             pm.step()
         elif op in (1, 2):
             T = int(rng.integers(1, T_max + 1))
             d = ins.drafts(T)
-            assert max_rel_err(host(lay.verify(to_dev(d))), ref.verify(d)) <= TOL, it
+            assert max_rel_err(host(lay.verify(to_dev(d))), ref.verify(d), ref.scale) <= TOL, it
             pm.verify(T)
             acc = rng.integers(0, T + 1, size=shape.batch).astype(np.int32)
             if op == 2 and it % 3 == 0:
                 acc[-1] = -1                             # out of range: clamped to 0, status bit
+            lay.commit(torch.from_numpy(acc).cuda())
+            ref.commit(acc)
+            pm.commit(acc)
+        elif op == 4:
+            # verify -> flush -> commit: the flush discards the pending drafts, so the
+            # commit advances nothing (and flags the counts it clamps)
+            T = int(rng.integers(1, T_max + 1))
+            d = ins.drafts(T)
+            assert max_rel_err(host(lay.verify(to_dev(d))), ref.verify(d), ref.scale) <= TOL, it
+            pm.verify(T)
+            mask = rng.integers(0, 2, size=shape.batch).astype(np.uint8)
+            lay.flush(torch.from_numpy(mask).cuda())
+            ref.flush(mask)
+            pm.flush(mask.astype(bool))
+            acc = rng.integers(0, T + 1, size=shape.batch).astype(np.int32)
             lay.commit(torch.from_numpy(acc).cuda())
             ref.commit(acc)
             pm.commit(acc)
@@ -118,7 +133,7 @@ def test_full_size_sampled():
     for t in range(2 * shape.window + 3):
         r = ins.record()
         y = lay.step(to_dev(r))
-        worst = max(worst, max_rel_err(host(y[torch.from_numpy(sample).cuda()]), ref.step(take_batch(r, sample))))
+        worst = max(worst, max_rel_err(host(y[torch.from_numpy(sample).cuda()]), ref.step(take_batch(r, sample)), ref.scale))
     pos, ck = pointers_host(lay)
     assert np.all(pos == 2 * shape.window + 3) and np.all(ck == 2 * shape.window)
     assert worst <= TOL, worst
@@ -141,7 +156,7 @@ def test_full_size_verify_sampled():
         d = ins.drafts(T)
         y = lay.verify(to_dev(d))
         pm.verify(T)
-        worst = max(worst, max_rel_err(host(y[torch.from_numpy(sample).cuda()]), ref.verify(take_batch(d, sample))))
+        worst = max(worst, max_rel_err(host(y[torch.from_numpy(sample).cuda()]), ref.verify(take_batch(d, sample)), ref.scale))
         acc = ins.accepted(T)
         lay.commit(torch.from_numpy(acc).cuda())
         pm.commit(acc)
@@ -164,11 +179,11 @@ def test_conventional_and_snapshot_baselines():
     ref2 = StepwiseSession("gdn", S0)
     for _ in range(5):
         r = ins.record()
-        assert max_rel_err(host(conv.step(to_dev(r))), ref.step(r)) <= TOL
+        assert max_rel_err(host(conv.step(to_dev(r))), ref.step(r), ref.scale) <= TOL
     assert ckpt_rel_err(host(conv.state), ref.state) <= TOL
     for T in (8, 2, 5):
         d = ins.drafts(T)
-        assert max_rel_err(host(snap.verify(to_dev(d))), ref2.verify(d)) <= TOL
+        assert max_rel_err(host(snap.verify(to_dev(d))), ref2.verify(d), ref2.scale) <= TOL
         acc = ins.accepted(T)
         snap.commit(torch.from_numpy(acc).cuda())
         ref2.commit(acc)
@@ -188,7 +203,7 @@ def test_snapshot_baseline_large_lds():
     ref = StepwiseSession("gdn", S0)
     for T in (16, 9):
         d = ins.drafts(T)
-        assert max_rel_err(host(snap.verify(to_dev(d))), ref.verify(d)) <= TOL
+        assert max_rel_err(host(snap.verify(to_dev(d))), ref.verify(d), ref.scale) <= TOL
         acc = ins.accepted(T)
         snap.commit(torch.from_numpy(acc).cuda())
         ref.commit(acc)

@@ -126,13 +126,13 @@ def test_steps_and_folds_match_oracle(cf, rf):
         if t in (9, 13):
             T = int(rng.integers(1, 4))
             d = ins.drafts(T)
-            e = max_rel_err(host(lay.verify(to_dev(d))), sess.verify(d))
+            e = max_rel_err(host(lay.verify(to_dev(d))), sess.verify(d), sess.scale)
             acc = ins.accepted(T)
             lay.commit(torch.from_numpy(acc).cuda())
             sess.commit(acc)
         else:
             r = ins.record()
-            e = max_rel_err(host(lay.step(to_dev(r))), sess.step(r))
+            e = max_rel_err(host(lay.step(to_dev(r))), sess.step(r), sess.scale)
         if t < shape.window:
             worst_pre = max(worst_pre, e)
         else:
@@ -165,7 +165,7 @@ def test_speculative_with_many_drafts(cf, rf):
         if rng.random() < 0.5:
             T = int(rng.integers(1, 13))
             d = ins.drafts(T)
-            e = max_rel_err(host(lay.verify(to_dev(d))), sess.verify(d))
+            e = max_rel_err(host(lay.verify(to_dev(d))), sess.verify(d), sess.scale)
             pm.verify(T)
             acc = ins.accepted(T)
             lay.commit(torch.from_numpy(acc).cuda())
@@ -173,7 +173,7 @@ def test_speculative_with_many_drafts(cf, rf):
             pm.commit(acc)
         else:
             r = ins.record()
-            e = max_rel_err(host(lay.step(to_dev(r))), sess.step(r))
+            e = max_rel_err(host(lay.step(to_dev(r))), sess.step(r), sess.scale)
             pm.step()
         folded = folded or bool(np.any(pm.ckpt_pos > 0))
         if folded:
@@ -262,14 +262,14 @@ def test_full_size_sampled(cf, rf):
     for t in range(24):
         r = ins.record()
         y = lay.step(to_dev(r))
-        e = max_rel_err(host(y[idx]), sess.step(take_batch(r, sample)))
+        e = max_rel_err(host(y[idx]), sess.step(take_batch(r, sample)), sess.scale)
         if t < shape.window:
             worst_pre = max(worst_pre, e)
         else:
             worst_post = max(worst_post, e)
     d = ins.drafts(4)
     y = lay.verify(to_dev(d))
-    worst_post = max(worst_post, max_rel_err(host(y[idx]), sess.verify(take_batch(d, sample))))
+    worst_post = max(worst_post, max_rel_err(host(y[idx]), sess.verify(take_batch(d, sample)), sess.scale))
     print(f"[split full] cf={cf} rf={rf} pre-fold {worst_pre:.2e} post-fold {worst_post:.2e}")
     assert worst_pre <= 1e-4, worst_pre
     assert worst_post <= POST_FOLD_TOL[rf], worst_post
@@ -299,7 +299,7 @@ def test_explicit_flush_matches_oracle(cf, rf):
             folded = True
             continue
         r = ins.record()
-        e = max_rel_err(host(lay.step(to_dev(r))), sess.step(r))
+        e = max_rel_err(host(lay.step(to_dev(r))), sess.step(r), sess.scale)
         if folded:
             worst_post = max(worst_post, e)
         else:
@@ -309,3 +309,142 @@ def test_explicit_flush_matches_oracle(cf, rf):
     assert worst_pre <= 1e-4, worst_pre
     assert flips <= 1e-3, flips
     assert worst_post <= POST_FOLD_TOL[rf], worst_post
+
+
+# ---- the fold step, the first fold's codes and the bound they give ----------------------
+def _bounds_for(sess, kind, params, dQ, lead_T=None):
+    """Per-output bounds [batch, (T,) H, P] from read-copy differences dQ[b] (None:
+    the sequence reads the same bytes as the oracle, or outputs from a fresh fold)."""
+    from _split_check import output_bound, query_weights
+    out = []
+    for b in range(sess.batch):
+        pos, ck = int(sess.ptr.pos[b]), int(sess.ptr.ckpt_pos[b])
+        wins = ([[sess.recs[b][p] for p in range(ck, pos + i + 1)] for i in range(lead_T)] if lead_T
+                else [[sess.recs[b][p] for p in range(ck, pos)]])
+        bs = [np.zeros_like(dQ[0][..., 0]) if dQ[b] is None else output_bound(dQ[b], query_weights(kind, w, params))
+              for w in wins]
+        out.append(np.stack(bs) if lead_T else bs[0])
+    return np.stack(out)
+
+
+def _read_copy_dq(lay, sess, shape, cf, rf, folded):
+    """Check both stored copies of the sequences in `folded` (just folded, from
+    the same inputs on both sides) and return the read-copy differences."""
+    from _split_check import check_copy, gpu_parts
+    hpn = (shape.heads, shape.head_dim, shape.state_dim)
+    ck, rd = lay.stored_copies()
+    R = gpu_parts(host(ck), cf, shape.batch, hpn)
+    Q = R if rd is None else gpu_parts(host(rd), rf, shape.batch, hpn)
+    dQ = []
+    for b in range(shape.batch):
+        if b not in folded:
+            dQ.append(None)
+            continue
+        S = sess.last_fold[b]
+        ckpt = int(sess.ptr.ckpt_pos[b])
+        check_copy(R[b], cf, S, SEED, b, ckpt)
+        q_gpu = check_copy(Q[b], rf, S, SEED, b, ckpt)
+        dQ.append(q_gpu - sess.read_state(b))
+    return dQ
+
+
+@pytest.mark.parametrize("cf,rf", PAIRS)
+def test_fold_outputs_come_from_the_fold_result(cf, rf):
+    """A step or verify that folds outputs from its float32 fold result, not from
+    the re-encoded copy [P3, Perspective, paragraph 2].  At the first fold both
+    sides fold the same stored bytes, so those outputs meet the float32 bar."""
+    import torch
+    shape = LayerShape("gdn", 2, 3, 128, 128, 3, 4)
+    announce("split fold outputs", shape, cf, rf)
+    for via_verify in (False, True):
+        ins = InputStream(shape, 31)
+        S0 = ins.initial_state(zeros=False, scale=0.3)
+        lay = _layer(shape, cf, rf, S0, max_draft=3)
+        sess = SplitReplaySession("gdn", S0, shape.window, None, cf, rf, seed=SEED)
+        n_pre = shape.window - 1 if via_verify else shape.window
+        for t in range(n_pre):
+            r = ins.record()
+            assert max_rel_err(host(lay.step(to_dev(r))), sess.step(r), sess.scale) <= 1e-4, t
+        if via_verify:
+            d = ins.drafts(3)                            # count 3 + 3 > 4: fold first
+            e = max_rel_err(host(lay.verify(to_dev(d))), sess.verify(d), sess.scale)
+        else:
+            r = ins.record()                             # count 4: fold first
+            e = max_rel_err(host(lay.step(to_dev(r))), sess.step(r), sess.scale)
+        print(f"[split fold output] cf={cf} rf={rf} via_verify={via_verify} err {e:.2e}")
+        assert e <= 1e-4, e
+
+
+@pytest.mark.parametrize("cf,rf", PAIRS)
+def test_first_fold_codes_and_window_outputs(cf, rf):
+    """After the first fold every stored code of both copies is the encoding of a
+    value within float32 rounding of the oracle's fold result (tests/_split_check.py),
+    and each later output of that window is within 1e-4 of the oracle's once the
+    effect of the accepted code differences, sum |dQ| |z|, is allowed for."""
+    from _split_check import bounded_rel_err
+    shape = LayerShape("gdn", 2, 3, 128, 128, 3, 4)
+    announce("split first fold", shape, cf, rf)
+    ins = InputStream(shape, 32)
+    S0 = ins.initial_state(zeros=False, scale=0.3)
+    lay = _layer(shape, cf, rf, S0)
+    sess = SplitReplaySession("gdn", S0, shape.window, None, cf, rf, seed=SEED)
+    for t in range(shape.window + 1):                   # the last one folds first
+        r = ins.record()
+        assert max_rel_err(host(lay.step(to_dev(r))), sess.step(r), sess.scale) <= 1e-4, t
+    dQ = _read_copy_dq(lay, sess, shape, cf, rf, folded=set(range(shape.batch)))
+    worst, moved = 0.0, 0.0
+    for t in range(shape.window - 1):
+        r = ins.record()
+        y = host(lay.step(to_dev(r)))
+        ref = sess.step(r)
+        bound = _bounds_for(sess, "gdn", None, dQ)
+        worst = max(worst, bounded_rel_err(y, ref, sess.scale, bound))
+        moved = max(moved, max_rel_err(y, ref, sess.scale))
+    print(f"[split first fold] cf={cf} rf={rf} raw {moved:.2e} beyond the code bound {worst:.2e}")
+    assert worst <= 1e-4, worst
+
+
+@pytest.mark.parametrize("cf,rf", PAIRS)
+def test_verify_flush_commit_step_verify(cf, rf):
+    """verify -> flush -> commit -> step -> verify: the flush folds the committed
+    records (the first fold here) and discards the pending drafts, so the commit
+    clamps its counts; later outputs are checked as in the test above."""
+    import torch
+    from _split_check import bounded_rel_err
+    shape = LayerShape("gdn", 2, 3, 128, 128, 3, 4)
+    announce("split verify-flush-commit", shape, cf, rf)
+    ins = InputStream(shape, 33)
+    S0 = ins.initial_state(zeros=False, scale=0.3)
+    lay = _layer(shape, cf, rf, S0, max_draft=3)
+    sess = SplitReplaySession("gdn", S0, shape.window, None, cf, rf, seed=SEED)
+    for t in range(3):
+        r = ins.record()
+        assert max_rel_err(host(lay.step(to_dev(r))), sess.step(r), sess.scale) <= 1e-4
+    d = ins.drafts(1)
+    assert max_rel_err(host(lay.verify(to_dev(d))), sess.verify(d), sess.scale) <= 1e-4
+    mask = np.array([1, 0], np.uint8)
+    lay.flush(torch.from_numpy(mask).cuda())
+    sess.flush(mask.astype(bool))
+    acc = np.array([1, 1], np.int32)
+    lay.commit(torch.from_numpy(acc).cuda())
+    sess.commit(acc)
+    assert lay.t_pending == 0 and lay.status == 0x1   # clamped: nothing was pending
+    pos, ck = (host(t) for t in lay.pointers())
+    assert list(pos) == [3, 3] and list(ck) == [3, 0]
+    dQ = _read_copy_dq(lay, sess, shape, cf, rf, folded={0})
+    r = ins.record()                                  # sequence 0 reads its new copy; sequence 1 folds no more
+    y = host(lay.step(to_dev(r)))
+    ref = sess.step(r)
+    e1 = bounded_rel_err(y, ref, sess.scale, _bounds_for(sess, "gdn", None, dQ))
+    d = ins.drafts(2)                                 # sequence 1: count 4 + 2 > 4, folds first
+    y = host(lay.verify(to_dev(d)))
+    ref = sess.verify(d)
+    dq_v = [dQ[0], None]                              # sequence 1 outputs from its fresh fold
+    e2 = bounded_rel_err(y, ref, sess.scale, _bounds_for(sess, "gdn", None, dq_v, lead_T=2))
+    print(f"[split vfc] cf={cf} rf={rf} step {e1:.2e} verify {e2:.2e}")
+    assert e1 <= 1e-4 and e2 <= 1e-4, (e1, e2)
+    acc = np.array([2, 1], np.int32)
+    lay.commit(torch.from_numpy(acc).cuda())
+    sess.commit(acc)
+    pos, ck = (host(t) for t in lay.pointers())
+    assert np.array_equal(pos, sess.ptr.pos) and np.array_equal(ck, sess.ptr.ckpt_pos)

@@ -72,14 +72,14 @@ def _spec_run(shape, seed, ops, T_max, bf16=False):
             r = ins.record()
             dr = to_dev(r, bf16)
             _produce(lay, dr)
-            worst = max(worst, max_rel_err(host(lay.step(dr)), ref.step(r)))
+            worst = max(worst, max_rel_err(host(lay.step(dr)), ref.step(r), ref.scale))
             pm.step()
         elif op in (1, 2):
             T = int(rng.integers(1, T_max + 1))
             d = ins.drafts(T)
             dd = to_dev(d, bf16)
             _produce(lay, dd)
-            worst = max(worst, max_rel_err(host(lay.verify(dd)), ref.verify(d)))
+            worst = max(worst, max_rel_err(host(lay.verify(dd)), ref.verify(d), ref.scale))
             pm.verify(T)
             acc = rng.integers(0, T + 1, size=shape.batch).astype(np.int32)
             if op == 2 and it % 3 == 0:
@@ -143,7 +143,7 @@ def test_gdn_split_precision():
             d = ins.drafts(T)
             dd = to_dev(d)
             _produce(lay, dd)
-            e = max_rel_err(host(lay.verify(dd)), sess.verify(d))
+            e = max_rel_err(host(lay.verify(dd)), sess.verify(d), sess.scale)
             acc = ins.accepted(T)
             lay.commit(torch.from_numpy(acc).cuda())
             sess.commit(acc)
@@ -151,7 +151,7 @@ def test_gdn_split_precision():
             r = ins.record()
             dr = to_dev(r)
             _produce(lay, dr)
-            e = max_rel_err(host(lay.step(dr)), sess.step(r))
+            e = max_rel_err(host(lay.step(dr)), sess.step(r), sess.scale)
         if t < shape.window:
             worst_pre = max(worst_pre, e)
         else:
@@ -185,7 +185,7 @@ def test_mamba2_with_decay_skip():
             d = ins.drafts(T)
             dd = to_dev(d)
             _produce(lay, dd)
-            worst = max(worst, max_rel_err(host(lay.verify(dd)), skip.verify(d)))
+            worst = max(worst, max_rel_err(host(lay.verify(dd)), skip.verify(d), skip.scale))
             acc = ins.accepted(T)
             lay.commit(torch.from_numpy(acc).cuda())
             skip.commit(acc)
@@ -193,7 +193,7 @@ def test_mamba2_with_decay_skip():
             r = ins.record()
             dr = to_dev(r)
             _produce(lay, dr)
-            worst = max(worst, max_rel_err(host(lay.step(dr)), skip.step(r)))
+            worst = max(worst, max_rel_err(host(lay.step(dr)), skip.step(r), skip.scale))
     lay.flush()
     skip.flush()
     assert worst <= TOL, worst

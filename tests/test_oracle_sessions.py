@@ -79,3 +79,28 @@ def test_commit_then_continue_equals_stepping_accepted(kind):
             ref.state[b], _ = ref.k.step(ref.state[b], {n: x[b, i] for n, x in d.items()})
     np.testing.assert_allclose(y_rep, ref.step(r1), rtol=1e-9, atol=1e-11)
     assert list(rep.ptr.pos) == [2, 3, 5, 6]
+
+
+def test_output_scale_bounds_the_output():
+    """The output scale is the sum of the terms' magnitudes: it bounds |y| for any
+    signs (triangle inequality) and equals it when every term is non-negative."""
+    from oracle import gdn, mamba2
+    rng = np.random.default_rng(2)
+    H, G, P, N = 4, 2, 8, 16
+    S, C, x = rng.standard_normal((H, P, N)), rng.standard_normal((G, N)), rng.standard_normal((H, P))
+    D = rng.standard_normal(H)
+    g = mamba2.head_group(H, G)
+    y = np.einsum("hpn,hn->hp", S, C[g]) + D[:, None] * x
+    assert np.all(mamba2.output_scale(S, C, D, x) >= np.abs(y).max(-1) - 1e-12)
+    Sp, Cp, xp, Dp = np.abs(S), np.abs(C), np.abs(x), np.abs(D)
+    yp = np.einsum("hpn,hn->hp", Sp, Cp[g]) + Dp[:, None] * xp
+    # equal when the largest row of |S||C| also holds the largest |x| (make x constant per head)
+    xc = np.ones_like(xp)
+    yc = np.einsum("hpn,hn->hp", Sp, Cp[g]) + Dp[:, None] * xc
+    np.testing.assert_allclose(mamba2.output_scale(Sp, Cp, Dp, xc), yc.max(-1), rtol=1e-14)
+    assert np.all(mamba2.output_scale(Sp, Cp, Dp, xp) >= yp.max(-1) - 1e-12)
+    Sg, q = rng.standard_normal((H, P, N)), rng.standard_normal((H, N))
+    o = np.einsum("hvk,hk->hv", Sg, q)
+    assert np.all(gdn.output_scale(Sg, q) >= np.abs(o).max(-1) - 1e-12)
+    np.testing.assert_allclose(gdn.output_scale(np.abs(Sg), np.abs(q)),
+                               np.einsum("hvk,hk->hv", np.abs(Sg), np.abs(q)).max(-1), rtol=1e-14)
