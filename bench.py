@@ -231,32 +231,37 @@ def bench_sweeps(torch, steps=64, warmup=16):
 
 
 SPLIT_PAIRS = ((0, 0), (0, 3), (1, 3), (2, 3), (3, 3), (0, 4), (1, 4))
+M2_SPLIT_PAIRS = ((0, 0), (0, 3), (1, 3), (2, 3), (3, 3), (1, 1), (2, 2))
 FMT_NAMES = {0: "f32", 1: "f16sr", 2: "e4m3", 3: "e2m1", 4: "e2m1cs"}
 
 
-def bench_split(torch, seed=5, layers=8, steps=64, warmup=32, flags=0, pairs=None):
-    """Split-precision Gated DeltaNet layer (32 heads, d = 128, L = 16, batch 64).
+def bench_split(torch, seed=5, layers=8, steps=64, warmup=32, flags=0, pairs=None, name="gdn_b64_h32_d128_l16"):
+    """Split-precision layer, by default Gated DeltaNet (32 heads, d = 128, L = 16,
+    batch 64); also the Mamba-2 layer with the 4 MiB float32 state at batch 256.
 
     `layers` independent layer instances are stepped in rotation, so that the
-    state is not served from the 256 MB Infinity Cache; reported per format pair
-    (checkpoint / read copy): microseconds per layer step and algorithmic GB/s
-    from the format-aware byte model.  (The accuracy of the same pairs against
-    the float64 oracle over 32768 steps is a GPU test, tests/test_gpu_split.py.)
+    stored copies are not served from the 256 MB Infinity Cache; reported per
+    format pair (checkpoint / read copy): microseconds per layer step (whole
+    windows) and algorithmic GB/s from the format-aware byte model.  (The
+    accuracy of the same pairs against the float64 oracle is a GPU test,
+    tests/test_gpu_split.py.)
     """
     from hybrid_model_ssm_replay_amd.layer import ReplayLayer
     from hybrid_model_ssm_replay_amd.traffic import Layer, split_window_mean
     from synth import WORKLOADS, InputStream
-    name = "gdn_b64_h32_d128_l16"
     shape = WORKLOADS[name]
-    lm = Layer("gdn", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.groups, shape.window,
+    lm = Layer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.groups, shape.window,
                2 if _bf16(flags) else 4)
-    recs = dev_records(torch, InputStream(shape, seed, bf16_vectors=_bf16(flags)), 16, _bf16(flags))
+    ins = InputStream(shape, seed, bf16_vectors=_bf16(flags))
+    recs = dev_records(torch, ins, 16, _bf16(flags))
+    kw = dict(A=ins.params["A"], D=ins.params["D"]) if shape.kind == "mamba2" else {}
     y = torch.empty((shape.batch, shape.heads, shape.head_dim), device="cuda")
     out = {"workload": name, "layers_rotated": layers, "pairs": {}}
     tm = Timer(torch)
     for cf, rf in pairs or SPLIT_PAIRS:
-        lays = [ReplayLayer("gdn", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
-                            ckpt_fmt=cf, read_fmt=rf, seed=seed, flags=flags) for _ in range(layers)]
+        lays = [ReplayLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
+                            groups=shape.groups, ckpt_fmt=cf, read_fmt=rf, seed=seed, flags=flags, **kw)
+                for _ in range(layers)]
         tm.run(lambda i: lays[i % layers].step(recs[(i // layers) % 16], y), warmup * layers)
         us = tm.run(lambda i: lays[i % layers].step(recs[(i // layers) % 16], y), steps * layers)
         rd, wr = split_window_mean(lm, cf, rf)
@@ -468,8 +473,8 @@ def cpu_baseline(shape, seed, budget_s=12.0):
 
 
 # Extras after the headline measurement, in run order.
-SECTIONS = ("conv", "skip", "verify", "gdn", "gdn_verify", "split", "split_error", "read_error", "bf16", "zero_copy",
-            "sweeps")
+SECTIONS = ("conv", "skip", "verify", "gdn", "gdn_verify", "split", "m2_split", "split_error", "read_error", "bf16",
+            "zero_copy", "sweeps")
 
 
 def main(argv=None):
@@ -579,6 +584,13 @@ def main(argv=None):
     if want("split"):
         log("split precision")
         extra["gdn_split_b64"] = bench_split(torch)
+    if want("m2_split"):
+        log("split precision, Mamba-2 batch 256")
+        extra["mamba2_split_b256"] = bench_split(torch, seed=1, layers=4, steps=32, warmup=16,
+                                                 pairs=M2_SPLIT_PAIRS, name="mamba2_b256_h128_p64_n128_g8_l16")
+        base = extra.get("replay_step_us")
+        for v in extra["mamba2_split_b256"]["pairs"].values():
+            v["speedup_vs_f32_replay_step"] = base / v["us_per_step"]
     if want("split_error"):
         log("split-precision error growth")
         extra["split_error_growth_b64"] = bench_split_error_growth(torch)

@@ -221,10 +221,10 @@ struct GdnSnapArgs {
   float *y;
 };
 
-// Stored copies of the GDN state: the checkpoint that carries the recurrence
+// Stored copies of a layer's state: the checkpoint that carries the recurrence
 // (ckpt_fmt) and the copy non-fold steps read (read_fmt; the same storage when
 // the formats are equal).  e2m1 copies keep their scales after the codes.
-struct GdnFormatBufs {
+struct FormatBufs {
   int ckpt_fmt, read_fmt;
   void *ckpt;
   uint8_t *ckpt_scales;
@@ -234,9 +234,9 @@ struct GdnFormatBufs {
   uint64_t seed;
 };
 
-struct GdnEncodeArgs {
+struct EncodeArgs {
   Shape s;
-  const float *src;         // [B][H][dv][dk] float32 state
+  const float *src;         // [B][H][P][N] float32 state (GDN: P = d_v, N = d_k)
   const int32_t *ckpt_pos;  // current ckpt_pos[B] (stochastic-rounding counter)
   int write_ckpt;           // 0: write only the read copy
 };
@@ -257,16 +257,16 @@ inline size_t state_bytes(int fmt, size_t n, size_t ncols) {
 }
 
 // Launchers (return a hipError_t value).
-int launch_gdn_step(const GdnStepArgs &a, const GdnFormatBufs &f, hipStream_t st);
-int launch_gdn_verify(const GdnVerifyArgs &a, const GdnFormatBufs &f, hipStream_t st);
-int launch_gdn_flush(const GdnFlushArgs &a, const GdnFormatBufs &f, hipStream_t st);
-int launch_gdn_encode(const GdnEncodeArgs &a, const GdnFormatBufs &f, hipStream_t st);
+int launch_gdn_step(const GdnStepArgs &a, const FormatBufs &f, hipStream_t st);
+int launch_gdn_verify(const GdnVerifyArgs &a, const FormatBufs &f, hipStream_t st);
+int launch_gdn_flush(const GdnFlushArgs &a, const FormatBufs &f, hipStream_t st);
+int launch_encode_state(const EncodeArgs &a, const FormatBufs &f, hipStream_t st);
 int launch_gdn_conv(const GdnConvArgs &a, hipStream_t st);
 int launch_gdn_snapshot(const GdnSnapArgs &a, hipStream_t st);
 int launch_record_slots(const int32_t *pos, int batch, int slots, int32_t *out, hipStream_t st);
-int launch_m2_step(const M2StepArgs &a, hipStream_t st);
-int launch_m2_verify(const M2VerifyArgs &a, hipStream_t st);
-int launch_m2_flush(const M2FlushArgs &a, hipStream_t st);
+int launch_m2_step(const M2StepArgs &a, const FormatBufs &f, hipStream_t st);
+int launch_m2_verify(const M2VerifyArgs &a, const FormatBufs &f, hipStream_t st);
+int launch_m2_flush(const M2FlushArgs &a, const FormatBufs &f, hipStream_t st);
 int launch_m2_conv(const M2ConvArgs &a, hipStream_t st);
 int launch_m2_snapshot(const M2SnapArgs &a, hipStream_t st);
 

@@ -13,9 +13,12 @@
 //
 // Kernel template parameters besides the tile shape: R, the element type of the
 // record vector fields and their ring copies (float, or bf16_t with bf16
-// records), SKIP (the decay skip below) and, for the step, ZC (zero-copy
-// append: the caller wrote this token's x, B, dt into their ring slots, and the
-// ring fields have 2L slots).
+// records), SKIP (the decay skip below), for the step ZC (zero-copy append: the
+// caller wrote this token's x, B, dt into their ring slots, and the ring fields
+// have 2L slots), and CF, RF, the formats of the checkpoint and of the read
+// copy (state_io.h; float32 both by default).  With a low-precision read copy
+// the column map of the register tile is contiguous per lane (colq), and the
+// MFMA row index M of chunk c stands for column mcol(c, M).
 //
 // Replay identities (derived from the Mamba-2 decode recurrence
 // S <- exp(dt A) S + dt x B^T, y = S C + D x by unrolling the window; the
@@ -26,7 +29,7 @@
 // where s_{a..b} is the sum of dt over records a..b.  Decays are formed from
 // these segment sums directly (never as ratios of cumulative decays, which
 // underflow for fast-decaying heads).
-#include "internal.h"
+#include "state_io.h"
 
 namespace rssm {
 namespace {
@@ -108,7 +111,7 @@ __device__ __forceinline__ float suffix_sum16(float v, int lane, float *total) {
 // Fold the cnt (1..L) committed records at positions base .. base+cnt-1 into
 // the register tile: s <- exp(A s_{1..cnt}) s + sum_r exp(A s_{r+1..cnt}) dt_r x_r B_r^T.
 // Ends with a barrier; sm.Bs is free again afterwards.
-template <int NCH, int RBW, bool SKIP, typename R>
+template <int NCH, int RBW, bool SKIP, typename R, int CM = kColIlv>
 __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm, int cnt, int base,
                                           float Ah, const R *rx, const float *rdt, const R *rB,
                                           int L, int Ls, size_t xs, const TileCtx &t) {
@@ -144,7 +147,7 @@ __device__ __forceinline__ void fold_tile(float4 (&s)[RBW][NCH], M2Smem<NCH> &sm
       floatx4 acc = {s[k][c].x * scale, s[k][c].y * scale, s[k][c].z * scale, s[k][c].w * scale};
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        if (st < nsteps) acc = mfma_16x16x4(sm.Bs[4 * st + t.q][16 * c + t.r16], xb[st], acc);
+        if (st < nsteps) acc = mfma_16x16x4(sm.Bs[4 * st + t.q][mcol<NCH, CM>(c, t.r16)], xb[st], acc);
       }
       s[k][c] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
@@ -174,12 +177,12 @@ template <int NCH, int RBW>
 struct FoldIn {
   float f;             // lanes 0..15: exp(A s_{r+1..cnt}) dt_r for record r = lane
   float scale;         // exp(A s_{1..cnt})
-  float aB[NCH][4];    // MFMA A operand: B_{4 st + q}[16 c + r16]
+  float aB[NCH][4];    // MFMA A operand: B_{4 st + q}[mcol(c, r16)]
   float xraw[4][RBW];  // x_{4 st + q}[row of block k]
   int nsteps;          // ceil(cnt / 4)
 };
 
-template <int NCH, int RBW, typename R>
+template <int NCH, int RBW, typename R, int CM = kColIlv>
 __device__ __forceinline__ void fold_load(FoldIn<NCH, RBW> &fi, int cnt, int s0, int s0b, const R *rx,
                                           const float *rdt, const R *rB, int L, int Ls, size_t xs, int rb0,
                                           int lane) {
@@ -196,7 +199,7 @@ __device__ __forceinline__ void fold_load(FoldIn<NCH, RBW> &fi, int cnt, int s0,
     const R *Br = rB + wrap(s0b, rc, 2 * L) * (16 * NCH);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const float v = ldr<R>(Br + 16 * c + r16);
+      const float v = ldr<R>(Br + mcol<NCH, CM>(c, r16));
       fi.aB[c][st] = r < cnt ? v : 0.f;
     }
     const R *xr = rx + wrap(s0, rc, Ls) * xs;
@@ -270,7 +273,7 @@ __device__ __forceinline__ float pick(const float (&acc)[RBW], int sel) {
 // region), bdot (the lane's partial B_{r16} . C), dtv (dt of record `lane`,
 // lanes 0..15), xr[st][k] (x of record 4 st + q at row block k).  Returns the
 // finished output of row 16 (rb0 + q) + r16 (lanes with q < RBW).
-template <int NCH, int RBW, bool SKIP, typename R>
+template <int NCH, int RBW, bool SKIP, typename R, int CM = kColIlv>
 __device__ __forceinline__ float replay_output(const float4 (&s)[RBW][NCH], const R *Cs, float bdot, float dtv,
                                                const float (&xr)[4][RBW], int m, float Ah, int lane) {
   const int q = lane >> 4;
@@ -284,7 +287,7 @@ __device__ __forceinline__ float replay_output(const float4 (&s)[RBW][NCH], cons
   for (int k = 0; k < RBW; ++k) {
     float v = 0.f;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) v += dot4(s[k][c], ldr4<R>(Cs + 16 * c + 4 * q));
+    for (int c = 0; c < NCH; ++c) v += dot4(s[k][c], ldr4<R>(Cs + colq<NCH, CM>(c, q)));
     v *= scale;
 #pragma unroll
     for (int st = 0; st < 4; ++st) v += __shfl(w, 4 * st + q, kWave) * xr[st][k];
@@ -313,14 +316,22 @@ constexpr int step_lds_wave() { return step_lds_row<NCH, R>() * (kMaxL + 1); }
 // Occupancy target: four waves per SIMD (at most 128 VGPRs) for the copying
 // step.  The zero-copy variants get no target: their ring-slot addressing
 // would then spill to scratch.
-template <bool ZC>
-constexpr int step_waves_per_eu() { return ZC ? 1 : 4; }
+// Low-precision copies: no target either (their codecs need the registers).
+template <bool ZC, int CF = REPLAY_FMT_F32, int RF = REPLAY_FMT_F32>
+constexpr int step_waves_per_eu() { return (ZC || CF != REPLAY_FMT_F32 || RF != REPLAY_FMT_F32) ? 1 : 4; }
 
-template <int NCH, int RBW, bool SKIP, typename R, bool ZC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(step_waves_per_eu<ZC>())))
-void m2_replay_step(M2StepArgs a) {
+// With low-precision copies (CF, RF not both F32) the step reads the read copy
+// and decodes it in registers; a fold decodes the checkpoint, folds in float32,
+// stores both copies and outputs from the float32 fold result (only the steps
+// that do not fold read the approximate copy [P3, Perspective, paragraph 2]).
+template <int NCH, int RBW, bool SKIP, typename R, bool ZC, int CF = REPLAY_FMT_F32, int RF = REPLAY_FMT_F32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(step_waves_per_eu<ZC, CF, RF>())))
+void m2_replay_step(M2StepArgs a, StateBufs sb) {
   constexpr int N = 16 * NCH;
   constexpr int kRow = step_lds_row<NCH, R>();
+  constexpr bool kF32 = CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32;
+  constexpr int CM = col_map(CF, RF);
+  static_assert(kF32 || (!SKIP && !ZC), "low-precision copies: no decay skip, no zero-copy append");
   extern __shared__ __align__(16) unsigned char m2_step_lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r16 = lane & 15;
@@ -335,7 +346,8 @@ void m2_replay_step(M2StepArgs a) {
   R *Cs = reinterpret_cast<R *>(wl);                             // this token's C
   unsigned char *Bs = wl + kRow;                                 // row j: B of window record j
   auto Brow = [&](int j) { return reinterpret_cast<R *>(Bs + j * kRow); };
-  float *S = a.ckpt + ((size_t)b * sh.H + h) * P * N;
+  const size_t head = ((size_t)b * sh.H + h) * P * N;  // element offset of the head's state
+  float *S = a.ckpt + head;
   const size_t xs = (size_t)sh.B * sh.H * P;  // x-ring slot stride (slot-major ring)
   R *rx = static_cast<R *>(a.ring.x) + ((size_t)b * sh.H + h) * P;
   float *rdt = a.ring.dt + ((size_t)b * sh.H + h) * Ls;
@@ -352,7 +364,9 @@ void m2_replay_step(M2StepArgs a) {
   //    With the decay skip the checkpoint stream waits for the decision, which
   //    needs the pointers and the head's dt ring row.
   float4 s[RBW][NCH];
-  if constexpr (!SKIP) load_rows<NCH, RBW>(s, S, rb0, lane);
+  typename SIO<RF, NCH, RBW, CM>::Raw raw;  // low-precision copies: the read copy's stored bits
+  if constexpr (!kF32) SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
+  else if constexpr (!SKIP) load_rows<NCH, RBW>(s, S, rb0, lane);
   const int pos_raw = a.ptr.pos_in[b], ck_raw = a.ptr.ckpt_in[b];
   float dt_in = zc ? 0.f : a.dt[(size_t)b * sh.H + h];
   const float Ah = a.A[h], Dh = a.D[h];
@@ -426,11 +440,12 @@ void m2_replay_step(M2StepArgs a) {
       for (int c = 0; c < NCH; ++c) bdot += dot4(ldr4<R>(Bj + 16 * c + 4 * q), ldr4<R>(Cs + 16 * c + 4 * q));
     }
     bdot = r16 < m ? bdot : 0.f;
+    if constexpr (!kF32) SIO<RF, NCH, RBW, CM>::decode(s, raw);
   } else {
     // Fold the full window into the checkpoint, store it, and start the next
     // window with this token as its only record.
     FoldIn<NCH, RBW> fi;
-    fold_load<NCH, RBW, R>(fi, L, s0, s0b, rx, rdt, rB, L, Ls, xs, rb0, lane);
+    fold_load<NCH, RBW, R, CM>(fi, L, s0, s0b, rx, rdt, rB, L, Ls, xs, rb0, lane);
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
       const float v = ldr<R>(xin + (rb0 + k) * 16 + r16);
@@ -438,10 +453,20 @@ void m2_replay_step(M2StepArgs a) {
       for (int st = 0; st < 4; ++st) xr[st][k] = (st == 0 && q == 0) ? v : 0.f;
     }
     dtv = lane == 0 ? dt_in : 0.f;
+    if constexpr (!kF32) {
+      if constexpr (CF == RF) {
+        SIO<RF, NCH, RBW, CM>::decode(s, raw);
+      } else {
+        typename SIO<CF, NCH, RBW, CM>::Raw rc;
+        SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
+        SIO<CF, NCH, RBW, CM>::decode(s, rc);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0);  // this token's C (global-to-LDS) has landed
     wave_lds_sync();
     fold_apply<NCH, RBW, SKIP>(s, fi, Ah, lane);
-    store_rows<NCH, RBW>(s, S, rb0, lane);
+    if constexpr (kF32) store_rows<NCH, RBW>(s, S, rb0, lane);
+    else store_copies<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
     // This token's B . C after the fold: computing it earlier keeps more
     // registers live across the fold.
@@ -450,7 +475,7 @@ void m2_replay_step(M2StepArgs a) {
     bdot = r16 == 0 ? bdot : 0.f;
   }
   const int m = pos - base + 1;
-  const float out = replay_output<NCH, RBW, SKIP, R>(s, Cs, bdot, dtv, xr, m, Ah, lane);
+  const float out = replay_output<NCH, RBW, SKIP, R, CM>(s, Cs, bdot, dtv, xr, m, Ah, lane);
 
   // 4. Append this token's record (unless the producer wrote it into the ring).
   //    After a fold the dt slot being written held a record that the other
@@ -482,9 +507,12 @@ void m2_replay_step(M2StepArgs a) {
 }
 
 // ---- explicit flush ---------------------------------------------------------
-template <int NCH, int RBW, bool SKIP, typename R>
-__global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
+template <int NCH, int RBW, bool SKIP, typename R, int CF = REPLAY_FMT_F32, int RF = REPLAY_FMT_F32>
+__global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a, StateBufs sb) {
   constexpr int N = 16 * NCH;
+  constexpr bool kF32 = CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32;
+  constexpr int CM = col_map(CF, RF);
+  static_assert(kF32 || !SKIP, "low-precision copies: no decay skip");
   __shared__ M2Smem<NCH> sm;
   const TileCtx t = tile_ctx();
   const Shape &sh = a.s;
@@ -502,7 +530,8 @@ __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
     a.ptr.ckpt_out[b] = fold ? pos : ck;
   }
   if (!fold) return;
-  float *S = a.ckpt + ((size_t)b * sh.H + h) * P * N;
+  const size_t head = ((size_t)b * sh.H + h) * P * N;
+  float *S = a.ckpt + head;
   const size_t xs = (size_t)sh.B * sh.H * P;
   const R *rx = static_cast<const R *>(a.ring.x) + ((size_t)b * sh.H + h) * P;
   const float *rdt = a.ring.dt + ((size_t)b * sh.H + h) * sh.Ls;
@@ -513,7 +542,11 @@ __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
     const float d = rdt[(ck + (t.r16 < count ? t.r16 : 0)) % sh.Ls];
     keep = !(a.A[h] * sum16(t.r16 < count ? d : 0.f) < kDecaySkipLog);
   }
-  if (keep) {
+  if constexpr (!kF32) {
+    typename SIO<CF, NCH, RBW, CM>::Raw rc;
+    SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, t.wave * RBW, t.lane);
+    SIO<CF, NCH, RBW, CM>::decode(s, rc);
+  } else if (keep) {
     load_tile<NCH, RBW>(s, S, t);
   } else {
 #pragma unroll
@@ -521,8 +554,9 @@ __global__ __launch_bounds__(256) void m2_flush(M2FlushArgs a) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) s[k][c] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  fold_tile<NCH, RBW, SKIP, R>(s, sm, count, ck, a.A[h], rx, rdt, rB, L, sh.Ls, xs, t);
-  store_tile<NCH, RBW>(s, S, t);
+  fold_tile<NCH, RBW, SKIP, R, CM>(s, sm, count, ck, a.A[h], rx, rdt, rB, L, sh.Ls, xs, t);
+  if constexpr (kF32) store_tile<NCH, RBW>(s, S, t);
+  else store_copies<CF, RF, NCH, RBW>(s, sb, head, t.wave * RBW, t.lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
 }
 
 // ---- speculative verify -------------------------------------------------
@@ -552,12 +586,15 @@ __device__ __forceinline__ floatx4 mfma_4x4x1(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
 
-template <int NCH, int RBW, bool SKIP, typename R>
-__global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
+template <int NCH, int RBW, bool SKIP, typename R, int CF = REPLAY_FMT_F32, int RF = REPLAY_FMT_F32>
+__global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a, StateBufs stb) {
   constexpr int N = 16 * NCH;
   constexpr int kPass = kMaxL / 4;
-  __shared__ float4 ldsB[NCH][64];          // [chunk cc][r + 16 q]: B_r[16 cc + 4 q .. + 3]
-  __shared__ float4 ldsC[kPass * NCH * 16];  // [(p NCH + cc) 16 + 4 m + q]: C_{4 p + m}[16 cc + 4 q .. + 3]
+  constexpr bool kF32 = CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32;
+  constexpr int CM = col_map(CF, RF);
+  static_assert(kF32 || !SKIP, "low-precision copies: no decay skip");
+  __shared__ float4 ldsB[NCH][64];          // [chunk cc][r + 16 q]: B_r[colq(cc, q) .. + 3]
+  __shared__ float4 ldsC[kPass * NCH * 16];  // [(p NCH + cc) 16 + 4 m + q]: C_{4 p + m}[colq(cc, q) .. + 3]
   __shared__ float dots_all[4][kMaxL][4];    // per wave: [record][draft of the pass] B_r . C_n
   // Per wave: x of draft i at the wave's rows (16 RBW elements of type R), for
   // the D x term; from LDS, the passes issue no global load, which would wait
@@ -573,7 +610,8 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   const int P = sh.P, L = sh.L, H = sh.H, G = sh.G, Ls = sh.Ls;
   const int rb0 = wave * RBW;
   const bool zc = a.in_ring;  // the drafts' x, B, dt are already in their ring slots
-  float *S = a.ckpt + ((size_t)b * H + h) * P * N;
+  const size_t head = ((size_t)b * H + h) * P * N;
+  float *S = a.ckpt + head;
   const size_t xs = (size_t)sh.B * H * P;
   R *rx = static_cast<R *>(a.ring.x) + ((size_t)b * H + h) * P;
   float *rdt = a.ring.dt + ((size_t)b * H + h) * Ls;
@@ -591,7 +629,9 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   //    The pointer words are read before any global-to-LDS load: the compiler
   //    keeps loads that follow such a load off the scalar unit.
   float4 s[RBW][NCH];
-  load_rows<NCH, RBW>(s, S, rb0, lane);
+  typename SIO<RF, NCH, RBW, CM>::Raw raw;  // low-precision copies: the read copy's stored bits
+  if constexpr (kF32) load_rows<NCH, RBW>(s, S, rb0, lane);
+  else SIO<RF, NCH, RBW, CM>::load(raw, stb.rd, head, rb0, lane);
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
   const float Ah = a.A[h], Dh = a.D[h];
   {
@@ -601,7 +641,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
       const int q2 = slot & 3, m2 = (slot >> 2) & 3, pc = slot >> 4;  // pc = p NCH + cc
       const int p2 = pc / NCH, cc = pc - p2 * NCH;
       const int n = 4 * p2 + m2;
-      stage4<R>(draft_C(n < T ? n : T - 1) + 16 * cc + 4 * q2, &ldsC[64 * j], lane);
+      stage4<R>(draft_C(n < T ? n : T - 1) + colq<NCH, CM>(cc, q2), &ldsC[64 * j], lane);
     }
   }
 
@@ -620,10 +660,22 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   int base = ck;
   if (fold) {
     FoldIn<NCH, RBW> fi;
-    fold_load<NCH, RBW, R>(fi, count, fmod_(ck, sh.fLs), fmod_(ck, sh.f2L), rx, rdt, rB, L, Ls, xs, rb0, lane);
+    fold_load<NCH, RBW, R, CM>(fi, count, fmod_(ck, sh.fLs), fmod_(ck, sh.f2L), rx, rdt, rB, L, Ls, xs, rb0, lane);
+    if constexpr (!kF32) {  // the drafts' outputs then come from the float32 fold result
+      if constexpr (CF == RF) {
+        SIO<RF, NCH, RBW, CM>::decode(s, raw);
+      } else {
+        typename SIO<CF, NCH, RBW, CM>::Raw rc;
+        SIO<CF, NCH, RBW, CM>::load(rc, stb.ck, head, rb0, lane);
+        SIO<CF, NCH, RBW, CM>::decode(s, rc);
+      }
+    }
     fold_apply<NCH, RBW, SKIP>(s, fi, Ah, lane);
-    store_rows<NCH, RBW>(s, S, rb0, lane);
+    if constexpr (kF32) store_rows<NCH, RBW>(s, S, rb0, lane);
+    else store_copies<CF, RF, NCH, RBW>(s, stb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
+  } else if constexpr (!kF32) {
+    SIO<RF, NCH, RBW, CM>::decode(s, raw);
   }
   c = pos - base;          // committed records in the window
   const int nrec = c + T;  // <= L
@@ -636,7 +688,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
   {
     const int rc = r16 < nrec ? r16 : nrec - 1;
     const R *Br = rc < c ? rB + (size_t)wrap(sbb, rc, 2 * L) * N : draft_B(rc - c);
-    for (int cc = wave; cc < NCH; cc += nwaves) stage4<R>(Br + 16 * cc + 4 * q, &ldsB[cc][0], lane);
+    for (int cc = wave; cc < NCH; cc += nwaves) stage4<R>(Br + colq<NCH, CM>(cc, q), &ldsB[cc][0], lane);
   }
   float xa[RBW][4];
 #pragma unroll
@@ -752,7 +804,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a) {
     if (lane >= c && lane < nrec) rdt[wrap(sb, lane, Ls)] = dtl;
     if (h - g * (H / G) == 0 && r16 >= c && r16 < nrec) {
 #pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) str4<R>(rB + (size_t)wrap(sbb, r16, 2 * L) * N + 16 * cc + 4 * q, ldsB[cc][lane]);
+      for (int cc = 0; cc < NCH; ++cc) str4<R>(rB + (size_t)wrap(sbb, r16, 2 * L) * N + colq<NCH, CM>(cc, q), ldsB[cc][lane]);
     }
   }
   if (h == 0 && threadIdx.x == 0) {
@@ -914,53 +966,94 @@ int dispatch(const Args &a, int N, int P, int B, int H, bool wave_per_head, hipS
   return (int)hipErrorInvalidValue;
 }
 
-// Kernel wrappers over the record element type (float32, or bf16 records).
-#define RSSM_WRAP(name, kern)                     \
-  template <typename R>                           \
-  struct name {                                   \
-    template <int NCH, int RBW>                   \
-    struct K {                                    \
-      static constexpr auto fn = kern<NCH, RBW, R>; \
-    };                                            \
-  };
-#define RSSM_WRAP_SKIP(name, kern, SKIP_)                \
-  template <typename R>                                  \
-  struct name {                                          \
-    template <int NCH, int RBW>                          \
-    struct K {                                           \
-      static constexpr auto fn = kern<NCH, RBW, SKIP_, R>; \
-    };                                                   \
-  };
-RSSM_WRAP_SKIP(FlushK, m2_flush, false)
-RSSM_WRAP_SKIP(FlushSkipK, m2_flush, true)
-RSSM_WRAP_SKIP(VerifyK, m2_replay_verify, false)
-RSSM_WRAP_SKIP(VerifySkipK, m2_replay_verify, true)
-RSSM_WRAP(ConvK, m2_conv_step)
-#undef RSSM_WRAP_SKIP
-#undef RSSM_WRAP
+// Format pairs (checkpoint, read copy) with low-precision copies: N = 128 only.
+#define RSSM_M2_FMT_PAIRS(X)                      \
+  X(REPLAY_FMT_F32, REPLAY_FMT_F4E2M1_B16)        \
+  X(REPLAY_FMT_F16_SR, REPLAY_FMT_F4E2M1_B16)     \
+  X(REPLAY_FMT_F8E4M3, REPLAY_FMT_F4E2M1_B16)     \
+  X(REPLAY_FMT_F4E2M1_B16, REPLAY_FMT_F4E2M1_B16) \
+  X(REPLAY_FMT_F16_SR, REPLAY_FMT_F16_SR)         \
+  X(REPLAY_FMT_F8E4M3, REPLAY_FMT_F8E4M3)
 
-// The step kernel takes step_lds_wave bytes of dynamic LDS per wave.
-template <bool SKIP, typename R, bool ZC>
-int launch_step_r(const M2StepArgs &a, hipStream_t st) {
+// Kernels that take the stored copies: K<CF, RF, NCH, RBW>::fn with
+// K<...>::lds(waves) bytes of dynamic LDS.  LP: the low-precision pairs are
+// instantiated too (the decay skip and zero-copy append are float32-only).
+template <template <int, int, int, int> class K, bool LP, typename Args>
+int dispatch_fmt(const Args &a, const StateBufs &sb, int cf, int rf, bool wave_per_head, hipStream_t st) {
   int waves, rbw;
-  if (!tile_geometry(a.s.P, true, &waves, &rbw)) return (int)hipErrorInvalidValue;
+  if (!tile_geometry(a.s.P, wave_per_head, &waves, &rbw)) return (int)hipErrorInvalidValue;
   const dim3 grid((unsigned)((size_t)a.s.B * a.s.H)), block(64 * waves);
-#define RSSM_CASE(NCH_, RBW_)                                                                    \
-  if (a.s.N == 16 * NCH_ && rbw == RBW_) {                                                       \
-    const size_t lds = (size_t)waves * step_lds_wave<NCH_, R>();                                \
-    hipLaunchKernelGGL((m2_replay_step<NCH_, RBW_, SKIP, R, ZC>), grid, block, lds, st, a);      \
-    return (int)hipGetLastError();                                                               \
+  const int N = a.s.N;
+#define RSSM_CASE(CF_, RF_, NCH_, RBW_)                                                                  \
+  if (cf == CF_ && rf == RF_ && N == 16 * NCH_ && rbw == RBW_) {                                        \
+    const size_t lds = K<CF_, RF_, NCH_, RBW_>::lds(waves);                                             \
+    hipLaunchKernelGGL((K<CF_, RF_, NCH_, RBW_>::fn), grid, block, lds, st, a, sb);                     \
+    return (int)hipGetLastError();                                                                      \
   }
-#define RSSM_NCH(RBW_) RSSM_CASE(1, RBW_) RSSM_CASE(2, RBW_) RSSM_CASE(4, RBW_) RSSM_CASE(8, RBW_)
+#define RSSM_NCH(RBW_)                               \
+  RSSM_CASE(REPLAY_FMT_F32, REPLAY_FMT_F32, 1, RBW_) \
+  RSSM_CASE(REPLAY_FMT_F32, REPLAY_FMT_F32, 2, RBW_) \
+  RSSM_CASE(REPLAY_FMT_F32, REPLAY_FMT_F32, 4, RBW_) \
+  RSSM_CASE(REPLAY_FMT_F32, REPLAY_FMT_F32, 8, RBW_)
   RSSM_NCH(1) RSSM_NCH(2)
+  if constexpr (LP) {
+#define RSSM_Q(CF_, RF_) RSSM_CASE(CF_, RF_, 8, 1) RSSM_CASE(CF_, RF_, 8, 2)
+    RSSM_M2_FMT_PAIRS(RSSM_Q)
+#undef RSSM_Q
+  }
 #undef RSSM_NCH
 #undef RSSM_CASE
   return (int)hipErrorInvalidValue;
 }
 
-template <bool SKIP, bool ZC>
-int launch_step(const M2StepArgs &a, hipStream_t st) {
-  return a.bf16 ? launch_step_r<SKIP, bf16_t, ZC>(a, st) : launch_step_r<SKIP, float, ZC>(a, st);
+// Kernel wrappers.  The step kernel takes step_lds_wave bytes of dynamic LDS per wave.
+template <bool SKIP, typename R, bool ZC>
+struct StepK {
+  template <int CF, int RF, int NCH, int RBW>
+  struct K {
+    static constexpr auto fn = m2_replay_step<NCH, RBW, SKIP, R, ZC, CF, RF>;
+    static size_t lds(int waves) { return (size_t)waves * step_lds_wave<NCH, R>(); }
+  };
+};
+template <bool SKIP, typename R>
+struct FlushK {
+  template <int CF, int RF, int NCH, int RBW>
+  struct K {
+    static constexpr auto fn = m2_flush<NCH, RBW, SKIP, R, CF, RF>;
+    static size_t lds(int) { return 0; }
+  };
+};
+template <bool SKIP, typename R>
+struct VerifyK {
+  template <int CF, int RF, int NCH, int RBW>
+  struct K {
+    static constexpr auto fn = m2_replay_verify<NCH, RBW, SKIP, R, CF, RF>;
+    static size_t lds(int) { return 0; }
+  };
+};
+#define RSSM_WRAP(name, kern)                       \
+  template <typename R>                             \
+  struct name {                                     \
+    template <int NCH, int RBW>                     \
+    struct K {                                      \
+      static constexpr auto fn = kern<NCH, RBW, R>; \
+    };                                              \
+  };
+RSSM_WRAP(ConvK, m2_conv_step)
+#undef RSSM_WRAP
+
+// The step by the record element type, the decay skip and zero-copy append.
+template <bool SKIP, bool ZC, typename Args>
+int launch_step_sz(const Args &a, const StateBufs &sb, int cf, int rf, hipStream_t st) {
+  constexpr bool LP = !SKIP && !ZC;
+  return a.bf16 ? dispatch_fmt<StepK<SKIP, bf16_t, ZC>::template K, LP>(a, sb, cf, rf, true, st)
+                : dispatch_fmt<StepK<SKIP, float, ZC>::template K, LP>(a, sb, cf, rf, true, st);
+}
+// Flush or verify (W) by the record element type and the decay skip.
+template <template <bool, typename> class W, bool SKIP, typename Args>
+int launch_fmt(const Args &a, const StateBufs &sb, int cf, int rf, bool wave_per_head, hipStream_t st) {
+  return a.bf16 ? dispatch_fmt<W<SKIP, bf16_t>::template K, !SKIP>(a, sb, cf, rf, wave_per_head, st)
+                : dispatch_fmt<W<SKIP, float>::template K, !SKIP>(a, sb, cf, rf, wave_per_head, st);
 }
 
 // Launch W<float>::K or W<bf16_t>::K by the record element type.
@@ -972,15 +1065,23 @@ int dispatch_rec(const Args &a, bool wave_per_head, hipStream_t st) {
 
 }  // namespace
 
-int launch_m2_step(const M2StepArgs &a, hipStream_t st) {
-  if (a.decay_skip) return a.in_ring ? launch_step<true, true>(a, st) : launch_step<true, false>(a, st);
-  return a.in_ring ? launch_step<false, true>(a, st) : launch_step<false, false>(a, st);
+int launch_m2_step(const M2StepArgs &a, const FormatBufs &f, hipStream_t st) {
+  const StateBufs sb = state_bufs(f);
+  if (a.decay_skip)
+    return a.in_ring ? launch_step_sz<true, true>(a, sb, f.ckpt_fmt, f.read_fmt, st)
+                     : launch_step_sz<true, false>(a, sb, f.ckpt_fmt, f.read_fmt, st);
+  return a.in_ring ? launch_step_sz<false, true>(a, sb, f.ckpt_fmt, f.read_fmt, st)
+                   : launch_step_sz<false, false>(a, sb, f.ckpt_fmt, f.read_fmt, st);
 }
-int launch_m2_flush(const M2FlushArgs &a, hipStream_t st) {
-  return a.decay_skip ? dispatch_rec<FlushSkipK>(a, false, st) : dispatch_rec<FlushK>(a, false, st);
+int launch_m2_flush(const M2FlushArgs &a, const FormatBufs &f, hipStream_t st) {
+  const StateBufs sb = state_bufs(f);
+  return a.decay_skip ? launch_fmt<FlushK, true>(a, sb, f.ckpt_fmt, f.read_fmt, false, st)
+                      : launch_fmt<FlushK, false>(a, sb, f.ckpt_fmt, f.read_fmt, false, st);
 }
-int launch_m2_verify(const M2VerifyArgs &a, hipStream_t st) {
-  return a.decay_skip ? dispatch_rec<VerifySkipK>(a, true, st) : dispatch_rec<VerifyK>(a, true, st);
+int launch_m2_verify(const M2VerifyArgs &a, const FormatBufs &f, hipStream_t st) {
+  const StateBufs sb = state_bufs(f);
+  return a.decay_skip ? launch_fmt<VerifyK, true>(a, sb, f.ckpt_fmt, f.read_fmt, true, st)
+                      : launch_fmt<VerifyK, false>(a, sb, f.ckpt_fmt, f.read_fmt, true, st);
 }
 int launch_m2_conv(const M2ConvArgs &a, hipStream_t st) { return dispatch_rec<ConvK>(a, true, st); }
 // The snapshot baseline takes T snap_lds_draft bytes of dynamic LDS per wave.

@@ -37,14 +37,22 @@ int check_cfg(const replay_config *c) {
   if (c->ckpt_fmt < REPLAY_FMT_F32 || c->ckpt_fmt > REPLAY_FMT_F4E2M1_CS) return REPLAY_EINVAL;
   if (c->read_fmt < REPLAY_FMT_F32 || c->read_fmt > REPLAY_FMT_F4E2M1_CS) return REPLAY_EINVAL;
   if (c->ckpt_fmt == REPLAY_FMT_F32 && c->read_fmt == REPLAY_FMT_F32) return REPLAY_OK;
-  // Low-precision copies: Gated DeltaNet with d_k = 128; the read copy is e2m1
-  // (split precision) or the checkpoint itself (one shared copy); an f32 read
-  // copy next to a lower-precision checkpoint is not a supported pair.
-  if (c->kind != REPLAY_KIND_GDN || c->state_dim != 128) return REPLAY_ENOTSUP;
+  // Low-precision copies: state_dim 128 (Mamba-2 also head_dim 64 or 128); the
+  // read copy is e2m1 (split precision) or the checkpoint itself (one shared
+  // copy); an f32 read copy next to a lower-precision checkpoint is not a
+  // supported pair.
+  if (c->state_dim != 128) return REPLAY_ENOTSUP;
   if (c->read_fmt != c->ckpt_fmt && c->read_fmt != REPLAY_FMT_F4E2M1_B16 && c->read_fmt != REPLAY_FMT_F4E2M1_CS)
     return REPLAY_ENOTSUP;
   // The two-axis copy is a read copy only: it never carries the recurrence.
   if (c->ckpt_fmt == REPLAY_FMT_F4E2M1_CS) return REPLAY_ENOTSUP;
+  if (c->kind == REPLAY_KIND_MAMBA2) {
+    // Mamba-2: block-scaled e2m1 read copy only (the two-axis encoder is the
+    // GDN tile's), and no decay skip or zero-copy append with low precision.
+    if (c->head_dim != 64 && c->head_dim != 128) return REPLAY_ENOTSUP;
+    if (c->read_fmt == REPLAY_FMT_F4E2M1_CS) return REPLAY_ENOTSUP;
+    if (c->flags & (REPLAY_FLAG_DECAY_SKIP | REPLAY_FLAG_RECORDS_IN_RING)) return REPLAY_ENOTSUP;
+  }
   return REPLAY_OK;
 }
 
@@ -77,10 +85,10 @@ GdnRing gdn_ring(const replay_ctx &ctx) {
                  (float *)(base + lay.off[3]), gdn_refold(ctx.cfg) ? (float *)(base + lay.off[4]) : nullptr};
 }
 
-GdnFormatBufs gdn_formats(const replay_ctx &ctx) {
+FormatBufs formats(const replay_ctx &ctx) {
   const replay_config &c = ctx.cfg;
   const size_t n = state_elems(c);
-  GdnFormatBufs f{};
+  FormatBufs f{};
   f.ckpt_fmt = c.ckpt_fmt;
   f.read_fmt = c.read_fmt;
   f.seed = c.seed;
@@ -177,14 +185,14 @@ int replay_init(replay_ctx *ctx, const replay_config *cfg, const replay_buffers 
   ctx->t_pending = 0;
   int e = launch_init_pointers(buf->pointers, (int)replay_pointer_words(cfg), buf->status, (hipStream_t)stream);
   if (e) return REPLAY_EHIP;
-  if (cfg->kind == REPLAY_KIND_GDN && cfg->ckpt_fmt == REPLAY_FMT_F32 && cfg->read_fmt != REPLAY_FMT_F32) {
+  if (cfg->ckpt_fmt == REPLAY_FMT_F32 && cfg->read_fmt != REPLAY_FMT_F32) {
     // The read copy starts as the encoding of the initial float32 checkpoint.
-    GdnEncodeArgs a{};
+    EncodeArgs a{};
     a.s = shape_of(*cfg);
     a.src = (const float *)buf->ckpt;
     a.ckpt_pos = buf->pointers;  // half 0: all zero after the init kernel
     a.write_ckpt = 0;
-    e = launch_gdn_encode(a, gdn_formats(*ctx), (hipStream_t)stream);
+    e = launch_encode_state(a, formats(*ctx), (hipStream_t)stream);
     if (e) return REPLAY_EHIP;
   }
   ctx->magic = kCtxMagic;
@@ -194,17 +202,17 @@ int replay_init(replay_ctx *ctx, const replay_config *cfg, const replay_buffers 
 int replay_set_state(replay_ctx *ctx, const float *state, void *stream) {
   if (check_ctx(ctx) != REPLAY_OK || !state || !aligned16(state)) return REPLAY_EINVAL;
   const replay_config &c = ctx->cfg;
-  if (c.kind == REPLAY_KIND_MAMBA2) {
+  if (c.kind == REPLAY_KIND_MAMBA2 && c.ckpt_fmt == REPLAY_FMT_F32 && c.read_fmt == REPLAY_FMT_F32) {
     const hipError_t e = hipMemcpyAsync(ctx->buf.ckpt, state, state_elems(c) * sizeof(float),
                                         hipMemcpyDeviceToDevice, (hipStream_t)stream);
     return e == hipSuccess ? REPLAY_OK : REPLAY_EHIP;
   }
-  GdnEncodeArgs a{};
+  EncodeArgs a{};
   a.s = shape_of(c);
   a.src = state;
   a.ckpt_pos = halves(*ctx).ckpt_in;
   a.write_ckpt = 1;
-  return hip_status(launch_gdn_encode(a, gdn_formats(*ctx), (hipStream_t)stream));
+  return hip_status(launch_encode_state(a, formats(*ctx), (hipStream_t)stream));
 }
 
 int replay_ring_fields(const replay_ctx *ctx, replay_ring_view *view) {
@@ -261,7 +269,7 @@ int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *strea
     a.bf16 = bf16_records(c);
     a.in_ring = records_in_ring(c) ? 1 : 0;
     a.y = y;
-    e = launch_m2_step(a, (hipStream_t)stream);
+    e = launch_m2_step(a, formats(*ctx), (hipStream_t)stream);
   } else {
     GdnStepArgs a{};
     a.s = shape_of(c);
@@ -276,7 +284,7 @@ int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *strea
     a.bf16 = bf16_records(c);
     a.in_ring = records_in_ring(c) ? 1 : 0;
     a.y = y;
-    e = launch_gdn_step(a, gdn_formats(*ctx), (hipStream_t)stream);
+    e = launch_gdn_step(a, formats(*ctx), (hipStream_t)stream);
   }
   if (e) return REPLAY_EHIP;
   ctx->parity ^= 1;
@@ -299,7 +307,7 @@ int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream) {
     a.A = ctx->buf.A;
     a.mask = seq_mask;
     a.bf16 = bf16_records(c);
-    e = launch_m2_flush(a, (hipStream_t)stream);
+    e = launch_m2_flush(a, formats(*ctx), (hipStream_t)stream);
   } else {
     GdnFlushArgs a{};
     a.s = shape_of(c);
@@ -308,7 +316,7 @@ int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream) {
     a.status = ctx->buf.status;
     a.mask = seq_mask;
     a.bf16 = bf16_records(c);
-    e = launch_gdn_flush(a, gdn_formats(*ctx), (hipStream_t)stream);
+    e = launch_gdn_flush(a, formats(*ctx), (hipStream_t)stream);
   }
   if (e) return REPLAY_EHIP;
   ctx->parity ^= 1;
@@ -340,7 +348,7 @@ int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float
     a.bf16 = bf16_records(c);
     a.in_ring = records_in_ring(c) ? 1 : 0;
     a.y = y;
-    e = launch_m2_verify(a, (hipStream_t)stream);
+    e = launch_m2_verify(a, formats(*ctx), (hipStream_t)stream);
   } else {
     GdnVerifyArgs a{};
     a.s = shape_of(c);
@@ -356,7 +364,7 @@ int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float
     a.bf16 = bf16_records(c);
     a.in_ring = records_in_ring(c) ? 1 : 0;
     a.y = y;
-    e = launch_gdn_verify(a, gdn_formats(*ctx), (hipStream_t)stream);
+    e = launch_gdn_verify(a, formats(*ctx), (hipStream_t)stream);
   }
   if (e) return REPLAY_EHIP;
   ctx->parity ^= 1;

@@ -117,9 +117,9 @@ def split_window_mean(l: Layer, ckpt_fmt: int, read_fmt: int) -> tuple[float, fl
     """Window-mean (read, write) bytes per step with a stored checkpoint in ckpt_fmt
     and a read copy in read_fmt (the same copy when equal): non-fold steps read the
     read copy; a fold reads the checkpoint and writes both copies (Gated DeltaNet;
-    a separate read copy adds the buffered values v)."""
+    a separate read copy adds the buffered values v; Mamba-2 keeps no extra field)."""
     ck, rd = stored_state_bytes(l, ckpt_fmt), stored_state_bytes(l, read_fmt)
-    vrec = l.heads * l.head_dim * l.vec_bytes if read_fmt != ckpt_fmt else 0
+    vrec = l.heads * l.head_dim * l.vec_bytes if (l.kind == "gdn" and read_fmt != ckpt_fmt) else 0
     rd_sum = wr_sum = 0.0
     for m in range(1, l.window + 1):
         fold = m == 1

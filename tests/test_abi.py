@@ -101,3 +101,29 @@ def test_calls_reject_uninitialised_context(B):
         B.replay_commit(ctx, 16, 0)
     with pytest.raises(B.ReplayError):
         B.replay_hbm_probe(16, 16, 15, 0, 0)
+
+
+def test_low_precision_format_pairs(B):
+    """Format pairs: split precision (F32 / FP16-SR / e4m3 checkpoint with an e2m1
+    read copy) and one shared low-precision copy, for both families at
+    state_dim 128; the two-axis read copy for GDN only; the decay skip and
+    zero-copy append stay float32-only for Mamba-2."""
+    F = (B.FMT_F32, B.FMT_F16_SR, B.FMT_F8E4M3, B.FMT_F4E2M1_B16)
+    split = [(c, B.FMT_F4E2M1_B16) for c in F[:3]] + [(c, c) for c in F[1:]]
+    for cf, rf in split:
+        assert B.replay_validate_config(B.make_config(0, 2, 8, 2, 64, 128, 16, 4, cf, rf)) == B.OK
+        assert B.replay_validate_config(B.make_config(1, 2, 8, 8, 128, 128, 16, 4, cf, rf)) == B.OK
+    assert B.replay_validate_config(B.make_config(1, 2, 8, 8, 128, 128, 16, 4, B.FMT_F32, B.FMT_F4E2M1_CS)) == B.OK
+    ns = B.ENOTSUP
+    assert B.replay_validate_config(B.make_config(0, 2, 8, 2, 64, 128, 16, 4, B.FMT_F32, B.FMT_F4E2M1_CS)) == ns
+    assert B.replay_validate_config(B.make_config(0, 2, 8, 2, 64, 64, 16, 4, B.FMT_F32, B.FMT_F4E2M1_B16)) == ns
+    assert B.replay_validate_config(B.make_config(0, 2, 8, 2, 32, 128, 16, 4, B.FMT_F32, B.FMT_F4E2M1_B16)) == ns
+    for fl in (B.FLAG_DECAY_SKIP, B.FLAG_RECORDS_IN_RING):
+        assert B.replay_validate_config(B.make_config(0, 2, 8, 2, 64, 128, 16, 4, B.FMT_F32, B.FMT_F4E2M1_B16,
+                                                      flags=fl)) == ns
+    assert B.replay_validate_config(B.make_config(0, 2, 8, 2, 64, 128, 16, 4, B.FMT_F32, B.FMT_F16_SR)) == ns
+    # sizes: e2m1 codes then, at the next 256 bytes, one e4m3 scale per 16 elements
+    cfg = B.make_config(0, 256, 128, 8, 64, 128, 16, 4, B.FMT_F32, B.FMT_F4E2M1_B16)
+    n = 256 * 128 * 64 * 128
+    assert B.replay_ckpt_bytes(cfg) == 4 * n
+    assert B.replay_read_copy_bytes(cfg) == (n // 2 + 255) // 256 * 256 + n // 16

@@ -1,4 +1,5 @@
-"""Split-precision Gated DeltaNet state on the GPU against the CPU oracle.
+"""Split-precision state (Gated DeltaNet and Mamba-2 layers) on the GPU against
+the CPU oracle.
 
 * Encoding: the stored checkpoint and read copy are byte-identical to the
   oracle's codecs (stochastic-rounding bits included) for the same float32 state.
@@ -27,6 +28,8 @@ pytestmark = pytest.mark.gpu
 PAIRS = [(FMT_F32, FMT_F4E2M1_B16), (FMT_F16_SR, FMT_F4E2M1_B16), (FMT_F8E4M3, FMT_F4E2M1_B16),
          (FMT_F4E2M1_B16, FMT_F4E2M1_B16), (FMT_F16_SR, FMT_F16_SR), (FMT_F8E4M3, FMT_F8E4M3),
          (FMT_F32, FMT_F4E2M1_CS), (FMT_F16_SR, FMT_F4E2M1_CS), (FMT_F8E4M3, FMT_F4E2M1_CS)]
+# (kind, checkpoint format, read format): every GDN pair; Mamba-2 has no two-axis read copy.
+KPAIRS = [("gdn", cf, rf) for cf, rf in PAIRS] + [("mamba2", cf, rf) for cf, rf in PAIRS if rf != FMT_F4E2M1_CS]
 SEED = 0x1234_5678_9ABC
 POST_FOLD_TOL = {FMT_F4E2M1_B16: 2e-2, FMT_F4E2M1_CS: 2e-2, FMT_F16_SR: 2.0 ** -8, FMT_F8E4M3: 2.0 ** -3,
                  FMT_F32: 1e-4}
@@ -68,10 +71,27 @@ def _split_gpu(buf, fmt, n, ncols):
     return parts
 
 
-def _layer(shape, cf, rf, ckpt0, max_draft=0):
+def _layer(shape, cf, rf, ckpt0, max_draft=0, params=None):
     from hybrid_model_ssm_replay_amd.layer import ReplayLayer
-    return ReplayLayer("gdn", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
-                       max_draft=max_draft, ckpt_fmt=cf, read_fmt=rf, seed=SEED, ckpt0=ckpt0)
+    kw = dict(groups=shape.groups, A=params["A"], D=params["D"]) if shape.kind == "mamba2" else {}
+    return ReplayLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
+                       max_draft=max_draft, ckpt_fmt=cf, read_fmt=rf, seed=SEED, ckpt0=ckpt0, **kw)
+
+
+def _shape(kind, batch=2, window=4):
+    """Small layers with state_dim 128 (the low-precision copies need it)."""
+    if kind == "mamba2":
+        return LayerShape("mamba2", batch, 4, 64, 128, 2, window)
+    return LayerShape("gdn", batch, 3, 128, 128, 3, window)
+
+
+def _mk(shape, cf, rf, seed, max_draft=0, zeros=False):
+    """Input stream, GPU layer and oracle session on the same seeded inputs."""
+    ins = InputStream(shape, seed)
+    S0 = ins.initial_state(zeros=zeros, scale=0.3)
+    lay = _layer(shape, cf, rf, S0, max_draft, ins.params)
+    sess = SplitReplaySession(shape.kind, S0, shape.window, ins.params, cf, rf, seed=SEED)
+    return ins, lay, sess
 
 
 def _check_copies(lay, sess, shape, cf, rf, exact=True):
@@ -101,25 +121,23 @@ def _check_copies(lay, sess, shape, cf, rf, exact=True):
     return max(fracs) if fracs else 0.0
 
 
-@pytest.mark.parametrize("cf,rf", PAIRS)
-def test_encoding_is_byte_exact(cf, rf):
-    shape = LayerShape("gdn", 2, 3, 64, 128, 3, 4)
+@pytest.mark.parametrize("kind,cf,rf", KPAIRS)
+def test_encoding_is_byte_exact(kind, cf, rf):
+    shape = LayerShape("gdn", 2, 3, 64, 128, 3, 4) if kind == "gdn" else _shape("mamba2")
     announce("split encode", shape, cf, rf)
     S0 = _state_for_codecs(shape, 1)
-    lay = _layer(shape, cf, rf, S0)
-    sess = SplitReplaySession("gdn", S0, shape.window, None, cf, rf, seed=SEED)
+    params = InputStream(shape, 1).params
+    lay = _layer(shape, cf, rf, S0, params=params)
+    sess = SplitReplaySession(kind, S0, shape.window, params, cf, rf, seed=SEED)
     _check_copies(lay, sess, shape, cf, rf, exact=True)
 
 
-@pytest.mark.parametrize("cf,rf", PAIRS)
-def test_steps_and_folds_match_oracle(cf, rf):
+@pytest.mark.parametrize("kind,cf,rf", KPAIRS)
+def test_steps_and_folds_match_oracle(kind, cf, rf):
     import torch
-    shape = LayerShape("gdn", 2, 3, 128, 128, 3, 4)
+    shape = _shape(kind)
     announce("split steps", shape, cf, rf)
-    ins = InputStream(shape, 3)
-    S0 = ins.initial_state(zeros=False, scale=0.3)
-    lay = _layer(shape, cf, rf, S0, max_draft=3)
-    sess = SplitReplaySession("gdn", S0, shape.window, None, cf, rf, seed=SEED)
+    ins, lay, sess = _mk(shape, cf, rf, 3, max_draft=3)
     worst_pre, worst_post, flips = 0.0, 0.0, 0.0
     rng = np.random.default_rng(3)
     for t in range(17):
@@ -144,19 +162,18 @@ def test_steps_and_folds_match_oracle(cf, rf):
     assert worst_post <= POST_FOLD_TOL[rf], worst_post
 
 
-@pytest.mark.parametrize("cf,rf", [(FMT_F32, FMT_F4E2M1_B16), (FMT_F4E2M1_B16, FMT_F4E2M1_B16),
-                                   (FMT_F8E4M3, FMT_F8E4M3), (FMT_F32, FMT_F4E2M1_CS)])
-def test_speculative_with_many_drafts(cf, rf):
+@pytest.mark.parametrize("kind,cf,rf", [("gdn", FMT_F32, FMT_F4E2M1_B16), ("gdn", FMT_F4E2M1_B16, FMT_F4E2M1_B16),
+                                        ("gdn", FMT_F8E4M3, FMT_F8E4M3), ("gdn", FMT_F32, FMT_F4E2M1_CS),
+                                        ("mamba2", FMT_F32, FMT_F4E2M1_B16), ("mamba2", FMT_F16_SR, FMT_F16_SR),
+                                        ("mamba2", FMT_F4E2M1_B16, FMT_F4E2M1_B16)])
+def test_speculative_with_many_drafts(kind, cf, rf):
     """Verify / commit / step sequences with up to 12 drafts (three passes) on a
     16-record window, against SplitReplaySession; the same bars as above."""
     import torch
     from oracle.pointers import PointerMachine
-    shape = LayerShape("gdn", 2, 3, 128, 128, 3, 16)
+    shape = _shape(kind, window=16)
     announce("split speculative", shape, cf, rf)
-    ins = InputStream(shape, 21)
-    S0 = ins.initial_state(zeros=False, scale=0.3)
-    lay = _layer(shape, cf, rf, S0, max_draft=12)
-    sess = SplitReplaySession("gdn", S0, shape.window, None, cf, rf, seed=SEED)
+    ins, lay, sess = _mk(shape, cf, rf, 21, max_draft=12)
     pm = PointerMachine(shape.batch, shape.window)
     rng = np.random.default_rng(21)
     worst_pre, worst_post = 0.0, 0.0
@@ -239,31 +256,37 @@ def test_error_curves_over_32768_steps():
     assert shared[-1] >= split[-1]
 
 
-@pytest.mark.parametrize("cf,rf", [(FMT_F32, FMT_F4E2M1_B16), (FMT_F8E4M3, FMT_F4E2M1_B16),
-                                   (FMT_F4E2M1_B16, FMT_F4E2M1_B16), (FMT_F32, FMT_F4E2M1_CS)])
-def test_full_size_sampled(cf, rf):
-    """The benchmarked split-precision layer (Gated DeltaNet, 32 heads, d = 128,
-    L = 16, batch 64) in the bench's launch configuration: 24 steps from a zero
-    state (one fold) and a T = 4 verify, checked on 4 sampled sequences against
-    SplitReplaySession on those sequences (these pairs draw no random bits, so the
-    sample's encodings equal the full batch's).  Bars as above: 1e-4 before the
-    first fold (the read copy is the exact zero state), the format step after it."""
+@pytest.mark.parametrize("name,cf,rf", [("gdn_b64_h32_d128_l16", FMT_F32, FMT_F4E2M1_B16),
+                                        ("gdn_b64_h32_d128_l16", FMT_F8E4M3, FMT_F4E2M1_B16),
+                                        ("gdn_b64_h32_d128_l16", FMT_F4E2M1_B16, FMT_F4E2M1_B16),
+                                        ("gdn_b64_h32_d128_l16", FMT_F32, FMT_F4E2M1_CS),
+                                        ("mamba2_b256_h128_p64_n128_g8_l16", FMT_F32, FMT_F4E2M1_B16),
+                                        ("mamba2_b256_h128_p64_n128_g8_l16", FMT_F8E4M3, FMT_F4E2M1_B16),
+                                        ("mamba2_b256_h128_p64_n128_g8_l16", FMT_F4E2M1_B16, FMT_F4E2M1_B16)])
+def test_full_size_sampled(name, cf, rf):
+    """The benchmarked split-precision layers (Gated DeltaNet, 32 heads, d = 128,
+    batch 64; Mamba-2 with the 4 MiB state, batch 256; L = 16) in the bench's
+    launch configuration: 24 steps from a zero state (one fold) and a T = 4
+    verify, checked on 4 sampled sequences against SplitReplaySession on those
+    sequences (these pairs draw no random bits, so the sample's encodings equal
+    the full batch's).  Bars as above: 1e-4 before the first fold (the read copy
+    is the exact zero state) and at the fold step, the format step after it."""
     import torch
     from synth import WORKLOADS, take_batch
-    shape = WORKLOADS["gdn_b64_h32_d128_l16"]
+    shape = WORKLOADS[name]
     announce("split full size", shape, cf, rf)
     ins = InputStream(shape, 61)
-    lay = _layer(shape, cf, rf, None, max_draft=4)
-    sample = np.array([0, 21, 42, 63])
+    lay = _layer(shape, cf, rf, None, max_draft=4, params=ins.params)
+    sample = np.array([0, shape.batch // 3, 2 * shape.batch // 3, shape.batch - 1])
     idx = torch.from_numpy(sample).cuda()
-    sess = SplitReplaySession("gdn", np.zeros((len(sample), shape.heads, shape.head_dim, shape.state_dim)),
-                              shape.window, None, cf, rf, seed=SEED)
+    sess = SplitReplaySession(shape.kind, np.zeros((len(sample), shape.heads, shape.head_dim, shape.state_dim)),
+                              shape.window, ins.params, cf, rf, seed=SEED)
     worst_pre = worst_post = 0.0
     for t in range(24):
         r = ins.record()
         y = lay.step(to_dev(r))
         e = max_rel_err(host(y[idx]), sess.step(take_batch(r, sample)), sess.scale)
-        if t < shape.window:
+        if t <= shape.window:                            # the (L+1)-th step outputs from its fold result
             worst_pre = max(worst_pre, e)
         else:
             worst_post = max(worst_post, e)
@@ -275,20 +298,17 @@ def test_full_size_sampled(cf, rf):
     assert worst_post <= POST_FOLD_TOL[rf], worst_post
 
 
-@pytest.mark.parametrize("cf,rf", PAIRS)
-def test_explicit_flush_matches_oracle(cf, rf):
+@pytest.mark.parametrize("kind,cf,rf", KPAIRS)
+def test_explicit_flush_matches_oracle(kind, cf, rf):
     """replay_flush with a sequence mask for every format pair: the masked
-    sequences fold their committed records (re-solving from the checkpoint with
-    a separate read copy) and re-encode both copies; outputs and stored bytes
-    against SplitReplaySession with the same flushes, bars as above (the first
-    flush is the first fold)."""
+    sequences fold their committed records (GDN: re-solving from the checkpoint
+    with a separate read copy) and re-encode both copies; outputs and stored
+    bytes against SplitReplaySession with the same flushes, bars as above (the
+    first flush is the first fold)."""
     import torch
-    shape = LayerShape("gdn", 3, 3, 128, 128, 3, 6)
+    shape = _shape(kind, batch=3, window=6)
     announce("split flush", shape, cf, rf)
-    ins = InputStream(shape, 12)
-    S0 = ins.initial_state(zeros=False, scale=0.3)
-    lay = _layer(shape, cf, rf, S0, max_draft=2)
-    sess = SplitReplaySession("gdn", S0, shape.window, None, cf, rf, seed=SEED)
+    ins, lay, sess = _mk(shape, cf, rf, 12, max_draft=2)
     worst_pre, worst_post, folded = 0.0, 0.0, False
     masks = {3: [1, 0, 1], 7: [0, 1, 1], 8: [1, 1, 1], 12: [0, 0, 1]}
     for t in range(15):
@@ -321,8 +341,8 @@ def _bounds_for(sess, kind, params, dQ, lead_T=None):
         pos, ck = int(sess.ptr.pos[b]), int(sess.ptr.ckpt_pos[b])
         wins = ([[sess.recs[b][p] for p in range(ck, pos + i + 1)] for i in range(lead_T)] if lead_T
                 else [[sess.recs[b][p] for p in range(ck, pos)]])
-        bs = [np.zeros_like(dQ[0][..., 0]) if dQ[b] is None else output_bound(dQ[b], query_weights(kind, w, params))
-              for w in wins]
+        bs = [np.zeros((sess.ckpt.shape[1], sess.ckpt.shape[2])) if dQ[b] is None
+              else output_bound(dQ[b], query_weights(kind, w, params)) for w in wins]
         out.append(np.stack(bs) if lead_T else bs[0])
     return np.stack(out)
 
@@ -348,19 +368,15 @@ def _read_copy_dq(lay, sess, shape, cf, rf, folded):
     return dQ
 
 
-@pytest.mark.parametrize("cf,rf", PAIRS)
-def test_fold_outputs_come_from_the_fold_result(cf, rf):
+@pytest.mark.parametrize("kind,cf,rf", KPAIRS)
+def test_fold_outputs_come_from_the_fold_result(kind, cf, rf):
     """A step or verify that folds outputs from its float32 fold result, not from
     the re-encoded copy [P3, Perspective, paragraph 2].  At the first fold both
     sides fold the same stored bytes, so those outputs meet the float32 bar."""
-    import torch
-    shape = LayerShape("gdn", 2, 3, 128, 128, 3, 4)
+    shape = _shape(kind)
     announce("split fold outputs", shape, cf, rf)
     for via_verify in (False, True):
-        ins = InputStream(shape, 31)
-        S0 = ins.initial_state(zeros=False, scale=0.3)
-        lay = _layer(shape, cf, rf, S0, max_draft=3)
-        sess = SplitReplaySession("gdn", S0, shape.window, None, cf, rf, seed=SEED)
+        ins, lay, sess = _mk(shape, cf, rf, 31, max_draft=3)
         n_pre = shape.window - 1 if via_verify else shape.window
         for t in range(n_pre):
             r = ins.record()
@@ -375,19 +391,16 @@ def test_fold_outputs_come_from_the_fold_result(cf, rf):
         assert e <= 1e-4, e
 
 
-@pytest.mark.parametrize("cf,rf", PAIRS)
-def test_first_fold_codes_and_window_outputs(cf, rf):
+@pytest.mark.parametrize("kind,cf,rf", KPAIRS)
+def test_first_fold_codes_and_window_outputs(kind, cf, rf):
     """After the first fold every stored code of both copies is the encoding of a
     value within float32 rounding of the oracle's fold result (tests/_split_check.py),
     and each later output of that window is within 1e-4 of the oracle's once the
     effect of the accepted code differences, sum |dQ| |z|, is allowed for."""
     from _split_check import bounded_rel_err
-    shape = LayerShape("gdn", 2, 3, 128, 128, 3, 4)
+    shape = _shape(kind)
     announce("split first fold", shape, cf, rf)
-    ins = InputStream(shape, 32)
-    S0 = ins.initial_state(zeros=False, scale=0.3)
-    lay = _layer(shape, cf, rf, S0)
-    sess = SplitReplaySession("gdn", S0, shape.window, None, cf, rf, seed=SEED)
+    ins, lay, sess = _mk(shape, cf, rf, 32)
     for t in range(shape.window + 1):                   # the last one folds first
         r = ins.record()
         assert max_rel_err(host(lay.step(to_dev(r))), sess.step(r), sess.scale) <= 1e-4, t
@@ -397,26 +410,23 @@ def test_first_fold_codes_and_window_outputs(cf, rf):
         r = ins.record()
         y = host(lay.step(to_dev(r)))
         ref = sess.step(r)
-        bound = _bounds_for(sess, "gdn", None, dQ)
+        bound = _bounds_for(sess, kind, ins.params, dQ)
         worst = max(worst, bounded_rel_err(y, ref, sess.scale, bound))
         moved = max(moved, max_rel_err(y, ref, sess.scale))
     print(f"[split first fold] cf={cf} rf={rf} raw {moved:.2e} beyond the code bound {worst:.2e}")
     assert worst <= 1e-4, worst
 
 
-@pytest.mark.parametrize("cf,rf", PAIRS)
-def test_verify_flush_commit_step_verify(cf, rf):
+@pytest.mark.parametrize("kind,cf,rf", KPAIRS)
+def test_verify_flush_commit_step_verify(kind, cf, rf):
     """verify -> flush -> commit -> step -> verify: the flush folds the committed
     records (the first fold here) and discards the pending drafts, so the commit
     clamps its counts; later outputs are checked as in the test above."""
     import torch
     from _split_check import bounded_rel_err
-    shape = LayerShape("gdn", 2, 3, 128, 128, 3, 4)
+    shape = _shape(kind)
     announce("split verify-flush-commit", shape, cf, rf)
-    ins = InputStream(shape, 33)
-    S0 = ins.initial_state(zeros=False, scale=0.3)
-    lay = _layer(shape, cf, rf, S0, max_draft=3)
-    sess = SplitReplaySession("gdn", S0, shape.window, None, cf, rf, seed=SEED)
+    ins, lay, sess = _mk(shape, cf, rf, 33, max_draft=3)
     for t in range(3):
         r = ins.record()
         assert max_rel_err(host(lay.step(to_dev(r))), sess.step(r), sess.scale) <= 1e-4
@@ -435,12 +445,12 @@ def test_verify_flush_commit_step_verify(cf, rf):
     r = ins.record()                                  # sequence 0 reads its new copy; sequence 1 folds no more
     y = host(lay.step(to_dev(r)))
     ref = sess.step(r)
-    e1 = bounded_rel_err(y, ref, sess.scale, _bounds_for(sess, "gdn", None, dQ))
+    e1 = bounded_rel_err(y, ref, sess.scale, _bounds_for(sess, kind, ins.params, dQ))
     d = ins.drafts(2)                                 # sequence 1: count 4 + 2 > 4, folds first
     y = host(lay.verify(to_dev(d)))
     ref = sess.verify(d)
     dq_v = [dQ[0], None]                              # sequence 1 outputs from its fresh fold
-    e2 = bounded_rel_err(y, ref, sess.scale, _bounds_for(sess, "gdn", None, dq_v, lead_T=2))
+    e2 = bounded_rel_err(y, ref, sess.scale, _bounds_for(sess, kind, ins.params, dq_v, lead_T=2))
     print(f"[split vfc] cf={cf} rf={rf} step {e1:.2e} verify {e2:.2e}")
     assert e1 <= 1e-4 and e2 <= 1e-4, (e1, e2)
     acc = np.array([2, 1], np.int32)

@@ -67,7 +67,7 @@ def _continue(lay, ins, n, T):
     return [o.cpu() for o in outs]
 
 
-CASES = [("mamba2", 0, 0), ("gdn", 0, 0), ("gdn", 0, 3), ("gdn", 1, 3), ("gdn", 3, 3)]
+CASES = [("mamba2", 0, 0), ("mamba2", 0, 3), ("mamba2", 1, 3), ("gdn", 0, 0), ("gdn", 0, 3), ("gdn", 1, 3), ("gdn", 3, 3)]
 
 
 @pytest.mark.parametrize("kind,cf,rf", CASES)
