@@ -30,6 +30,15 @@ newest output is then
 
 Only S0 k_j (j <= m) and S0 q_m touch the checkpoint, so one read of S0
 serves the whole window.
+
+Decay skip (optional; the pages' future direction for heads whose decay has
+made the checkpoint irrelevant [P3, Perspective, paragraph 1], with no
+threshold given).  Every way the checkpoint enters the newest output or the
+fold carries the factor exp(g_m): S_m = exp(g_m) S0 prod_t (I - beta_t k_t
+k_t^T) + (terms without S0), and each factor I - beta k k^T has norm at most 1
+for unit keys and 0 <= beta <= 2.  Reading taken, as for Mamba-2: when
+g_m < ln 2^-24 the computation (its pseudo-values and output, or the fold)
+uses a zero checkpoint, which moves an output by at most 2^-24 |S0| |q|.
 """
 from __future__ import annotations
 
@@ -77,11 +86,19 @@ def pseudo_values(S0, recs):
     return np.stack(U)
 
 
-def replay_output(S0, recs, q):
+def _skip_checkpoint(S0, g_last, skip_below):
+    """S0 with the heads whose window log-decay is below skip_below zeroed."""
+    if skip_below is None:
+        return S0
+    return np.where((g_last < skip_below)[:, None, None], 0.0, S0)
+
+
+def replay_output(S0, recs, q, skip_below=None):
     """Output for the newest record (query q [H, dk]) from S0 and the window."""
     S0 = np.asarray(S0, np.float64)
     q = np.asarray(q, np.float64)
     g = _log_decay_cumsum(recs)
+    S0 = _skip_checkpoint(S0, g[-1], skip_below)
     U = pseudo_values(S0, recs)
     o = np.exp(g[-1])[:, None] * np.einsum("hvk,hk->hv", S0, q)
     for j, r in enumerate(recs):
@@ -90,12 +107,13 @@ def replay_output(S0, recs, q):
     return o
 
 
-def fold(S0, recs):
+def fold(S0, recs, skip_below=None):
     """New checkpoint after folding records 1..m into S0 (one sequence)."""
     S0 = np.asarray(S0, np.float64)
     if not recs:
         return S0.copy()
     g = _log_decay_cumsum(recs)
+    S0 = _skip_checkpoint(S0, g[-1], skip_below)
     U = pseudo_values(S0, recs)
     S = np.exp(g[-1])[:, None, None] * S0
     for j, r in enumerate(recs):

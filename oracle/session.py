@@ -51,12 +51,12 @@ class _Kind:
     def output(self, S0, recs, skip_below=None):
         if self.kind == "mamba2":
             return mamba2.replay_output(S0, recs, self.params["A"], self.params["D"], skip_below)
-        return gdn.replay_output(S0, recs, recs[-1]["q"])
+        return gdn.replay_output(S0, recs, recs[-1]["q"], skip_below)
 
     def fold(self, S0, recs, skip_below=None):
         if self.kind == "mamba2":
             return mamba2.fold(S0, recs, self.params["A"], skip_below)
-        return gdn.fold(S0, recs)
+        return gdn.fold(S0, recs, skip_below)
 
     def scale(self, S, r):
         """Output term size for the state S after record r (one sequence)."""
@@ -124,8 +124,8 @@ class StepwiseSession:
 
 class ReplaySession:
     """The method: checkpoint + ring of the last L records, lazy folds.  With
-    decay_skip (Mamba-2), heads whose window decay is below 2^-24 drop the
-    checkpoint term in outputs and folds (see oracle/mamba2.py)."""
+    decay_skip, heads whose window decay is below 2^-24 drop the checkpoint
+    term in outputs and folds (see oracle/mamba2.py, oracle/gdn.py)."""
 
     def __init__(self, kind: str, state0, window: int, params: dict | None = None, decay_skip: bool = False):
         self.k = _Kind(kind, params or {})

@@ -126,3 +126,42 @@ def test_replay_session_equals_stepwise(L):
         np.testing.assert_allclose(rep.step(r), ref.step(r), rtol=1e-10, atol=1e-12)
         if L == 1 and t > 0:
             np.testing.assert_allclose(rep.ckpt, state_before, rtol=1e-12, atol=1e-12)
+
+
+def test_decay_skip_drops_exactly_the_checkpoint_term():
+    """With the decay skip, a head whose window log-decay g_m is below ln 2^-24
+    gives exactly the output (and fold) of a zero checkpoint, every other head
+    exactly the full replay form, and the skipped term moves the output by at
+    most 2^-24 ||S0||_2 ||q||: S0 enters only through exp(g_m) S0 times a product
+    of I - beta k k^T, each of norm <= 1 [P3, Perspective, paragraph 1]."""
+    from oracle.mamba2 import DECAY_SKIP_LOG as thr
+    rng = np.random.default_rng(12)
+    H, dv, dk, m = 4, 6, 8, 9
+    S0 = rng.standard_normal((H, dv, dk))
+    log_alpha = np.array([-30.0, -0.01, -2.5, -0.5])     # per record
+    recs = []
+    for _ in range(m):
+        k = rng.standard_normal((H, dk))
+        q = rng.standard_normal((H, dk))
+        recs.append({"k": k / np.linalg.norm(k, axis=-1, keepdims=True),
+                     "q": q / np.linalg.norm(q, axis=-1, keepdims=True),
+                     "v": rng.standard_normal((H, dv)), "beta": rng.uniform(0.1, 0.9, H),
+                     "alpha": np.exp(log_alpha * rng.uniform(0.8, 1.2, H))})
+    zero = np.zeros_like(S0)
+    for n in range(1, m + 1):
+        w = recs[:n]
+        g = np.sum([np.log(r["alpha"]) for r in w], axis=0)
+        skipped = g < thr
+        q = w[-1]["q"]
+        y_skip, y_full, y_zero = (gdn.replay_output(S, w, q, skip_below=sk)
+                                  for S, sk in ((S0, thr), (S0, None), (zero, None)))
+        f_skip, f_full, f_zero = (gdn.fold(S, w, skip_below=sk) for S, sk in ((S0, thr), (S0, None), (zero, None)))
+        for h in range(H):
+            want_y, want_f = (y_zero[h], f_zero[h]) if skipped[h] else (y_full[h], f_full[h])
+            np.testing.assert_allclose(y_skip[h], want_y, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(f_skip[h], want_f, rtol=0, atol=1e-12)
+            if skipped[h]:
+                bound = 2.0 ** -24 * np.linalg.norm(S0[h], 2) * np.linalg.norm(q[h])
+                assert np.linalg.norm(y_skip[h] - y_full[h]) <= bound * (1 + 1e-9)
+    g_all = np.cumsum([np.log(r["alpha"]) for r in recs], axis=0)
+    assert g_all[0, 0] < thr and g_all[-1, 1] > thr and g_all[0, 2] > thr > g_all[-1, 2]
