@@ -207,6 +207,10 @@ __device__ __forceinline__ int fdiv(int n, const FastDiv &f) {
 }
 __device__ __forceinline__ int fmod_(int n, const FastDiv &f) { return n - fdiv(n, f) * (int)f.d; }
 
+// Decay skip (REPLAY_FLAG_DECAY_SKIP): a head whose window log-decay is below
+// ln 2^-24 drops its checkpoint term [P3, Perspective, paragraph 1].
+constexpr float kDecaySkipLog = -16.635532333438686f;  // ln 2^-24
+
 // A pointer pair the kernels act on: 0 <= ckpt_pos <= pos <= ckpt_pos + L.
 // Any other pair (corrupted, or negative) flags its sequence, which is then
 // skipped: ring slots are only ever computed from non-negative positions, the

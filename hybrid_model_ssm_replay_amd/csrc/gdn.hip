@@ -241,9 +241,10 @@ __device__ __forceinline__ void load_ring_rows(float (&vr)[16], int cnt, const E
 // computed from the read copy, so the fold re-solves them from the checkpoint
 // and the values v (a full-window solve through sm), and the read copy's
 // rounding never enters the recurrence.
-template <int CF, int RF, int NCH, int RBW, typename R>
+template <int CF, int RF, int NCH, int RBW, typename R, bool SKIP = false>
 __device__ __forceinline__ void gdn_fold(float4 (&s)[RBW][NCH], int cnt, int s0, const GdnRingPtrs<R> &rp, int Ls,
                                          int rb0, int lane, GdnLds<RBW> *sm) {
+  static_assert(!SKIP || CF == RF, "the decay skip folds the cached pseudo-values");
   constexpr int CM = col_map(CF, RF);
   const int q = lane >> 4, r16 = lane & 15;
   const int j = r16 < cnt ? r16 : cnt - 1;
@@ -267,7 +268,7 @@ __device__ __forceinline__ void gdn_fold(float4 (&s)[RBW][NCH], int cnt, int s0,
     const float g = prefix_sum16(la, lane);
     const float gl = __shfl(g, cnt - 1, kWave);
     const float us = lane < cnt ? __expf(gl - g) : 0.f;  // lane t: weight of record t
-    escale = __expf(gl);
+    escale = (SKIP && gl < kDecaySkipLog) ? 0.f : __expf(gl);  // decay skip: a pure write of the records
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int r = 4 * st + q;
@@ -315,13 +316,19 @@ __device__ __forceinline__ void load_cols(float (&v)[NCH], const R *p) {
   }
 }
 
-// Float32 copies: held to 128 VGPRs (four waves per SIMD), which fits without spills.
-template <int CF, int RF, int NCH, int RBW, typename R>
+// Float32 copies: held to 128 VGPRs (four waves per SIMD), which fits without
+// spills; with the decay skip 256 (two): its checkpoint loads sit behind the
+// decision's branch, and at three waves per SIMD the tile spills.
+// SKIP (decay skip, float32 copies): a head whose window log-decay (over the
+// records the step's output or fold uses) is below ln 2^-24 does not read its
+// checkpoint; its fold is a pure write of the folded records.
+template <int CF, int RF, int NCH, int RBW, typename R, bool SKIP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
-    CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32 ? 4 : 1))) void gdn_replay_step(GdnStepArgs a, StateBufs sb) {
+    CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32 ? (SKIP ? 2 : 4) : 1))) void gdn_replay_step(GdnStepArgs a, StateBufs sb) {
   constexpr int DK = 16 * NCH;
   constexpr int CM = col_map(CF, RF);
   constexpr bool kLossy = RF != REPLAY_FMT_F32;  // the read copy is not the float32 fold result
+  static_assert(!SKIP || (CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32), "decay skip: float32 copies only");
   constexpr int kMaxOld = 15;            // older records of a window (L <= 16)
   __shared__ float4 kq_s[2][DK / 4];     // k_m, q_m in natural column order
   __shared__ float dot_s[2][16];         // [0][j] = k_j . k_m, [1][j] = k_j . q_m; [1][15] = k_m . q_m
@@ -341,9 +348,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   const R *vin = static_cast<const R *>(a.v) + bh * DV;
   const int orow = (rb0 + (q < RBW ? q : 0)) * 16 + r16;  // this lane's output row (q < RBW)
 
-  // 1. The read copy first (a non-fold step reads only it), then what needs no pointer.
+  // 1. The read copy first (a non-fold step reads only it), then what needs no
+  //    pointer.  With the decay skip the read waits for the decision (below).
   typename SIO<RF, NCH, RBW, CM>::Raw raw;
-  SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
+  float4 s[RBW][NCH];      // the checkpoint rows of this wave (decay skip: read into s directly)
+  if constexpr (!SKIP) SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
   float km[NCH], qm[NCH];  // columns NCH r16 .. of k_m and q_m
   if (!zc) load_cols<NCH, R>(km, kin + NCH * r16);
   load_cols<NCH, R>(qm, qin + NCH * r16);
@@ -371,14 +380,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     al_in = __shfl(al_row, slot, kWave);
     be_in = rp.rbe[slot];
   }
+  if constexpr (SKIP) {
+    // The records whose decay multiplies the checkpoint term: the fold's L, or
+    // this output's count + 1.  Read the checkpoint only if the term stays.
+    const int n = fold ? L : count + 1;
+    const int j = r16 < n ? r16 : 0;
+    const float aj = __shfl(al_row, wrap(s0, j < count ? j : 0, Ls), kWave);
+    const float ak = (!fold && r16 == count) ? al_in : aj;
+    // Every 16-lane row computes the same sum: take lane 0's, so the branch is uniform.
+    const float tot = sum16(r16 < n ? __logf(ak) : 0.f);
+    if (__builtin_amdgcn_readfirstlane(tot < kDecaySkipLog ? 1 : 0)) {
+#pragma unroll
+      for (int k = 0; k < RBW; ++k)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) s[k][c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      load_rows_g<NCH, RBW, CM>(s, static_cast<const float *>(sb.rd.data) + head, rb0, lane);
+    }
+  }
   int base = ck, sb0 = s0;
-  float4 s[RBW][NCH];
   float kj[NCH];         // this thread's slice of key grp (an older record)
   float uo[kMaxOld];     // older pseudo-values of this lane's row
   if (fold) {
     if constexpr (RF == CF) {
-      SIO<RF, NCH, RBW, CM>::decode(s, raw);
-      gdn_fold<CF, RF, NCH, RBW, R>(s, L, s0, rp, Ls, rb0, lane, nullptr);
+      if constexpr (!SKIP) SIO<RF, NCH, RBW, CM>::decode(s, raw);
+      gdn_fold<CF, RF, NCH, RBW, R, SKIP>(s, L, s0, rp, Ls, rb0, lane, nullptr);
     } else {
       __shared__ GdnLds<RBW> lds_all[4];
       typename SIO<CF, NCH, RBW, CM>::Raw rc;
@@ -405,7 +431,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       const float v = rp.ru[(size_t)wrap(s0, tc, Ls) * rp.vs + orow];
       uo[t] = t < count ? v : 0.f;
     }
-    SIO<RF, NCH, RBW, CM>::decode(s, raw);
+    if constexpr (!SKIP) SIO<RF, NCH, RBW, CM>::decode(s, raw);
   }
   const int nold = pos - base;  // older records in this window
 
@@ -449,7 +475,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   }
   const float g = prefix_sum16(lane < 16 ? __logf(al) : 0.f, lane);
   const float gm = __shfl(g, nold, kWave);
-  const float egm = __expf(gm);
+  // Weight of the checkpoint terms (0 for a head the decay skip drops).
+  const float egm = (SKIP && gm < kDecaySkipLog) ? 0.f : __expf(gm);
   const float dec = __expf(gm - g);
   const float wk = r16 < nold ? dec * dot_s[0][r16] : 0.f;
   const float wq = r16 < nold ? dec * dot_s[1][r16] : 0.f;
@@ -520,10 +547,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 }
 
 // ---- explicit flush -------------------------------------------------------------
-template <int CF, int RF, int NCH, int RBW, typename R>
+template <int CF, int RF, int NCH, int RBW, typename R, bool SKIP = false>
 __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a, StateBufs sb) {
   constexpr int DK = 16 * NCH;
   constexpr int CM = col_map(CF, RF);
+  static_assert(!SKIP || (CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32), "decay skip: float32 copies only");
   __shared__ GdnLds<RBW> lds_all[RF != CF ? 4 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const Shape &sh = a.s;
@@ -543,13 +571,25 @@ __global__ __launch_bounds__(256) void gdn_flush(GdnFlushArgs a, StateBufs sb) {
   }
   if (!fold) return;
   const GdnRingPtrs<R> rp = gdn_ring_ptrs<R>(a.ring, sh, b, h);
+  const int s0 = fmod_(ck, sh.fLs);
+  bool keep = true;  // the checkpoint term survives the decay skip
+  if constexpr (SKIP) {
+    const int r16 = lane & 15;
+    const float aj = rp.ral[wrap(s0, r16 < count ? r16 : 0, sh.Ls)];
+    keep = !(sum16(r16 < count ? __logf(aj) : 0.f) < kDecaySkipLog);
+  }
   float4 s[RBW][NCH];
-  {
+  if (keep) {
     typename SIO<CF, NCH, RBW, CM>::Raw rc;
     SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
     SIO<CF, NCH, RBW, CM>::decode(s, rc);
+  } else {
+#pragma unroll
+    for (int k = 0; k < RBW; ++k)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) s[k][c] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  gdn_fold<CF, RF, NCH, RBW, R>(s, count, fmod_(ck, sh.fLs), rp, sh.Ls, rb0, lane, &lds_all[RF != CF ? wave : 0]);
+  gdn_fold<CF, RF, NCH, RBW, R, SKIP>(s, count, s0, rp, sh.Ls, rb0, lane, &lds_all[RF != CF ? wave : 0]);
   store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
 }
 
@@ -596,13 +636,16 @@ union GdnWaveLds {
 template <int CF, int RF>
 constexpr int verify_waves_per_eu() { return (CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32) ? 3 : 1; }
 
-template <int CF, int RF, int NCH, int RBW, typename R>
+// SKIP (decay skip, float32 copies): the rule applies to the fold-first and to
+// each draft's output, but the checkpoint is always read.
+template <int CF, int RF, int NCH, int RBW, typename R, bool SKIP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<CF, RF>())))
 void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
   constexpr int DK = 16 * NCH;
   constexpr int CM = col_map(CF, RF);
   constexpr int kPass = kMaxL / 4;
   constexpr bool kLossy = RF != REPLAY_FMT_F32;  // the read copy is not the float32 fold result
+  static_assert(!SKIP || (CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32), "decay skip: float32 copies only");
   __shared__ float4 ldsK[NCH][64];                 // [chunk cc][record j + 16 q]: k_j at colq(cc, q)
   __shared__ float4 ldsD[kPass * 2 * NCH * 16];    // [((p 2 + w) NCH + cc) 16 + 4 m + q]: w = 0: k, 1: q of draft 4 p + m
   __shared__ GdnWaveLds<RBW, kLossy> lds_all[4];
@@ -669,7 +712,7 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
       SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
       SIO<CF, NCH, RBW, CM>::decode(s, rc);
     }
-    gdn_fold<CF, RF, NCH, RBW, R>(s, count, s0, rp, Ls, rb0, lane, &lds_all[wave].fold);
+    gdn_fold<CF, RF, NCH, RBW, R, SKIP>(s, count, s0, rp, Ls, rb0, lane, &lds_all[wave].fold);
     // Float32 copies: s already is what the copy holds.  Otherwise the drafts'
     // outputs come from the fold result s, and the copies are stored after
     // the passes (below).
@@ -827,7 +870,8 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
     for (int t = 0; t < kMaxL; ++t) {
       if (t >= c && t < nrec) {
         const int d = t - c;
-        const float bt = sv.beta[t], et = __expf(sv.g[t]);
+        const float bt = sv.beta[t];
+        const float et = (SKIP && sv.g[t] < kDecaySkipLog) ? 0.f : __expf(sv.g[t]);  // checkpoint-term weight
         float v = bt * vrow[d] - bt * et * sv.W[lane][d];
 #pragma unroll
         for (int j = 0; j < t; ++j) v -= sv.A[d][j] * u[j];
@@ -1022,7 +1066,8 @@ __global__ __launch_bounds__(256) void gdn_snapshot_verify(GdnSnapArgs a) {
   X(REPLAY_FMT_F16_SR, REPLAY_FMT_F16_SR)                                                           \
   X(REPLAY_FMT_F8E4M3, REPLAY_FMT_F8E4M3)
 
-template <template <int, int, int, int> class K, typename Args>
+// LP: the low-precision format pairs are instantiated too (not with the decay skip).
+template <template <int, int, int, int> class K, bool LP = true, typename Args>
 int gdn_dispatch(const Args &a, const StateBufs &sb, int cf, int rf, hipStream_t st) {
   const int DK = a.s.N, DV = a.s.P;
   if (DV != 64 && DV != 128) return (int)hipErrorInvalidValue;
@@ -1035,9 +1080,11 @@ int gdn_dispatch(const Args &a, const StateBufs &sb, int cf, int rf, hipStream_t
   }
 #define RSSM_F32(NCH_) RSSM_CASE(REPLAY_FMT_F32, REPLAY_FMT_F32, NCH_, 1) RSSM_CASE(REPLAY_FMT_F32, REPLAY_FMT_F32, NCH_, 2)
   RSSM_F32(2) RSSM_F32(4) RSSM_F32(8)
+  if constexpr (LP) {
 #define RSSM_Q(CF_, RF_) RSSM_CASE(CF_, RF_, 8, 1) RSSM_CASE(CF_, RF_, 8, 2)
-  RSSM_FMT_PAIRS(RSSM_Q)
+    RSSM_FMT_PAIRS(RSSM_Q)
 #undef RSSM_Q
+  }
 #undef RSSM_F32
 #undef RSSM_CASE
   return (int)hipErrorInvalidValue;
@@ -1060,13 +1107,13 @@ int gdn_dispatch_f32(const Args &a, hipStream_t st) {
 }
 
 // Kernel wrappers over the record element type (float32, or bf16 records).
-#define RSSM_WRAP4(name, kern)                              \
-  template <typename R>                                     \
-  struct name {                                             \
-    template <int CF, int RF, int NCH, int RBW>             \
-    struct K {                                              \
-      static constexpr auto fn = kern<CF, RF, NCH, RBW, R>; \
-    };                                                      \
+#define RSSM_WRAP4(name, kern)                                    \
+  template <typename R, bool SKIP = false>                        \
+  struct name {                                                   \
+    template <int CF, int RF, int NCH, int RBW>                   \
+    struct K {                                                    \
+      static constexpr auto fn = kern<CF, RF, NCH, RBW, R, SKIP>; \
+    };                                                            \
   };
 RSSM_WRAP4(GStepK, gdn_replay_step)
 RSSM_WRAP4(GFlushK, gdn_flush)
@@ -1087,20 +1134,23 @@ struct GEncodeK {
 RSSM_WRAP(GConvK, gdn_conv_step)
 #undef RSSM_WRAP
 
+// By the record element type and the decay skip (float32 copies only).
+template <template <typename, bool> class W, typename Args>
+int launch_gdn(const Args &a, const FormatBufs &f, hipStream_t st) {
+  const StateBufs sb = state_bufs(f);
+  if (a.decay_skip)
+    return a.bf16 ? gdn_dispatch<W<bf16_t, true>::template K, false>(a, sb, f.ckpt_fmt, f.read_fmt, st)
+                  : gdn_dispatch<W<float, true>::template K, false>(a, sb, f.ckpt_fmt, f.read_fmt, st);
+  return a.bf16 ? gdn_dispatch<W<bf16_t, false>::template K>(a, sb, f.ckpt_fmt, f.read_fmt, st)
+                : gdn_dispatch<W<float, false>::template K>(a, sb, f.ckpt_fmt, f.read_fmt, st);
+}
 
 }  // namespace
 
-int launch_gdn_step(const GdnStepArgs &a, const FormatBufs &f, hipStream_t st) {
-  return a.bf16 ? gdn_dispatch<GStepK<bf16_t>::template K>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st)
-                : gdn_dispatch<GStepK<float>::template K>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
-}
-int launch_gdn_flush(const GdnFlushArgs &a, const FormatBufs &f, hipStream_t st) {
-  return a.bf16 ? gdn_dispatch<GFlushK<bf16_t>::template K>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st)
-                : gdn_dispatch<GFlushK<float>::template K>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
-}
+int launch_gdn_step(const GdnStepArgs &a, const FormatBufs &f, hipStream_t st) { return launch_gdn<GStepK>(a, f, st); }
+int launch_gdn_flush(const GdnFlushArgs &a, const FormatBufs &f, hipStream_t st) { return launch_gdn<GFlushK>(a, f, st); }
 int launch_gdn_verify(const GdnVerifyArgs &a, const FormatBufs &f, hipStream_t st) {
-  return a.bf16 ? gdn_dispatch<GVerifyK<bf16_t>::template K>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st)
-                : gdn_dispatch<GVerifyK<float>::template K>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
+  return launch_gdn<GVerifyK>(a, f, st);
 }
 int launch_encode_state(const EncodeArgs &a, const FormatBufs &f, hipStream_t st) {
   return gdn_dispatch<GEncodeK>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);

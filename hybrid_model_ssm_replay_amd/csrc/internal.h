@@ -169,6 +169,7 @@ struct GdnRing {
 
 struct GdnStepArgs {
   Shape s;  // P = d_v, N = d_k
+  int decay_skip;  // REPLAY_FLAG_DECAY_SKIP set (float32 copies only)
   GdnRing ring;
   PtrHalves ptr;
   int32_t *status;
@@ -181,6 +182,7 @@ struct GdnStepArgs {
 
 struct GdnVerifyArgs {
   Shape s;
+  int decay_skip;  // REPLAY_FLAG_DECAY_SKIP set (float32 copies only)
   int T;
   GdnRing ring;
   PtrHalves ptr;
@@ -194,6 +196,7 @@ struct GdnVerifyArgs {
 
 struct GdnFlushArgs {
   Shape s;
+  int decay_skip;  // REPLAY_FLAG_DECAY_SKIP set (float32 copies only)
   GdnRing ring;
   PtrHalves ptr;
   int32_t *status;

@@ -39,7 +39,6 @@ namespace {
 // does not read its checkpoint; its fold is then a pure write of the folded
 // records [P3, Perspective, paragraph 1].  The comparison is A s < ln 2^-24 in
 // float32, with s the dt summed over the window records the computation uses.
-constexpr float kDecaySkipLog = -16.635532333438686f;  // ln 2^-24
 
 // exp(A s), or 0 when the decay skip drops it.
 template <bool SKIP>

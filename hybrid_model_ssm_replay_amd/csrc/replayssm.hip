@@ -33,7 +33,9 @@ int check_cfg(const replay_config *c) {
   }
   if ((c->flags & ~(REPLAY_FLAG_DECAY_SKIP | REPLAY_FLAG_BF16_RECORDS | REPLAY_FLAG_RECORDS_IN_RING)) || c->reserved)
     return REPLAY_EINVAL;
-  if ((c->flags & REPLAY_FLAG_DECAY_SKIP) && c->kind != REPLAY_KIND_MAMBA2) return REPLAY_ENOTSUP;
+  // The decay skip is float32-only for both families.
+  if ((c->flags & REPLAY_FLAG_DECAY_SKIP) && (c->ckpt_fmt != REPLAY_FMT_F32 || c->read_fmt != REPLAY_FMT_F32))
+    return REPLAY_ENOTSUP;
   if (c->ckpt_fmt < REPLAY_FMT_F32 || c->ckpt_fmt > REPLAY_FMT_F4E2M1_CS) return REPLAY_EINVAL;
   if (c->read_fmt < REPLAY_FMT_F32 || c->read_fmt > REPLAY_FMT_F4E2M1_CS) return REPLAY_EINVAL;
   if (c->ckpt_fmt == REPLAY_FMT_F32 && c->read_fmt == REPLAY_FMT_F32) return REPLAY_OK;
@@ -273,6 +275,7 @@ int replay_step(replay_ctx *ctx, const replay_record *rec, float *y, void *strea
   } else {
     GdnStepArgs a{};
     a.s = shape_of(c);
+    a.decay_skip = (c.flags & REPLAY_FLAG_DECAY_SKIP) ? 1 : 0;
     a.ring = gdn_ring(*ctx);
     a.ptr = halves(*ctx);
     a.status = ctx->buf.status;
@@ -311,6 +314,7 @@ int replay_flush(replay_ctx *ctx, const uint8_t *seq_mask, void *stream) {
   } else {
     GdnFlushArgs a{};
     a.s = shape_of(c);
+    a.decay_skip = (c.flags & REPLAY_FLAG_DECAY_SKIP) ? 1 : 0;
     a.ring = gdn_ring(*ctx);
     a.ptr = halves(*ctx);
     a.status = ctx->buf.status;
@@ -352,6 +356,7 @@ int replay_verify(replay_ctx *ctx, int32_t T, const replay_record *drafts, float
   } else {
     GdnVerifyArgs a{};
     a.s = shape_of(c);
+    a.decay_skip = (c.flags & REPLAY_FLAG_DECAY_SKIP) ? 1 : 0;
     a.T = T;
     a.ring = gdn_ring(*ctx);
     a.ptr = halves(*ctx);

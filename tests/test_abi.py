@@ -107,7 +107,8 @@ def test_low_precision_format_pairs(B):
     """Format pairs: split precision (F32 / FP16-SR / e4m3 checkpoint with an e2m1
     read copy) and one shared low-precision copy, for both families at
     state_dim 128; the two-axis read copy for GDN only; the decay skip and
-    zero-copy append stay float32-only for Mamba-2."""
+    zero-copy append stay float32-only for Mamba-2, and the decay skip is
+    float32-only for both families."""
     F = (B.FMT_F32, B.FMT_F16_SR, B.FMT_F8E4M3, B.FMT_F4E2M1_B16)
     split = [(c, B.FMT_F4E2M1_B16) for c in F[:3]] + [(c, c) for c in F[1:]]
     for cf, rf in split:
@@ -118,6 +119,9 @@ def test_low_precision_format_pairs(B):
     assert B.replay_validate_config(B.make_config(0, 2, 8, 2, 64, 128, 16, 4, B.FMT_F32, B.FMT_F4E2M1_CS)) == ns
     assert B.replay_validate_config(B.make_config(0, 2, 8, 2, 64, 64, 16, 4, B.FMT_F32, B.FMT_F4E2M1_B16)) == ns
     assert B.replay_validate_config(B.make_config(0, 2, 8, 2, 32, 128, 16, 4, B.FMT_F32, B.FMT_F4E2M1_B16)) == ns
+    assert B.replay_validate_config(B.make_config(1, 2, 8, 8, 128, 128, 16, 4, flags=B.FLAG_DECAY_SKIP)) == B.OK
+    assert B.replay_validate_config(B.make_config(1, 2, 8, 8, 128, 128, 16, 4, B.FMT_F32, B.FMT_F4E2M1_B16,
+                                                  flags=B.FLAG_DECAY_SKIP)) == ns
     for fl in (B.FLAG_DECAY_SKIP, B.FLAG_RECORDS_IN_RING):
         assert B.replay_validate_config(B.make_config(0, 2, 8, 2, 64, 128, 16, 4, B.FMT_F32, B.FMT_F4E2M1_B16,
                                                       flags=fl)) == ns

@@ -208,3 +208,60 @@ def test_snapshot_baseline_large_lds():
         snap.commit(torch.from_numpy(acc).cuda())
         ref.commit(acc)
         assert ckpt_rel_err(host(snap.state()), ref.state) <= TOL
+
+
+def test_decay_skip_matches_oracle():
+    """REPLAY_FLAG_DECAY_SKIP on Gated DeltaNet heads: heads whose window
+    log-decay falls below ln 2^-24 drop the checkpoint term (reading: see
+    oracle/gdn.py).  Heads 0 and 2 get strong decays (alpha = e^-30: below the
+    threshold from the first record; alpha ~ e^-2.5: from about the seventh),
+    head 1 the usual ones.  Against ReplaySession with the same rule (and the
+    exact form) through steps, folds, verifies, commits and a flush."""
+    import torch
+    from hybrid_model_ssm_replay_amd import binding as B
+    from hybrid_model_ssm_replay_amd.layer import ReplayLayer
+    shape = LayerShape("gdn", 3, 4, 128, 128, 4, 8)
+    announce("gdn decay skip", shape)
+    ins = InputStream(shape, 19)
+    S0 = ins.initial_state(zeros=False, scale=0.3)
+    lay = ReplayLayer("gdn", shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
+                      max_draft=4, ckpt0=S0, flags=B.FLAG_DECAY_SKIP)
+    skip = ReplaySession("gdn", S0, shape.window, decay_skip=True)
+    exact = ReplaySession("gdn", S0, shape.window)
+
+    def strong(r):
+        r["alpha"][..., 0] = np.float32(np.exp(-30.0))
+        r["alpha"][..., 2] = np.float32(np.exp(-2.5))
+        return r
+
+    rng = np.random.default_rng(19)
+    worst_skip = worst_exact = 0.0
+    for it in range(40):
+        if it % 7 == 6:
+            T = int(rng.integers(1, 5))
+            d = strong(ins.drafts(T))
+            y = host(lay.verify(to_dev(d)))
+            ys, ye = skip.verify(d), exact.verify(d)
+            acc = ins.accepted(T)
+            lay.commit(torch.from_numpy(acc).cuda())
+            skip.commit(acc)
+            exact.commit(acc)
+        elif it == 20:
+            lay.flush()
+            skip.flush()
+            exact.flush()
+            continue
+        else:
+            r = strong(ins.record())
+            y = host(lay.step(to_dev(r)))
+            ys, ye = skip.step(r), exact.step(r)
+        worst_skip = max(worst_skip, max_rel_err(y, ys, skip.scale))
+        worst_exact = max(worst_exact, max_rel_err(y, ye, exact.scale))
+    lay.flush()
+    skip.flush()
+    torch.cuda.synchronize()
+    print(f"[gdn skip] vs skip rule {worst_skip:.2e}, vs exact {worst_exact:.2e}")
+    assert worst_skip <= TOL, worst_skip
+    assert worst_exact <= TOL, worst_exact
+    assert ckpt_rel_err(host(lay.checkpoint), skip.ckpt) <= TOL
+    assert lay.status == 0
