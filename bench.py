@@ -77,11 +77,13 @@ class Timer:
         return e0.elapsed_time(e1) * 1e3 / n  # microseconds per call
 
 
-def dev_records(torch, ins, n, bf16=False):
-    """n device records; with bf16 the vector fields are bfloat16 tensors."""
+def dev_records(torch, ins, n, bf16=False, rec_fn=None):
+    """n device records; with bf16 the vector fields are bfloat16 tensors; rec_fn
+    (optional) edits each host record first."""
     from synth import VECTOR_FIELDS
     cast = (lambda k, t: t.to(torch.bfloat16) if bf16 and k in VECTOR_FIELDS else t)  # noqa: E731
-    return [{k: cast(k, torch.from_numpy(v).cuda()) for k, v in ins.record().items()} for _ in range(n)]
+    edit = rec_fn or (lambda r: r)  # noqa: E731
+    return [{k: cast(k, torch.from_numpy(v).cuda()) for k, v in edit(ins.record()).items()} for _ in range(n)]
 
 
 def _bf16(flags):
@@ -89,11 +91,11 @@ def _bf16(flags):
     return bool(flags & FLAG_BF16_RECORDS)
 
 
-def bench_replay(torch, shape, seed, steps, warmup, pool=32, flags=0):
+def bench_replay(torch, shape, seed, steps, warmup, pool=32, flags=0, rec_fn=None):
     from hybrid_model_ssm_replay_amd.layer import ReplayLayer
     from synth import InputStream
     ins = InputStream(shape, seed, bf16_vectors=_bf16(flags))
-    recs = dev_records(torch, ins, pool, _bf16(flags))
+    recs = dev_records(torch, ins, pool, _bf16(flags), rec_fn)
     kw = dict(A=ins.params["A"], D=ins.params["D"]) if shape.kind == "mamba2" else {}
     lay = ReplayLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.window,
                       groups=shape.groups, flags=flags, **kw)
@@ -154,8 +156,9 @@ def bench_conv(torch, shape, seed, steps, warmup, pool=32, flags=0):
     return tm.run(lambda i: conv.step(recs[(warmup + i) % pool], y), steps)
 
 
-def bench_verify(torch, shape, T, seed, reps=16):
-    """Replay verify + commit vs snapshot verify + commit, batch as in shape (accepted counts uniform in 0..T)."""
+def bench_verify(torch, shape, T, seed, reps=16, snapshot=True):
+    """Replay verify + commit vs snapshot verify + commit (None without `snapshot`),
+    batch as in shape (accepted counts uniform in 0..T)."""
     from hybrid_model_ssm_replay_amd.layer import ReplayLayer, SnapshotLayer
     from synth import InputStream
     ins = InputStream(shape, seed)
@@ -174,6 +177,9 @@ def bench_verify(torch, shape, T, seed, reps=16):
     tm.run(rv, 8)
     us_replay = tm.run(rv, reps)
     del lay
+    if not snapshot:
+        torch.cuda.empty_cache()
+        return us_replay, None
     snap = SnapshotLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, T,
                          groups=shape.groups, **kw)
 
@@ -573,6 +579,23 @@ def main(argv=None):
                              "tokens_per_s": gshape.batch / us_g * 1e6,
                              "traffic_bytes_per_launch": stored_traffic("gdn_replay_step_b256_traffic.txt", "gdn")}
         extra["gdn_b256"]["replay_step_distribution"] = step_distribution(torch, gshape, 2)
+        if want("skip"):
+            import numpy as np
+
+            from hybrid_model_ssm_replay_amd.binding import FLAG_DECAY_SKIP
+
+            def fast_decay(r):  # every other head decays by e^-2.5 per token: below 2^-24 within 7 records
+                r["alpha"][..., ::2] = np.float32(np.exp(-2.5))
+                return r
+            log("gdn replay step with the decay skip", gname)
+            us_gs = bench_replay(torch, gshape, 2, steps_timed, warmup_timed, flags=FLAG_DECAY_SKIP)
+            us_gf = bench_replay(torch, gshape, 2, steps_timed, warmup_timed, rec_fn=fast_decay)
+            us_gfs = bench_replay(torch, gshape, 2, steps_timed, warmup_timed, flags=FLAG_DECAY_SKIP,
+                                  rec_fn=fast_decay)
+            extra["gdn_b256"]["decay_skip"] = {
+                "synthetic_inputs": {"exact_us": us_g, "skip_us": us_gs, "speedup": us_g / us_gs},
+                "half_heads_fast_decay": {"exact_us": us_gf, "skip_us": us_gfs, "speedup": us_gf / us_gfs},
+                "rule": "checkpoint term dropped where exp(g) < 2^-24 (an approximation)"}
 
         for T in (4, 8) if want("gdn_verify") else ():
             log("gdn verify T", T)

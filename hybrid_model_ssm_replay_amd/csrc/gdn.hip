@@ -401,6 +401,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   int base = ck, sb0 = s0;
   float kj[NCH];         // this thread's slice of key grp (an older record)
   float uo[kMaxOld];     // older pseudo-values of this lane's row
+  float sk_fold = 0.f, sq_fold = 0.f;  // low-precision read copy: S k_m, S q_m of the fold result
   if (fold) {
     if constexpr (RF == CF) {
       if constexpr (!SKIP) SIO<RF, NCH, RBW, CM>::decode(s, raw);
@@ -412,9 +413,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       SIO<CF, NCH, RBW, CM>::decode(s, rc);
       gdn_fold<CF, RF, NCH, RBW, R>(s, L, s0, rp, Ls, rb0, lane, &lds_all[wave]);
     }
-    // Float32 copies: s already is what the copy holds.  Otherwise the copies
-    // are stored after this token's products with the fold result (below).
-    if constexpr (!kLossy) store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
+    if constexpr (kLossy) {
+      // This token's output comes from the float32 fold result: its products
+      // S k_m and S q_m first (k_m, q_m reach every wave through LDS), then
+      // both copies are stored and s becomes what the read copy holds, the S0
+      // of the window's later steps (and of the pseudo-value cached here).
+      if (grp == 0) {
+        float *kd = reinterpret_cast<float *>(kq_s[0]), *qd = reinterpret_cast<float *>(kq_s[1]);
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          kd[NCH * r16 + i] = km[i];
+          qd[NCH * r16 + i] = qm[i];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < RBW; ++k) {
+        float ak = 0.f, aq = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const int c4 = colq<NCH, CM>(c, q) >> 2;
+          ak += dot4(s[k][c], kq_s[0][c4]);
+          aq += dot4(s[k][c], kq_s[1][c4]);
+        }
+        ak = sum_quarters(ak);
+        aq = sum_quarters(aq);
+        if (q == k) {
+          sk_fold = ak;
+          sq_fold = aq;
+        }
+      }
+    }
+    // s becomes what the read copy now holds (float32 copies: the fold result itself).
+    store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
     base = pos;
     sb0 = slot;
 #pragma unroll
@@ -454,7 +485,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       dot_s[0][grp] = dk;
       dot_s[1][grp] = dq;
     }
-    if (grp == 0) {
+    if (grp == 0 && !(kLossy && fold)) {  // (a lossy fold step has written them already)
       float *kd = reinterpret_cast<float *>(kq_s[0]), *qd = reinterpret_cast<float *>(kq_s[1]);
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
@@ -499,32 +530,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       sqr = aq;
     }
   }
-  // After a fold of a low-precision read copy, skr and sqr came from the fold
-  // result; store both copies now and take S0 k_m for the cached pseudo-value
-  // from what the read copy holds, which the window's later steps read.
-  float skc = skr;
-  if constexpr (kLossy) {
-    if (fold) {
-      store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
-#pragma unroll
-      for (int k = 0; k < RBW; ++k) {
-        float ak = 0.f;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) ak += dot4(s[k][c], kq_s[0][colq<NCH, CM>(c, q) >> 2]);
-        ak = sum_quarters(ak);
-        if (q == k) skc = ak;
-      }
-    }
-  }
+  // After a fold of a low-precision read copy the output takes the fold
+  // result's products; the cached pseudo-value, those of the read copy (skr).
+  const bool from_fold = kLossy && fold;
+  const float sk_out = from_fold ? sk_fold : skr, sq_out = from_fold ? sq_fold : sqr;
   float acc_k = 0.f, acc_q = 0.f;
 #pragma unroll
   for (int t = 0; t < kMaxOld; ++t) {
     acc_k += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), t)) * uo[t];
     acc_q += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), t)) * uo[t];
   }
-  const float um = be_in * (v_in - egm * skr - acc_k);  // this token's pseudo-value for its output
-  const float uc = kLossy ? be_in * (v_in - egm * skc - acc_k) : um;  // ... as the window's S0 (the read copy) gives it
-  const float o = egm * sqr + acc_q + kmq * um;
+  const float uc = be_in * (v_in - egm * skr - acc_k);  // this token's pseudo-value from the window's S0
+  const float um = kLossy ? be_in * (v_in - egm * sk_out - acc_k) : uc;  // ... and for its output
+  const float o = egm * sq_out + acc_q + kmq * um;
 
   // 3. Output and append.
   if (q < RBW) {
@@ -615,43 +633,53 @@ __device__ __forceinline__ floatx4 mfma_4x4x1(float a, float b, floatx4 c) {
 // lane per row) with the committed rows known.  The drafts' keys, pseudo-
 // values and scalars are staged in the ring, so that a commit is only a
 // pointer move.
-template <int RBW, bool DUAL>
+// Per wave; ND = 4 NP drafts at most.
+template <int RBW, bool DUAL, int ND = kMaxL>
 struct GdnVerifyLds {
-  float W[16 * RBW][17];   // [row][draft]: S0 k_d
-  float SQ[16 * RBW][17];  // [row][draft]: S0 q_d
-  float A[16][17];         // [draft][record]: beta_t e^{g_t - g_j} (k_j . k_t) for j < t, else 0
-  float Bq[16][17];        // [draft][record]: e^{g_t - g_j} (k_j . q_d) for j <= t, else 0
-  float g[16], beta[16];   // record j: decay prefix, beta
-  float WQ[DUAL ? 16 * RBW : 1][17];  // after a fold-first: Q k_d for the read copy Q (cached pseudo-values)
+  float W[16 * RBW][ND + 1];   // [row][draft]: S0 k_d
+  float SQ[16 * RBW][ND + 1];  // [row][draft]: S0 q_d
+  float A[ND][17];             // [draft][record]: beta_t e^{g_t - g_j} (k_j . k_t) for j < t, else 0
+  float Bq[ND][17];            // [draft][record]: e^{g_t - g_j} (k_j . q_d) for j <= t, else 0
+  float g[16], beta[16];       // record j: decay prefix, beta
+  // [record][row of the wave]: the committed records' pseudo-values, then the
+  // drafts' values (c + T <= 16), staged by direct global-to-LDS loads issued
+  // with the window's keys, so the solve finds them in LDS.
+  float wst[16][16 * RBW];
+  float WQ[DUAL ? 16 * RBW : 1][ND + 1];  // after a fold-first: Q k_d for the read copy Q (cached pseudo-values)
 };
 
-template <int RBW, bool DUAL>
+// The fold part only for a re-solving fold-first (a separate read copy).
+template <int RBW, bool DUAL, int ND, bool REFOLD>
 union GdnWaveLds {
-  GdnLds<RBW> fold;                // a re-solving fold-first
-  GdnVerifyLds<RBW, DUAL> verify;  // the drafts (after the fold)
+  GdnLds<REFOLD ? RBW : 1> fold;       // a re-solving fold-first
+  GdnVerifyLds<RBW, DUAL, ND> verify;  // the drafts (after the fold)
 };
 
 // Occupancy target for the float32 copies: three waves per SIMD (at most 168
 // VGPRs; the LDS of three workgroups fits a CU).
 template <int CF, int RF>
-constexpr int verify_waves_per_eu() { return (CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32) ? 3 : 1; }
+constexpr int verify_waves_per_eu() { return (CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32) ? 4 : 1; }
 
 // SKIP (decay skip, float32 copies): the rule applies to the fold-first and to
 // each draft's output, but the checkpoint is always read.
-template <int CF, int RF, int NCH, int RBW, typename R, bool SKIP = false>
+// NP: the most passes of four drafts the launch needs (T <= 4 NP); it sizes the
+// drafts' LDS staging, so that short verifies leave LDS for more workgroups.
+template <int CF, int RF, int NCH, int RBW, typename R, bool SKIP = false, int NP = kMaxL / 4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<CF, RF>())))
 void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
   constexpr int DK = 16 * NCH;
   constexpr int CM = col_map(CF, RF);
-  constexpr int kPass = kMaxL / 4;
+  constexpr int kPass = NP;
+  constexpr int RW = 16 * RBW;                     // state rows of one wave
+  constexpr bool kStage = sizeof(R) == 4;          // float32 records: staged by 4-byte direct loads
   constexpr bool kLossy = RF != REPLAY_FMT_F32;  // the read copy is not the float32 fold result
   static_assert(!SKIP || (CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32), "decay skip: float32 copies only");
   __shared__ float4 ldsK[NCH][64];                 // [chunk cc][record j + 16 q]: k_j at colq(cc, q)
   __shared__ float4 ldsD[kPass * 2 * NCH * 16];    // [((p 2 + w) NCH + cc) 16 + 4 m + q]: w = 0: k, 1: q of draft 4 p + m
-  __shared__ GdnWaveLds<RBW, kLossy> lds_all[4];
+  __shared__ GdnWaveLds<RBW, kLossy, 4 * NP, (CF != RF)> lds_all[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r16 = lane & 15, gq = r16 >> 2, m4 = r16 & 3;
-  GdnVerifyLds<RBW, kLossy> &sv = lds_all[wave].verify;
+  GdnVerifyLds<RBW, kLossy, 4 * NP> &sv = lds_all[wave].verify;
   const Shape &sh = a.s;
   const int T = a.T;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -668,14 +696,19 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
   auto dk_ = [&](int i) { return zc ? rp.rk + (size_t)wrap(sp, i, Ls) * rp.ks : gk_ + (((size_t)b * T + i) * H + h) * DK; };
   auto dv_ = [&](int i) { return gv_ + (((size_t)b * T + i) * H + h) * DV; };
   auto dsc = [&](const float *f, int i) { return f[((size_t)b * T + i) * H + h]; };
-  const int npass = (T + 3) >> 2;
+  const int npass = min((T + 3) >> 2, kPass);
 
   // 1. The read copy first, the pointer words (before any global-to-LDS load:
   //    the compiler keeps loads that follow such a load off the scalar unit),
   //    the drafts' keys and queries into LDS (load j of the tile by wave
   //    j % nwaves) and this lane's row of the drafts' values.
+  // Float32 copies load straight into the tile s; other formats keep the stored
+  // bits in raw until they are decoded.
+  constexpr bool kF32 = CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32;
+  float4 s[RBW][NCH];
   typename SIO<RF, NCH, RBW, CM>::Raw raw;
-  SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
+  if constexpr (kF32) load_rows_g<NCH, RBW, CM>(s, static_cast<const float *>(sb.rd.data) + head, rb0, lane);
+  else SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
   const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
   sp = fmod_(pos > 0 ? pos : 0, sh.fLs);  // never from a negative position (a flagged pair stores nothing)
   {
@@ -703,16 +736,16 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
   const bool fold = count + T > L;  // implies count >= 1 because T <= L
   const int s0 = fmod_(ck, sh.fLs);
   int base = ck, sb0 = s0;
-  float4 s[RBW][NCH];
   if (fold) {
     if constexpr (RF == CF) {
-      SIO<RF, NCH, RBW, CM>::decode(s, raw);
+      if constexpr (!kF32) SIO<RF, NCH, RBW, CM>::decode(s, raw);
     } else {
       typename SIO<CF, NCH, RBW, CM>::Raw rc;
       SIO<CF, NCH, RBW, CM>::load(rc, sb.ck, head, rb0, lane);
       SIO<CF, NCH, RBW, CM>::decode(s, rc);
     }
-    gdn_fold<CF, RF, NCH, RBW, R, SKIP>(s, count, s0, rp, Ls, rb0, lane, &lds_all[wave].fold);
+    if constexpr (CF != RF) gdn_fold<CF, RF, NCH, RBW, R, SKIP>(s, count, s0, rp, Ls, rb0, lane, &lds_all[wave].fold);
+    else gdn_fold<CF, RF, NCH, RBW, R, SKIP>(s, count, s0, rp, Ls, rb0, lane, nullptr);
     // Float32 copies: s already is what the copy holds.  Otherwise the drafts'
     // outputs come from the fold result s, and the copies are stored after
     // the passes (below).
@@ -724,10 +757,27 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
 
   // 3. Window records: every key into LDS (committed from the ring, drafts from
   //    the input; chunk cc by wave cc % nwaves), and alpha, beta of record r16.
+  //    The rows of this wave of the committed pseudo-values and of the drafts'
+  //    values go to the wave's LDS (64 / RW records per load).
   {
     const int j = r16 < nrec ? r16 : nrec - 1;
     const R *kj = j < c ? rp.rk + (size_t)wrap(sb0, j, Ls) * rp.ks : dk_(j - c);
     for (int cc = wave; cc < NCH; cc += nwaves) stage4<R>(kj + colq<NCH, CM>(cc, q), &ldsK[cc][0], lane);
+  }
+  if constexpr (kStage) {
+    constexpr int kPer = 64 / RW;  // records per load instruction
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int r = rb0 * 16 + lane % RW;
+    const float *ru = rp.ru + r, *vd = reinterpret_cast<const float *>(dv_(0)) + r;
+    const size_t vstride = (size_t)H * DV;  // draft to draft in the values input
+#pragma unroll
+    for (int j0 = 0; j0 < kMaxL; j0 += kPer) {
+      if (j0 < nrec) {
+        const int j = min(j0 + lane / RW, nrec - 1);
+        const float *src = j < c ? ru + (size_t)wrap(sb0, j, Ls) * rp.vs : vd + (size_t)(j - c) * vstride;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src), (lds_void *)&sv.wst[j0][0], 4, 0, 0);
+      }
+    }
   }
   float al, be;
   {
@@ -737,7 +787,8 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
     al = r16 < nrec ? a1 : 1.f;
     be = r16 < nrec ? b1 : 0.f;
   }
-  if (!fold) SIO<RF, NCH, RBW, CM>::decode(s, raw);
+  if constexpr (!kF32)
+    if (!fold) SIO<RF, NCH, RBW, CM>::decode(s, raw);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's global-to-LDS loads have landed
   __syncthreads();                // and every other wave's; all ring reads are done
 
@@ -754,20 +805,36 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
     const int d = 4 * p + m4;  // this lane's draft
     const float4 *kd = &ldsD[(p * 2 * NCH) * 16 + 4 * m4 + q];        // k_d at chunk cc: kd[16 cc]
     const float4 *qd = &ldsD[((p * 2 + 1) * NCH) * 16 + 4 * m4 + q];  // q_d at chunk cc: qd[16 cc]
-    {
-      floatx4 dk = {0.f, 0.f, 0.f, 0.f}, dqq = {0.f, 0.f, 0.f, 0.f};
+    // One sweep over the column chunks feeds all six accumulation chains, so
+    // each chunk of k_d, q_d is read from LDS once and dies at once.
+    floatx4 dk = {0.f, 0.f, 0.f, 0.f}, dqq = {0.f, 0.f, 0.f, 0.f}, w[RBW], sq[RBW];
 #pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
-        const float4 kj = ldsK[cc][lane], kv = kd[16 * cc], qv = qd[16 * cc];
-        dk = mfma_4x4x1(kj.x, kv.x, dk);
-        dk = mfma_4x4x1(kj.y, kv.y, dk);
-        dk = mfma_4x4x1(kj.z, kv.z, dk);
-        dk = mfma_4x4x1(kj.w, kv.w, dk);
-        dqq = mfma_4x4x1(kj.x, qv.x, dqq);
-        dqq = mfma_4x4x1(kj.y, qv.y, dqq);
-        dqq = mfma_4x4x1(kj.z, qv.z, dqq);
-        dqq = mfma_4x4x1(kj.w, qv.w, dqq);
+    for (int k = 0; k < RBW; ++k) w[k] = sq[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+      const float4 kj = ldsK[cc][lane], kv = kd[16 * cc], qv = qd[16 * cc];
+      dk = mfma_4x4x1(kj.x, kv.x, dk);
+      dqq = mfma_4x4x1(kj.x, qv.x, dqq);
+      dk = mfma_4x4x1(kj.y, kv.y, dk);
+      dqq = mfma_4x4x1(kj.y, qv.y, dqq);
+      dk = mfma_4x4x1(kj.z, kv.z, dk);
+      dqq = mfma_4x4x1(kj.z, qv.z, dqq);
+      dk = mfma_4x4x1(kj.w, kv.w, dk);
+      dqq = mfma_4x4x1(kj.w, qv.w, dqq);
+#pragma unroll
+      for (int k = 0; k < RBW; ++k) {
+        w[k] = mfma_4x4x1(s[k][cc].x, kv.x, w[k]);
+        sq[k] = mfma_4x4x1(s[k][cc].x, qv.x, sq[k]);
+        w[k] = mfma_4x4x1(s[k][cc].y, kv.y, w[k]);
+        sq[k] = mfma_4x4x1(s[k][cc].y, qv.y, sq[k]);
+        w[k] = mfma_4x4x1(s[k][cc].z, kv.z, w[k]);
+        sq[k] = mfma_4x4x1(s[k][cc].z, qv.z, sq[k]);
+        w[k] = mfma_4x4x1(s[k][cc].w, kv.w, w[k]);
+        sq[k] = mfma_4x4x1(s[k][cc].w, qv.w, sq[k]);
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep each chunk's LDS reads with its MFMAs (register pressure)
+    }
+    {
       float kk[4], kq[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -788,24 +855,11 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
     }
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
-      floatx4 w = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
-        const float4 kv = kd[16 * cc], qv = qd[16 * cc];
-        w = mfma_4x4x1(s[k][cc].x, kv.x, w);
-        w = mfma_4x4x1(s[k][cc].y, kv.y, w);
-        w = mfma_4x4x1(s[k][cc].z, kv.z, w);
-        w = mfma_4x4x1(s[k][cc].w, kv.w, w);
-        sq = mfma_4x4x1(s[k][cc].x, qv.x, sq);
-        sq = mfma_4x4x1(s[k][cc].y, qv.y, sq);
-        sq = mfma_4x4x1(s[k][cc].z, qv.z, sq);
-        sq = mfma_4x4x1(s[k][cc].w, qv.w, sq);
-      }
       float wv[4], sqv[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        wv[v] = sum_quarters(w[v]);
-        sqv[v] = sum_quarters(sq[v]);
+        wv[v] = sum_quarters(w[k][v]);
+        sqv[v] = sum_quarters(sq[k][v]);
       }
       if (q == 0) {
 #pragma unroll
@@ -856,15 +910,25 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
   //    loaded only now: held through the passes above it would cost a wave per
   //    SIMD.
   if (lane < 16 * RBW) {
-    float u[kMaxL], vrow[kMaxL];
+    // u[t]: this row of pseudo-value t (committed, then solved); vrow[d] (bf16
+    // records only): this row of draft d's value.  Float32 records come from
+    // the wave's LDS (staged in section 3): wst[t] is committed u_t for t < c
+    // and the value of draft t - c after.
+    float u[kMaxL], vrow[kStage ? 1 : kMaxL];
+    if constexpr (kStage) {
 #pragma unroll
-    for (int j = 0; j < kMaxL; ++j) {
-      const int jc = j < c ? j : 0;
-      const float v = rp.ru[(size_t)wrap(sb0, jc, Ls) * rp.vs + row];
-      u[j] = j < c ? v : 0.f;
+      for (int j = 0; j < kMaxL; ++j) u[j] = j < c ? sv.wst[j][lane] : 0.f;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kMaxL; ++j) {
+        const int jc = j < c ? j : 0;
+        const float v = rp.ru[(size_t)wrap(sb0, jc, Ls) * rp.vs + row];
+        u[j] = j < c ? v : 0.f;
+      }
+#pragma unroll
+      for (int d = 0; d < kMaxL; ++d) vrow[d] = ldr<R>(dv_(d < T ? d : T - 1) + row);
     }
-#pragma unroll
-    for (int d = 0; d < kMaxL; ++d) vrow[d] = ldr<R>(dv_(d < T ? d : T - 1) + row);
+    auto vval = [&](int t) { return kStage ? sv.wst[t][lane] : vrow[t - c]; };  // value of window record t
     const bool dual = kLossy && fold;  // outputs from the fold result, cached values from the read copy
 #pragma unroll
     for (int t = 0; t < kMaxL; ++t) {
@@ -872,7 +936,7 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
         const int d = t - c;
         const float bt = sv.beta[t];
         const float et = (SKIP && sv.g[t] < kDecaySkipLog) ? 0.f : __expf(sv.g[t]);  // checkpoint-term weight
-        float v = bt * vrow[d] - bt * et * sv.W[lane][d];
+        float v = bt * vval(t) - bt * et * sv.W[lane][d];
 #pragma unroll
         for (int j = 0; j < t; ++j) v -= sv.A[d][j] * u[j];
         u[t] = v;
@@ -881,7 +945,7 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
         for (int j = 0; j <= t; ++j) o += sv.Bq[d][j] * u[j];
         a.y[(((size_t)b * T + d) * H + h) * DV + row] = o;
         if (!dual) rp.ru[(size_t)wrap(sb0, t, Ls) * rp.vs + row] = v;  // stage the pseudo-value
-        if constexpr (RF != CF) str<R>(rp.rv + (size_t)wrap(sb0, t, Ls) * rp.vs + row, vrow[d]);
+        if constexpr (RF != CF) str<R>(rp.rv + (size_t)wrap(sb0, t, Ls) * rp.vs + row, vval(t));
       }
     }
     if constexpr (kLossy) {
@@ -890,7 +954,7 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
         for (int t = 0; t < kMaxL; ++t) {
           if (t < nrec) {
             const float bt = sv.beta[t], et = __expf(sv.g[t]);
-            float v = bt * vrow[t] - bt * et * sv.WQ[lane][t];
+            float v = bt * vval(t) - bt * et * sv.WQ[lane][t];
 #pragma unroll
             for (int j = 0; j < t; ++j) v -= sv.A[t][j] * u[j];
             u[t] = v;
@@ -1117,8 +1181,20 @@ int gdn_dispatch_f32(const Args &a, hipStream_t st) {
   };
 RSSM_WRAP4(GStepK, gdn_replay_step)
 RSSM_WRAP4(GFlushK, gdn_flush)
-RSSM_WRAP4(GVerifyK, gdn_replay_verify)
 #undef RSSM_WRAP4
+// The verify by its largest pass count NP (T <= 4 NP).
+#define RSSM_WRAPV(name, NP_)                                                        \
+  template <typename R, bool SKIP = false>                                           \
+  struct name {                                                                      \
+    template <int CF, int RF, int NCH, int RBW>                                      \
+    struct K {                                                                       \
+      static constexpr auto fn = gdn_replay_verify<CF, RF, NCH, RBW, R, SKIP, NP_>; \
+    };                                                                               \
+  };
+RSSM_WRAPV(GVerifyK1, 1)
+RSSM_WRAPV(GVerifyK2, 2)
+RSSM_WRAPV(GVerifyK4, 4)
+#undef RSSM_WRAPV
 template <int CF, int RF, int NCH, int RBW>
 struct GEncodeK {
   static constexpr auto fn = gdn_encode_state<CF, RF, NCH, RBW>;
@@ -1150,7 +1226,9 @@ int launch_gdn(const Args &a, const FormatBufs &f, hipStream_t st) {
 int launch_gdn_step(const GdnStepArgs &a, const FormatBufs &f, hipStream_t st) { return launch_gdn<GStepK>(a, f, st); }
 int launch_gdn_flush(const GdnFlushArgs &a, const FormatBufs &f, hipStream_t st) { return launch_gdn<GFlushK>(a, f, st); }
 int launch_gdn_verify(const GdnVerifyArgs &a, const FormatBufs &f, hipStream_t st) {
-  return launch_gdn<GVerifyK>(a, f, st);
+  if (a.T <= 4) return launch_gdn<GVerifyK1>(a, f, st);
+  if (a.T <= 8) return launch_gdn<GVerifyK2>(a, f, st);
+  return launch_gdn<GVerifyK4>(a, f, st);
 }
 int launch_encode_state(const EncodeArgs &a, const FormatBufs &f, hipStream_t st) {
   return gdn_dispatch<GEncodeK>(a, state_bufs(f), f.ckpt_fmt, f.read_fmt, st);
