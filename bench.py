@@ -108,6 +108,31 @@ def bench_replay(torch, shape, seed, steps, warmup, pool=32, flags=0, rec_fn=Non
     return us
 
 
+def bench_replay_staggered(torch, shape, seed, steps, warmup, pool=32):
+    """The replay step with the sequences' windows out of phase, as in serving:
+    one verify of L - 1 drafts whose accepted counts are b mod L moves sequence b
+    to window phase b mod L, so each step folds 1/L of the sequences instead of
+    all of them every L-th step.  Same layer, same bytes per step on average."""
+    from hybrid_model_ssm_replay_amd.layer import ReplayLayer
+    from synth import InputStream
+    L = shape.window
+    ins = InputStream(shape, seed)
+    recs = dev_records(torch, ins, pool)
+    kw = dict(A=ins.params["A"], D=ins.params["D"]) if shape.kind == "mamba2" else {}
+    lay = ReplayLayer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, L,
+                      groups=shape.groups, max_draft=L - 1, **kw)
+    d = {k: torch.from_numpy(v).cuda() for k, v in ins.drafts(L - 1).items()}
+    lay.verify(d)
+    lay.commit(torch.arange(shape.batch, dtype=torch.int32, device="cuda") % L)
+    y = torch.empty((shape.batch, shape.heads, shape.head_dim), device="cuda")
+    tm = Timer(torch)
+    tm.run(lambda i: lay.step(recs[i % pool], y), warmup)
+    us = tm.run(lambda i: lay.step(recs[(warmup + i) % pool], y), steps)
+    if lay.status != 0:
+        raise RuntimeError(f"device status {lay.status:#x}")
+    return us
+
+
 def step_distribution(torch, shape, seed, windows=8, pool=32):
     """Per-step times of the replay step (an event pair around every step) over
     `windows` whole windows after one warm-up window: p50 and p99 over all
@@ -528,6 +553,11 @@ def main(argv=None):
              "tokens_per_s": shape.batch / us * 1e6}
     log("per-step distribution", name)
     extra["replay_step_distribution"] = step_distribution(torch, shape, 1)
+    log("replay step, windows out of phase", name)
+    us_st = bench_replay_staggered(torch, shape, 1, steps_timed, warmup_timed)
+    extra["replay_step_staggered"] = {"us": us_st, "gbs": (rd + wr) / us_st / 1e3,
+                                      "frac_of_peak": (rd + wr) / us_st / 1e3 / HBM_PEAK_GBS,
+                                      "note": "sequence b at window phase b mod L: each step folds 1/L of them"}
     log("hbm probe")
     rgbs, cgbs = bench_probe(torch)
     extra.update({"hbm_probe_read_gbs": rgbs, "hbm_probe_copy_gbs": cgbs})

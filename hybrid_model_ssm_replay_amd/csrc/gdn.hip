@@ -350,9 +350,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 
   // 1. The read copy first (a non-fold step reads only it), then what needs no
   //    pointer.  With the decay skip the read waits for the decision (below).
+  // Float32 copies load straight into the tile s (decay skip: once decided);
+  // other formats keep the stored bits in raw until they are decoded.
+  constexpr bool kF32 = CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32;
   typename SIO<RF, NCH, RBW, CM>::Raw raw;
-  float4 s[RBW][NCH];      // the checkpoint rows of this wave (decay skip: read into s directly)
-  if constexpr (!SKIP) SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
+  float4 s[RBW][NCH];
+  if constexpr (kF32 && !SKIP) load_rows_g<NCH, RBW, CM>(s, static_cast<const float *>(sb.rd.data) + head, rb0, lane);
+  else if constexpr (!SKIP) SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
   float km[NCH], qm[NCH];  // columns NCH r16 .. of k_m and q_m
   if (!zc) load_cols<NCH, R>(km, kin + NCH * r16);
   load_cols<NCH, R>(qm, qin + NCH * r16);
@@ -404,7 +408,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   float sk_fold = 0.f, sq_fold = 0.f;  // low-precision read copy: S k_m, S q_m of the fold result
   if (fold) {
     if constexpr (RF == CF) {
-      if constexpr (!SKIP) SIO<RF, NCH, RBW, CM>::decode(s, raw);
+      if constexpr (!SKIP && !kF32) SIO<RF, NCH, RBW, CM>::decode(s, raw);
       gdn_fold<CF, RF, NCH, RBW, R, SKIP>(s, L, s0, rp, Ls, rb0, lane, nullptr);
     } else {
       __shared__ GdnLds<RBW> lds_all[4];
@@ -462,7 +466,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       const float v = rp.ru[(size_t)wrap(s0, tc, Ls) * rp.vs + orow];
       uo[t] = t < count ? v : 0.f;
     }
-    if constexpr (!SKIP) SIO<RF, NCH, RBW, CM>::decode(s, raw);
+    if constexpr (!SKIP && !kF32) SIO<RF, NCH, RBW, CM>::decode(s, raw);
   }
   const int nold = pos - base;  // older records in this window
 
