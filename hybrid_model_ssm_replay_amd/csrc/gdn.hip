@@ -439,6 +439,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
           const int c4 = colq<NCH, CM>(c, q) >> 2;
           ak += dot4(s[k][c], kq_s[0][c4]);
           aq += dot4(s[k][c], kq_s[1][c4]);
+          __builtin_amdgcn_sched_barrier(0);  // one chunk of k_m, q_m live at a time
         }
         ak = sum_quarters(ak);
         aq = sum_quarters(aq);
