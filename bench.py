@@ -31,8 +31,8 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 _CSRC = "hybrid_model_ssm_replay_amd/csrc/"
 # Sources each kernel family is built from: a stored counter summary is used only
 # while the hash of these files matches the one it records.
-KERNEL_SOURCES = {"m2": [_CSRC + f for f in ("mamba2.hip", "common.h", "internal.h")],
-                  "gdn": [_CSRC + f for f in ("gdn.hip", "codecs.h", "common.h", "internal.h")]}
+KERNEL_SOURCES = {"m2": [_CSRC + f for f in ("mamba2.hip", "state_io.h", "codecs.h", "common.h", "internal.h")],
+                  "gdn": [_CSRC + f for f in ("gdn.hip", "state_io.h", "codecs.h", "common.h", "internal.h")]}
 
 
 def log(*a):

@@ -408,6 +408,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   float sk_fold = 0.f, sq_fold = 0.f;  // low-precision read copy: S k_m, S q_m of the fold result
   if (fold) {
     if constexpr (RF == CF) {
+      // (e2m1: decoded apart from the non-fold branch's decode; 190 -> 155 VGPRs)
+      if constexpr (RF == REPLAY_FMT_F4E2M1_B16) opaque_words(raw);
       if constexpr (!SKIP && !kF32) SIO<RF, NCH, RBW, CM>::decode(s, raw);
       gdn_fold<CF, RF, NCH, RBW, R, SKIP>(s, L, s0, rp, Ls, rb0, lane, nullptr);
     } else {

@@ -513,6 +513,18 @@ __device__ __forceinline__ int mcol(int c, int M) {
   return colq<NCH, CM>(c, M >> 2) + (M & 3);
 }
 
+// An empty register constraint on every word of x: the compiler can no longer
+// treat x as the same value on both sides, so code that decodes it in two
+// branches is not hoisted above them (which would keep the decoded tile live
+// across the branch).
+template <typename T>
+__device__ __forceinline__ void opaque_words(T &x) {
+  static_assert(sizeof(T) % 4 == 0, "whole words");
+  uint32_t *w = reinterpret_cast<uint32_t *>(&x);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" : "+v"(w[i]));
+}
+
 // Views of one launch's stored copies from the host-side description.
 inline StateBufs state_bufs(const FormatBufs &f) {
   StateBufs sb;
