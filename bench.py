@@ -662,7 +662,7 @@ def main(argv=None):
 
     traffic = stored_traffic("m2_replay_step_b256_traffic.txt", "m2")
     roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-            "traffic": traffic, "kernel": "m2_replay_step<8, 2, false, float, false>",
+            "traffic": traffic, "kernel": "m2_replay_step<8, 2, false, float, false, 0, 0>",
             "bytes_per_launch": rd + wr}
     cpu = None if args.no_cpu else cpu_baseline(shape, 1)
     out = {

@@ -97,11 +97,18 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int | None 
             "factor_write": f_w, "traffic_bytes_per_launch": kf * 1024 * f_r + kw * 1024 * f_w}
 
 
-# The verify runs of bench.py: workload, seed, T values, launches per T of the
-# replay kernel (8 warm-up + 16 timed) and of the snapshot kernel (4 + 16).
-VERIFY_RUNS = (("mamba2_b512_h128_p64_n128_g8_l16", 3, "m2_replay_verify<8, 2, false, float>",
+# The verify runs of bench.py: workload, seed, launch grid (work-items), the
+# replay kernel for each T with the launches of that kernel to skip (the
+# Gated DeltaNet verify is compiled per pass count, one kernel per T here), and
+# the snapshot kernel.  Launches per T: 8 warm-up + 16 timed (replay), 4 + 16
+# (snapshot).
+VERIFY_RUNS = (("mamba2_b512_h128_p64_n128_g8_l16", 3, 8388608,
+                {4: ("m2_replay_verify<8, 2, false, float, 0, 0>", 0),
+                 8: ("m2_replay_verify<8, 2, false, float, 0, 0>", 1)},
                 "m2_snapshot_verify<8, 2, float>"),
-               ("gdn_b256_h32_d128_l16", 2, "gdn_replay_verify<0, 0, 8, 2, float>",
+               ("gdn_b256_h32_d128_l16", 2, 2097152,
+                {4: ("gdn_replay_verify<0, 0, 8, 2, float, false, 1>", 0),
+                 8: ("gdn_replay_verify<0, 0, 8, 2, float, false, 2>", 0)},
                 "gdn_snapshot_verify<8, 2, float>"))
 VERIFY_TS, REPLAY_CALLS, SNAP_CALLS, DRAFT_SETS = (4, 8), 24, 20, 4
 
@@ -111,10 +118,10 @@ def verify(fetch_csv: str, write_csv: str, trace_csv: str, copy_bytes: int = 1 <
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     from synth import WORKLOADS, InputStream
     from hybrid_model_ssm_replay_amd.traffic import Layer, snapshot_verify_bytes, verify_session_bytes
-    dur = _by_kernel(trace_csv, "duration")
     lines = ["| workload | T | kernel | launches | mean us | traffic GB | model GB | traffic / model | GB/s (model) |",
              "|---|---|---|---|---|---|---|---|---|"]
-    for name, seed, rk, sk in VERIFY_RUNS:
+    for name, seed, grid, rks, sk in VERIFY_RUNS:
+        dur = _by_kernel(trace_csv, "duration", grid)
         shape = WORKLOADS[name]
         lay = Layer(shape.kind, shape.batch, shape.heads, shape.head_dim, shape.state_dim, shape.groups, shape.window)
         for ti, T in enumerate(VERIFY_TS):
@@ -124,9 +131,10 @@ def verify(fetch_csv: str, write_csv: str, trace_csv: str, copy_bytes: int = 1 <
             accs = [ins.accepted(T) for _ in range(DRAFT_SETS)]
             rd, wr = verify_session_bytes(lay, T, accs, REPLAY_CALLS)
             srd, swr = snapshot_verify_bytes(lay, T)
-            for kern, calls, model in ((rk, REPLAY_CALLS, rd + wr), (sk, SNAP_CALLS, srd + swr)):
-                r = traffic(fetch_csv, write_csv, kern, copy_bytes, None, calls, ti * calls)
-                ds = dur[_find(dur, kern)][ti * calls:(ti + 1) * calls]
+            rk, rskip = rks[T]
+            for kern, calls, skip, model in ((rk, REPLAY_CALLS, rskip, rd + wr), (sk, SNAP_CALLS, ti, srd + swr)):
+                r = traffic(fetch_csv, write_csv, kern, copy_bytes, grid, calls, skip * calls)
+                ds = dur[_find(dur, kern)][skip * calls:(skip + 1) * calls]
                 us = sum(ds) / len(ds)
                 t = r["traffic_bytes_per_launch"]
                 lines.append(f"| {name} | {T} | `{kern}` | {r['dispatches']} | {us:.1f} | {t / 1e9:.3f} | "
