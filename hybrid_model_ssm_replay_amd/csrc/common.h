@@ -163,11 +163,17 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Sum over the four lanes l, l^16, l^32, l^48 (the four k-quarters of an MFMA row).
+// Sum over the four lanes l, l^16, l^32, l^48 (the four k-quarters of an MFMA
+// row), by the gfx950 row-swap instructions instead of LDS permutes: with both
+// operands v, v_permlane16_swap leaves row r of v in one result and row r ^ 1 in
+// the other (rows of 16 lanes), and v_permlane32_swap does the same for the two
+// halves of the wave.  Every lane adds the same two values (in either order),
+// so all four lanes get the same sum.  All 64 lanes must be active.
 __device__ __forceinline__ float sum_quarters(float v) {
-  v += __shfl_xor(v, 16, kWave);
-  v += __shfl_xor(v, 32, kWave);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // Double-buffered pointer words: half p holds pos[batch] then ckpt_pos[batch].

@@ -705,19 +705,71 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
   auto dsc = [&](const float *f, int i) { return f[((size_t)b * T + i) * H + h]; };
   const int npass = min((T + 3) >> 2, kPass);
 
-  // 1. The read copy first, the pointer words (before any global-to-LDS load:
-  //    the compiler keeps loads that follow such a load off the scalar unit),
-  //    the drafts' keys and queries into LDS (load j of the tile by wave
-  //    j % nwaves) and this lane's row of the drafts' values.
-  // Float32 copies load straight into the tile s; other formats keep the stored
-  // bits in raw until they are decoded.
+  // 1. The pointer words first (scalar loads issued ahead of the checkpoint
+  //    stream), then, with one stored copy, the window's ring records, so
+  //    that their loads do not queue behind the checkpoint's.
   constexpr bool kF32 = CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32;
+  const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
+  __builtin_amdgcn_sched_barrier(0);
+  const int count = pos - ck;
+  if (count < 0 || count > L || ck < 0) {
+    if (h == 0 && threadIdx.x == 0) {
+      atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
+      a.ptr.pos_out[b] = pos;
+      a.ptr.ckpt_out[b] = ck;
+    }
+    return;
+  }
+  sp = fmod_(pos, sh.fLs);
+  const bool fold = count + T > L;  // implies count >= 1 because T <= L
+  const int s0 = fmod_(ck, sh.fLs);
+  const int base = fold ? pos : ck, sb0 = fold ? wrap(s0, count, Ls) : s0;
+  const int c = pos - base, nrec = c + T;
+
+  // Window records: every key into LDS (committed from the ring, drafts from
+  // the input; chunk cc by wave cc % nwaves), and alpha, beta of record r16.
+  // The rows of this wave of the committed pseudo-values and of the drafts'
+  // values go to the wave's LDS (64 / RW records per load).  With a separate
+  // read copy the fold-first uses the same LDS, so these loads follow it.
+  auto stage_window = [&]() {
+    {
+      const int j = r16 < nrec ? r16 : nrec - 1;
+      const R *kj = j < c ? rp.rk + (size_t)wrap(sb0, j, Ls) * rp.ks : dk_(j - c);
+      for (int cc = wave; cc < NCH; cc += nwaves) stage4<R>(kj + colq<NCH, CM>(cc, q), &ldsK[cc][0], lane);
+    }
+    if constexpr (kStage) {
+      constexpr int kPer = 64 / RW;  // records per load instruction
+      typedef __attribute__((address_space(3))) void lds_void;
+      const int r = rb0 * 16 + lane % RW;
+      const float *ru = rp.ru + r, *vd = reinterpret_cast<const float *>(dv_(0)) + r;
+      const size_t vstride = (size_t)H * DV;  // draft to draft in the values input
+#pragma unroll
+      for (int j0 = 0; j0 < kMaxL; j0 += kPer) {
+        if (j0 < nrec) {
+          const int j = min(j0 + lane / RW, nrec - 1);
+          const float *src = j < c ? ru + (size_t)wrap(sb0, j, Ls) * rp.vs : vd + (size_t)(j - c) * vstride;
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src), (lds_void *)&sv.wst[j0][0], 4, 0, 0);
+        }
+      }
+    }
+  };
+  float al, be;
+  {
+    const int j = r16 < nrec ? r16 : nrec - 1;
+    const float a1 = (j < c || zc) ? rp.ral[wrap(sb0, j, Ls)] : dsc(a.alpha, j - c);
+    const float b1 = (j < c || zc) ? rp.rbe[wrap(sb0, j, Ls)] : dsc(a.beta, j - c);
+    al = r16 < nrec ? a1 : 1.f;
+    be = r16 < nrec ? b1 : 0.f;
+  }
+  if constexpr (CF == RF) stage_window();
+
+  // 2. The read copy, then the drafts' keys and queries into LDS (load j of
+  //    the tile by wave j % nwaves).  Float32 copies load straight into the
+  //    tile s; other formats keep the stored bits in raw until decoded.
   float4 s[RBW][NCH];
   typename SIO<RF, NCH, RBW, CM>::Raw raw;
   if constexpr (kF32) load_rows_g<NCH, RBW, CM>(s, static_cast<const float *>(sb.rd.data) + head, rb0, lane);
   else SIO<RF, NCH, RBW, CM>::load(raw, sb.rd, head, rb0, lane);
-  const int pos = a.ptr.pos_in[b], ck = a.ptr.ckpt_in[b];
-  sp = fmod_(pos > 0 ? pos : 0, sh.fLs);  // never from a negative position (a flagged pair stores nothing)
   {
     const int nload = (npass * 2 * NCH * 16) >> 6;
     for (int j = wave; j < nload; j += nwaves) {
@@ -729,20 +781,7 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
       stage4<R>(src + colq<NCH, CM>(cc, q2), &ldsD[64 * j], lane);
     }
   }
-  // 2. Pointers; fold-first when the window cannot take T more records.
-  const int count = pos - ck;
-  if (count < 0 || count > L || ck < 0) {
-    if (h == 0 && threadIdx.x == 0) {
-      atomicOr(a.status, REPLAY_STATUS_BAD_POINTERS);
-      a.ptr.pos_out[b] = pos;
-      a.ptr.ckpt_out[b] = ck;
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // no global-to-LDS load outlives the workgroup
-    return;
-  }
-  const bool fold = count + T > L;  // implies count >= 1 because T <= L
-  const int s0 = fmod_(ck, sh.fLs);
-  int base = ck, sb0 = s0;
+  // 3. Fold-first when the window cannot take T more records.
   if (fold) {
     if constexpr (RF == CF) {
       if constexpr (!kF32) SIO<RF, NCH, RBW, CM>::decode(s, raw);
@@ -757,42 +796,10 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
     // outputs come from the fold result s, and the copies are stored after
     // the passes (below).
     if constexpr (!kLossy) store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
-    base = pos;
-    sb0 = wrap(s0, count, Ls);
   }
-  const int c = pos - base, nrec = c + T;
-
-  // 3. Window records: every key into LDS (committed from the ring, drafts from
-  //    the input; chunk cc by wave cc % nwaves), and alpha, beta of record r16.
-  //    The rows of this wave of the committed pseudo-values and of the drafts'
-  //    values go to the wave's LDS (64 / RW records per load).
-  {
-    const int j = r16 < nrec ? r16 : nrec - 1;
-    const R *kj = j < c ? rp.rk + (size_t)wrap(sb0, j, Ls) * rp.ks : dk_(j - c);
-    for (int cc = wave; cc < NCH; cc += nwaves) stage4<R>(kj + colq<NCH, CM>(cc, q), &ldsK[cc][0], lane);
-  }
-  if constexpr (kStage) {
-    constexpr int kPer = 64 / RW;  // records per load instruction
-    typedef __attribute__((address_space(3))) void lds_void;
-    const int r = rb0 * 16 + lane % RW;
-    const float *ru = rp.ru + r, *vd = reinterpret_cast<const float *>(dv_(0)) + r;
-    const size_t vstride = (size_t)H * DV;  // draft to draft in the values input
-#pragma unroll
-    for (int j0 = 0; j0 < kMaxL; j0 += kPer) {
-      if (j0 < nrec) {
-        const int j = min(j0 + lane / RW, nrec - 1);
-        const float *src = j < c ? ru + (size_t)wrap(sb0, j, Ls) * rp.vs : vd + (size_t)(j - c) * vstride;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src), (lds_void *)&sv.wst[j0][0], 4, 0, 0);
-      }
-    }
-  }
-  float al, be;
-  {
-    const int j = r16 < nrec ? r16 : nrec - 1;
-    const float a1 = (j < c || zc) ? rp.ral[wrap(sb0, j, Ls)] : dsc(a.alpha, j - c);
-    const float b1 = (j < c || zc) ? rp.rbe[wrap(sb0, j, Ls)] : dsc(a.beta, j - c);
-    al = r16 < nrec ? a1 : 1.f;
-    be = r16 < nrec ? b1 : 0.f;
+  if constexpr (CF != RF) {
+    __syncthreads();  // every wave's fold is done with the LDS the window now takes
+    stage_window();
   }
   if constexpr (!kF32)
     if (!fold) SIO<RF, NCH, RBW, CM>::decode(s, raw);
@@ -972,16 +979,23 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
     }
   }
   // 6. Stage the drafts' keys and scalars (unless the producer put them in the
-  //    ring).  The workgroup barrier above already ordered every wave's reads
-  //    of the folded slots before these writes.
-  for (int i = 0; i < (zc ? 0 : T); ++i) {
-    const int sl = wrap(sb0, c + i, Ls);
-    for (int e = threadIdx.x; e < DK; e += 64 * nwaves) rp.rk[(size_t)sl * rp.ks + e] = dk_(i)[e];
-  }
-  if (!zc && threadIdx.x < T) {
-    const int sl = wrap(sb0, c + threadIdx.x, Ls);
-    rp.ral[sl] = dsc(a.alpha, threadIdx.x);
-    rp.rbe[sl] = dsc(a.beta, threadIdx.x);
+  //    ring) from what the workgroup already holds, so that no store waits for
+  //    a load: the keys from the passes' LDS operand (one 16-byte piece per
+  //    thread), alpha and beta from the lanes of wave 0 that hold record r16.
+  //    The workgroup barrier above already ordered every wave's reads of the
+  //    folded slots before these writes.
+  if (!zc) {
+    constexpr int kPieces = NCH * 4;  // 16-byte pieces of a key
+    for (int e = threadIdx.x; e < T * kPieces; e += 64 * nwaves) {
+      const int d = e / kPieces, rem = e - d * kPieces, cc = rem >> 2, q2 = rem & 3;
+      const float4 kv = ldsD[((d >> 2) * 2 * NCH + cc) * 16 + 4 * (d & 3) + q2];
+      str4<R>(rp.rk + (size_t)wrap(sb0, c + d, Ls) * rp.ks + colq<NCH, CM>(cc, q2), kv);
+    }
+    if (wave == 0 && q == 0 && r16 >= c && r16 < nrec) {
+      const int sl = wrap(sb0, r16, Ls);
+      rp.ral[sl] = al;
+      rp.rbe[sl] = be;
+    }
   }
   if (h == 0 && threadIdx.x == 0) {
     a.ptr.pos_out[b] = pos;
