@@ -815,71 +815,118 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
     }
   }
   wave_lds_sync();
-  for (int p = 0; p < npass; ++p) {
-    const int d = 4 * p + m4;  // this lane's draft
-    const float4 *kd = &ldsD[(p * 2 * NCH) * 16 + 4 * m4 + q];        // k_d at chunk cc: kd[16 cc]
-    const float4 *qd = &ldsD[((p * 2 + 1) * NCH) * 16 + 4 * m4 + q];  // q_d at chunk cc: qd[16 cc]
-    // One sweep over the column chunks feeds all six accumulation chains, so
-    // each chunk of k_d, q_d is read from LDS once and dies at once.
-    floatx4 dk = {0.f, 0.f, 0.f, 0.f}, dqq = {0.f, 0.f, 0.f, 0.f}, w[RBW], sq[RBW];
+  if constexpr (NP == 2) {
+    // Five to eight drafts: one sweep over the column chunks on
+    // v_mfma_f32_16x16x4f32, whose 16 output columns n = lane % 16 are k_n
+    // (n < 8) and q_{n - 8} (n >= 8).  The K index of an MFMA is the lane
+    // quarter q, which holds column colq(cc, q) + e of its row in the tile (and
+    // of its record in ldsK), so the products need no sum over the quarters:
+    // lane (r, q) gets rows 4 q + 0..3 of column n, ready for LDS.
+    const int dn = r16 & 7, wn = r16 >> 3;  // draft and vector (0: k, 1: q) of column n
+    const float4 *bop = &ldsD[(((dn >> 2) * 2 + wn) * NCH) * 16 + 4 * (dn & 3) + q];  // chunk cc: bop[16 cc]
+    floatx4 dd = {0.f, 0.f, 0.f, 0.f}, ws[RBW];
 #pragma unroll
-    for (int k = 0; k < RBW; ++k) w[k] = sq[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < RBW; ++k) ws[k] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
-      const float4 kj = ldsK[cc][lane], kv = kd[16 * cc], qv = qd[16 * cc];
-      dk = mfma_4x4x1(kj.x, kv.x, dk);
-      dqq = mfma_4x4x1(kj.x, qv.x, dqq);
-      dk = mfma_4x4x1(kj.y, kv.y, dk);
-      dqq = mfma_4x4x1(kj.y, qv.y, dqq);
-      dk = mfma_4x4x1(kj.z, kv.z, dk);
-      dqq = mfma_4x4x1(kj.z, qv.z, dqq);
-      dk = mfma_4x4x1(kj.w, kv.w, dk);
-      dqq = mfma_4x4x1(kj.w, qv.w, dqq);
+      const float4 kj = ldsK[cc][lane], bv = bop[16 * cc];
+      dd = mfma_16x16x4(kj.x, bv.x, dd);
+      dd = mfma_16x16x4(kj.y, bv.y, dd);
+      dd = mfma_16x16x4(kj.z, bv.z, dd);
+      dd = mfma_16x16x4(kj.w, bv.w, dd);
 #pragma unroll
       for (int k = 0; k < RBW; ++k) {
-        w[k] = mfma_4x4x1(s[k][cc].x, kv.x, w[k]);
-        sq[k] = mfma_4x4x1(s[k][cc].x, qv.x, sq[k]);
-        w[k] = mfma_4x4x1(s[k][cc].y, kv.y, w[k]);
-        sq[k] = mfma_4x4x1(s[k][cc].y, qv.y, sq[k]);
-        w[k] = mfma_4x4x1(s[k][cc].z, kv.z, w[k]);
-        sq[k] = mfma_4x4x1(s[k][cc].z, qv.z, sq[k]);
-        w[k] = mfma_4x4x1(s[k][cc].w, kv.w, w[k]);
-        sq[k] = mfma_4x4x1(s[k][cc].w, qv.w, sq[k]);
+        ws[k] = mfma_16x16x4(s[k][cc].x, bv.x, ws[k]);
+        ws[k] = mfma_16x16x4(s[k][cc].y, bv.y, ws[k]);
+        ws[k] = mfma_16x16x4(s[k][cc].z, bv.z, ws[k]);
+        ws[k] = mfma_16x16x4(s[k][cc].w, bv.w, ws[k]);
       }
-      __builtin_amdgcn_sched_barrier(0);  // keep each chunk's LDS reads with its MFMAs (register pressure)
     }
     {
-      float kk[4], kq[4];
+      const int t = c + dn;
+      const float gt = sv.g[t < kMaxL ? t : kMaxL - 1], bt = sv.beta[t < kMaxL ? t : kMaxL - 1];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        kk[v] = sum_quarters(dk[v]);
-        kq[v] = sum_quarters(dqq[v]);
-      }
-      if (q == 0) {
-        const int t = c + d;
-        const float gt = sv.g[t < kMaxL ? t : kMaxL - 1], bt = sv.beta[t < kMaxL ? t : kMaxL - 1];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int j = 4 * gq + v;  // record
-          const float e = __expf(gt - sv.g[j]);
-          sv.A[d][j] = (d < T && j < t) ? bt * e * kk[v] : 0.f;
-          sv.Bq[d][j] = (d < T && j <= t) ? e * kq[v] : 0.f;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * q + i;  // record
+        const float e = __expf(gt - sv.g[j]);
+        if (wn == 0) sv.A[dn][j] = (dn < T && j < t) ? bt * e * dd[i] : 0.f;
+        else sv.Bq[dn][j] = (dn < T && j <= t) ? e * dd[i] : 0.f;
       }
     }
 #pragma unroll
-    for (int k = 0; k < RBW; ++k) {
-      float wv[4], sqv[4];
+    for (int k = 0; k < RBW; ++k)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        wv[v] = sum_quarters(w[k][v]);
-        sqv[v] = sum_quarters(sq[k][v]);
+      for (int i = 0; i < 4; ++i) {
+        if (wn == 0) sv.W[16 * k + 4 * q + i][dn] = ws[k][i];
+        else sv.SQ[16 * k + 4 * q + i][dn] = ws[k][i];
       }
-      if (q == 0) {
+  } else {
+    for (int p = 0; p < npass; ++p) {
+      const int d = 4 * p + m4;  // this lane's draft
+      const float4 *kd = &ldsD[(p * 2 * NCH) * 16 + 4 * m4 + q];        // k_d at chunk cc: kd[16 cc]
+      const float4 *qd = &ldsD[((p * 2 + 1) * NCH) * 16 + 4 * m4 + q];  // q_d at chunk cc: qd[16 cc]
+      // One sweep over the column chunks feeds all six accumulation chains, so
+      // each chunk of k_d, q_d is read from LDS once and dies at once.
+      floatx4 dk = {0.f, 0.f, 0.f, 0.f}, dqq = {0.f, 0.f, 0.f, 0.f}, w[RBW], sq[RBW];
+#pragma unroll
+      for (int k = 0; k < RBW; ++k) w[k] = sq[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) {
+        const float4 kj = ldsK[cc][lane], kv = kd[16 * cc], qv = qd[16 * cc];
+        dk = mfma_4x4x1(kj.x, kv.x, dk);
+        dqq = mfma_4x4x1(kj.x, qv.x, dqq);
+        dk = mfma_4x4x1(kj.y, kv.y, dk);
+        dqq = mfma_4x4x1(kj.y, qv.y, dqq);
+        dk = mfma_4x4x1(kj.z, kv.z, dk);
+        dqq = mfma_4x4x1(kj.z, qv.z, dqq);
+        dk = mfma_4x4x1(kj.w, kv.w, dk);
+        dqq = mfma_4x4x1(kj.w, qv.w, dqq);
+#pragma unroll
+        for (int k = 0; k < RBW; ++k) {
+          w[k] = mfma_4x4x1(s[k][cc].x, kv.x, w[k]);
+          sq[k] = mfma_4x4x1(s[k][cc].x, qv.x, sq[k]);
+          w[k] = mfma_4x4x1(s[k][cc].y, kv.y, w[k]);
+          sq[k] = mfma_4x4x1(s[k][cc].y, qv.y, sq[k]);
+          w[k] = mfma_4x4x1(s[k][cc].z, kv.z, w[k]);
+          sq[k] = mfma_4x4x1(s[k][cc].z, qv.z, sq[k]);
+          w[k] = mfma_4x4x1(s[k][cc].w, kv.w, w[k]);
+          sq[k] = mfma_4x4x1(s[k][cc].w, qv.w, sq[k]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep each chunk's LDS reads with its MFMAs (register pressure)
+      }
+      {
+        float kk[4], kq[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          sv.W[16 * k + 4 * gq + v][d] = wv[v];
-          sv.SQ[16 * k + 4 * gq + v][d] = sqv[v];
+          kk[v] = sum_quarters(dk[v]);
+          kq[v] = sum_quarters(dqq[v]);
+        }
+        if (q == 0) {
+          const int t = c + d;
+          const float gt = sv.g[t < kMaxL ? t : kMaxL - 1], bt = sv.beta[t < kMaxL ? t : kMaxL - 1];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int j = 4 * gq + v;  // record
+            const float e = __expf(gt - sv.g[j]);
+            sv.A[d][j] = (d < T && j < t) ? bt * e * kk[v] : 0.f;
+            sv.Bq[d][j] = (d < T && j <= t) ? e * kq[v] : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < RBW; ++k) {
+        float wv[4], sqv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          wv[v] = sum_quarters(w[k][v]);
+          sqv[v] = sum_quarters(sq[k][v]);
+        }
+        if (q == 0) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            sv.W[16 * k + 4 * gq + v][d] = wv[v];
+            sv.SQ[16 * k + 4 * gq + v][d] = sqv[v];
+          }
         }
       }
     }
