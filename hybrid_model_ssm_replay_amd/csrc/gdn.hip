@@ -792,10 +792,9 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
     }
     if constexpr (CF != RF) gdn_fold<CF, RF, NCH, RBW, R, SKIP>(s, count, s0, rp, Ls, rb0, lane, &lds_all[wave].fold);
     else gdn_fold<CF, RF, NCH, RBW, R, SKIP>(s, count, s0, rp, Ls, rb0, lane, nullptr);
-    // Float32 copies: s already is what the copy holds.  Otherwise the drafts'
-    // outputs come from the fold result s, and the copies are stored after
-    // the passes (below).
-    if constexpr (!kLossy) store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
+    // Float32 copies: s already is what the copy holds, stored after the
+    // wait below.  Otherwise the drafts' outputs come from the fold result s,
+    // and the copies are stored after the passes (4b).
   }
   if constexpr (CF != RF) {
     __syncthreads();  // every wave's fold is done with the LDS the window now takes
@@ -805,6 +804,11 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
     if (!fold) SIO<RF, NCH, RBW, CM>::decode(s, raw);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's global-to-LDS loads have landed
   __syncthreads();                // and every other wave's; all ring reads are done
+  // A float32 fold-first's checkpoint stores go out only now: loads and stores
+  // share one counter, so stores issued before the wait above would hold it
+  // until they completed.  They drain during the passes.
+  if constexpr (!kLossy)
+    if (fold) store_both<CF, RF, NCH, RBW>(s, sb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
 
   // 4. Record scalars (record j in lane j), then the passes.
   {
@@ -892,7 +896,7 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
           w[k] = mfma_4x4x1(s[k][cc].w, kv.w, w[k]);
           sq[k] = mfma_4x4x1(s[k][cc].w, qv.w, sq[k]);
         }
-        __builtin_amdgcn_sched_barrier(0);  // keep each chunk's LDS reads with its MFMAs (register pressure)
+        if constexpr (NP != 1) __builtin_amdgcn_sched_barrier(0);  // keep each chunk's LDS reads with its MFMAs (register pressure)
       }
       {
         float kk[4], kq[4];

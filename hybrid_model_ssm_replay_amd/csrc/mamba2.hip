@@ -669,9 +669,7 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a, StateBuf
         SIO<CF, NCH, RBW, CM>::decode(s, rc);
       }
     }
-    fold_apply<NCH, RBW, SKIP>(s, fi, Ah, lane);
-    if constexpr (kF32) store_rows<NCH, RBW>(s, S, rb0, lane);
-    else store_copies<CF, RF, NCH, RBW>(s, stb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
+    fold_apply<NCH, RBW, SKIP>(s, fi, Ah, lane);  // stored after the wait in 3
     base = pos;
   } else if constexpr (!kF32) {
     SIO<RF, NCH, RBW, CM>::decode(s, raw);
@@ -710,6 +708,14 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a, StateBuf
   for (int i = 0; i < T; ++i) dma_vec<16 * RBW, R>(draft_x(i) + rb0 * 16, ldsX[wave][i], lane);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's global-to-LDS loads have landed
   __syncthreads();                // and every other wave's
+  // A fold-first's checkpoint stores go out only now: loads and stores share
+  // one counter, so stores issued before the wait above would hold it until
+  // they completed (and the window loads behind them).  They drain during
+  // the passes.
+  if (fold) {
+    if constexpr (kF32) store_rows<NCH, RBW>(s, S, rb0, lane);
+    else store_copies<CF, RF, NCH, RBW>(s, stb, head, rb0, lane, (uint32_t)h, (uint32_t)b, (uint32_t)pos);
+  }
 
   // 4. Passes of four drafts.
   const int nsteps = (nrec + 3) >> 2;
