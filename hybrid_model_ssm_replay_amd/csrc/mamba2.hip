@@ -107,6 +107,18 @@ __device__ __forceinline__ float suffix_sum16(float v, int lane, float *total) {
   return lane < 15 ? nxt : 0.f;
 }
 
+// Inclusive suffix sum within each row of 16 lanes: lane (row, i) gets
+// sum_{j >= i} v_(row, j).
+__device__ __forceinline__ float row_suffix_sum16(float v, int lane) {
+  float t = v;
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    const float u = __shfl_down(t, off, kWave);
+    if ((lane & 15) + off < 16) t += u;
+  }
+  return t;
+}
+
 // Fold the cnt (1..L) committed records at positions base .. base+cnt-1 into
 // the register tile: s <- exp(A s_{1..cnt}) s + sum_r exp(A s_{r+1..cnt}) dt_r x_r B_r^T.
 // Ends with a barrier; sm.Bs is free again afterwards.
@@ -748,17 +760,25 @@ __global__ __launch_bounds__(256) void m2_replay_verify(M2VerifyArgs a, StateBuf
       }
       wave_lds_sync();
     }
-    // Record-sum operand: coef[n][r], r = 4 st + q, with each segment sum
-    // accumulated directly from the newest record down; and the S0 weight.
+    // Record-sum operand: coef[n][r], r = 4 st + q, and the S0 weight, from
+    // segment sums of dt over records r+1 .. last (summed as they are, not as
+    // differences of prefix sums).  Row q of the wave scans draft 4 p + q
+    // (every row holds dt of record j in lane j); lane (q, r16) reads the sums
+    // of its own draft m4 from row m4.
     const int last = n < T ? c + n : -1;
-    float seg[4] = {0.f, 0.f, 0.f, 0.f};
-    float tot = 0.f;
+    float seg[4];
+    float tot;
+    {
+      const int nq = 4 * p + q;
+      const int lastq = nq < T ? c + nq : -1;
+      const float sfx = row_suffix_sum16(r16 <= lastq ? dtl : 0.f, lane);  // records r16 .. lastq
+      tot = __shfl(sfx, 16 * m4, kWave);
 #pragma unroll
-    for (int j = kMaxL - 1; j >= 0; --j) {
-      if (j <= last) tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dtl), j));
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        if (j == 4 * st + q + 1) seg[st] = tot;
+      for (int st = 0; st < 4; ++st) {
+        const int r1 = 4 * st + q + 1;  // first record after r
+        const float v = __shfl(sfx, 16 * m4 + (r1 < 16 ? r1 : 0), kWave);
+        seg[st] = r1 < 16 ? v : 0.f;
+      }
     }
     const float sc = s0_weight<SKIP>(Ah * tot);
     float cb[4];
