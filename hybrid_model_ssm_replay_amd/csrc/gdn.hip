@@ -317,14 +317,14 @@ __device__ __forceinline__ void load_cols(float (&v)[NCH], const R *p) {
 }
 
 // Float32 copies: held to 128 VGPRs (four waves per SIMD), which fits without
-// spills; with the decay skip 256 (two): its checkpoint loads sit behind the
-// decision's branch, and at three waves per SIMD the tile spills.
+// spills; with the decay skip to 168 (three), where the decision's registers
+// fit without spills.
 // SKIP (decay skip, float32 copies): a head whose window log-decay (over the
 // records the step's output or fold uses) is below ln 2^-24 does not read its
 // checkpoint; its fold is a pure write of the folded records.
 template <int CF, int RF, int NCH, int RBW, typename R, bool SKIP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
-    CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32 ? (SKIP ? 2 : 4) : 1))) void gdn_replay_step(GdnStepArgs a, StateBufs sb) {
+    CF == REPLAY_FMT_F32 && RF == REPLAY_FMT_F32 ? (SKIP ? 3 : 4) : 1))) void gdn_replay_step(GdnStepArgs a, StateBufs sb) {
   constexpr int DK = 16 * NCH;
   constexpr int CM = col_map(CF, RF);
   constexpr bool kLossy = RF != REPLAY_FMT_F32;  // the read copy is not the float32 fold result
@@ -391,16 +391,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     const int j = r16 < n ? r16 : 0;
     const float aj = __shfl(al_row, wrap(s0, j < count ? j : 0, Ls), kWave);
     const float ak = (!fold && r16 == count) ? al_in : aj;
-    // Every 16-lane row computes the same sum: take lane 0's, so the branch is uniform.
+    // Every 16-lane row computes the same sum: take lane 0's, so every lane
+    // takes the same decision.  A dropped head's loads see an empty range and
+    // return zeros without reading memory.
     const float tot = sum16(r16 < n ? __logf(ak) : 0.f);
-    if (__builtin_amdgcn_readfirstlane(tot < kDecaySkipLog ? 1 : 0)) {
-#pragma unroll
-      for (int k = 0; k < RBW; ++k)
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) s[k][c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    } else {
-      load_rows_g<NCH, RBW, CM>(s, static_cast<const float *>(sb.rd.data) + head, rb0, lane);
-    }
+    const bool drop = __builtin_amdgcn_readfirstlane(tot < kDecaySkipLog ? 1 : 0);
+    load_rows_masked<NCH, RBW, CM>(s, static_cast<const float *>(sb.rd.data) + head,
+                                   drop ? 0u : (uint32_t)(DV * DK * sizeof(float)), rb0, lane);
   }
   int base = ck, sb0 = s0;
   float kj[NCH];         // this thread's slice of key grp (an older record)

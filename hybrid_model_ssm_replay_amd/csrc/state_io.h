@@ -55,6 +55,27 @@ __device__ __forceinline__ void load_rows_g(float4 (&s)[RBW][NCH], const float *
   }
 }
 
+// load_rows_g through a buffer resource that covers nbytes of the head from
+// S: loads past nbytes return zeros without a memory access, so a head that
+// reads nothing (nbytes = 0) runs the same code, with the same registers, as
+// one that reads its rows (no branch around the loads).
+template <int NCH, int RBW, int CM>
+__device__ __forceinline__ void load_rows_masked(float4 (&s)[RBW][NCH], const float *S, uint32_t nbytes, int rb0,
+                                                 int lane) {
+  constexpr int DK = 16 * NCH;
+  const int q = lane >> 4, r16 = lane & 15;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(S), (short)0, (int)nbytes,
+                                                                      0x00020000);
+#pragma unroll
+  for (int k = 0; k < RBW; ++k) {
+    const int row = (rb0 + k) * 16 + r16;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      s[k][c] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rs, (row * DK + colq<NCH, CM>(c, q)) * 4, 0, 0));
+  }
+}
+
 template <int NCH, int RBW, int CM>
 __device__ __forceinline__ void store_rows_g(const float4 (&s)[RBW][NCH], float *S, int rb0, int lane) {
   constexpr int DK = 16 * NCH;
