@@ -642,8 +642,8 @@ template <int RBW, bool DUAL, int ND = kMaxL>
 struct GdnVerifyLds {
   float W[16 * RBW][ND + 1];   // [row][draft]: S0 k_d
   float SQ[16 * RBW][ND + 1];  // [row][draft]: S0 q_d
-  float A[ND][17];             // [draft][record]: beta_t e^{g_t - g_j} (k_j . k_t) for j < t, else 0
-  float Bq[ND][17];            // [draft][record]: e^{g_t - g_j} (k_j . q_d) for j <= t, else 0
+  alignas(16) float A[ND][16];  // [draft][record]: beta_t e^{g_t - g_j} (k_j . k_t) for j < t, else 0
+  alignas(16) float Bq[ND][16]; // [draft][record]: e^{g_t - g_j} (k_j . q_d) for j <= t, else 0
   float g[16], beta[16];       // record j: decay prefix, beta
   // [record][row of the wave]: the committed records' pseudo-values, then the
   // drafts' values (c + T <= 16), staged by direct global-to-LDS loads issued
