@@ -816,51 +816,55 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
     }
   }
   wave_lds_sync();
-  if constexpr (NP == 2) {
-    // Five to eight drafts: one sweep over the column chunks on
-    // v_mfma_f32_16x16x4f32, whose 16 output columns n = lane % 16 are k_n
-    // (n < 8) and q_{n - 8} (n >= 8).  The K index of an MFMA is the lane
-    // quarter q, which holds column colq(cc, q) + e of its row in the tile (and
-    // of its record in ldsK), so the products need no sum over the quarters:
-    // lane (r, q) gets rows 4 q + 0..3 of column n, ready for LDS.
-    const int dn = r16 & 7, wn = r16 >> 3;  // draft and vector (0: k, 1: q) of column n
-    const float4 *bop = &ldsD[(((dn >> 2) * 2 + wn) * NCH) * 16 + 4 * (dn & 3) + q];  // chunk cc: bop[16 cc]
-    floatx4 dd = {0.f, 0.f, 0.f, 0.f}, ws[RBW];
+  if constexpr (NP >= 2) {
+    // More than four drafts: sweeps over the column chunks on
+    // v_mfma_f32_16x16x4f32, eight drafts per sweep, whose 16 output columns
+    // n = lane % 16 are k and q of the sweep's drafts (n < 8: k, n >= 8: q).
+    // The K index of an MFMA is the lane quarter q, which holds column
+    // colq(cc, q) + e of its row in the tile (and of its record in ldsK), so
+    // the products need no sum over the quarters: lane (r, q) gets rows
+    // 4 q + 0..3 of column n, ready for LDS.
 #pragma unroll
-    for (int k = 0; k < RBW; ++k) ws[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int sw = 0; sw < NP / 2; ++sw) {
+      const int dn = 8 * sw + (r16 & 7), wn = r16 >> 3;  // draft and vector (0: k, 1: q) of column n
+      const float4 *bop = &ldsD[(((dn >> 2) * 2 + wn) * NCH) * 16 + 4 * (dn & 3) + q];  // chunk cc: bop[16 cc]
+      floatx4 dd = {0.f, 0.f, 0.f, 0.f}, ws[RBW];
 #pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-      const float4 kj = ldsK[cc][lane], bv = bop[16 * cc];
-      dd = mfma_16x16x4(kj.x, bv.x, dd);
-      dd = mfma_16x16x4(kj.y, bv.y, dd);
-      dd = mfma_16x16x4(kj.z, bv.z, dd);
-      dd = mfma_16x16x4(kj.w, bv.w, dd);
+      for (int k = 0; k < RBW; ++k) ws[k] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < RBW; ++k) {
-        ws[k] = mfma_16x16x4(s[k][cc].x, bv.x, ws[k]);
-        ws[k] = mfma_16x16x4(s[k][cc].y, bv.y, ws[k]);
-        ws[k] = mfma_16x16x4(s[k][cc].z, bv.z, ws[k]);
-        ws[k] = mfma_16x16x4(s[k][cc].w, bv.w, ws[k]);
+      for (int cc = 0; cc < NCH; ++cc) {
+        const float4 kj = ldsK[cc][lane], bv = bop[16 * cc];
+        dd = mfma_16x16x4(kj.x, bv.x, dd);
+        dd = mfma_16x16x4(kj.y, bv.y, dd);
+        dd = mfma_16x16x4(kj.z, bv.z, dd);
+        dd = mfma_16x16x4(kj.w, bv.w, dd);
+#pragma unroll
+        for (int k = 0; k < RBW; ++k) {
+          ws[k] = mfma_16x16x4(s[k][cc].x, bv.x, ws[k]);
+          ws[k] = mfma_16x16x4(s[k][cc].y, bv.y, ws[k]);
+          ws[k] = mfma_16x16x4(s[k][cc].z, bv.z, ws[k]);
+          ws[k] = mfma_16x16x4(s[k][cc].w, bv.w, ws[k]);
+        }
       }
+      {
+        const int t = c + dn;
+        const float gt = sv.g[t < kMaxL ? t : kMaxL - 1], bt = sv.beta[t < kMaxL ? t : kMaxL - 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 4 * q + i;  // record
+          const float e = __expf(gt - sv.g[j]);
+          if (wn == 0) sv.A[dn][j] = (dn < T && j < t) ? bt * e * dd[i] : 0.f;
+          else sv.Bq[dn][j] = (dn < T && j <= t) ? e * dd[i] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < RBW; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (wn == 0) sv.W[16 * k + 4 * q + i][dn] = ws[k][i];
+          else sv.SQ[16 * k + 4 * q + i][dn] = ws[k][i];
+        }
     }
-    {
-      const int t = c + dn;
-      const float gt = sv.g[t < kMaxL ? t : kMaxL - 1], bt = sv.beta[t < kMaxL ? t : kMaxL - 1];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 4 * q + i;  // record
-        const float e = __expf(gt - sv.g[j]);
-        if (wn == 0) sv.A[dn][j] = (dn < T && j < t) ? bt * e * dd[i] : 0.f;
-        else sv.Bq[dn][j] = (dn < T && j <= t) ? e * dd[i] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < RBW; ++k)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (wn == 0) sv.W[16 * k + 4 * q + i][dn] = ws[k][i];
-        else sv.SQ[16 * k + 4 * q + i][dn] = ws[k][i];
-      }
   } else {
     for (int p = 0; p < npass; ++p) {
       const int d = 4 * p + m4;  // this lane's draft
