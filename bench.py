@@ -627,7 +627,7 @@ def main(argv=None):
                 "half_heads_fast_decay": {"exact_us": us_gf, "skip_us": us_gfs, "speedup": us_gf / us_gfs},
                 "rule": "checkpoint term dropped where exp(g) < 2^-24 (an approximation)"}
 
-        for T in (4, 8) if want("gdn_verify") else ():
+        for T in (4, 8, 16) if want("gdn_verify") else ():
             log("gdn verify T", T)
             us_rv, us_sv = bench_verify(torch, gshape, T, 2)
             extra["gdn_b256"][f"verify_T{T}"] = {"replay_verify_commit_us": us_rv, "snapshot_verify_commit_us": us_sv,
