@@ -40,9 +40,14 @@ def log(*a):
 
 
 def kernel_source_hash(family: str) -> str:
+    """Hash of a kernel family's sources with comments and blank space removed,
+    so that a counter summary stays matched across comment-only edits."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[family]:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        src = open(os.path.join(ROOT, f), encoding="utf-8").read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

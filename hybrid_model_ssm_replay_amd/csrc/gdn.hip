@@ -624,13 +624,14 @@ __device__ __forceinline__ floatx4 mfma_4x4x1(float a, float b, floatx4 c) {
 // (c + T <= L after a fold-first).  Draft d is window record t = c + d:
 //   u_t = beta_t v_t - beta_t e^{g_t} S0 k_t - sum_{j<t} beta_t e^{g_t - g_j} (k_j . k_t) u_j
 //   o_d = e^{g_t} S0 q_d + sum_{j<=t} e^{g_t - g_j} (k_j . q_d) u_j.
-// The products run in passes of four drafts on v_mfma_f32_4x4x1_16b_f32 (16
-// blocks of 4 x 4 x 1; lane l feeds row / column l % 4 of block l / 4 and gets
-// rows 0..3 of column l % 4): with lane l = r + 16 q of the register tile,
-// g = r / 4, m = r % 4, block (g, q) takes rows 16 rb + 4 g + 0..3 (S0 k_d,
-// S0 q_d) or records 4 g + 0..3 (k_j . k_d, k_j . q_d) over the columns of
-// quarter q, and a sum over the quarters completes them, so absent drafts
-// cost no MFMA work.  The drafts' keys and queries and the window's keys
+// Up to four drafts, the products run in one pass on
+// v_mfma_f32_4x4x1_16b_f32 (16 blocks of 4 x 4 x 1; lane l feeds row / column
+// l % 4 of block l / 4 and gets rows 0..3 of column l % 4): with lane
+// l = r + 16 q of the register tile, g = r / 4, m = r % 4, block (g, q) takes
+// rows 16 rb + 4 g + 0..3 (S0 k_d, S0 q_d) or records 4 g + 0..3 (k_j . k_d,
+// k_j . q_d) over the columns of quarter q, and a sum over the quarters
+// completes them, so absent drafts cost no MFMA work.  More drafts take one
+// v_mfma_f32_16x16x4f32 sweep per eight (section 4).  The drafts' keys and queries and the window's keys
 // reach LDS by direct global-to-LDS loads in the lane-linear operand layout
 // (bf16 records: a load, exact widening and LDS store in the same layout).
 // The draft rows of the triangular system are then solved per state row (one
