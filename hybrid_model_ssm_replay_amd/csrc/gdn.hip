@@ -643,8 +643,6 @@ template <int RBW, bool DUAL, int ND = kMaxL>
 struct GdnVerifyLds {
   float W[16 * RBW][ND + 1];   // [row][draft]: S0 k_d
   float SQ[16 * RBW][ND + 1];  // [row][draft]: S0 q_d
-  alignas(16) float A[ND][16];  // [draft][record]: beta_t e^{g_t - g_j} (k_j . k_t) for j < t, else 0
-  alignas(16) float Bq[ND][16]; // [draft][record]: e^{g_t - g_j} (k_j . q_d) for j <= t, else 0
   float g[16], beta[16];       // record j: decay prefix, beta
   // [record][row of the wave]: the committed records' pseudo-values, then the
   // drafts' values (c + T <= 16), staged by direct global-to-LDS loads issued
@@ -682,6 +680,10 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
   __shared__ float4 ldsK[NCH][64];                 // [chunk cc][record j + 16 q]: k_j at colq(cc, q)
   __shared__ float4 ldsD[kPass * 2 * NCH * 16];    // [((p 2 + w) NCH + cc) 16 + 4 m + q]: w = 0: k, 1: q of draft 4 p + m
   __shared__ GdnWaveLds<RBW, kLossy, 4 * NP, (CF != RF)> lds_all[4];
+  // The draft-record coefficients, the same for every wave: written by wave 0.
+  //   cA[d][j] = beta_t e^{g_t - g_j} (k_j . k_t) for j < t, else 0;
+  //   cB[d][j] = e^{g_t - g_j} (k_j . q_d) for j <= t, else 0  (t = c + d).
+  __shared__ __align__(16) float cA[4 * NP][16], cB[4 * NP][16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r16 = lane & 15, gq = r16 >> 2, m4 = r16 & 3;
   GdnVerifyLds<RBW, kLossy, 4 * NP> &sv = lds_all[wave].verify;
@@ -854,8 +856,10 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
         for (int i = 0; i < 4; ++i) {
           const int j = 4 * q + i;  // record
           const float e = __expf(gt - sv.g[j]);
-          if (wn == 0) sv.A[dn][j] = (dn < T && j < t) ? bt * e * dd[i] : 0.f;
-          else sv.Bq[dn][j] = (dn < T && j <= t) ? e * dd[i] : 0.f;
+          if (wave == 0) {
+            if (wn == 0) cA[dn][j] = (dn < T && j < t) ? bt * e * dd[i] : 0.f;
+            else cB[dn][j] = (dn < T && j <= t) ? e * dd[i] : 0.f;
+          }
         }
       }
 #pragma unroll
@@ -907,15 +911,15 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
           kk[v] = sum_quarters(dk[v]);
           kq[v] = sum_quarters(dqq[v]);
         }
-        if (q == 0) {
+        if (q == 0 && wave == 0) {
           const int t = c + d;
           const float gt = sv.g[t < kMaxL ? t : kMaxL - 1], bt = sv.beta[t < kMaxL ? t : kMaxL - 1];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int j = 4 * gq + v;  // record
             const float e = __expf(gt - sv.g[j]);
-            sv.A[d][j] = (d < T && j < t) ? bt * e * kk[v] : 0.f;
-            sv.Bq[d][j] = (d < T && j <= t) ? e * kq[v] : 0.f;
+            cA[d][j] = (d < T && j < t) ? bt * e * kk[v] : 0.f;
+            cB[d][j] = (d < T && j <= t) ? e * kq[v] : 0.f;
           }
         }
       }
@@ -937,7 +941,7 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
       }
     }
   }
-  wave_lds_sync();
+  __syncthreads();  // wave 0's coefficients and each wave's own tables are in LDS
 
   // 4b. After a fold-first of a low-precision read copy: store both copies,
   //     then Q k_d from the read copy Q they now hold, for the pseudo-values
@@ -1005,11 +1009,11 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
         const float et = (SKIP && sv.g[t] < kDecaySkipLog) ? 0.f : __expf(sv.g[t]);  // checkpoint-term weight
         float v = bt * vval(t) - bt * et * sv.W[lane][d];
 #pragma unroll
-        for (int j = 0; j < t; ++j) v -= sv.A[d][j] * u[j];
+        for (int j = 0; j < t; ++j) v -= cA[d][j] * u[j];
         u[t] = v;
         float o = et * sv.SQ[lane][d];
 #pragma unroll
-        for (int j = 0; j <= t; ++j) o += sv.Bq[d][j] * u[j];
+        for (int j = 0; j <= t; ++j) o += cB[d][j] * u[j];
         a.y[(((size_t)b * T + d) * H + h) * DV + row] = o;
         if (!dual) rp.ru[(size_t)wrap(sb0, t, Ls) * rp.vs + row] = v;  // stage the pseudo-value
         if constexpr (RF != CF) str<R>(rp.rv + (size_t)wrap(sb0, t, Ls) * rp.vs + row, vval(t));
@@ -1023,7 +1027,7 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
             const float bt = sv.beta[t], et = __expf(sv.g[t]);
             float v = bt * vval(t) - bt * et * sv.WQ[lane][t];
 #pragma unroll
-            for (int j = 0; j < t; ++j) v -= sv.A[t][j] * u[j];
+            for (int j = 0; j < t; ++j) v -= cA[t][j] * u[j];
             u[t] = v;
             rp.ru[(size_t)wrap(sb0, t, Ls) * rp.vs + row] = v;
           }
