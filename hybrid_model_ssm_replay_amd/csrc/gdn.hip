@@ -836,11 +836,14 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
       for (int k = 0; k < RBW; ++k) ws[k] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cc = 0; cc < NCH; ++cc) {
-        const float4 kj = ldsK[cc][lane], bv = bop[16 * cc];
-        dd = mfma_16x16x4(kj.x, bv.x, dd);
-        dd = mfma_16x16x4(kj.y, bv.y, dd);
-        dd = mfma_16x16x4(kj.z, bv.z, dd);
-        dd = mfma_16x16x4(kj.w, bv.w, dd);
+        const float4 bv = bop[16 * cc];
+        if (wave == 0) {  // only wave 0's key dots are kept
+          const float4 kj = ldsK[cc][lane];
+          dd = mfma_16x16x4(kj.x, bv.x, dd);
+          dd = mfma_16x16x4(kj.y, bv.y, dd);
+          dd = mfma_16x16x4(kj.z, bv.z, dd);
+          dd = mfma_16x16x4(kj.w, bv.w, dd);
+        }
 #pragma unroll
         for (int k = 0; k < RBW; ++k) {
           ws[k] = mfma_16x16x4(s[k][cc].x, bv.x, ws[k]);
@@ -882,15 +885,18 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
       for (int k = 0; k < RBW; ++k) w[k] = sq[k] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cc = 0; cc < NCH; ++cc) {
-        const float4 kj = ldsK[cc][lane], kv = kd[16 * cc], qv = qd[16 * cc];
-        dk = mfma_4x4x1(kj.x, kv.x, dk);
-        dqq = mfma_4x4x1(kj.x, qv.x, dqq);
-        dk = mfma_4x4x1(kj.y, kv.y, dk);
-        dqq = mfma_4x4x1(kj.y, qv.y, dqq);
-        dk = mfma_4x4x1(kj.z, kv.z, dk);
-        dqq = mfma_4x4x1(kj.z, qv.z, dqq);
-        dk = mfma_4x4x1(kj.w, kv.w, dk);
-        dqq = mfma_4x4x1(kj.w, qv.w, dqq);
+        const float4 kv = kd[16 * cc], qv = qd[16 * cc];
+        if (wave == 0) {  // only wave 0's key dots are kept
+          const float4 kj = ldsK[cc][lane];
+          dk = mfma_4x4x1(kj.x, kv.x, dk);
+          dqq = mfma_4x4x1(kj.x, qv.x, dqq);
+          dk = mfma_4x4x1(kj.y, kv.y, dk);
+          dqq = mfma_4x4x1(kj.y, qv.y, dqq);
+          dk = mfma_4x4x1(kj.z, kv.z, dk);
+          dqq = mfma_4x4x1(kj.z, qv.z, dqq);
+          dk = mfma_4x4x1(kj.w, kv.w, dk);
+          dqq = mfma_4x4x1(kj.w, qv.w, dqq);
+        }
 #pragma unroll
         for (int k = 0; k < RBW; ++k) {
           w[k] = mfma_4x4x1(s[k][cc].x, kv.x, w[k]);
@@ -904,14 +910,14 @@ void gdn_replay_verify(GdnVerifyArgs a, StateBufs sb) {
         }
         if constexpr (NP != 1) __builtin_amdgcn_sched_barrier(0);  // keep each chunk's LDS reads with its MFMAs (register pressure)
       }
-      {
+      if (wave == 0) {
         float kk[4], kq[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           kk[v] = sum_quarters(dk[v]);
           kq[v] = sum_quarters(dqq[v]);
         }
-        if (q == 0 && wave == 0) {
+        if (q == 0) {
           const int t = c + d;
           const float gt = sv.g[t < kMaxL ? t : kMaxL - 1], bt = sv.beta[t < kMaxL ? t : kMaxL - 1];
 #pragma unroll
